@@ -1,0 +1,188 @@
+"""ctypes binding of libdflash (include/dflash.h): argument marshalling only.
+
+Each function has the C entry point's name and arguments; torch tensors supply
+device pointers and the current HIP stream.  Every computation runs in the HIP
+library; there is no fallback, and loading fails loudly if the library is absent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+from .configs import BF16, Dims
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdflash.so")
+
+DFLASH_OK, DFLASH_E_INVALID, DFLASH_E_UNSUPPORTED, DFLASH_E_WORKSPACE, DFLASH_E_HIP = 0, -1, -2, -3, -4
+DEVERR_TOKEN, DEVERR_ROWS, DEVERR_CTXLEN = 1, 2, 4
+
+_INT_FIELDS = ("batch", "block_k", "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim",
+               "ffn", "vocab", "n_taps", "tap_dim", "window", "cache_slots", "dtype",
+               "max_inject_rows")
+WEIGHT_FIELDS = ("fuse_w", "fuse_norm", "embed", "mask_embed", "attn_norm", "w_qkv", "w_o",
+                 "mlp_norm", "w_gate_up", "w_down", "final_norm", "lm_head")
+
+
+class DflashDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in _INT_FIELDS] + [("rms_eps", ctypes.c_float),
+                                                            ("rope_theta", ctypes.c_float)]
+
+
+class DflashWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class DflashCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("ctx_len", ctypes.c_void_p),
+                ("anchor", ctypes.c_void_p), ("dev_error", ctypes.c_void_p)]
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+EXPORTED = ("dflash_workspace_bytes", "dflash_status_string", "dflash_fuse_inject",
+            "dflash_draft_step", "dflash_verify_commit", "dflash_draft_step_timed")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdflash.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_diffusion_speculative_dflash_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.dflash_workspace_bytes.argtypes = [ctypes.POINTER(DflashDims)]
+    L.dflash_workspace_bytes.restype = S
+    L.dflash_status_string.argtypes = [ctypes.c_int]
+    L.dflash_status_string.restype = ctypes.c_char_p
+    L.dflash_fuse_inject.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashWeights), P, P,
+                                     I, I, ctypes.POINTER(DflashCache), P, S, P]
+    L.dflash_fuse_inject.restype = ctypes.c_int
+    L.dflash_draft_step.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashWeights),
+                                    ctypes.POINTER(DflashCache), P, P, P, S, P]
+    L.dflash_draft_step.restype = ctypes.c_int
+    L.dflash_draft_step_timed.argtypes = L.dflash_draft_step.argtypes + [P, P]
+    L.dflash_draft_step_timed.restype = ctypes.c_int
+    L.dflash_verify_commit.argtypes = [ctypes.POINTER(DflashDims), P, P, ctypes.POINTER(DflashCache),
+                                       P, P, P]
+    L.dflash_verify_commit.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().dflash_status_string(int(status)).decode()
+
+
+# ----------------------------------------------------------------------------- structs
+def dims_struct(d: Dims) -> DflashDims:
+    vals = {n: getattr(d, n) for n in _INT_FIELDS if n != "dtype"}
+    vals["dtype"] = 1 if d.dtype == BF16 else 0
+    return DflashDims(**vals, rms_eps=d.rms_eps, rope_theta=d.rope_theta)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libdflash must be contiguous")
+    return t.data_ptr()
+
+
+def weights_struct(W: Dict[str, torch.Tensor]) -> DflashWeights:
+    return DflashWeights(**{n: _ptr(W[n]) for n in WEIGHT_FIELDS})
+
+
+def cache_struct(cache: Dict[str, torch.Tensor]) -> DflashCache:
+    return DflashCache(k=_ptr(cache["k"]), v=_ptr(cache["v"]), ctx_len=_ptr(cache["ctx_len"]),
+                       anchor=_ptr(cache["anchor"]), dev_error=_ptr(cache["dev_error"]))
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != DFLASH_OK:
+        raise DFlashError(fn, status)
+
+
+# ----------------------------------------------------------------------------- entry points
+def dflash_workspace_bytes(dims: Dims) -> int:
+    n = lib().dflash_workspace_bytes(ctypes.byref(dims_struct(dims)))
+    if n == 0:
+        raise DFlashError("dflash_workspace_bytes", DFLASH_E_INVALID)
+    return int(n)
+
+
+def dflash_fuse_inject(dims: Dims, weights, taps: torch.Tensor, n_rows: torch.Tensor, n_max: int,
+                       commit: bool, cache, workspace: torch.Tensor, stream=None) -> None:
+    ds, ws, cs = dims_struct(dims), weights_struct(weights), cache_struct(cache)
+    st = lib().dflash_fuse_inject(ctypes.byref(ds), ctypes.byref(ws), _ptr(taps), _ptr(n_rows),
+                                  int(n_max), int(bool(commit)), ctypes.byref(cs), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dflash_fuse_inject", st)
+
+
+def dflash_draft_step(dims: Dims, weights, cache, draft: torch.Tensor,
+                      logits_out: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
+    ds, ws, cs = dims_struct(dims), weights_struct(weights), cache_struct(cache)
+    st = lib().dflash_draft_step(ctypes.byref(ds), ctypes.byref(ws), ctypes.byref(cs), _ptr(draft),
+                                 _ptr(logits_out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dflash_draft_step", st)
+
+
+def dflash_draft_step_timed(dims: Dims, weights, cache, draft: torch.Tensor,
+                            logits_out: Optional[torch.Tensor], workspace: torch.Tensor,
+                            head_begin: int, head_end: int, stream=None) -> None:
+    ds, ws, cs = dims_struct(dims), weights_struct(weights), cache_struct(cache)
+    st = lib().dflash_draft_step_timed(ctypes.byref(ds), ctypes.byref(ws), ctypes.byref(cs),
+                                       _ptr(draft), _ptr(logits_out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream), head_begin, head_end)
+    _check("dflash_draft_step_timed", st)
+
+
+def dflash_verify_commit(dims: Dims, draft: torch.Tensor, target: torch.Tensor, cache,
+                         accept_len: torch.Tensor, out_tokens: torch.Tensor, stream=None) -> None:
+    ds, cs = dims_struct(dims), cache_struct(cache)
+    st = lib().dflash_verify_commit(ctypes.byref(ds), _ptr(draft), _ptr(target), ctypes.byref(cs),
+                                    _ptr(accept_len), _ptr(out_tokens), _stream(stream))
+    _check("dflash_verify_commit", st)
+
+
+# ----------------------------------------------------------------------------- buffers
+def alloc_cache(dims: Dims, device="cuda", ctx_len=None, anchor=None) -> Dict[str, torch.Tensor]:
+    """Caller-owned decode state: K/V rings, committed lengths, anchors, error word."""
+    dt = torch.bfloat16 if dims.dtype == BF16 else torch.float32
+    shape = (dims.n_layers, dims.batch, dims.n_kv_heads, dims.cache_slots, dims.head_dim)
+    B = dims.batch
+
+    def ints(v):
+        if v is None:
+            return torch.zeros(B, dtype=torch.int32, device=device)
+        return torch.as_tensor(v, dtype=torch.int32).reshape(B).to(device)
+
+    return {"k": torch.zeros(shape, dtype=dt, device=device),
+            "v": torch.zeros(shape, dtype=dt, device=device),
+            "ctx_len": ints(ctx_len), "anchor": ints(anchor),
+            "dev_error": torch.zeros(1, dtype=torch.int32, device=device)}
+
+
+def alloc_workspace(dims: Dims, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace of dflash_workspace_bytes(dims) bytes."""
+    return torch.zeros(dflash_workspace_bytes(dims), dtype=torch.uint8, device=device)

@@ -1,0 +1,448 @@
+// C ABI of libdflash: host-side validation, workspace layout, launch plans and
+// the kernel sequence of each call.  See include/dflash.h for the contract.
+#include <algorithm>
+#include <cstring>
+
+#include "../../include/dflash.h"
+#include "internal.h"
+
+using namespace dflash;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kPartialCap = size_t(32) << 20;   // split-K partial tiles
+constexpr int kGemmCounters = 1 << 16;
+constexpr int kTargetWorkgroups = 512;             // 2 per CU on 256 CUs
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int elem_bytes(const dflash_dims& d) { return d.dtype == DFLASH_BF16 ? 2 : 4; }
+
+bool dims_ok(const dflash_dims* d) {
+  if (d == nullptr) return false;
+  if (d->batch < 1 || d->block_k < 1 || d->block_k > 63 || d->n_layers < 1) return false;
+  if (d->hidden < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return false;
+  if (d->n_q_heads % d->n_kv_heads != 0) return false;
+  if (d->head_dim != 64 && d->head_dim != 128) return false;
+  if (d->ffn < 1 || d->vocab < 2 || d->n_taps < 1 || d->tap_dim < 1) return false;
+  if (d->window < 1 || d->cache_slots < d->window + d->block_k) return false;
+  if (d->dtype != DFLASH_F32 && d->dtype != DFLASH_BF16) return false;
+  if (d->max_inject_rows < d->block_k + 1) return false;
+  if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.f)) return false;
+  // 32-bit row indices inside the kernels
+  const double mi = double(d->batch) * d->max_inject_rows;
+  if (mi * d->hidden > 2.0e9 || double(d->batch) * d->block_k * d->vocab > 4.0e9) return false;
+  return true;
+}
+
+struct AttnPlan {
+  int n_rb, kps, max_splits;
+};
+
+AttnPlan attn_plan(const dflash_dims& d) {
+  AttnPlan p;
+  const int G = d.n_q_heads / d.n_kv_heads;
+  p.n_rb = cdiv(G * d.block_k, 64);
+  const int max_keys = d.window + d.block_k;
+  const double per_group = double(max_keys) * d.batch * d.n_kv_heads * p.n_rb / 1024.0;
+  int kps = std::max(64, int(per_group + 0.999));
+  kps = cdiv(kps, 32) * 32;
+  p.kps = std::min(kps, std::max(64, cdiv(max_keys, 32) * 32));
+  p.max_splits = cdiv(max_keys, p.kps);
+  return p;
+}
+
+struct Layout {
+  size_t h, xa, ssq, q, kb, vb, o, act, cu, ssq_c, partials, counters, keys, attn_cnt, attn_o,
+      attn_ml, total;
+  int np_d;
+  AttnPlan ap;
+};
+
+Layout layout(const dflash_dims& d) {
+  Layout L{};
+  const size_t sz = elem_bytes(d);
+  const size_t Mb = size_t(d.batch) * d.block_k;
+  const size_t Mi = size_t(d.batch) * d.max_inject_rows;
+  L.np_d = cdiv(d.hidden, kBN);
+  L.ap = attn_plan(d);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  L.h = take(Mb * d.hidden * 4);
+  L.xa = take(Mb * d.hidden * sz);
+  L.ssq = take(Mb * L.np_d * 4);
+  L.q = take(Mb * d.n_q_heads * d.head_dim * sz);
+  L.kb = take(Mb * d.n_kv_heads * d.head_dim * sz);
+  L.vb = take(Mb * d.n_kv_heads * d.head_dim * sz);
+  L.o = take(Mb * d.n_q_heads * d.head_dim * sz);
+  L.act = take(Mb * d.ffn * sz);
+  L.cu = take(Mi * d.hidden * sz);
+  L.ssq_c = take(Mi * L.np_d * 4);
+  L.partials = take(kPartialCap);
+  L.counters = take(size_t(kGemmCounters) * 4);
+  L.keys = take(Mb * 8);
+  const size_t groups = size_t(d.batch) * d.n_kv_heads * L.ap.n_rb;
+  L.attn_cnt = take(groups * 4);
+  L.attn_o = take(groups * L.ap.max_splits * 64 * d.head_dim * 4);
+  L.attn_ml = take(groups * L.ap.max_splits * 64 * 2 * 4);
+  L.total = off;
+  return L;
+}
+
+// Tile plan of one GEMM.  Split K only while the grid is below the target size,
+// every split keeps >= 256 elements, the partial tiles fit their region, and their
+// traffic stays below a quarter of the weight bytes.
+GemmPlan gemm_plan(int M, int n_tiles, int K, int lda, int ldw, bool allow_split) {
+  GemmPlan p{};
+  p.bm = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+  p.m_tiles = cdiv(M, p.bm);
+  p.n_tiles = n_tiles;
+  p.vec = (K % 8 == 0) && (lda % 8 == 0) && (ldw % 8 == 0);
+  int splits = 1;
+  if (allow_split) {
+    const int m_pad = p.m_tiles * p.bm;
+    while (true) {
+      const int s2 = splits * 2;
+      const int ks = cdiv(cdiv(K, s2), 256) * 256;
+      if (n_tiles * p.m_tiles * splits >= kTargetWorkgroups) break;
+      if (cdiv(K, ks) < s2) break;
+      if (double(s2) * M * n_tiles * kBN * 4 > double(kPartialCap)) break;
+      if (s2 > std::max(1, K / (16 * m_pad))) break;
+      if (size_t(p.m_tiles) * n_tiles > size_t(kGemmCounters)) break;
+      splits = s2;
+    }
+  }
+  if (splits == 1) {
+    p.splits = 1;
+    p.k_split = K;
+  } else {
+    p.k_split = cdiv(cdiv(K, splits), 256) * 256;
+    p.splits = cdiv(K, p.k_split);
+  }
+  return p;
+}
+
+struct Ctx {
+  const dflash_dims& d;
+  const Layout& L;
+  char* ws;
+  template <typename X> X* at(size_t off) const { return reinterpret_cast<X*>(ws + off); }
+};
+
+GemmArgs base_args(const Ctx& c) {
+  GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.partials = c.at<float>(c.L.partials);
+  a.counters = c.at<unsigned>(c.L.counters);
+  a.eps = c.d.rms_eps;
+  a.norm_dim = c.d.hidden;
+  a.n_q_heads = c.d.n_q_heads;
+  a.n_kv_heads = c.d.n_kv_heads;
+  a.head_dim = c.d.head_dim;
+  a.n_layers = c.d.n_layers;
+  a.batch = c.d.batch;
+  a.cache_slots = c.d.cache_slots;
+  a.ffn = c.d.ffn;
+  a.theta = c.d.rope_theta;
+  return a;
+}
+
+#define DF_CHECK(call)                        \
+  do {                                        \
+    if ((call) != hipSuccess) return DFLASH_E_HIP; \
+  } while (0)
+
+int run_gemm(int epi, const Ctx& c, GemmArgs a, bool allow_split, hipStream_t s) {
+  const GemmPlan p = gemm_plan(a.M, a.n_tiles, a.K, a.lda, a.ldw, allow_split);
+  a.splits = p.splits;
+  a.k_split = p.k_split;
+  a.m_tiles = p.m_tiles;
+  DF_CHECK(launch_gemm(epi, elem_bytes(c.d), p, a, s));
+  return DFLASH_OK;
+}
+
+int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_cache* cache,
+               int32_t* draft, float* logits_out, void* workspace, size_t workspace_bytes,
+               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (!dims_ok(dims) || w == nullptr || cache == nullptr || draft == nullptr) return DFLASH_E_INVALID;
+  const dflash_dims& d = *dims;
+  const void* wp[] = {w->embed, w->mask_embed, w->attn_norm, w->w_qkv, w->w_o, w->mlp_norm,
+                      w->w_gate_up, w->w_down, w->final_norm, w->lm_head};
+  for (const void* p : wp)
+    if (p == nullptr || !aligned16(p)) return DFLASH_E_INVALID;
+  if (!cache->k || !cache->v || !aligned16(cache->k) || !aligned16(cache->v)) return DFLASH_E_INVALID;
+  if (!cache->ctx_len || !cache->anchor || !cache->dev_error || !aligned4(draft)) return DFLASH_E_INVALID;
+  if (logits_out != nullptr && !aligned4(logits_out)) return DFLASH_E_INVALID;
+  const Layout L = layout(d);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < L.total) return DFLASH_E_WORKSPACE;
+
+  const Ctx c{d, L, static_cast<char*>(workspace)};
+  const int sz = elem_bytes(d);
+  const int D = d.hidden, k = d.block_k, B = d.batch, F = d.ffn;
+  const int Mb = B * k;
+  const int qkv_rows = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+  const int hq_dh = d.n_q_heads * d.head_dim;
+  const size_t layer_cache = size_t(B) * d.n_kv_heads * d.cache_slots * d.head_dim * sz;
+  auto wl = [&](const void* base, size_t elems_per_layer, int l) {
+    return static_cast<const char*>(base) + size_t(l) * elems_per_layer * sz;
+  };
+
+  EmbedArgs e{};
+  e.anchor = cache->anchor;
+  e.ctx_len = cache->ctx_len;
+  e.embed = w->embed;
+  e.mask_embed = w->mask_embed;
+  e.gain = w->attn_norm;
+  e.h = c.at<float>(L.h);
+  e.xa = c.at<void>(L.xa);
+  e.ssq = c.at<float>(L.ssq);
+  e.batch = B;
+  e.block_k = k;
+  e.hidden = D;
+  e.vocab = d.vocab;
+  e.dev_error = cache->dev_error;
+  DF_CHECK(launch_embed(sz, e, stream));
+
+  for (int l = 0; l < d.n_layers; ++l) {
+    // RMSNorm + fused QKV projection + RoPE
+    GemmArgs a = base_args(c);
+    a.A = c.at<void>(L.xa);
+    a.lda = D;
+    a.M = Mb;
+    a.K = D;
+    a.W = wl(w->w_qkv, size_t(qkv_rows) * D, l);
+    a.ldw = D;
+    a.N = qkv_rows;
+    a.n_tiles = qkv_rows / kBN;
+    a.ssq_in = c.at<float>(L.ssq);
+    a.np_in = l == 0 ? 1 : L.np_d;
+    a.out = c.at<void>(L.q);
+    a.out2 = c.at<void>(L.kb);
+    a.out3 = c.at<void>(L.vb);
+    a.rows_per_seq = k;
+    a.ctx_len = cache->ctx_len;
+    if (int st = run_gemm(EPI_QKV, c, a, true, stream)) return st;
+
+    // block attention over window + block
+    AttnArgs at{};
+    at.q = c.at<void>(L.q);
+    at.kb = c.at<void>(L.kb);
+    at.vb = c.at<void>(L.vb);
+    at.cache_k = static_cast<const char*>(cache->k) + size_t(l) * layer_cache;
+    at.cache_v = static_cast<const char*>(cache->v) + size_t(l) * layer_cache;
+    at.ctx_len = cache->ctx_len;
+    at.out = c.at<void>(L.o);
+    at.part_o = c.at<float>(L.attn_o);
+    at.part_ml = c.at<float>(L.attn_ml);
+    at.counters = c.at<unsigned>(L.attn_cnt);
+    at.batch = B;
+    at.block_k = k;
+    at.n_q_heads = d.n_q_heads;
+    at.n_kv_heads = d.n_kv_heads;
+    at.head_dim = d.head_dim;
+    at.cache_slots = d.cache_slots;
+    at.window = d.window;
+    at.keys_per_split = L.ap.kps;
+    at.max_splits = L.ap.max_splits;
+    at.n_rb = L.ap.n_rb;
+    DF_CHECK(launch_attention(sz, at, stream));
+
+    // output projection + residual; produces the MLP's RMSNorm input
+    a = base_args(c);
+    a.A = c.at<void>(L.o);
+    a.lda = hq_dh;
+    a.M = Mb;
+    a.K = hq_dh;
+    a.W = wl(w->w_o, size_t(D) * hq_dh, l);
+    a.ldw = hq_dh;
+    a.N = D;
+    a.n_tiles = L.np_d;
+    a.h = c.at<float>(L.h);
+    a.out = c.at<void>(L.xa);
+    a.ldo = D;
+    a.gain = wl(w->mlp_norm, D, l);
+    a.ssq_out = c.at<float>(L.ssq);
+    a.np_out = L.np_d;
+    if (int st = run_gemm(EPI_RESID, c, a, true, stream)) return st;
+
+    // RMSNorm + gate/up projection + SwiGLU
+    a = base_args(c);
+    a.A = c.at<void>(L.xa);
+    a.lda = D;
+    a.M = Mb;
+    a.K = D;
+    a.W = wl(w->w_gate_up, size_t(2) * F * D, l);
+    a.ldw = D;
+    a.N = F;
+    a.n_tiles = cdiv(F, kBN / 2);
+    a.ssq_in = c.at<float>(L.ssq);
+    a.np_in = L.np_d;
+    a.out = c.at<void>(L.act);
+    a.ldo = F;
+    if (int st = run_gemm(EPI_SWIGLU, c, a, true, stream)) return st;
+
+    // down projection + residual; produces the next RMSNorm input
+    a = base_args(c);
+    a.A = c.at<void>(L.act);
+    a.lda = F;
+    a.M = Mb;
+    a.K = F;
+    a.W = wl(w->w_down, size_t(D) * F, l);
+    a.ldw = F;
+    a.N = D;
+    a.n_tiles = L.np_d;
+    a.h = c.at<float>(L.h);
+    a.out = c.at<void>(L.xa);
+    a.ldo = D;
+    a.gain = l + 1 < d.n_layers ? wl(w->attn_norm, D, l + 1) : w->final_norm;
+    a.ssq_out = c.at<float>(L.ssq);
+    a.np_out = L.np_d;
+    if (int st = run_gemm(EPI_RESID, c, a, true, stream)) return st;
+  }
+
+  // final RMSNorm + LM head + split-vocab argmax
+  GemmArgs a = base_args(c);
+  a.A = c.at<void>(L.xa);
+  a.lda = D;
+  a.M = Mb;
+  a.K = D;
+  a.W = w->lm_head;
+  a.ldw = D;
+  a.N = d.vocab;
+  a.n_tiles = cdiv(d.vocab, kBN);
+  a.ssq_in = c.at<float>(L.ssq);
+  a.np_in = L.np_d;
+  a.keys = c.at<unsigned long long>(L.keys);
+  a.draft = draft;
+  a.logits = logits_out;
+  if (ev0) DF_CHECK(hipEventRecord(ev0, stream));
+  if (int st = run_gemm(EPI_ARGMAX, c, a, false, stream)) return st;
+  if (ev1) DF_CHECK(hipEventRecord(ev1, stream));
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dflash_workspace_bytes(const dflash_dims* dims) {
+  if (!dims_ok(dims)) return 0;
+  return layout(*dims).total;
+}
+
+const char* dflash_status_string(int status) {
+  switch (status) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_E_INVALID: return "invalid argument";
+    case DFLASH_E_UNSUPPORTED: return "unsupported configuration";
+    case DFLASH_E_WORKSPACE: return "workspace missing or too small";
+    case DFLASH_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const void* taps,
+                       const int32_t* n_rows, int32_t n_max, int32_t commit,
+                       const dflash_cache* cache, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  if (!dims_ok(dims) || w == nullptr || cache == nullptr) return DFLASH_E_INVALID;
+  const dflash_dims& d = *dims;
+  if (taps == nullptr || !aligned16(taps) || n_rows == nullptr || !aligned4(n_rows)) return DFLASH_E_INVALID;
+  if (n_max < 1 || n_max > d.max_inject_rows || (commit != 0 && commit != 1)) return DFLASH_E_INVALID;
+  if (!w->fuse_w || !w->fuse_norm || !w->w_qkv || !aligned16(w->fuse_w) || !aligned16(w->fuse_norm) ||
+      !aligned16(w->w_qkv))
+    return DFLASH_E_INVALID;
+  if (!cache->k || !cache->v || !aligned16(cache->k) || !aligned16(cache->v)) return DFLASH_E_INVALID;
+  if (!cache->ctx_len || !cache->dev_error) return DFLASH_E_INVALID;
+  const Layout L = layout(d);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < L.total) return DFLASH_E_WORKSPACE;
+
+  const Ctx c{d, L, static_cast<char*>(workspace)};
+  const int D = d.hidden;
+  const int Mi = d.batch * n_max;
+  const int K = d.n_taps * d.tap_dim;
+
+  GemmArgs a = base_args(c);
+  a.A = taps;
+  a.lda = K;
+  a.M = Mi;
+  a.K = K;
+  a.W = w->fuse_w;
+  a.ldw = K;
+  a.N = D;
+  a.n_tiles = L.np_d;
+  a.out = c.at<void>(L.cu);
+  a.ldo = D;
+  a.gain = w->fuse_norm;
+  a.ssq_out = c.at<float>(L.ssq_c);
+  a.np_out = L.np_d;
+  if (int st = run_gemm(EPI_FUSE, c, a, true, stream)) return st;
+
+  a = base_args(c);
+  a.A = c.at<void>(L.cu);
+  a.lda = D;
+  a.M = Mi;
+  a.K = D;
+  a.W = w->w_qkv;
+  a.ldw = D;
+  a.N = d.n_layers * 2 * d.n_kv_heads * d.head_dim;
+  a.n_tiles = a.N / kBN;
+  a.ssq_in = c.at<float>(L.ssq_c);
+  a.np_in = L.np_d;
+  a.rows_per_seq = n_max;
+  a.ctx_len = cache->ctx_len;
+  a.n_rows = n_rows;
+  a.cache_k = cache->k;
+  a.cache_v = cache->v;
+  a.dev_error = cache->dev_error;
+  if (int st = run_gemm(EPI_INJECT, c, a, true, stream)) return st;
+
+  if (commit) DF_CHECK(launch_commit_rows(cache->ctx_len, n_rows, d.batch, n_max, cache->dev_error, stream));
+  return DFLASH_OK;
+}
+
+int dflash_draft_step(const dflash_dims* dims, const dflash_weights* w, const dflash_cache* cache,
+                      int32_t* draft, float* logits_out, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return draft_impl(dims, w, cache, draft, logits_out, workspace, workspace_bytes, stream, nullptr,
+                    nullptr);
+}
+
+int dflash_draft_step_timed(const dflash_dims* dims, const dflash_weights* w,
+                            const dflash_cache* cache, int32_t* draft, float* logits_out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream,
+                            hipEvent_t head_begin, hipEvent_t head_end) {
+  return draft_impl(dims, w, cache, draft, logits_out, workspace, workspace_bytes, stream,
+                    head_begin, head_end);
+}
+
+int dflash_verify_commit(const dflash_dims* dims, const int32_t* draft, const int32_t* target,
+                         const dflash_cache* cache, int32_t* accept_len, int32_t* out_tokens,
+                         hipStream_t stream) {
+  if (!dims_ok(dims) || cache == nullptr) return DFLASH_E_INVALID;
+  if (!draft || !target || !accept_len || !out_tokens || !cache->ctx_len || !cache->anchor ||
+      !cache->dev_error)
+    return DFLASH_E_INVALID;
+  if (!aligned4(draft) || !aligned4(target) || !aligned4(accept_len) || !aligned4(out_tokens))
+    return DFLASH_E_INVALID;
+  VerifyArgs v{};
+  v.draft = draft;
+  v.target = target;
+  v.ctx_len = cache->ctx_len;
+  v.anchor = cache->anchor;
+  v.accept_len = accept_len;
+  v.out_tokens = out_tokens;
+  v.dev_error = cache->dev_error;
+  v.batch = dims->batch;
+  v.block_k = dims->block_k;
+  v.vocab = dims->vocab;
+  DF_CHECK(launch_verify(v, stream));
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Shared device helpers for the gfx950 kernels: element types, 8-element MFMA
+// fragments, conversions, wavefront reductions, the RoPE rotation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;  // 4 wavefronts per workgroup everywhere
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
+  return static_cast<bf16>(x);  // round to nearest even
+}
+
+// ---------------------------------------------------------------------------
+// 8-element fragments.  One K-step of the GEMMs is 32 reduction elements: lane l
+// of a wavefront holds 8 consecutive elements, rows/columns indexed by l % 16,
+// reduction offset 8 * (l / 16).  A and B use the same lane -> k mapping, so
+// any permutation of k inside one step still yields the full dot product.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+
+template <> struct Frag<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void zero() {
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<bf16>(0.0f);
+  }
+  // 16-byte aligned vector load of 8 elements
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  // element-wise load of the first `valid` elements, zeros after (any alignment)
+  __device__ __forceinline__ void load_masked(const bf16* p, int valid) {
+    for (int i = 0; i < 8; ++i) v[i] = (i < valid) ? p[i] : static_cast<bf16>(0.0f);
+  }
+  // acc[16x16] += A[16x32] * B[32x16]; lane holds A row (l%16) and B column (l%16)
+  static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+  }
+};
+
+template <> struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void zero() {
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  __device__ __forceinline__ void load(const float* p) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ void load_masked(const float* p, int valid) {
+    for (int i = 0; i < 8; ++i) v[i] = (i < valid) ? p[i] : 0.0f;
+  }
+  // fp32 MFMA takes one reduction element per lane: eight 16x16x4 steps, step j
+  // using element j of every lane, cover the lane's 8 elements.
+  static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// wavefront reductions (64 lanes)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// (value, index) max with ties to the smaller index
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(i, o, kWave);
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  }
+}
+
+// Order-preserving map of a float onto uint32 (larger float -> larger integer).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 64-bit argmax key: value in the high word, (~index) in the low word, so the
+// maximum key is the largest value and, among equal values, the smallest index.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
+  return (static_cast<unsigned long long>(ordered_bits(v)) << 32) |
+         static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(idx));
+}
+
+__device__ __forceinline__ int argmax_key_index(unsigned long long key) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFull));
+}
+
+// ---------------------------------------------------------------------------
+// RoPE, rotate-half pairing (i, i + dh/2), angle pos * theta^(-2i/dh).  The angle
+// is formed and reduced modulo 2*pi in double precision, because positions reach
+// 2.6e5 where one float ulp of the angle is already 0.03 rad; sin/cos of the
+// reduced angle are then taken in float.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double rope_inv_freq(int i, int head_dim, float theta) {
+  return pow(static_cast<double>(theta), -2.0 * static_cast<double>(i) / static_cast<double>(head_dim));
+}
+
+__device__ __forceinline__ void rope_sincos(int pos, double inv_freq, float* s, float* c) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double a = static_cast<double>(pos) * inv_freq;
+  a -= two_pi * floor(a / two_pi);
+  sincosf(static_cast<float>(a), s, c);
+}
+
+}  // namespace dflash

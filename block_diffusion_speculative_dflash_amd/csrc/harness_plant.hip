@@ -1,0 +1,50 @@
+// Target stand-in for benchmarks (not part of libdflash): plants the target's
+// tokens from the device drafts so that exactly a* drafts of each sequence are
+// accepted, with a* taken from a precomputed per-step table.  This replaces the
+// target model's verify forward, which needs trained weights.
+//   T[i] = draft[i] for i < a*;  T[a*] = a token different from draft[a*] when
+//   a* < k;  every other entry (and the bonus T[k] when a* = k) is filler.
+// It also accumulates the accepted lengths of the previous step into a 64-bit
+// running total, so a timed run can report accepted tokens without host syncs.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+extern "C" {
+
+__global__ void plant_kernel(const int32_t* draft, int32_t* target, const int32_t* a_star_tab,
+                             const int32_t* fill_tab, int32_t* step_counter, int n_tab_steps,
+                             const int32_t* accept_len, long long* accept_total, int batch, int k,
+                             int vocab) {
+  __shared__ int step_s;
+  if (threadIdx.x == 0) step_s = step_counter[0];
+  __syncthreads();
+  const int s = step_s % n_tab_steps;
+  for (int idx = threadIdx.x; idx < batch * (k + 1); idx += blockDim.x) {
+    const int b = idx / (k + 1), i = idx % (k + 1);
+    const int a = min(max(a_star_tab[s * batch + b], 0), k);
+    const int f = fill_tab[(static_cast<long long>(s) * batch + b) * (k + 1) + i];
+    int t;
+    if (i < a) t = draft[b * k + i];
+    else if (i == a && a < k) t = (draft[b * k + i] + 1 + f % (vocab - 1)) % vocab;
+    else t = f % vocab;
+    target[idx] = t;
+  }
+  if (threadIdx.x == 0) {
+    long long add = 0;
+    for (int b = 0; b < batch; ++b) add += accept_len[b];
+    accept_total[0] += add;
+    step_counter[0] = step_s + 1;
+  }
+}
+
+int dflash_harness_plant(const int32_t* draft, int32_t* target, const int32_t* a_star_tab,
+                         const int32_t* fill_tab, int32_t* step_counter, int n_tab_steps,
+                         const int32_t* accept_len, long long* accept_total, int batch, int k,
+                         int vocab, hipStream_t stream) {
+  if (batch < 1 || k < 1 || vocab < 2 || n_tab_steps < 1) return -1;
+  hipLaunchKernelGGL(plant_kernel, dim3(1), dim3(256), 0, stream, draft, target, a_star_tab,
+                     fill_tab, step_counter, n_tab_steps, accept_len, accept_total, batch, k, vocab);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Small kernels of the step: block construction, greedy verify + commit, and the
+// committed-length update of a prefill injection.
+#include "common.h"
+#include "internal.h"
+
+namespace dflash {
+
+// Block construction (hotdry blog, block-level masked parallel prediction): row 0
+// of sequence b is the anchor's embedding at position P_b, rows 1..k-1 the mask
+// embedding.  Writes the fp32 residual h, the first layer's RMSNorm input h*g and
+// the row's sum of squares (one partial per row).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
+  __shared__ float red[kThreads / kWave];
+  const int m = blockIdx.x;
+  const int b = m / a.block_k, i = m % a.block_k;
+  const int d = a.hidden;
+  int tok = a.anchor[b];
+  if (tok < 0 || tok >= a.vocab) {
+    if (threadIdx.x == 0 && i == 0) atomicOr(a.dev_error, 1u);
+    tok = min(max(tok, 0), a.vocab - 1);
+  }
+  if (threadIdx.x == 0 && i == 0 && a.ctx_len[b] < 0) atomicOr(a.dev_error, 4u);
+  const T* src = i == 0 ? static_cast<const T*>(a.embed) + static_cast<size_t>(tok) * d
+                        : static_cast<const T*>(a.mask_embed);
+  const T* gain = static_cast<const T*>(a.gain);
+  T* xa = static_cast<T*>(a.xa) + static_cast<size_t>(m) * d;
+  float* h = a.h + static_cast<size_t>(m) * d;
+  float ss = 0.f;
+  for (int n = threadIdx.x; n < d; n += kThreads) {
+    const float v = to_f32(src[n]);
+    h[n] = v;
+    xa[n] = from_f32<T>(v * to_f32(gain[n]));
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
+    a.ssq[m] = t;
+  }
+}
+
+hipError_t launch_embed(int elem_bytes, const EmbedArgs& a, hipStream_t stream) {
+  const dim3 grid(a.batch * a.block_k);
+  if (elem_bytes == 2) hipLaunchKernelGGL(embed_kernel<bf16>, grid, dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Greedy verification (zhihu answer §2: accept until the first error; the target
+// takes over there).  One wavefront per sequence: lane i tests draft[i] ==
+// target[i]; the accepted length is the length of the all-true prefix, i.e. the
+// index of the first zero of the ballot mask (an AND prefix scan over the block).
+// The bonus token target[a] becomes the next anchor and the committed length moves
+// past it; the ring rows of rejected positions stay behind as dead rows.
+__global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  if (b >= a.batch) return;
+  const int k = a.block_k;
+  const int32_t* dr = a.draft + static_cast<size_t>(b) * k;
+  const int32_t* tg = a.target + static_cast<size_t>(b) * (k + 1);
+  bool bad = false;
+  int t = 0;
+  if (lane <= k) {
+    t = tg[lane];
+    if (t < 0 || t >= a.vocab) { bad = true; t = min(max(t, 0), a.vocab - 1); }
+  }
+  bool match = false;
+  if (lane < k) {
+    int dv = dr[lane];
+    if (dv < 0 || dv >= a.vocab) { bad = true; dv = min(max(dv, 0), a.vocab - 1); }
+    match = (dv == t);
+  }
+  const unsigned long long ones = __ballot(match);
+  // lanes >= k never match, so the first zero bit is at most k
+  const int acc = __ffsll(static_cast<long long>(~ones)) - 1;
+  const int bonus = __shfl(t, acc, kWave);
+  if (lane <= k) a.out_tokens[static_cast<size_t>(b) * (k + 1) + lane] = lane <= acc ? t : -1;
+  if (__ballot(bad) != 0ull && lane == 0) atomicOr(a.dev_error, 1u);
+  if (lane == 0) {
+    const int P = a.ctx_len[b];
+    if (P < 0) atomicOr(a.dev_error, 4u);
+    a.accept_len[b] = acc;
+    a.anchor[b] = bonus;
+    a.ctx_len[b] = max(P, 0) + acc + 1;
+  }
+}
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
+  const dim3 grid((a.batch + 3) / 4);
+  hipLaunchKernelGGL(verify_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+__global__ void commit_rows_kernel(int32_t* ctx_len, const int32_t* n_rows, int batch, int n_max,
+                                   uint32_t* dev_error) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  int n = n_rows[b];
+  if (n < 0 || n > n_max) { atomicOr(dev_error, 2u); n = min(max(n, 0), n_max); }
+  const int P = ctx_len[b];
+  if (P < 0) atomicOr(dev_error, 4u);
+  ctx_len[b] = max(P, 0) + n;
+}
+
+hipError_t launch_commit_rows(int32_t* ctx_len, const int32_t* n_rows, int batch, int n_max,
+                              uint32_t* dev_error, hipStream_t stream) {
+  hipLaunchKernelGGL(commit_rows_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, ctx_len,
+                     n_rows, batch, n_max, dev_error);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,183 @@
+/*
+ * dflash.h — C ABI of the MI355X (gfx950) DFlash block draft-and-verify step.
+ *
+ * The method (DFlash, "Block Diffusion for Flash Speculative Decoding", as the
+ * zhihu answer on MiMo-V2.5-Pro-UltraSpeed explains it in §5.1-§5.4, and as the
+ * hotdry blog on MiMo-V2.5 speculative-decoding draft scheduling deploys it):
+ *   1. fuse the hidden states of 5 target layers with one linear projection and
+ *      RMSNorm into a context feature, and inject that feature into every draft
+ *      layer's K/V, kept in a KV cache (zhihu §5.1, §5.2);
+ *   2. fill a whole block of k positions — the visible anchor token plus k-1 mask
+ *      positions — with one forward pass of a small transformer whose attention is
+ *      a 128-token sliding window over the committed context (hotdry blog: block
+ *      level masked parallel prediction, SWA drafter; zhihu §5.3, §5.4);
+ *   3. verify the block greedily: accept drafts up to the first one that differs
+ *      from the target's token, take the target's token there as a bonus, and
+ *      commit or roll back (zhihu §2, draft / verify / accept steps).
+ *
+ * Conventions shared by every call
+ *   - All pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer: weights, taps, the decode state, the workspace and the outputs.  The
+ *     library allocates nothing, keeps no pointer after a call returns, and holds
+ *     no global state apart from read-only kernel code.
+ *   - Every call only enqueues work on `stream` and returns; results are valid once
+ *     the stream reaches that point.  Calls on one workspace must not overlap.
+ *   - Synchronous errors: argument validation happens on the host before anything
+ *     is enqueued, and a failure returns a negative dflash_status with nothing
+ *     enqueued.  A failed kernel launch returns DFLASH_E_HIP.
+ *   - Asynchronous errors: contract violations only the device can see (a token id
+ *     outside [0, vocab), a row count outside [0, n_max], a negative committed
+ *     length) are clamped into range and OR-ed into *cache->dev_error as the
+ *     DFLASH_DEVERR_* bits.  The caller reads that word after synchronising.
+ *   - Matrices use the nn.Linear layout [out, in], row-major, rows contiguous.
+ *   - dims->dtype selects the element type of weights, taps and the K/V cache:
+ *     DFLASH_BF16 (bfloat16) or DFLASH_F32 (float).  Token ids are int32.
+ *   - Order of one decode round: dflash_draft_step -> (target model verifies) ->
+ *     dflash_fuse_inject(commit = 0) -> dflash_verify_commit.  The K/V rows for the
+ *     k+1 positions the target just processed are written as tentative rows, and
+ *     verify_commit moves the committed length past the accepted ones; rows past it
+ *     are rolled back simply by not being committed (nothing is copied).
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_INVALID = -1,     /* bad dims, NULL or misaligned pointer, bad argument */
+  DFLASH_E_UNSUPPORTED = -2, /* valid but not handled by this build (e.g. head_dim) */
+  DFLASH_E_WORKSPACE = -3,   /* workspace NULL or smaller than dflash_workspace_bytes */
+  DFLASH_E_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Bits OR-ed into cache->dev_error by the device. */
+#define DFLASH_DEVERR_TOKEN 1u   /* anchor, draft or target token outside [0, vocab): clamped */
+#define DFLASH_DEVERR_ROWS 2u    /* n_rows[b] outside [0, n_max]: clamped */
+#define DFLASH_DEVERR_CTXLEN 4u  /* ctx_len[b] negative: treated as 0 */
+
+/* (host) Static shapes of one drafter; read during a call only.
+ *   batch B, block_k k (1..63), n_layers L, hidden d, n_q_heads Hq, n_kv_heads Hkv
+ *   (Hq % Hkv == 0), head_dim dh (64 or 128), ffn F (SwiGLU width), vocab V,
+ *   n_taps (the pages fix 5), tap_dim d_t, window W (committed positions each block
+ *   query sees), cache_slots C (ring slots per layer/sequence/kv head, C >= W + k),
+ *   dtype (dflash_dtype), max_inject_rows (largest n_max a fuse_inject call may
+ *   use, >= k + 1; sizes the workspace), rms_eps, rope_theta (RoPE base). */
+typedef struct {
+  int32_t batch, block_k, n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn,
+      vocab, n_taps, tap_dim, window, cache_slots, dtype, max_inject_rows;
+  float rms_eps, rope_theta;
+} dflash_dims;
+
+/* (host) Device pointers to the drafter weights, all in dims->dtype, all
+ * 16-byte aligned, no biases:
+ *   fuse_w [d, n_taps*d_t]   projection of the concatenated taps (ascending depth)
+ *   fuse_norm [d]            RMSNorm gain of the fused feature
+ *   embed [V, d]             token embedding (the anchor row)
+ *   mask_embed [d]           embedding of every mask position of the block
+ *   attn_norm [L, d]         pre-attention RMSNorm gains
+ *   w_qkv [L, (Hq+2Hkv)*dh, d]  q rows, then k rows, then v rows; the k and v rows
+ *                            also project the fused feature into the cache
+ *   w_o [L, d, Hq*dh]        attention output projection
+ *   mlp_norm [L, d]          pre-MLP RMSNorm gains
+ *   w_gate_up [L, 2F, d]     SwiGLU gate rows (first F) then up rows
+ *   w_down [L, d, F]         SwiGLU down projection
+ *   final_norm [d]           RMSNorm gain before the LM head
+ *   lm_head [V, d]           LM head (independent of embed) */
+typedef struct {
+  const void *fuse_w, *fuse_norm, *embed, *mask_embed, *attn_norm, *w_qkv, *w_o,
+      *mlp_norm, *w_gate_up, *w_down, *final_norm, *lm_head;
+} dflash_weights;
+
+/* (host) The whole decode state, caller-owned device memory:
+ *   k, v       [L, B, Hkv, C, dh] in dims->dtype; logical position p of sequence b
+ *              lives in slot p % C; k rows carry RoPE at position p
+ *   ctx_len    [B] int32 committed length P_b (a logical position, may exceed C)
+ *   anchor     [B] int32 token at position P_b (the visible first row of the block)
+ *   dev_error  [1] uint32 sticky DFLASH_DEVERR_* bits */
+typedef struct {
+  void *k, *v;
+  int32_t *ctx_len, *anchor;
+  uint32_t *dev_error;
+} dflash_cache;
+
+/* Bytes of device workspace the three calls need for these dims.  The workspace
+ * must be zero-filled once before its first use; every call leaves the counters it
+ * uses at zero again.  Returns 0 for invalid dims. */
+size_t dflash_workspace_bytes(const dflash_dims *dims);
+
+/* Static string naming a dflash_status value. */
+const char *dflash_status_string(int status);
+
+/* Feature fusion + KV injection (zhihu answer §5.1 feature fusion, §5.2 KV
+ * injection; hotdry blog: all-SWA drafter with a 128-token window).
+ *   taps     [B, n_max, n_taps, d_t] in dims->dtype: for sequence b, rows
+ *            0..n_rows[b]-1 are the tapped target hidden states of logical positions
+ *            ctx_len[b] .. ctx_len[b]+n_rows[b]-1, taps in ascending target depth;
+ *            rows past n_rows[b] are ignored
+ *   n_rows   [B] int32 device array, each in [0, n_max]
+ *   n_max    (host) 1 .. dims->max_inject_rows
+ *   commit   (host) 0: rows are tentative (the per-round path, n_rows = k+1);
+ *            1: also advance ctx_len[b] by n_rows[b] (prefill)
+ * For every row and layer l: c = RMSNorm(fuse_w . concat(taps)) * fuse_norm, then
+ * K = RoPE(W_k^l c, position) and V = W_v^l c are written to slot position % C. */
+int dflash_fuse_inject(const dflash_dims *dims, const dflash_weights *w,
+                       const void *taps, const int32_t *n_rows, int32_t n_max,
+                       int32_t commit, const dflash_cache *cache, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* One block draft (hotdry blog: block-level masked parallel prediction, one
+ * forward fills the whole block; zhihu §5.3, §5.4).  Row 0 of sequence b's block is
+ * embed[anchor[b]] at position P_b = ctx_len[b]; rows 1..k-1 are mask_embed at
+ * P_b+1 .. P_b+k-1.  Each of the L pre-norm layers applies RMSNorm, the fused QKV
+ * projection with RoPE, attention of every block row over the last min(P_b, W)
+ * committed positions plus all k block rows (bidirectional inside the block, GQA),
+ * the output projection with residual, and a SwiGLU MLP with residual.  A final
+ * RMSNorm and the LM head give logits; row i's argmax (lowest id on ties) is the
+ * draft for position P_b+i+1.
+ *   draft       [B, k] int32 output
+ *   logits_out  NULL, or [B, k, V] float output of the logits (for tests)
+ * Reads the cache, writes only draft, logits_out and the workspace. */
+int dflash_draft_step(const dflash_dims *dims, const dflash_weights *w,
+                      const dflash_cache *cache, int32_t *draft, float *logits_out,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Greedy verification, bonus token, commit / rollback, in place (zhihu answer §2:
+ * accept drafts up to the first error, the target takes over there; §6: the
+ * accepted output equals what the target would emit by itself).
+ *   draft       [B, k] int32 drafts of dflash_draft_step
+ *   target      [B, k+1] int32: target[b, i] is the target's greedy token for
+ *               position P_b+i+1 given the anchor and draft[b, 0..i-1]
+ *   accept_len  [B] int32 output a_b in [0, k]: leading drafts equal to target
+ *   out_tokens  [B, k+1] int32 output: target[b, 0..a_b], then -1
+ * Updates ctx_len[b] += a_b + 1 and anchor[b] = target[b, a_b].  The K/V rows the
+ * preceding fuse_inject wrote for positions P_b .. P_b+a_b become committed; those
+ * for P_b+a_b+1 .. P_b+k are rolled back (never read again before being
+ * rewritten). */
+int dflash_verify_commit(const dflash_dims *dims, const int32_t *draft,
+                         const int32_t *target, const dflash_cache *cache,
+                         int32_t *accept_len, int32_t *out_tokens, hipStream_t stream);
+
+/* Same as dflash_draft_step, and records head_begin / head_end on `stream` right
+ * before and after the fused final-norm + LM-head + argmax kernel, so a caller can
+ * time that kernel alone with hipEventElapsedTime.  Either event may be NULL. */
+int dflash_draft_step_timed(const dflash_dims *dims, const dflash_weights *w,
+                            const dflash_cache *cache, int32_t *draft,
+                            float *logits_out, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream, hipEvent_t head_begin,
+                            hipEvent_t head_end);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

@@ -1,0 +1,183 @@
+"""Side-by-side runner: the HIP library (through its C ABI) and the fp64 oracle on
+the same seeded inputs, step by step, with the parity rules:
+
+* fp32 drafters: logits normwise max|z_gpu - z_ref| / max|z_ref| <= 1e-4; drafts
+  bit-exact wherever the oracle's top-1/top-2 margin is >= 1e-3;
+* bf16 drafters: max |z_gpu - z_ref| <= 0.05; drafts bit-exact wherever the
+  oracle's margin is >= 0.1;
+* accepted lengths, emitted tokens, committed lengths and anchors bit-exact for
+  every sequence whose deciding positions (0 .. min(a, k-1)) all pass the margin
+  gate; K/V rows of the committed window within the logit tolerance.
+The oracle plants the target tokens from its own drafts; a sequence whose GPU
+accepted length differs at a low-margin position is re-synchronised to the
+oracle's committed length and anchor (counted as excluded).
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from block_diffusion_speculative_dflash_amd import binding as bd
+from block_diffusion_speculative_dflash_amd import synth
+from block_diffusion_speculative_dflash_amd.configs import BF16, Dims
+from oracle import dflash_oracle as orc
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_weights(W) -> dict:
+    """Exact host copies (float32 holds every bf16 value) of the device weights."""
+    return {k: v.float().cpu().numpy() for k, v in W.items()}
+
+
+@dataclass
+class Tol:
+    margin: float
+    logit_abs: Optional[float]
+    logit_rel: Optional[float]
+
+    @staticmethod
+    def for_dims(d: Dims) -> "Tol":
+        return Tol(0.1, 0.05, None) if d.dtype == BF16 else Tol(1e-3, None, 1e-4)
+
+    def logit_ok(self, err_abs: float, ref_max: float) -> bool:
+        if self.logit_abs is not None:
+            return err_abs <= self.logit_abs
+        return err_abs <= self.logit_rel * ref_max
+
+
+@dataclass
+class StepReport:
+    logit_err: float
+    logit_ref_max: float
+    logits_ok: bool
+    drafts_checked: int
+    drafts_total: int
+    draft_mismatch: int
+    seqs_checked: int
+    seqs_excluded: int
+    state_mismatch: int
+    kv_err: float
+    kv_ref_max: float
+    kv_ok: bool
+    accept: List[int] = field(default_factory=list)
+
+    @property
+    def ok(self) -> bool:
+        return self.logits_ok and self.draft_mismatch == 0 and self.state_mismatch == 0 and self.kv_ok
+
+
+class ParityRun:
+    def __init__(self, dims: Dims, W, ctx_start: Sequence[int], anchors: Sequence[int],
+                 prefill_rows: Sequence[int], sample: Optional[Sequence[int]] = None, seed: int = 0,
+                 check_kv: bool = True):
+        self.d, self.W, self.seed, self.check_kv = dims, W, seed, check_kv
+        self.Wn = oracle_weights(W)
+        self.tol = Tol.for_dims(dims)
+        B = dims.batch
+        self.sample = list(range(B)) if sample is None else list(sample)
+        ctx_start = np.asarray(ctx_start, np.int64)
+        pre = np.asarray(prefill_rows, np.int64)
+        anchors = np.asarray(anchors, np.int64)
+        p0 = ctx_start - pre
+        self.cache = bd.alloc_cache(dims, ctx_len=p0, anchor=anchors)
+        self.ws = bd.alloc_workspace(dims)
+        n_pre = int(pre.max())
+        n_max = dims.max_inject_rows
+        if n_pre > 0:
+            taps = synth.make_taps(dims, n_pre, seed=seed, stream=0, device="cuda")
+            say(f"[parity] prefill {n_pre} rows in chunks of {n_max} (B={B})")
+            for r0 in range(0, n_pre, n_max):
+                chunk = taps[:, r0:r0 + n_max].contiguous()
+                n_rows = torch.as_tensor(np.clip(pre - r0, 0, chunk.shape[1]), dtype=torch.int32).cuda()
+                bd.dflash_fuse_inject(dims, W, chunk, n_rows, chunk.shape[1], True, self.cache, self.ws)
+            torch.cuda.synchronize()
+        s = self.sample
+        self.st = orc.new_state(dims, batch=len(s), ctx_len=p0[s], anchor=anchors[s])
+        if n_pre > 0:
+            orc.fuse_inject(dims, self.Wn, self.st, taps[s].float().cpu().numpy(), pre[s], commit=True)
+        self.step_idx = 0
+
+    def dev_error(self) -> int:
+        return int(self.cache["dev_error"].item())
+
+    def step(self, a_star: Sequence[int]) -> StepReport:
+        d, W, s = self.d, self.W, self.sample
+        B, k, V = d.batch, d.block_k, d.vocab
+        say(f"[parity] step {self.step_idx}: draft_step B={B} k={k} V={V}")
+        draft = torch.empty((B, k), dtype=torch.int32, device="cuda")
+        logits = torch.empty((B, k, V), dtype=torch.float32, device="cuda")
+        bd.dflash_draft_step(d, W, self.cache, draft, logits, self.ws)
+        torch.cuda.synchronize()
+        o = orc.draft_step(d, self.Wn, self.st)
+        zg = logits[s].cpu().numpy().astype(np.float64)
+        dg = draft[s].cpu().numpy().astype(np.int64)
+        zr, dr, mr = o["logits"], o["draft"], o["margin"]
+        err = float(np.max(np.abs(zg - zr)))
+        ref_max = float(np.max(np.abs(zr)))
+        gate = mr >= self.tol.margin
+        mism = int(np.sum((dg != dr) & gate))
+
+        # target stand-in: planted from the oracle's drafts for sampled sequences
+        fill = synth.target_fill(k, 1, B, seed=self.seed + 7919 * (self.step_idx + 1))[0]
+        a_star = np.asarray(a_star, np.int64)
+        T = synth.plant_targets(draft.cpu().numpy(), a_star, fill, V)
+        T[s] = synth.plant_targets(dr, a_star[s], fill[s], V)
+        taps = synth.make_taps(d, k + 1, seed=self.seed, stream=1 + self.step_idx, device="cuda")
+        n_rows = torch.full((B,), k + 1, dtype=torch.int32, device="cuda")
+        say(f"[parity] step {self.step_idx}: fuse_inject + verify_commit")
+        bd.dflash_fuse_inject(d, W, taps, n_rows, k + 1, False, self.cache, self.ws)
+        acc = torch.empty(B, dtype=torch.int32, device="cuda")
+        out = torch.empty((B, k + 1), dtype=torch.int32, device="cuda")
+        Tt = torch.as_tensor(T, dtype=torch.int32).cuda()
+        bd.dflash_verify_commit(d, draft, Tt, self.cache, acc, out)
+        torch.cuda.synchronize()
+        orc.fuse_inject(d, self.Wn, self.st, taps[s].float().cpu().numpy(), np.full(len(s), k + 1), commit=False)
+        r = orc.verify_commit(d, self.st, dr, T[s])
+
+        acc_g = acc[s].cpu().numpy()
+        out_g = out[s].cpu().numpy()
+        ctx_g = self.cache["ctx_len"][s].cpu().numpy()
+        anc_g = self.cache["anchor"][s].cpu().numpy()
+        checked = excluded = state_mism = 0
+        for j, b in enumerate(s):
+            a_ref = int(r["accept_len"][j])
+            deciding = range(0, min(a_ref, k - 1) + 1)
+            if all(mr[j, i] >= self.tol.margin for i in deciding):
+                checked += 1
+                same = (acc_g[j] == a_ref and np.array_equal(out_g[j], r["out_tokens"][j])
+                        and ctx_g[j] == self.st.ctx_len[j] and anc_g[j] == self.st.anchor[j])
+                state_mism += int(not same)
+            else:
+                excluded += 1
+                self.cache["ctx_len"][b] = int(self.st.ctx_len[j])
+                self.cache["anchor"][b] = int(self.st.anchor[j])
+
+        kv_err, kv_max = 0.0, 0.0
+        if self.check_kv:
+            kc = self.cache["k"][:, s].float().cpu().numpy()
+            vc = self.cache["v"][:, s].float().cpu().numpy()
+            for j in range(len(s)):
+                P = int(self.st.ctx_len[j])
+                slots = orc.window_positions(d, P) % d.cache_slots
+                for ring, cache_np in ((self.st.k_ring, kc), (self.st.v_ring, vc)):
+                    ref = ring[:, j][:, :, slots]
+                    got = cache_np[:, j][:, :, slots]
+                    kv_err = max(kv_err, float(np.max(np.abs(got - ref))) if ref.size else 0.0)
+                    kv_max = max(kv_max, float(np.max(np.abs(ref))) if ref.size else 0.0)
+        self.step_idx += 1
+        rep = StepReport(err, ref_max, self.tol.logit_ok(err, ref_max), int(gate.sum()), gate.size,
+                         mism, checked, excluded, state_mism, kv_err, kv_max,
+                         self.tol.logit_ok(kv_err, max(kv_max, 1e-30)), list(map(int, acc_g)))
+        say(f"[parity] step {self.step_idx - 1}: logit_err={err:.3g} (ref max {ref_max:.3g}) "
+            f"drafts {rep.drafts_checked}/{rep.drafts_total} gated, mismatches {mism}; "
+            f"seqs checked {checked}, excluded {excluded}, state mismatches {state_mism}; "
+            f"kv_err={kv_err:.3g} accept={rep.accept[:8]}")
+        return rep

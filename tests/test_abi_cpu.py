@@ -1,0 +1,96 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/dflash.h declares, and rejects bad arguments on the host before anything
+is enqueued (so no device is touched)."""
+import ctypes
+import os
+import re
+from dataclasses import replace
+
+import pytest
+
+from block_diffusion_speculative_dflash_amd import binding as bd
+from block_diffusion_speculative_dflash_amd import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(bd.LIB_PATH), reason="libdflash.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("dflash_fuse_inject", "dflash_draft_step", "dflash_verify_commit"):
+        assert n in names
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    L = bd.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(bd.EXPORTED) <= set(declared_functions())
+
+
+@needs_lib
+def test_status_strings_and_workspace_query():
+    assert bd.status_string(0) == "ok"
+    assert "workspace" in bd.status_string(bd.DFLASH_E_WORKSPACE)
+    for w in configs.ALL:
+        n = bd.dflash_workspace_bytes(w.dims)
+        assert n > 0 and n % 256 == 0
+    L = bd.lib()
+    bad = bd.dims_struct(replace(configs.C1.dims, block_k=0))
+    assert L.dflash_workspace_bytes(ctypes.byref(bad)) == 0
+    bad = bd.dims_struct(replace(configs.C1.dims, n_kv_heads=3))
+    assert L.dflash_workspace_bytes(ctypes.byref(bad)) == 0
+    bad = bd.dims_struct(replace(configs.C1.dims, cache_slots=configs.C1.dims.window))
+    assert L.dflash_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned host integer, never dereferenced: validation fails first
+
+
+def _weights(ptr=FAKE):
+    return bd.DflashWeights(**{n: ptr for n in bd.WEIGHT_FIELDS})
+
+
+def _cache(ptr=FAKE):
+    return bd.DflashCache(k=ptr, v=ptr, ctx_len=ptr, anchor=ptr, dev_error=ptr)
+
+
+@needs_lib
+def test_invalid_arguments_are_rejected_on_the_host():
+    L = bd.lib()
+    d = bd.dims_struct(configs.C2.dims)
+    w, c = _weights(), _cache()
+    ws = bd.dflash_workspace_bytes(configs.C2.dims)
+    by = ctypes.byref
+    # bad dims
+    bad = bd.dims_struct(replace(configs.C2.dims, head_dim=96))
+    assert L.dflash_draft_step(by(bad), by(w), by(c), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
+    # NULL weight, misaligned weight
+    w0 = _weights()
+    w0.lm_head = None
+    assert L.dflash_draft_step(by(d), by(w0), by(c), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
+    w0.lm_head = FAKE + 2
+    assert L.dflash_draft_step(by(d), by(w0), by(c), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
+    # workspace missing or too small
+    assert L.dflash_draft_step(by(d), by(w), by(c), FAKE, None, None, ws, None) == bd.DFLASH_E_WORKSPACE
+    assert L.dflash_draft_step(by(d), by(w), by(c), FAKE, None, FAKE, ws - 1, None) == bd.DFLASH_E_WORKSPACE
+    # fuse_inject: n_max out of range, bad commit flag, small workspace
+    assert L.dflash_fuse_inject(by(d), by(w), FAKE, FAKE, 0, 0, by(c), FAKE, ws, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_fuse_inject(by(d), by(w), FAKE, FAKE, 65, 0, by(c), FAKE, ws, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_fuse_inject(by(d), by(w), FAKE, FAKE, 17, 2, by(c), FAKE, ws, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_fuse_inject(by(d), by(w), FAKE, FAKE, 17, 0, by(c), FAKE, 100, None) == bd.DFLASH_E_WORKSPACE
+    # verify: NULL outputs, misaligned target
+    assert L.dflash_verify_commit(by(d), FAKE, FAKE, by(c), None, FAKE, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_verify_commit(by(d), FAKE, FAKE + 1, by(c), FAKE, FAKE, None) == bd.DFLASH_E_INVALID
+    # block size beyond one wavefront
+    bad = bd.dims_struct(replace(configs.C2.dims, block_k=64, max_inject_rows=80))
+    assert L.dflash_verify_commit(by(bad), FAKE, FAKE, by(c), FAKE, FAKE, None) == bd.DFLASH_E_INVALID

@@ -1,0 +1,153 @@
+"""GPU parity of the HIP library against the fp64 oracle, through the C ABI.
+
+Small shapes that the oracle finishes in seconds but that still span several
+GEMM tiles, split-K, ragged tails (ffn 683, vocab tails), ring wrap, GQA, both
+head sizes, k = 1 and empty contexts.  The full-size workloads are in
+test_gpu_fullsize.py.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_speculative_dflash_amd import binding as bd
+from block_diffusion_speculative_dflash_amd import configs, synth
+from block_diffusion_speculative_dflash_amd.configs import BF16, F32
+from oracle import dflash_oracle as orc
+from tests.parity import ParityRun, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(dims, ctx, prefill, a_stars, seed=0, sample=None, anchors=None):
+    W = synth.make_weights(dims, seed=seed, device="cuda")
+    if anchors is None:
+        anchors = synth.make_anchors(dims, seed=seed)
+    run = ParityRun(dims, W, ctx, anchors, prefill, sample=sample, seed=seed)
+    reps = [run.step(a) for a in a_stars]
+    assert run.dev_error() == 0
+    return reps
+
+
+def _assert_ok(reps):
+    for i, r in enumerate(reps):
+        assert r.logits_ok, f"step {i}: logit error {r.logit_err} (ref max {r.logit_ref_max})"
+        assert r.draft_mismatch == 0, f"step {i}: {r.draft_mismatch} gated draft mismatches"
+        assert r.state_mismatch == 0, f"step {i}: {r.state_mismatch} state mismatches"
+        assert r.kv_ok, f"step {i}: kv error {r.kv_err}"
+
+
+def test_tiny_fp32_every_planted_length():
+    """Tiny fp32 drafter (batch 1, context 128, block 8): planted a* = 0..8."""
+    w = configs.C1
+    d = w.dims
+    say(f"[test] tiny fp32 {d}")
+    planted = list(range(9))
+    reps = _run(d, [w.context], [w.prefill], [[a] for a in planted])
+    _assert_ok(reps)
+    for a, r in zip(planted, reps):
+        if r.seqs_checked:
+            assert r.accept[0] == a
+    assert sum(r.drafts_checked for r in reps) > 0.9 * sum(r.drafts_total for r in reps)
+
+
+def test_tiny_bf16():
+    d = replace(configs.C1.dims, dtype=BF16)
+    say(f"[test] tiny bf16 {d}")
+    _assert_ok(_run(d, [128], [128], [[8], [3], [0], [5]]))
+
+
+def test_gqa_swa_ring_wrap_ragged_bf16():
+    """GQA 4/2, window 16 over contexts longer than the ring, ragged batch."""
+    d = replace(configs.C1.dims, batch=3, block_k=4, n_q_heads=4, n_kv_heads=2, window=16,
+                cache_slots=20, dtype=BF16, max_inject_rows=16)
+    say(f"[test] gqa swa ring {d}")
+    _assert_ok(_run(d, [40, 17, 5], [40, 17, 5], [[4, 0, 2], [1, 4, 3], [2, 2, 4], [0, 1, 1], [3, 3, 0]]))
+
+
+def test_gqa_swa_fp32():
+    d = replace(configs.C1.dims, batch=2, block_k=5, n_q_heads=4, n_kv_heads=1, window=24,
+                cache_slots=29, max_inject_rows=16)
+    say(f"[test] gqa swa fp32 {d}")
+    _assert_ok(_run(d, [50, 23], [30, 23], [[5, 2], [0, 5], [3, 1]]))
+
+
+def test_head_dim_128_bf16():
+    d = replace(configs.C1.dims, batch=2, n_q_heads=4, n_kv_heads=2, head_dim=128, hidden=512,
+                tap_dim=128, ffn=1000, vocab=2000, window=64, cache_slots=72, dtype=BF16)
+    say(f"[test] head_dim 128 {d}")
+    _assert_ok(_run(d, [70, 64], [64, 64], [[8, 1], [2, 7], [4, 4]]))
+
+
+def test_block_of_one_and_empty_context():
+    d = replace(configs.C1.dims, batch=2, block_k=1, window=32, cache_slots=33, max_inject_rows=8)
+    say(f"[test] k=1, empty context {d}")
+    _assert_ok(_run(d, [0, 9], [0, 9], [[1, 0], [0, 1], [1, 1], [1, 0]]))
+
+
+def test_empty_context_bf16_block():
+    d = replace(configs.C1.dims, batch=2, dtype=BF16, window=32, cache_slots=40)
+    _assert_ok(_run(d, [0, 0], [0, 0], [[8, 2], [3, 8]]))
+
+
+def test_verify_exhaustive_patterns_on_gpu():
+    """All 2^10 match patterns of a k = 10 block in one batch, plus planted lengths."""
+    k = 10
+    B = 2 ** k
+    d = replace(configs.C1.dims, batch=B, block_k=k, vocab=50000, cache_slots=configs.C1.dims.window + k)
+    rng = np.random.default_rng(5)
+    draft = rng.integers(0, 40000, size=(B, k))
+    bits = (np.arange(B)[:, None] >> np.arange(k)[None, :]) & 1
+    target = np.concatenate([np.where(bits == 1, draft, draft + 1), rng.integers(0, 40000, (B, 1))], 1)
+    ctx0 = rng.integers(0, 100000, B)
+    anchors = rng.integers(0, 40000, B)
+    cache = bd.alloc_cache(d, ctx_len=ctx0, anchor=anchors)
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, k + 1), dtype=torch.int32, device="cuda")
+    say("[test] verify exhaustive 2^10")
+    bd.dflash_verify_commit(d, torch.as_tensor(draft, dtype=torch.int32).cuda(),
+                            torch.as_tensor(target, dtype=torch.int32).cuda(), cache, acc, out)
+    torch.cuda.synchronize()
+    # verification only touches integers; a one-slot ring stands in for the cache
+    st = orc.State(np.zeros((1, B, 1, 1, 1)), np.zeros((1, B, 1, 1, 1)),
+                   ctx0.astype(np.int64), anchors.astype(np.int64))
+    ref = orc.verify_commit(replace(d, cache_slots=1), st, draft, target)
+    assert np.array_equal(acc.cpu().numpy(), ref["accept_len"])
+    assert np.array_equal(out.cpu().numpy(), ref["out_tokens"])
+    assert np.array_equal(cache["ctx_len"].cpu().numpy(), st.ctx_len)
+    assert np.array_equal(cache["anchor"].cpu().numpy(), st.anchor)
+    assert int(cache["dev_error"].item()) == 0
+
+
+def test_out_of_range_tokens_set_the_error_word():
+    d = replace(configs.C1.dims, batch=2, block_k=4, vocab=100)
+    cache = bd.alloc_cache(d, ctx_len=[5, 5], anchor=[3, 4])
+    draft = torch.tensor([[1, 2, 3, 4], [1, 2, 3, 4]], dtype=torch.int32, device="cuda")
+    target = torch.tensor([[1, 2, 500, 4, 5], [1, 2, 3, 4, 5]], dtype=torch.int32, device="cuda")
+    acc = torch.empty(2, dtype=torch.int32, device="cuda")
+    out = torch.empty((2, 5), dtype=torch.int32, device="cuda")
+    bd.dflash_verify_commit(d, draft, target, cache, acc, out)
+    torch.cuda.synchronize()
+    assert int(cache["dev_error"].item()) & bd.DEVERR_TOKEN
+    assert acc.cpu().tolist() == [2, 4]
+    assert out.cpu().tolist()[0] == [1, 2, 99, -1, -1]     # clamped into [0, vocab)
+
+
+def test_draft_is_deterministic_and_logits_optional():
+    d = replace(configs.C1.dims, batch=2, dtype=BF16)
+    W = synth.make_weights(d, device="cuda")
+    cache = bd.alloc_cache(d, ctx_len=[0, 0], anchor=[5, 6])
+    ws = bd.alloc_workspace(d)
+    taps = synth.make_taps(d, 40, device="cuda")
+    bd.dflash_fuse_inject(d, W, taps, torch.tensor([40, 33], dtype=torch.int32, device="cuda"), 40, True, cache, ws)
+    outs = []
+    for with_logits in (True, True, False):
+        dr = torch.empty((2, d.block_k), dtype=torch.int32, device="cuda")
+        lg = torch.empty((2, d.block_k, d.vocab), device="cuda") if with_logits else None
+        bd.dflash_draft_step(d, W, cache, dr, lg, ws)
+        torch.cuda.synchronize()
+        outs.append((dr.cpu(), None if lg is None else lg.cpu()))
+    assert torch.equal(outs[0][1], outs[1][1])          # bitwise reproducible
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][0], outs[2][0])
+    assert cache["ctx_len"].cpu().tolist() == [40, 33]
