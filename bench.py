@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash block draft-and-verify step on one MI355X.
+
+One step = dflash_draft_step -> target stand-in (planted target tokens) ->
+dflash_fuse_inject(commit = 0) -> dflash_verify_commit over the whole batch, with
+synthetic seeded inputs already resident in HBM.  Steps are captured as HIP
+graphs and replayed.  Prints one JSON line:
+  value      block steps/s (all B sequences per step)
+  roofline   the dominant kernel (fused final-norm + LM-head + argmax), timed with
+             HIP events on its own stream, against the 8 TB/s HBM peak
+  cpu_baseline  the fp64 oracle timed on this host on a bounded sample
+Default workload: the Qwen3-8B-shaped drafter (batch 1, block 16, context 4096).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    from block_diffusion_speculative_dflash_amd import configs
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=configs.C2.name, choices=sorted(configs.WORKLOADS))
+    p.add_argument("--accept-q", type=float, default=None,
+                   help="override the planted geometric q (sub-runs of the SWA workload)")
+    p.add_argument("--head-launches", type=int, default=50)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-steps", type=int, default=2)
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime (the library records them on the
+    stream its kernels run on)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        f = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def destroy(self, e: int) -> None:
+        self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs the DFlash step on one GPU only; "
+                          "run with --gpus 1", "n_gpus": args.gpus}), flush=True)
+        return 2
+    import torch
+    from block_diffusion_speculative_dflash_amd import binding as bd
+    from block_diffusion_speculative_dflash_amd import configs, harness, synth
+    from block_diffusion_speculative_dflash_amd.roofline import HBM_PEAK_GBS, step_cost
+
+    wl = configs.WORKLOADS[args.workload]
+    d = wl.dims
+    B, k, V = d.batch, d.block_k, d.vocab
+    dev = "cuda"
+    torch.cuda.init()
+    log(f"[bench] workload {wl.name}: {wl.description}")
+    W = bd.pack_weights(d, synth.make_weights(d, seed=args.seed, device=dev))
+    ctx = synth.make_context_lengths(wl, seed=args.seed)
+    pre = np.minimum(ctx, wl.prefill)
+    anchors = synth.make_anchors(d, seed=args.seed)
+    cache = bd.alloc_cache(d, device=dev, ctx_len=ctx - pre, anchor=anchors)
+    ws = bd.alloc_workspace(d, device=dev)
+
+    # prefill: inject the committed context (all of it, or the last W for SWA)
+    n_max = d.max_inject_rows
+    n_pre = int(pre.max())
+    for r0 in range(0, n_pre, n_max):
+        taps = prefill_taps(d, n_pre, r0, args.seed)
+        n_rows = torch.as_tensor(np.clip(pre - r0, 0, taps.shape[1]), dtype=torch.int32, device=dev)
+        bd.dflash_fuse_inject(d, W, taps, n_rows, taps.shape[1], True, cache, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache["ctx_len"].cpu().numpy(), ctx), "prefill did not reach the context"
+    log(f"[bench] prefilled {n_pre} rows; context {int(ctx.min())}..{int(ctx.max())}")
+
+    # planted acceptance and the target stand-in tables
+    kind, q = wl.accept
+    if args.accept_q is not None:
+        kind, q = "geometric", args.accept_q
+    n_tab = args.warmup + args.steps + 8
+    a_tab = synth.planted_accept(kind, q, k, n_tab, B, seed=args.seed)
+    fill = synth.target_fill(k, n_tab, B, seed=args.seed)
+    a_tab_d = torch.as_tensor(a_tab, dtype=torch.int32, device=dev)
+    fill_d = torch.as_tensor(fill, dtype=torch.int32, device=dev)
+    step_ctr = torch.zeros(1, dtype=torch.int32, device=dev)
+    acc_total = torch.zeros(1, dtype=torch.int64, device=dev)
+    draft = torch.zeros((B, k), dtype=torch.int32, device=dev)
+    target = torch.zeros((B, k + 1), dtype=torch.int32, device=dev)
+    accept = torch.zeros(B, dtype=torch.int32, device=dev)
+    out_tok = torch.zeros((B, k + 1), dtype=torch.int32, device=dev)
+    n_rows_step = torch.full((B,), k + 1, dtype=torch.int32, device=dev)
+    pool = [synth.make_taps(d, k + 1, seed=args.seed, stream=1 + i, device=dev) for i in range(4)]
+    saved_ctx = cache["ctx_len"].clone()
+
+    def step(taps):
+        bd.dflash_draft_step(d, W, cache, draft, None, ws)
+        harness.plant(draft, target, a_tab_d, fill_d, step_ctr, accept, acc_total, V)
+        bd.dflash_fuse_inject(d, W, taps, n_rows_step, k + 1, False, cache, ws)
+        bd.dflash_verify_commit(d, draft, target, cache, accept, out_tok)
+
+    # eager warm-up of every code path, then capture one graph per taps slot
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step(pool[0])
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graphs = []
+    for taps in pool:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(taps)
+        graphs.append(g)
+    # the eager warm-up and the captures consumed table entries; restart the tables
+    cache["ctx_len"].copy_(saved_ctx)
+    step_ctr.zero_()
+    acc_total.zero_()
+    accept.zero_()
+    torch.cuda.synchronize()
+
+    def run(n, s0):
+        for s in range(s0, s0 + n):
+            graphs[s % len(graphs)].replay()
+            if wl.rewind and (s + 1) % wl.rewind == 0:
+                cache["ctx_len"].copy_(saved_ctx)
+
+    run(args.warmup, 0)
+    torch.cuda.synchronize()
+    tot0, acc0 = int(acc_total.item()), accept.clone()
+    t0 = time.perf_counter()
+    run(args.steps, args.warmup)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tot1 = int(acc_total.item())
+    accepted = tot1 - tot0 - int(acc0.sum().item()) + int(accept.sum().item())
+    elapsed = t1 - t0
+    planted = int(a_tab[args.warmup:args.warmup + args.steps].sum())
+    err = int(cache["dev_error"].item())
+    steps_per_s = args.steps / elapsed
+    committed = accepted + args.steps * B
+    log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms: {steps_per_s:.1f} steps/s, "
+        f"accepted {accepted} (planted {planted}), dev_error {err}")
+
+    # dominant kernel: final norm + LM head + argmax, timed with HIP events
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.head_launches)]
+    for e0, e1 in pairs:
+        bd.dflash_draft_step_timed(d, W, cache, draft, None, ws, e0, e1)
+    torch.cuda.synchronize()
+    head_ms = float(np.mean([ev.elapsed_ms(e0, e1) for e0, e1 in pairs]))
+    for e0, e1 in pairs:
+        ev.destroy(e0)
+        ev.destroy(e1)
+    cost = step_cost(d, float(ctx.mean()))
+    head_gbs = cost.head_bytes / (head_ms * 1e-3) / 1e9
+    step_gbs = cost.bytes_total * steps_per_s / 1e9
+    log(f"[bench] head kernel {head_ms * 1e3:.1f} us = {head_gbs:.0f} GB/s; step {step_gbs:.0f} GB/s "
+        f"({cost.bytes_total / 1e9:.3f} GB/step)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, wl, W, ctx, pre, anchors, a_tab)
+
+    res = {
+        "metric": "draft+verify block steps/s & accepted tok/s at batch B; % of HBM/MFMA roofline",
+        "value": round(steps_per_s, 3),
+        "unit": "block steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if d.dtype == configs.BF16 else "f32",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps, planted targets)",
+        "config": {"workload": wl.name, "batch": B, "block_k": k, "context": int(ctx.max()),
+                   "window": d.window, "layers": d.n_layers, "hidden": d.hidden, "ffn": d.ffn,
+                   "vocab": V, "accept": [kind, q]},
+        "accepted_tok_s": round(accepted / elapsed, 1),
+        "committed_tok_s": round(committed / elapsed, 1),
+        "mean_accept": round(accepted / (args.steps * B), 4),
+        "planted_accept_matches": accepted == planted,
+        "step_roofline": {"bound": "hbm", "bytes_per_step": cost.bytes_total,
+                          "achieved_GBs": round(step_gbs, 1), "peak_GBs": HBM_PEAK_GBS,
+                          "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "gemm_kernel<bf16,*,EPI_ARGMAX> (final norm + LM head + argmax)",
+                     "bound": "hbm", "achieved": round(head_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(head_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_us": round(head_ms * 1e3, 2), "bytes_per_launch": cost.head_bytes},
+        "cpu_baseline": cpu,
+        "dev_error": err,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def prefill_taps(d, n_pre: int, r0: int, seed: int):
+    """Taps of prefill rows r0 .. r0 + n_max of every sequence (one seeded draw per chunk)."""
+    from block_diffusion_speculative_dflash_amd import synth
+    return synth.make_taps(d, min(d.max_inject_rows, n_pre - r0), seed=seed, stream=10_000 + r0,
+                           device="cuda")
+
+
+def cpu_baseline(args, wl, W, ctx, pre, anchors, a_tab):
+    """The fp64 oracle, as it stands, on this host: a bounded sample of the same
+    workload (sequence 0's block steps; at batch 1 that is the whole batch)."""
+    import torch
+    from block_diffusion_speculative_dflash_amd import synth
+    from oracle import dflash_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = None
+    d = wl.dims
+    k = d.block_k
+    cores = len(os.sched_getaffinity(0))
+    log(f"[bench] cpu baseline: oracle on sequence 0, {args.cpu_steps} block steps, {cores} cores")
+    Wn = {n: t.float().cpu().numpy() for n, t in W.items() if n != "packed"}
+    st = orc.new_state(d, batch=1, ctx_len=[int(ctx[0] - pre[0])], anchor=[int(anchors[0])])
+    n_pre, n_all = int(pre[0]), int(pre.max())
+    if n_pre:
+        rows = [prefill_taps(d, n_all, r0, args.seed)[:1] for r0 in range(0, n_all, d.max_inject_rows)]
+        taps = torch.cat(rows, dim=1)[:, :n_pre].float().cpu().numpy()
+        orc.fuse_inject(d, Wn, st, taps, [n_pre], commit=True)
+    taps_step = synth.make_taps(d, k + 1, seed=args.seed, stream=1, device="cuda")[:1].float().cpu().numpy()
+    fill = synth.target_fill(k, 1, 1, seed=args.seed + 1)[0]
+    t0 = time.perf_counter()
+    committed = 0
+    for s in range(args.cpu_steps):
+        o = orc.draft_step(d, Wn, st, want_logits=False)
+        T = synth.plant_targets(o["draft"], a_tab[s, :1], fill, d.vocab)
+        orc.fuse_inject(d, Wn, st, taps_step, [k + 1], commit=False)
+        r = orc.verify_commit(d, st, o["draft"], T)
+        committed += int(r["accept_len"][0]) + 1
+    dt = time.perf_counter() - t0
+    per_seq_step = dt / args.cpu_steps
+    steps_per_s = 1.0 / (per_seq_step * d.batch)   # a full-batch block step costs B sequence steps
+    return {"value": round(steps_per_s, 6), "unit": "block steps/s", "cores": cores,
+            "blas_threads": threads, "kind": "oracle",
+            "committed_tok_s": round(committed / dt, 4),
+            "seconds": round(dt, 2),
+            "sample": f"{args.cpu_steps} block steps of sequence 0 (of {d.batch}), fp64 numpy; "
+                      f"full-batch rate = per-sequence rate / {d.batch}"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -24,7 +24,7 @@ _INT_FIELDS = ("batch", "block_k", "n_layers", "hidden", "n_q_heads", "n_kv_head
                "ffn", "vocab", "n_taps", "tap_dim", "window", "cache_slots", "dtype",
                "max_inject_rows")
 WEIGHT_FIELDS = ("fuse_w", "fuse_norm", "embed", "mask_embed", "attn_norm", "w_qkv", "w_o",
-                 "mlp_norm", "w_gate_up", "w_down", "final_norm", "lm_head")
+                 "mlp_norm", "w_gate_up", "w_down", "final_norm", "lm_head", "packed")
 
 
 class DflashDims(ctypes.Structure):
@@ -49,8 +49,9 @@ class DFlashError(RuntimeError):
 
 _lib: Optional[ctypes.CDLL] = None
 
-EXPORTED = ("dflash_workspace_bytes", "dflash_status_string", "dflash_fuse_inject",
-            "dflash_draft_step", "dflash_verify_commit", "dflash_draft_step_timed")
+EXPORTED = ("dflash_workspace_bytes", "dflash_status_string", "dflash_packed_bytes",
+            "dflash_pack_weights", "dflash_fuse_inject", "dflash_draft_step",
+            "dflash_verify_commit", "dflash_draft_step_timed")
 
 
 def lib() -> ctypes.CDLL:
@@ -67,6 +68,11 @@ def lib() -> ctypes.CDLL:
     L.dflash_workspace_bytes.restype = S
     L.dflash_status_string.argtypes = [ctypes.c_int]
     L.dflash_status_string.restype = ctypes.c_char_p
+    L.dflash_packed_bytes.argtypes = [ctypes.POINTER(DflashDims)]
+    L.dflash_packed_bytes.restype = S
+    L.dflash_pack_weights.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashWeights), P, S,
+                                      P, P]
+    L.dflash_pack_weights.restype = ctypes.c_int
     L.dflash_fuse_inject.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashWeights), P, P,
                                      I, I, ctypes.POINTER(DflashCache), P, S, P]
     L.dflash_fuse_inject.restype = ctypes.c_int
@@ -102,7 +108,7 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def weights_struct(W: Dict[str, torch.Tensor]) -> DflashWeights:
-    return DflashWeights(**{n: _ptr(W[n]) for n in WEIGHT_FIELDS})
+    return DflashWeights(**{n: _ptr(W.get(n)) for n in WEIGHT_FIELDS})
 
 
 def cache_struct(cache: Dict[str, torch.Tensor]) -> DflashCache:
@@ -126,6 +132,34 @@ def dflash_workspace_bytes(dims: Dims) -> int:
     if n == 0:
         raise DFlashError("dflash_workspace_bytes", DFLASH_E_INVALID)
     return int(n)
+
+
+def dflash_packed_bytes(dims: Dims) -> int:
+    n = lib().dflash_packed_bytes(ctypes.byref(dims_struct(dims)))
+    if n == 0:
+        raise DFlashError("dflash_packed_bytes", DFLASH_E_INVALID)
+    return int(n)
+
+
+def dflash_pack_weights(dims: Dims, weights, packed: torch.Tensor, dev_error: torch.Tensor,
+                        stream=None) -> None:
+    ds, ws = dims_struct(dims), weights_struct(weights)
+    st = lib().dflash_pack_weights(ctypes.byref(ds), ctypes.byref(ws), _ptr(packed),
+                                   packed.numel() * packed.element_size(), _ptr(dev_error),
+                                   _stream(stream))
+    _check("dflash_pack_weights", st)
+
+
+def pack_weights(dims: Dims, weights: Dict[str, torch.Tensor], device="cuda") -> Dict[str, torch.Tensor]:
+    """Add the packed GEMM copy (dflash_pack_weights) to a weight dict, in place."""
+    packed = torch.empty(dflash_packed_bytes(dims), dtype=torch.uint8, device=device)
+    err = torch.zeros(1, dtype=torch.int32, device=device)
+    dflash_pack_weights(dims, weights, packed, err)
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise DFlashError("dflash_pack_weights (weight outside the fp16 range)", int(err.item()))
+    weights["packed"] = packed
+    return weights
 
 
 def dflash_fuse_inject(dims: Dims, weights, taps: torch.Tensor, n_rows: torch.Tensor, n_max: int,
@@ -167,8 +201,9 @@ def dflash_verify_commit(dims: Dims, draft: torch.Tensor, target: torch.Tensor, 
 
 # ----------------------------------------------------------------------------- buffers
 def alloc_cache(dims: Dims, device="cuda", ctx_len=None, anchor=None) -> Dict[str, torch.Tensor]:
-    """Caller-owned decode state: K/V rings, committed lengths, anchors, error word."""
-    dt = torch.bfloat16 if dims.dtype == BF16 else torch.float32
+    """Caller-owned decode state: K/V rings (fp16 for bf16 drafters, fp32 for fp32
+    drafters), committed lengths, anchors, error word."""
+    dt = cache_dtype(dims)
     shape = (dims.n_layers, dims.batch, dims.n_kv_heads, dims.cache_slots, dims.head_dim)
     B = dims.batch
 
@@ -181,6 +216,10 @@ def alloc_cache(dims: Dims, device="cuda", ctx_len=None, anchor=None) -> Dict[st
             "v": torch.zeros(shape, dtype=dt, device=device),
             "ctx_len": ints(ctx_len), "anchor": ints(anchor),
             "dev_error": torch.zeros(1, dtype=torch.int32, device=device)}
+
+
+def cache_dtype(dims: Dims) -> torch.dtype:
+    return torch.float16 if dims.dtype == BF16 else torch.float32
 
 
 def alloc_workspace(dims: Dims, device="cuda") -> torch.Tensor:

@@ -1,5 +1,5 @@
-// C ABI of libdflash: host-side validation, workspace layout, launch plans and
-// the kernel sequence of each call.  See include/dflash.h for the contract.
+// C ABI of libdflash: host-side validation, packed-weight and workspace layouts,
+// launch plans and the kernel sequence of each call.  See include/dflash.h.
 #include <algorithm>
 #include <cstring>
 
@@ -11,22 +11,24 @@ using namespace dflash;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr size_t kPartialCap = size_t(32) << 20;   // split-K partial tiles
+constexpr size_t kPartialCap = size_t(32) << 20;  // split-K partial tiles
 constexpr int kGemmCounters = 1 << 16;
-constexpr int kTargetWorkgroups = 512;             // 2 per CU on 256 CUs
+constexpr int kTargetWorkgroups = 512;            // 2 per CU on 256 CUs
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
+int round_up(int a, int b) { return cdiv(a, b) * b; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int elem_bytes(const dflash_dims& d) { return d.dtype == DFLASH_BF16 ? 2 : 4; }
+bool is_f32(const dflash_dims& d) { return d.dtype == DFLASH_F32; }
+size_t elem(const dflash_dims& d) { return is_f32(d) ? 4 : 2; }  // weights, activations, cache
 
 bool dims_ok(const dflash_dims* d) {
   if (d == nullptr) return false;
   if (d->batch < 1 || d->block_k < 1 || d->block_k > 63 || d->n_layers < 1) return false;
-  if (d->hidden < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return false;
+  if (d->hidden < 64 || d->hidden % 64 != 0 || d->n_q_heads < 1 || d->n_kv_heads < 1) return false;
   if (d->n_q_heads % d->n_kv_heads != 0) return false;
   if (d->head_dim != 64 && d->head_dim != 128) return false;
   if (d->ffn < 1 || d->vocab < 2 || d->n_taps < 1 || d->tap_dim < 1) return false;
@@ -40,6 +42,46 @@ bool dims_ok(const dflash_dims* d) {
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// packed weights: one region per matrix, [tiles][K steps][4][64][8]
+// ---------------------------------------------------------------------------
+struct Region {
+  size_t off;  // bytes
+  int tiles, S;
+};
+
+struct PackLayout {
+  Region fuse, lm;
+  Region qkv[64], o[64], gu[64], down[64];  // per layer (n_layers <= 64 checked)
+  size_t total;
+};
+
+bool pack_layout(const dflash_dims& d, PackLayout& P) {
+  if (d.n_layers > 64) return false;
+  const size_t e = elem(d);
+  size_t off = 0;
+  auto region = [&](int tiles, int K) {
+    Region r{off, tiles, ksteps(K)};
+    off = align_up(off + size_t(tiles) * r.S * kTileStepElems * e);
+    return r;
+  };
+  const int qkv_tiles = (d.n_q_heads + 2 * d.n_kv_heads) * (d.head_dim / kBN);
+  // Region sizes are multiples of one tile step (4 KB), so the QKV regions of all
+  // layers are contiguous: layer l's tiles follow layer l-1's (the injection GEMM
+  // walks the K/V head tiles of every layer with one stride).
+  P.fuse = region(cdiv(d.hidden, kBN), d.n_taps * d.tap_dim);
+  for (int l = 0; l < d.n_layers; ++l) P.qkv[l] = region(qkv_tiles, d.hidden);
+  for (int l = 0; l < d.n_layers; ++l) P.o[l] = region(cdiv(d.hidden, kBN), d.n_q_heads * d.head_dim);
+  for (int l = 0; l < d.n_layers; ++l) P.gu[l] = region(cdiv(d.ffn, kBN / 2), d.hidden);
+  for (int l = 0; l < d.n_layers; ++l) P.down[l] = region(cdiv(d.hidden, kBN), d.ffn);
+  P.lm = region(cdiv(d.vocab, kBN), d.hidden);
+  P.total = off;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// workspace
+// ---------------------------------------------------------------------------
 struct AttnPlan {
   int n_rb, kps, max_splits;
 };
@@ -48,11 +90,12 @@ AttnPlan attn_plan(const dflash_dims& d) {
   AttnPlan p;
   const int G = d.n_q_heads / d.n_kv_heads;
   p.n_rb = cdiv(G * d.block_k, 64);
+  // Split a group's keys over workgroups only when the groups alone leave the
+  // CUs idle and each split keeps >= 512 keys; splits need a merge launch.
   const int max_keys = d.window + d.block_k;
-  const double per_group = double(max_keys) * d.batch * d.n_kv_heads * p.n_rb / 1024.0;
-  int kps = std::max(64, int(per_group + 0.999));
-  kps = cdiv(kps, 32) * 32;
-  p.kps = std::min(kps, std::max(64, cdiv(max_keys, 32) * 32));
+  const double per_wg = double(max_keys) * d.batch * d.n_kv_heads * p.n_rb / 256.0;
+  const int kps = round_up(std::max(512, int(per_wg + 0.999)), 32);
+  p.kps = std::min(kps, round_up(max_keys, 32));
   p.max_splits = cdiv(max_keys, p.kps);
   return p;
 }
@@ -60,28 +103,32 @@ AttnPlan attn_plan(const dflash_dims& d) {
 struct Layout {
   size_t h, xa, ssq, q, kb, vb, o, act, cu, ssq_c, partials, counters, keys, attn_cnt, attn_o,
       attn_ml, total;
-  int np_d;
+  int np_d, S_d, S_o, S_f;
   AttnPlan ap;
 };
 
 Layout layout(const dflash_dims& d) {
   Layout L{};
-  const size_t sz = elem_bytes(d);
+  const size_t e = elem(d);
   const size_t Mb = size_t(d.batch) * d.block_k;
   const size_t Mi = size_t(d.batch) * d.max_inject_rows;
+  const size_t Mb64 = round_up(int(Mb), 64), Mi64 = round_up(int(Mi), 64);  // packed A row padding
   L.np_d = cdiv(d.hidden, kBN);
+  L.S_d = ksteps(d.hidden);
+  L.S_o = ksteps(d.n_q_heads * d.head_dim);
+  L.S_f = ksteps(d.ffn);
   L.ap = attn_plan(d);
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
   L.h = take(Mb * d.hidden * 4);
-  L.xa = take(Mb * d.hidden * sz);
+  L.xa = take(Mb64 * L.S_d * 32 * e);
   L.ssq = take(Mb * L.np_d * 4);
-  L.q = take(Mb * d.n_q_heads * d.head_dim * sz);
-  L.kb = take(Mb * d.n_kv_heads * d.head_dim * sz);
-  L.vb = take(Mb * d.n_kv_heads * d.head_dim * sz);
-  L.o = take(Mb * d.n_q_heads * d.head_dim * sz);
-  L.act = take(Mb * d.ffn * sz);
-  L.cu = take(Mi * d.hidden * sz);
+  L.q = take(Mb * d.n_q_heads * d.head_dim * e);
+  L.kb = take(Mb * d.n_kv_heads * d.head_dim * e);
+  L.vb = take(Mb * d.n_kv_heads * d.head_dim * e);
+  L.o = take(Mb64 * L.S_o * 32 * e);
+  L.act = take(Mb64 * L.S_f * 32 * e);
+  L.cu = take(Mi64 * L.S_d * 32 * e);
   L.ssq_c = take(Mi * L.np_d * 4);
   L.partials = take(kPartialCap);
   L.counters = take(size_t(kGemmCounters) * 4);
@@ -95,43 +142,41 @@ Layout layout(const dflash_dims& d) {
 }
 
 // Tile plan of one GEMM.  Split K only while the grid is below the target size,
-// every split keeps >= 256 elements, the partial tiles fit their region, and their
+// every split keeps >= 8 steps, the partial tiles fit their region, and their
 // traffic stays below a quarter of the weight bytes.
-GemmPlan gemm_plan(int M, int n_tiles, int K, int lda, int ldw, bool allow_split) {
+GemmPlan gemm_plan(int M, int n_tiles, int S, bool allow_split) {
   GemmPlan p{};
-  p.bm = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
-  p.m_tiles = cdiv(M, p.bm);
+  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  p.depth = p.mt == 4 ? 2 : 4;
+  p.m_tiles = cdiv(M, 16 * p.mt);
   p.n_tiles = n_tiles;
-  p.vec = (K % 8 == 0) && (lda % 8 == 0) && (ldw % 8 == 0);
   int splits = 1;
   if (allow_split) {
-    const int m_pad = p.m_tiles * p.bm;
+    const int m_pad = p.m_tiles * 16 * p.mt;
+    const int K = S * kKStep;
     while (true) {
       const int s2 = splits * 2;
-      const int ks = cdiv(cdiv(K, s2), 256) * 256;
       if (n_tiles * p.m_tiles * splits >= kTargetWorkgroups) break;
-      if (cdiv(K, ks) < s2) break;
+      if (cdiv(S, s2) < 8) break;
       if (double(s2) * M * n_tiles * kBN * 4 > double(kPartialCap)) break;
       if (s2 > std::max(1, K / (16 * m_pad))) break;
       if (size_t(p.m_tiles) * n_tiles > size_t(kGemmCounters)) break;
       splits = s2;
     }
   }
-  if (splits == 1) {
-    p.splits = 1;
-    p.k_split = K;
-  } else {
-    p.k_split = cdiv(cdiv(K, splits), 256) * 256;
-    p.splits = cdiv(K, p.k_split);
-  }
+  p.steps_per_split = cdiv(S, splits);
+  p.splits = cdiv(S, p.steps_per_split);
   return p;
 }
 
 struct Ctx {
   const dflash_dims& d;
   const Layout& L;
+  const PackLayout& P;
   char* ws;
+  const char* packed;
   template <typename X> X* at(size_t off) const { return reinterpret_cast<X*>(ws + off); }
+  const void* reg(const Region& r) const { return packed + r.off; }
 };
 
 GemmArgs base_args(const Ctx& c) {
@@ -152,17 +197,17 @@ GemmArgs base_args(const Ctx& c) {
   return a;
 }
 
-#define DF_CHECK(call)                        \
-  do {                                        \
+#define DF_CHECK(call)                             \
+  do {                                             \
     if ((call) != hipSuccess) return DFLASH_E_HIP; \
   } while (0)
 
 int run_gemm(int epi, const Ctx& c, GemmArgs a, bool allow_split, hipStream_t s) {
-  const GemmPlan p = gemm_plan(a.M, a.n_tiles, a.K, a.lda, a.ldw, allow_split);
+  const GemmPlan p = gemm_plan(a.M, a.n_tiles, a.S, allow_split);
   a.splits = p.splits;
-  a.k_split = p.k_split;
+  a.steps_per_split = p.steps_per_split;
   a.m_tiles = p.m_tiles;
-  DF_CHECK(launch_gemm(epi, elem_bytes(c.d), p, a, s));
+  DF_CHECK(launch_gemm(epi, is_f32(c.d), p, a, s));
   return DFLASH_OK;
 }
 
@@ -171,54 +216,52 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
                hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   if (!dims_ok(dims) || w == nullptr || cache == nullptr || draft == nullptr) return DFLASH_E_INVALID;
   const dflash_dims& d = *dims;
-  const void* wp[] = {w->embed, w->mask_embed, w->attn_norm, w->w_qkv, w->w_o, w->mlp_norm,
-                      w->w_gate_up, w->w_down, w->final_norm, w->lm_head};
+  const void* wp[] = {w->embed, w->mask_embed, w->attn_norm, w->mlp_norm, w->final_norm, w->packed};
   for (const void* p : wp)
     if (p == nullptr || !aligned16(p)) return DFLASH_E_INVALID;
   if (!cache->k || !cache->v || !aligned16(cache->k) || !aligned16(cache->v)) return DFLASH_E_INVALID;
   if (!cache->ctx_len || !cache->anchor || !cache->dev_error || !aligned4(draft)) return DFLASH_E_INVALID;
   if (logits_out != nullptr && !aligned4(logits_out)) return DFLASH_E_INVALID;
+  PackLayout P;
+  if (!pack_layout(d, P)) return DFLASH_E_UNSUPPORTED;
   const Layout L = layout(d);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < L.total) return DFLASH_E_WORKSPACE;
 
-  const Ctx c{d, L, static_cast<char*>(workspace)};
-  const int sz = elem_bytes(d);
+  const Ctx c{d, L, P, static_cast<char*>(workspace), static_cast<const char*>(w->packed)};
+  const bool f32 = is_f32(d);
+  const size_t e = elem(d);
   const int D = d.hidden, k = d.block_k, B = d.batch, F = d.ffn;
   const int Mb = B * k;
-  const int qkv_rows = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
   const int hq_dh = d.n_q_heads * d.head_dim;
-  const size_t layer_cache = size_t(B) * d.n_kv_heads * d.cache_slots * d.head_dim * sz;
-  auto wl = [&](const void* base, size_t elems_per_layer, int l) {
-    return static_cast<const char*>(base) + size_t(l) * elems_per_layer * sz;
-  };
+  const size_t layer_cache = size_t(B) * d.n_kv_heads * d.cache_slots * d.head_dim * e;
+  auto gain = [&](const void* base, int l) { return static_cast<const char*>(base) + size_t(l) * D * e; };
 
-  EmbedArgs e{};
-  e.anchor = cache->anchor;
-  e.ctx_len = cache->ctx_len;
-  e.embed = w->embed;
-  e.mask_embed = w->mask_embed;
-  e.gain = w->attn_norm;
-  e.h = c.at<float>(L.h);
-  e.xa = c.at<void>(L.xa);
-  e.ssq = c.at<float>(L.ssq);
-  e.batch = B;
-  e.block_k = k;
-  e.hidden = D;
-  e.vocab = d.vocab;
-  e.dev_error = cache->dev_error;
-  DF_CHECK(launch_embed(sz, e, stream));
+  EmbedArgs em{};
+  em.anchor = cache->anchor;
+  em.ctx_len = cache->ctx_len;
+  em.embed = w->embed;
+  em.mask_embed = w->mask_embed;
+  em.gain = w->attn_norm;
+  em.h = c.at<float>(L.h);
+  em.xa = c.at<void>(L.xa);
+  em.ssq = c.at<float>(L.ssq);
+  em.batch = B;
+  em.block_k = k;
+  em.hidden = D;
+  em.vocab = d.vocab;
+  em.dev_error = cache->dev_error;
+  DF_CHECK(launch_embed(f32, em, stream));
 
   for (int l = 0; l < d.n_layers; ++l) {
     // RMSNorm + fused QKV projection + RoPE
     GemmArgs a = base_args(c);
     a.A = c.at<void>(L.xa);
-    a.lda = D;
     a.M = Mb;
     a.K = D;
-    a.W = wl(w->w_qkv, size_t(qkv_rows) * D, l);
-    a.ldw = D;
-    a.N = qkv_rows;
-    a.n_tiles = qkv_rows / kBN;
+    a.S = L.S_d;
+    a.W = c.reg(P.qkv[l]);
+    a.N = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+    a.n_tiles = P.qkv[l].tiles;
     a.ssq_in = c.at<float>(L.ssq);
     a.np_in = l == 0 ? 1 : L.np_d;
     a.out = c.at<void>(L.q);
@@ -237,6 +280,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     at.cache_v = static_cast<const char*>(cache->v) + size_t(l) * layer_cache;
     at.ctx_len = cache->ctx_len;
     at.out = c.at<void>(L.o);
+    at.out_steps = L.S_o;
     at.part_o = c.at<float>(L.attn_o);
     at.part_ml = c.at<float>(L.attn_ml);
     at.counters = c.at<unsigned>(L.attn_cnt);
@@ -250,22 +294,21 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     at.keys_per_split = L.ap.kps;
     at.max_splits = L.ap.max_splits;
     at.n_rb = L.ap.n_rb;
-    DF_CHECK(launch_attention(sz, at, stream));
+    DF_CHECK(launch_attention(f32, at, stream));
 
     // output projection + residual; produces the MLP's RMSNorm input
     a = base_args(c);
     a.A = c.at<void>(L.o);
-    a.lda = hq_dh;
     a.M = Mb;
     a.K = hq_dh;
-    a.W = wl(w->w_o, size_t(D) * hq_dh, l);
-    a.ldw = hq_dh;
+    a.S = L.S_o;
+    a.W = c.reg(P.o[l]);
     a.N = D;
-    a.n_tiles = L.np_d;
+    a.n_tiles = P.o[l].tiles;
     a.h = c.at<float>(L.h);
     a.out = c.at<void>(L.xa);
-    a.ldo = D;
-    a.gain = wl(w->mlp_norm, D, l);
+    a.out_steps = L.S_d;
+    a.gain = gain(w->mlp_norm, l);
     a.ssq_out = c.at<float>(L.ssq);
     a.np_out = L.np_d;
     if (int st = run_gemm(EPI_RESID, c, a, true, stream)) return st;
@@ -273,33 +316,31 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     // RMSNorm + gate/up projection + SwiGLU
     a = base_args(c);
     a.A = c.at<void>(L.xa);
-    a.lda = D;
     a.M = Mb;
     a.K = D;
-    a.W = wl(w->w_gate_up, size_t(2) * F * D, l);
-    a.ldw = D;
+    a.S = L.S_d;
+    a.W = c.reg(P.gu[l]);
     a.N = F;
-    a.n_tiles = cdiv(F, kBN / 2);
+    a.n_tiles = P.gu[l].tiles;
     a.ssq_in = c.at<float>(L.ssq);
     a.np_in = L.np_d;
     a.out = c.at<void>(L.act);
-    a.ldo = F;
+    a.out_steps = L.S_f;
     if (int st = run_gemm(EPI_SWIGLU, c, a, true, stream)) return st;
 
     // down projection + residual; produces the next RMSNorm input
     a = base_args(c);
     a.A = c.at<void>(L.act);
-    a.lda = F;
     a.M = Mb;
     a.K = F;
-    a.W = wl(w->w_down, size_t(D) * F, l);
-    a.ldw = F;
+    a.S = L.S_f;
+    a.W = c.reg(P.down[l]);
     a.N = D;
-    a.n_tiles = L.np_d;
+    a.n_tiles = P.down[l].tiles;
     a.h = c.at<float>(L.h);
     a.out = c.at<void>(L.xa);
-    a.ldo = D;
-    a.gain = l + 1 < d.n_layers ? wl(w->attn_norm, D, l + 1) : w->final_norm;
+    a.out_steps = L.S_d;
+    a.gain = l + 1 < d.n_layers ? gain(w->attn_norm, l + 1) : w->final_norm;
     a.ssq_out = c.at<float>(L.ssq);
     a.np_out = L.np_d;
     if (int st = run_gemm(EPI_RESID, c, a, true, stream)) return st;
@@ -308,13 +349,12 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   // final RMSNorm + LM head + split-vocab argmax
   GemmArgs a = base_args(c);
   a.A = c.at<void>(L.xa);
-  a.lda = D;
   a.M = Mb;
   a.K = D;
-  a.W = w->lm_head;
-  a.ldw = D;
+  a.S = L.S_d;
+  a.W = c.reg(P.lm);
   a.N = d.vocab;
-  a.n_tiles = cdiv(d.vocab, kBN);
+  a.n_tiles = P.lm.tiles;
   a.ssq_in = c.at<float>(L.ssq);
   a.np_in = L.np_d;
   a.keys = c.at<unsigned long long>(L.keys);
@@ -335,6 +375,12 @@ size_t dflash_workspace_bytes(const dflash_dims* dims) {
   return layout(*dims).total;
 }
 
+size_t dflash_packed_bytes(const dflash_dims* dims) {
+  PackLayout P;
+  if (!dims_ok(dims) || !pack_layout(*dims, P)) return 0;
+  return P.total;
+}
+
 const char* dflash_status_string(int status) {
   switch (status) {
     case DFLASH_OK: return "ok";
@@ -346,6 +392,50 @@ const char* dflash_status_string(int status) {
   }
 }
 
+int dflash_pack_weights(const dflash_dims* dims, const dflash_weights* w, void* packed,
+                        size_t packed_bytes, uint32_t* dev_error, hipStream_t stream) {
+  if (!dims_ok(dims) || w == nullptr || packed == nullptr || !aligned16(packed)) return DFLASH_E_INVALID;
+  const dflash_dims& d = *dims;
+  PackLayout P;
+  if (!pack_layout(d, P)) return DFLASH_E_UNSUPPORTED;
+  if (packed_bytes < P.total) return DFLASH_E_INVALID;
+  const void* src[] = {w->fuse_w, w->w_qkv, w->w_o, w->w_gate_up, w->w_down, w->lm_head};
+  for (const void* p : src)
+    if (p == nullptr || !aligned16(p)) return DFLASH_E_INVALID;
+  if (dev_error == nullptr) return DFLASH_E_INVALID;
+  const bool f32 = is_f32(d);
+  const size_t e = elem(d);
+  char* base = static_cast<char*>(packed);
+  const int D = d.hidden, F = d.ffn;
+  const int qkv_rows = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
+  const int hq_dh = d.n_q_heads * d.head_dim;
+  auto pack = [&](const Region& r, const void* srcp, int K, int N, int kind, int dst_f16) {
+    PackArgs a{};
+    a.src = srcp;
+    a.K = K;
+    a.N = N;
+    a.n_tiles = r.tiles;
+    a.S = r.S;
+    a.kind = kind;
+    a.head_dim = d.head_dim;
+    a.ffn = F;
+    a.dst = base + r.off;
+    a.dst_f16 = dst_f16;
+    a.dev_error = dev_error;
+    return launch_pack(f32, a, stream);
+  };
+  auto layer = [&](const void* p, size_t elems, int l) { return static_cast<const char*>(p) + size_t(l) * elems * e; };
+  DF_CHECK(pack(P.fuse, w->fuse_w, d.n_taps * d.tap_dim, D, PACK_PLAIN, 0));
+  for (int l = 0; l < d.n_layers; ++l) {
+    DF_CHECK(pack(P.qkv[l], layer(w->w_qkv, size_t(qkv_rows) * D, l), D, qkv_rows, PACK_HEADS, 1));
+    DF_CHECK(pack(P.o[l], layer(w->w_o, size_t(D) * hq_dh, l), hq_dh, D, PACK_PLAIN, 1));
+    DF_CHECK(pack(P.gu[l], layer(w->w_gate_up, size_t(2) * F * D, l), D, F, PACK_SWIGLU, 1));
+    DF_CHECK(pack(P.down[l], layer(w->w_down, size_t(D) * F, l), F, D, PACK_PLAIN, 1));
+  }
+  DF_CHECK(pack(P.lm, w->lm_head, D, d.vocab, PACK_PLAIN, 1));
+  return DFLASH_OK;
+}
+
 int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const void* taps,
                        const int32_t* n_rows, int32_t n_max, int32_t commit,
                        const dflash_cache* cache, void* workspace, size_t workspace_bytes,
@@ -354,44 +444,48 @@ int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const v
   const dflash_dims& d = *dims;
   if (taps == nullptr || !aligned16(taps) || n_rows == nullptr || !aligned4(n_rows)) return DFLASH_E_INVALID;
   if (n_max < 1 || n_max > d.max_inject_rows || (commit != 0 && commit != 1)) return DFLASH_E_INVALID;
-  if (!w->fuse_w || !w->fuse_norm || !w->w_qkv || !aligned16(w->fuse_w) || !aligned16(w->fuse_norm) ||
-      !aligned16(w->w_qkv))
-    return DFLASH_E_INVALID;
+  if (!w->fuse_norm || !w->packed || !aligned16(w->fuse_norm) || !aligned16(w->packed)) return DFLASH_E_INVALID;
   if (!cache->k || !cache->v || !aligned16(cache->k) || !aligned16(cache->v)) return DFLASH_E_INVALID;
   if (!cache->ctx_len || !cache->dev_error) return DFLASH_E_INVALID;
+  PackLayout P;
+  if (!pack_layout(d, P)) return DFLASH_E_UNSUPPORTED;
   const Layout L = layout(d);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < L.total) return DFLASH_E_WORKSPACE;
 
-  const Ctx c{d, L, static_cast<char*>(workspace)};
+  const Ctx c{d, L, P, static_cast<char*>(workspace), static_cast<const char*>(w->packed)};
   const int D = d.hidden;
   const int Mi = d.batch * n_max;
   const int K = d.n_taps * d.tap_dim;
+  const int tph = d.head_dim / kBN;
 
   GemmArgs a = base_args(c);
   a.A = taps;
   a.lda = K;
   a.M = Mi;
   a.K = K;
-  a.W = w->fuse_w;
-  a.ldw = K;
+  a.S = P.fuse.S;
+  a.W = c.reg(P.fuse);
   a.N = D;
-  a.n_tiles = L.np_d;
+  a.n_tiles = P.fuse.tiles;
   a.out = c.at<void>(L.cu);
-  a.ldo = D;
+  a.out_steps = L.S_d;
   a.gain = w->fuse_norm;
   a.ssq_out = c.at<float>(L.ssq_c);
   a.np_out = L.np_d;
   if (int st = run_gemm(EPI_FUSE, c, a, true, stream)) return st;
 
+  // K/V injection: the K and V head tiles of every layer's packed QKV region
   a = base_args(c);
   a.A = c.at<void>(L.cu);
-  a.lda = D;
   a.M = Mi;
   a.K = D;
-  a.W = w->w_qkv;
-  a.ldw = D;
+  a.S = L.S_d;
+  a.W = c.reg(P.qkv[0]);
+  a.layer_tiles = P.qkv[0].tiles;
+  a.inj_tile0 = d.n_q_heads * tph;
+  a.inj_tiles = 2 * d.n_kv_heads * tph;
   a.N = d.n_layers * 2 * d.n_kv_heads * d.head_dim;
-  a.n_tiles = a.N / kBN;
+  a.n_tiles = d.n_layers * a.inj_tiles;
   a.ssq_in = c.at<float>(L.ssq_c);
   a.np_in = L.np_d;
   a.rows_per_seq = n_max;

@@ -9,6 +9,8 @@ namespace dflash {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -16,11 +18,27 @@ constexpr int kThreads = 256;  // 4 wavefronts per workgroup everywhere
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ float to_f32(f16 x) { return static_cast<float>(x); }
 
+// round to nearest even
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
-template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
-  return static_cast<bf16>(x);  // round to nearest even
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return static_cast<f16>(x); }
+
+// Activation / compute type of a drafter whose weights arrive as T: bf16 drafters
+// compute in fp16, fp32 drafters in fp32.
+template <typename T> struct ActOf;
+template <> struct ActOf<bf16> { typedef f16 type; };
+template <> struct ActOf<float> { typedef float type; };
+
+// Element offset of (row m, reduction index k) in a fragment-packed operand:
+// [m / 16][k / 32][lane][8] with lane = 16 * ((k % 32) / 8) + m % 16, i.e. one
+// 32-wide K step of 16 rows is 64 lanes x 8 contiguous elements, exactly the
+// MFMA operand a wavefront loads with one 16-byte load per lane.
+__host__ __device__ __forceinline__ size_t pa_index(int m, int k, int ksteps) {
+  return ((static_cast<size_t>(m >> 4) * ksteps + (k >> 5)) * 64 + (((k & 31) >> 3) * 16 + (m & 15))) * 8 +
+         (k & 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -45,6 +63,20 @@ template <> struct Frag<bf16> {
   // acc[16x16] += A[16x32] * B[32x16]; lane holds A row (l%16) and B column (l%16)
   static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+  }
+};
+
+template <> struct Frag<f16> {
+  f16x8 v;
+  __device__ __forceinline__ void zero() {
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<f16>(0.0f);
+  }
+  __device__ __forceinline__ void load(const f16* p) { v = *reinterpret_cast<const f16x8*>(p); }
+  __device__ __forceinline__ void load_masked(const f16* p, int valid) {
+    for (int i = 0; i < 8; ++i) v[i] = (i < valid) ? p[i] : static_cast<f16>(0.0f);
+  }
+  static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
   }
 };
 
@@ -104,6 +136,38 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
 
 __device__ __forceinline__ int argmax_key_index(unsigned long long key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFull));
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup hand-off without cache maintenance.  Data another workgroup
+// will read inside the same kernel is written with device-coherent (agent-scope)
+// stores and read with device-coherent loads; the writer waits for its stores to
+// complete before it bumps the arrival counter (an atomic), so the workgroup that
+// sees the last arrival also sees every store.  Agent-scope fences, which write
+// back and invalidate the L2 of the CU's XCD, are never used: at one per
+// workgroup they cost more than the work itself.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// All of this thread's memory operations have completed.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+// Arrival counter: returns true in exactly one thread block, the last of `expected`.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, int* flag_lds) {
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag_lds = prev == expected - 1;
+  }
+  __syncthreads();
+  return *flag_lds != 0;
+}
+__device__ __forceinline__ void reset_counter(unsigned* counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,4 +1,12 @@
 // Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+//
+// Element types.  A drafter whose caller-facing dtype is bf16 keeps weights and
+// taps in bf16 but computes in fp16: the packed weight copy, the activations that
+// feed MFMA, q/k/v and the K/V cache are fp16 (bf16 values in fp16's normal range
+// convert exactly; fp16 rounds 8x finer than bf16 at the same bytes and MFMA
+// rate), accumulation and the residual stream are fp32.  The fusion GEMM multiplies
+// the caller's bf16 taps by a bf16 packed copy of fuse_w, both exact.  An fp32
+// drafter is fp32 throughout.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,33 +15,32 @@
 
 namespace dflash {
 
-// Epilogues of the weight-streaming GEMM; each fuses the step that follows the
-// projection so no intermediate makes an extra HBM round trip.
 enum Epi : int {
-  EPI_FUSE = 0,    // fused feature: cu = u * fuse_norm (bf16/f32) + per-tile sum of u^2
-  EPI_INJECT = 1,  // K/V injection: scale by RMSNorm factor, RoPE on K, write ring slots
-  EPI_QKV = 2,     // block q/k/v: scale by RMSNorm factor, RoPE on q and k
-  EPI_RESID = 3,   // residual add into h, next RMSNorm input h*g + per-tile sum of h^2
-  EPI_SWIGLU = 4,  // silu(gate) * up with the RMSNorm factor applied to both
-  EPI_ARGMAX = 5,  // logits = scale * acc, split-vocab argmax, optional logits out
+  EPI_FUSE = 0,    // fused feature: cu = u * fuse_norm (packed) + per-tile sum of u^2
+  EPI_INJECT = 1,  // K/V injection: RMSNorm factor, RoPE on K, write ring slots
+  EPI_QKV = 2,     // block q/k/v: RMSNorm factor, RoPE on q and k
+  EPI_RESID = 3,   // residual add into h, next RMSNorm input h*g (packed) + per-tile sum of h^2
+  EPI_SWIGLU = 4,  // silu(gate) * up with the RMSNorm factor applied to both (packed)
+  EPI_ARGMAX = 5,  // logits = factor * acc, split-vocab argmax, optional logits out
 };
 
-constexpr int kBN = 64;      // output columns per workgroup tile
-constexpr int kKStep = 32;   // reduction elements per MFMA step
+constexpr int kBN = 64;           // output columns per workgroup tile (4 MFMA column blocks)
+constexpr int kKStep = 32;        // reduction elements per MFMA step
+constexpr int kTileStepElems = 4 * 512;  // one packed weight tile step: 4 fragments x 64 lanes x 8
 
-// Everything any epilogue needs; unused fields stay zero.
+inline int ksteps(int K) { return (K + kKStep - 1) / kKStep; }
+
 struct GemmArgs {
-  // A operand: activations [M, K], row stride lda elements
+  // A operand: fragment-packed [M/16][S][64][8] activations, or (fusion GEMM only)
+  // the caller's row-major taps with row stride lda
   const void* A;
-  int lda, M, K;
-  // B operand: weight rows; how a tile column maps to a row depends on the epilogue
+  int lda, M, K, S;
+  // B operand: packed weight region; tile t starts at W + wtile(t) * S * kTileStepElems
   const void* W;
-  int ldw;        // row stride of W (elements)
-  int N;          // real output columns (F for SWIGLU, V for ARGMAX)
-  int n_tiles;    // workgroup tiles along N
-  int m_tiles;
+  int N, n_tiles, m_tiles;
+  int layer_tiles, inj_tile0, inj_tiles;  // INJECT: K/V head tiles inside per-layer QKV regions
   // split-K
-  int splits, k_split;
+  int splits, steps_per_split;
   float* partials;     // [splits, M, n_tiles * kBN] fp32
   unsigned* counters;  // zero-initialised; one per (m tile, n tile), or per m tile (ARGMAX)
   // RMSNorm of the A rows, folded into the epilogue as a per-row factor
@@ -41,39 +48,56 @@ struct GemmArgs {
   int np_in, norm_dim;
   float eps;
   // next RMSNorm input produced by FUSE / RESID
-  float* ssq_out;    // [M, np_out]
+  float* ssq_out;  // [M, np_out]
   int np_out;
-  const void* gain;  // [N] gain of the next RMSNorm (fuse_norm, mlp_norm, ...)
+  const void* gain;  // [N] gain of the next RMSNorm, caller's weight type
   // outputs
-  void* out;   // FUSE: cu [M, N]; RESID: x = h*g [M, N]; SWIGLU: act [M, ldo]; QKV: q
-  int ldo;
-  void* out2;  // QKV: block k  [M, Hkv, dh]
-  void* out3;  // QKV: block v  [M, Hkv, dh]
-  float* h;    // RESID: residual stream [M, N] fp32
-  // geometry of QKV / INJECT
-  int rows_per_seq;         // k (QKV) or n_max (INJECT)
-  const int32_t* ctx_len;   // [B]
-  const int32_t* n_rows;    // [B] (INJECT)
+  void* out;      // FUSE cu, RESID x, SWIGLU act: packed with out_steps K steps; QKV: q rows
+  int out_steps;
+  void* out2;     // QKV: block k  [M, Hkv, dh]
+  void* out3;     // QKV: block v  [M, Hkv, dh]
+  float* h;       // RESID: residual stream [M, N] fp32
+  int rows_per_seq;        // k (QKV) or n_max (INJECT)
+  const int32_t* ctx_len;  // [B]
+  const int32_t* n_rows;   // [B] (INJECT)
   int n_q_heads, n_kv_heads, head_dim, n_layers, batch, cache_slots, ffn;
   float theta;
   void* cache_k;  // [L, B, Hkv, C, dh]
   void* cache_v;
-  // ARGMAX
-  unsigned long long* keys;  // [M] zero-initialised argmax keys
+  unsigned long long* keys;  // [M] zero-initialised argmax keys (ARGMAX)
   int32_t* draft;            // [M]
   float* logits;             // [M, N] or nullptr
   uint32_t* dev_error;
 };
 
 struct GemmPlan {
-  int bm, m_tiles, n_tiles, splits, k_split;
-  bool vec;  // rows 16-byte aligned and K multiple of 8: vector loads
+  int mt;       // 16-row MFMA blocks per workgroup (1, 2 or 4)
+  int m_tiles, n_tiles, splits, steps_per_split, depth;
 };
 
-// elem_bytes: 2 (bf16) or 4 (f32)
-hipError_t launch_gemm(int epi, int elem_bytes, const GemmPlan& plan, const GemmArgs& args,
+// f32: true for an fp32 drafter, false for a bf16 drafter (fp16 compute)
+hipError_t launch_gemm(int epi, bool f32, const GemmPlan& plan, const GemmArgs& args,
                        hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// weight packing
+// ---------------------------------------------------------------------------
+enum PackKind : int {
+  PACK_PLAIN = 0,   // tile column c -> row tile*64 + c
+  PACK_SWIGLU = 1,  // 32 gate rows then the 32 matching up rows
+  PACK_HEADS = 2,   // per head: 32 RoPE pairs (dim, dim + dh/2) per tile
+};
+
+struct PackArgs {
+  const void* src;  // [rows, K] row-major, caller's type
+  int K, N, n_tiles, S, kind, head_dim, ffn;
+  void* dst;        // packed [n_tiles][S][4][64][8]
+  int dst_f16;      // bf16 source -> 1: fp16 copy, 0: bf16 copy (float source: float copy)
+  uint32_t* dev_error;
+};
+hipError_t launch_pack(bool f32, const PackArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
 struct EmbedArgs {
   const int32_t* anchor;   // [B]
   const int32_t* ctx_len;  // [B] (checked only)
@@ -81,12 +105,12 @@ struct EmbedArgs {
   const void* mask_embed;  // [d]
   const void* gain;        // attn_norm of layer 0 [d]
   float* h;                // [M, d]
-  void* xa;                // [M, d]
+  void* xa;                // packed [M/16][d/32][64][8]
   float* ssq;              // [M, 1]
   int batch, block_k, hidden, vocab;
   uint32_t* dev_error;
 };
-hipError_t launch_embed(int elem_bytes, const EmbedArgs& a, hipStream_t stream);
+hipError_t launch_embed(bool f32, const EmbedArgs& a, hipStream_t stream);
 
 struct AttnArgs {
   const void* q;   // [B*k, Hq, dh]
@@ -95,14 +119,15 @@ struct AttnArgs {
   const void* cache_k;  // layer base: [B, Hkv, C, dh]
   const void* cache_v;
   const int32_t* ctx_len;
-  void* out;  // [B*k, Hq*dh]
+  void* out;       // packed [B*k / 16][Hq*dh / 32][64][8]
+  int out_steps;
   float* part_o;   // [B, Hkv, n_rb, max_splits, 64, dh]
   float* part_ml;  // [B, Hkv, n_rb, max_splits, 64, 2]
   unsigned* counters;  // [B, Hkv, n_rb]
   int batch, block_k, n_q_heads, n_kv_heads, head_dim, cache_slots, window;
   int keys_per_split, max_splits, n_rb;
 };
-hipError_t launch_attention(int elem_bytes, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attention(bool f32, const AttnArgs& a, hipStream_t stream);
 
 struct VerifyArgs {
   const int32_t* draft;   // [B, k]

@@ -11,6 +11,7 @@ namespace dflash {
 // the row's sum of squares (one partial per row).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
+  typedef typename ActOf<T>::type TA;
   __shared__ float red[kThreads / kWave];
   const int m = blockIdx.x;
   const int b = m / a.block_k, i = m % a.block_k;
@@ -24,14 +25,19 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
   const T* src = i == 0 ? static_cast<const T*>(a.embed) + static_cast<size_t>(tok) * d
                         : static_cast<const T*>(a.mask_embed);
   const T* gain = static_cast<const T*>(a.gain);
-  T* xa = static_cast<T*>(a.xa) + static_cast<size_t>(m) * d;
+  TA* xa = static_cast<TA*>(a.xa);
   float* h = a.h + static_cast<size_t>(m) * d;
+  const int steps = (d + kKStep - 1) / kKStep;
   float ss = 0.f;
-  for (int n = threadIdx.x; n < d; n += kThreads) {
-    const float v = to_f32(src[n]);
-    h[n] = v;
-    xa[n] = from_f32<T>(v * to_f32(gain[n]));
-    ss += v * v;
+  for (int n0 = threadIdx.x * 8; n0 < d; n0 += kThreads * 8) {  // d is a multiple of 64
+    TA* dst = xa + pa_index(m, n0, steps);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = to_f32(src[n0 + j]);
+      h[n0 + j] = v;
+      dst[j] = from_f32<TA>(v * to_f32(gain[n0 + j]));
+      ss += v * v;
+    }
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -43,9 +49,9 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
   }
 }
 
-hipError_t launch_embed(int elem_bytes, const EmbedArgs& a, hipStream_t stream) {
+hipError_t launch_embed(bool f32, const EmbedArgs& a, hipStream_t stream) {
   const dim3 grid(a.batch * a.block_k);
-  if (elem_bytes == 2) hipLaunchKernelGGL(embed_kernel<bf16>, grid, dim3(kThreads), 0, stream, a);
+  if (!f32) hipLaunchKernelGGL(embed_kernel<bf16>, grid, dim3(kThreads), 0, stream, a);
   else hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

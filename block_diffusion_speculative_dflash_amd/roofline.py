@@ -1,0 +1,51 @@
+"""Algorithmic bytes and FLOPs of one block step (draft + inject + verify).
+
+Counted: every weight matrix once per call that uses it (so the K/V rows of w_qkv
+count in both the injection and the draft), the committed K/V window each layer
+reads, the new K/V rows, the taps, the embedding row of each anchor, and tokens.
+Not counted: activations between kernels (fusible) and logits (never written).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from .configs import BF16, Dims
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3
+
+
+@dataclass
+class StepCost:
+    bytes_total: float
+    flops_total: float
+    bytes_weights: float
+    bytes_kv_read: float
+    bytes_kv_write: float
+    bytes_taps: float
+    head_bytes: float   # final-norm + LM-head + argmax kernel, per launch
+    head_flops: float
+
+
+def step_cost(d: Dims, mean_ctx: float) -> StepCost:
+    e = 2 if d.dtype == BF16 else 4
+    B, k, L, D = d.batch, d.block_k, d.n_layers, d.hidden
+    Hq, Hkv, dh, F, V = d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn, d.vocab
+    kv_rows = 2 * Hkv * dh
+    p_fuse = D * d.n_taps * d.tap_dim
+    p_inject = L * kv_rows * D
+    p_layer = (Hq + 2 * Hkv) * dh * D + D * Hq * dh + 2 * F * D + D * F
+    p_head = V * D
+    weights = (p_fuse + p_inject + L * p_layer + p_head + 2 * L * D + 3 * D) * e
+    n_ctx = min(mean_ctx, d.window)
+    kv_read = L * B * n_ctx * kv_rows * e
+    kv_write = L * B * (k + 1) * kv_rows * e
+    taps = B * (k + 1) * d.n_taps * d.tap_dim * e
+    tokens = B * (k + (k + 1) * 3 + 4) * 4 + B * D * e
+    rows_d, rows_i = B * k, B * (k + 1)
+    flops = (2 * rows_d * (L * p_layer + p_head) + 4 * rows_d * L * Hq * dh * (n_ctx + k)
+             + 2 * rows_i * (p_fuse + p_inject))
+    head_bytes = p_head * e + rows_d * D * e + rows_d * 4 * ((D + 63) // 64) + rows_d * 4
+    return StepCost(weights + kv_read + kv_write + taps + tokens, flops, weights, kv_read,
+                    kv_write, taps, head_bytes, 2.0 * rows_d * p_head)

@@ -30,8 +30,15 @@
  *     length) are clamped into range and OR-ed into *cache->dev_error as the
  *     DFLASH_DEVERR_* bits.  The caller reads that word after synchronising.
  *   - Matrices use the nn.Linear layout [out, in], row-major, rows contiguous.
- *   - dims->dtype selects the element type of weights, taps and the K/V cache:
- *     DFLASH_BF16 (bfloat16) or DFLASH_F32 (float).  Token ids are int32.
+ *   - dims->dtype is the element type of the caller's weights and taps:
+ *     DFLASH_BF16 (bfloat16) or DFLASH_F32 (float).  A bf16 drafter computes in
+ *     fp16 with fp32 accumulation: its K/V cache, q/k/v and the activations that
+ *     feed the matrix cores are fp16 (bf16 weights convert to fp16 exactly inside
+ *     fp16's normal range, and fp16 rounds 8x finer than bf16 at the same bytes);
+ *     the residual stream is fp32.  An fp32 drafter is fp32 throughout.  Token ids
+ *     are int32.
+ *   - The GEMM weights are read from a packed copy (dflash_pack_weights), laid out
+ *     so every wavefront load is 1 KB of contiguous memory.
  *   - Order of one decode round: dflash_draft_step -> (target model verifies) ->
  *     dflash_fuse_inject(commit = 0) -> dflash_verify_commit.  The K/V rows for the
  *     k+1 positions the target just processed are written as tentative rows, and
@@ -64,6 +71,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 #define DFLASH_DEVERR_TOKEN 1u   /* anchor, draft or target token outside [0, vocab): clamped */
 #define DFLASH_DEVERR_ROWS 2u    /* n_rows[b] outside [0, n_max]: clamped */
 #define DFLASH_DEVERR_CTXLEN 4u  /* ctx_len[b] negative: treated as 0 */
+#define DFLASH_DEVERR_RANGE 8u   /* a bf16 weight beyond the fp16 range: saturated when packed */
 
 /* (host) Static shapes of one drafter; read during a call only.
  *   batch B, block_k k (1..63), n_layers L, hidden d, n_q_heads Hq, n_kv_heads Hkv
@@ -79,7 +87,7 @@ typedef struct {
 } dflash_dims;
 
 /* (host) Device pointers to the drafter weights, all in dims->dtype, all
- * 16-byte aligned, no biases:
+ * 16-byte aligned, no biases (hidden must be a multiple of 64):
  *   fuse_w [d, n_taps*d_t]   projection of the concatenated taps (ascending depth)
  *   fuse_norm [d]            RMSNorm gain of the fused feature
  *   embed [V, d]             token embedding (the anchor row)
@@ -92,14 +100,21 @@ typedef struct {
  *   w_gate_up [L, 2F, d]     SwiGLU gate rows (first F) then up rows
  *   w_down [L, d, F]         SwiGLU down projection
  *   final_norm [d]           RMSNorm gain before the LM head
- *   lm_head [V, d]           LM head (independent of embed) */
+ *   lm_head [V, d]           LM head (independent of embed)
+ *   packed                   dflash_packed_bytes(dims) bytes written by
+ *                            dflash_pack_weights from the six matrices above
+ *                            (fuse_w, w_qkv, w_o, w_gate_up, w_down, lm_head).
+ * dflash_fuse_inject and dflash_draft_step read those six matrices only through
+ * `packed`; after packing they may be freed (set to NULL).  embed, mask_embed and
+ * the norm gains are always read directly. */
 typedef struct {
   const void *fuse_w, *fuse_norm, *embed, *mask_embed, *attn_norm, *w_qkv, *w_o,
-      *mlp_norm, *w_gate_up, *w_down, *final_norm, *lm_head;
+      *mlp_norm, *w_gate_up, *w_down, *final_norm, *lm_head, *packed;
 } dflash_weights;
 
 /* (host) The whole decode state, caller-owned device memory:
- *   k, v       [L, B, Hkv, C, dh] in dims->dtype; logical position p of sequence b
+ *   k, v       [L, B, Hkv, C, dh], fp16 for a bf16 drafter and float for an fp32
+ *              drafter (16-byte aligned); logical position p of sequence b
  *              lives in slot p % C; k rows carry RoPE at position p
  *   ctx_len    [B] int32 committed length P_b (a logical position, may exceed C)
  *   anchor     [B] int32 token at position P_b (the visible first row of the block)
@@ -117,6 +132,17 @@ size_t dflash_workspace_bytes(const dflash_dims *dims);
 
 /* Static string naming a dflash_status value. */
 const char *dflash_status_string(int status);
+
+/* Bytes of the packed weight copy for these dims (0 for invalid dims). */
+size_t dflash_packed_bytes(const dflash_dims *dims);
+
+/* Repack the GEMM weights (w->fuse_w, w_qkv, w_o, w_gate_up, w_down, lm_head, in
+ * nn.Linear layout) into `packed` (packed_bytes >= dflash_packed_bytes(dims),
+ * 16-byte aligned), once, before the first fuse_inject / draft_step.  Enqueued on
+ * `stream`; dev_error (device, may be NULL) receives DFLASH_DEVERR_RANGE if a bf16
+ * weight exceeds the fp16 range (it is saturated). */
+int dflash_pack_weights(const dflash_dims *dims, const dflash_weights *w, void *packed,
+                        size_t packed_bytes, uint32_t *dev_error, hipStream_t stream);
 
 /* Feature fusion + KV injection (zhihu answer §5.1 feature fusion, §5.2 KV
  * injection; hotdry blog: all-SWA drafter with a 128-token window).

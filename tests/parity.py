@@ -34,7 +34,7 @@ def say(msg: str) -> None:
 
 def oracle_weights(W) -> dict:
     """Exact host copies (float32 holds every bf16 value) of the device weights."""
-    return {k: v.float().cpu().numpy() for k, v in W.items()}
+    return {k: v.float().cpu().numpy() for k, v in W.items() if k != "packed"}
 
 
 @dataclass
@@ -80,6 +80,8 @@ class ParityRun:
                  check_kv: bool = True):
         self.d, self.W, self.seed, self.check_kv = dims, W, seed, check_kv
         self.Wn = oracle_weights(W)
+        if "packed" not in W:
+            bd.pack_weights(dims, W)
         self.tol = Tol.for_dims(dims)
         B = dims.batch
         self.sample = list(range(B)) if sample is None else list(sample)

@@ -44,6 +44,7 @@ def test_status_strings_and_workspace_query():
     for w in configs.ALL:
         n = bd.dflash_workspace_bytes(w.dims)
         assert n > 0 and n % 256 == 0
+        assert bd.dflash_packed_bytes(w.dims) > 0
     L = bd.lib()
     bad = bd.dims_struct(replace(configs.C1.dims, block_k=0))
     assert L.dflash_workspace_bytes(ctypes.byref(bad)) == 0
@@ -66,6 +67,11 @@ def _cache(ptr=FAKE):
 
 @needs_lib
 def test_invalid_arguments_are_rejected_on_the_host():
+    # every call below must fail host validation; the pointers are fake, so never
+    # run this where a GPU could receive a launch by mistake
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation probe runs on CPU-only hosts")
     L = bd.lib()
     d = bd.dims_struct(configs.C2.dims)
     w, c = _weights(), _cache()
@@ -74,12 +80,22 @@ def test_invalid_arguments_are_rejected_on_the_host():
     # bad dims
     bad = bd.dims_struct(replace(configs.C2.dims, head_dim=96))
     assert L.dflash_draft_step(by(bad), by(w), by(c), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
-    # NULL weight, misaligned weight
+    # NULL or misaligned packed weights, NULL norm gain
+    w0 = _weights()
+    w0.packed = None
+    assert L.dflash_draft_step(by(d), by(w0), by(c), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
+    w0.packed = FAKE + 2
+    assert L.dflash_draft_step(by(d), by(w0), by(c), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
+    w0 = _weights()
+    w0.final_norm = None
+    assert L.dflash_draft_step(by(d), by(w0), by(c), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
+    # pack: missing source matrix, small destination, NULL error word
     w0 = _weights()
     w0.lm_head = None
-    assert L.dflash_draft_step(by(d), by(w0), by(c), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
-    w0.lm_head = FAKE + 2
-    assert L.dflash_draft_step(by(d), by(w0), by(c), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
+    pb = bd.dflash_packed_bytes(configs.C2.dims)
+    assert L.dflash_pack_weights(by(d), by(w0), FAKE, pb, FAKE, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_pack_weights(by(d), by(w), FAKE, pb - 1, FAKE, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_pack_weights(by(d), by(w), FAKE, pb, None, None) == bd.DFLASH_E_INVALID
     # workspace missing or too small
     assert L.dflash_draft_step(by(d), by(w), by(c), FAKE, None, None, ws, None) == bd.DFLASH_E_WORKSPACE
     assert L.dflash_draft_step(by(d), by(w), by(c), FAKE, None, FAKE, ws - 1, None) == bd.DFLASH_E_WORKSPACE

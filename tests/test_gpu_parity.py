@@ -136,7 +136,7 @@ def test_out_of_range_tokens_set_the_error_word():
 
 def test_draft_is_deterministic_and_logits_optional():
     d = replace(configs.C1.dims, batch=2, dtype=BF16)
-    W = synth.make_weights(d, device="cuda")
+    W = bd.pack_weights(d, synth.make_weights(d, device="cuda"))
     cache = bd.alloc_cache(d, ctx_len=[0, 0], anchor=[5, 6])
     ws = bd.alloc_workspace(d)
     taps = synth.make_taps(d, 40, device="cuda")
