@@ -42,7 +42,10 @@ def parse():
                    help="override the planted geometric q (sub-runs of the SWA workload)")
     p.add_argument("--head-launches", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-steps", type=int, default=2)
+    p.add_argument("--cpu-steps", type=int, default=8)
+    p.add_argument("--pmc-probe", action="store_true",
+                   help="for hardware-counter runs: 5 draft steps, then 5 copies of 1 GiB "
+                        "(the copy calibrates FETCH_SIZE / WRITE_SIZE against known bytes)")
     p.add_argument("--seed", type=int, default=0)
     return p.parse_args()
 
@@ -83,7 +86,8 @@ def main() -> int:
     import torch
     from block_diffusion_speculative_dflash_amd import binding as bd
     from block_diffusion_speculative_dflash_amd import configs, harness, synth
-    from block_diffusion_speculative_dflash_amd.roofline import HBM_PEAK_GBS, step_cost
+    from block_diffusion_speculative_dflash_amd.roofline import (HBM_PEAK_GBS, measured_head_traffic,
+                                                                  step_cost)
 
     wl = configs.WORKLOADS[args.workload]
     d = wl.dims
@@ -108,6 +112,18 @@ def main() -> int:
     torch.cuda.synchronize()
     assert np.array_equal(cache["ctx_len"].cpu().numpy(), ctx), "prefill did not reach the context"
     log(f"[bench] prefilled {n_pre} rows; context {int(ctx.min())}..{int(ctx.max())}")
+
+    if args.pmc_probe:
+        draft = torch.zeros((B, k), dtype=torch.int32, device=dev)
+        for _ in range(5):
+            bd.dflash_draft_step(d, W, cache, draft, None, ws)
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] pmc probe done: 5 draft steps, 5 copies of 1073741824 bytes")
+        return 0
 
     # planted acceptance and the target stand-in tables
     kind, q = wl.accept
@@ -222,7 +238,8 @@ def main() -> int:
                           "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"kernel": "gemm_kernel<bf16,*,EPI_ARGMAX> (final norm + LM head + argmax)",
                      "bound": "hbm", "achieved": round(head_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(head_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(head_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_head_traffic(wl.name),
                      "avg_us": round(head_ms * 1e3, 2), "bytes_per_launch": cost.head_bytes},
         "cpu_baseline": cpu,
         "dev_error": err,

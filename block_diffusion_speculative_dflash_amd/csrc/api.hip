@@ -13,7 +13,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr size_t kPartialCap = size_t(32) << 20;  // split-K partial tiles
 constexpr int kGemmCounters = 1 << 16;
-constexpr int kTargetWorkgroups = 512;            // 2 per CU on 256 CUs
+constexpr int kTargetWorkgroups = 256;            // one per CU
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -83,13 +83,19 @@ bool pack_layout(const dflash_dims& d, PackLayout& P) {
 // workspace
 // ---------------------------------------------------------------------------
 struct AttnPlan {
-  int n_rb, kps, max_splits;
+  int n_rb, rows, kps, max_splits;
 };
 
 AttnPlan attn_plan(const dflash_dims& d) {
   AttnPlan p;
   const int G = d.n_q_heads / d.n_kv_heads;
-  p.n_rb = cdiv(G * d.block_k, 64);
+  const int row_tiles = cdiv(G * d.block_k, 16);
+  // few (sequence, kv head) groups: one 16-row tile per workgroup for parallelism;
+  // many: up to four tiles, so the group's keys are read once
+  const int groups = d.batch * d.n_kv_heads;
+  const int rt = groups >= 256 ? std::min(4, row_tiles) : 1;
+  p.rows = 16 * rt;
+  p.n_rb = cdiv(row_tiles, rt);
   // Split a group's keys over workgroups only when the groups alone leave the
   // CUs idle and each split keeps >= 512 keys; splits need a merge launch.
   const int max_keys = d.window + d.block_k;
@@ -132,7 +138,7 @@ Layout layout(const dflash_dims& d) {
   L.ssq_c = take(Mi * L.np_d * 4);
   L.partials = take(kPartialCap);
   L.counters = take(size_t(kGemmCounters) * 4);
-  L.keys = take(Mb * 8);
+  L.keys = take(Mb * 8 * kKeyStride);
   const size_t groups = size_t(d.batch) * d.n_kv_heads * L.ap.n_rb;
   L.attn_cnt = take(groups * 4);
   L.attn_o = take(groups * L.ap.max_splits * 64 * d.head_dim * 4);
@@ -160,6 +166,7 @@ GemmPlan gemm_plan(int M, int n_tiles, int S, bool allow_split) {
       if (cdiv(S, s2) < 8) break;
       if (double(s2) * M * n_tiles * kBN * 4 > double(kPartialCap)) break;
       if (s2 > std::max(1, K / (16 * m_pad))) break;
+      if (s2 > 16 / p.mt) break;  // partial sums of one thread stay in registers
       if (size_t(p.m_tiles) * n_tiles > size_t(kGemmCounters)) break;
       splits = s2;
     }
@@ -294,6 +301,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     at.keys_per_split = L.ap.kps;
     at.max_splits = L.ap.max_splits;
     at.n_rb = L.ap.n_rb;
+    at.rows_per_block = L.ap.rows;
     DF_CHECK(launch_attention(f32, at, stream));
 
     // output projection + residual; produces the MLP's RMSNorm input

@@ -20,7 +20,7 @@
 
 namespace dflash {
 
-constexpr int kRows = 64;  // query rows per workgroup (RT <= 4 tiles of 16)
+constexpr int kRows = 64;  // row stride of the split partials (RT <= 4 tiles of 16 per workgroup)
 constexpr int kKC = 32;    // keys per wavefront chunk (one MFMA K step for P V)
 constexpr int kPad = 8;    // LDS row padding (elements)
 
@@ -59,8 +59,8 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   if (split >= n_split_b) return;
   const int j0 = split * a.keys_per_split;
   const int j1 = min(n_keys, j0 + a.keys_per_split);
-  const int r0 = rb * kRows;
-  const int nr = min(kRows, G * k - r0);
+  const int r0 = rb * RT * 16;
+  const int nr = min(RT * 16, G * k - r0);
 
   const T* qg = static_cast<const T*>(a.q);
   const T* kbg = static_cast<const T*>(a.kb);
@@ -102,30 +102,34 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 
   T(*vt)[kKC + kPad] = sm.u.loop.vt[wave];
   T(*pp)[kKC + kPad] = sm.u.loop.p[wave];
-  for (int c0 = j0 + wave * kKC; c0 < j1; c0 += 4 * kKC) {
-    // K fragments of keys c0 + kt*16 + lane%16 (past j1: a valid row, masked below)
-    Frag<T> kf[2][KS];
+  // K fragments of keys c + kt*16 + lane%16 and this lane's V slice (key c + lane/2,
+  // half the head dim); past j1 a valid row is loaded and masked later.
+  constexpr int VE = DH / 2 / 8;  // V fragments per lane
+  Frag<T> kf[2][KS], vr[VE], kf_n[2][KS], vr_n[VE];
+  auto load_chunk = [&](int c, Frag<T>(&kk)[2][KS], Frag<T>(&vv)[VE]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int j = min(c0 + kt * 16 + (lane & 15), j1 - 1);
-      const T* krow = key_row(j, ck, kbg);
+      const T* krow = key_row(min(c + kt * 16 + (lane & 15), j1 - 1), ck, kbg);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[kt][ks].load(krow + ks * 32 + 8 * (lane >> 4));
+      for (int ks = 0; ks < KS; ++ks) kk[kt][ks].load(krow + ks * 32 + 8 * (lane >> 4));
     }
-    // V chunk -> LDS, transposed: lane handles key lane/2, half of the head dim
+    const T* vrow = key_row(min(c + (lane >> 1), j1 - 1), cv, vbg) + (lane & 1) * (DH / 2);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) vv[e].load(vrow + 8 * e);
+  };
+  int c0 = j0 + wave * kKC;
+  if (c0 < j1) load_chunk(c0, kf, vr);
+  for (; c0 < j1; c0 += 4 * kKC) {
+    const int cn = c0 + 4 * kKC;
+    if (cn < j1) load_chunk(cn, kf_n, vr_n);  // next chunk in flight during this one
+    // V chunk -> LDS, transposed: [dh][key]
     {
       const int jj = lane >> 1, h0 = (lane & 1) * (DH / 2);
-      const int j = min(c0 + jj, j1 - 1);
-      const T* vrow = key_row(j, cv, vbg) + h0;
       const bool ok = c0 + jj < j1;
 #pragma unroll
-      for (int e = 0; e < DH / 2; e += 8) {
-        Frag<T> v;
-        v.load(vrow + e);
-        if (!ok) v.zero();
+      for (int e = 0; e < VE; ++e)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vt[h0 + e + i][jj] = v.v[i];
-      }
+        for (int i = 0; i < 8; ++i) vt[h0 + 8 * e + i][jj] = ok ? vr[e].v[i] : from_f32<T>(0.f);
     }
     // S = Q K^T, scaled, masked
     f32x4 s[RT][2];
@@ -176,6 +180,12 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
       }
     }
     lds_written();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = kf_n[kt][ks];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) vr[e] = vr_n[e];
   }
 
   // merge the four wavefronts: global row max M, weights exp(m_w - M)
@@ -265,8 +275,9 @@ __global__ __launch_bounds__(kThreads) void attention_merge_kernel(AttnArgs a) {
   if (n_split_b == 1) return;
   const int rr = threadIdx.x >> 2;
   const int d0 = blockIdx.x * 32 + (threadIdx.x & 3) * 8;
-  const int r0 = rb * kRows;
-  if (rr >= min(kRows, G * k - r0)) return;
+  const int rows = a.rows_per_block;
+  const int r0 = rb * rows;
+  if (rr >= min(rows, G * k - r0)) return;
   const size_t grp = (static_cast<size_t>(b) * a.n_kv_heads + g) * a.n_rb + rb;
   float M = -INFINITY;
   for (int s = 0; s < n_split_b; ++s) M = fmaxf(M, a.part_ml[((grp * a.max_splits + s) * kRows + rr) * 2]);
@@ -297,8 +308,7 @@ static void launch_rt(const AttnArgs& a, hipStream_t s) {
 
 template <typename T, int DH>
 static hipError_t launch_dh(const AttnArgs& a, hipStream_t s) {
-  const int rows = a.n_rb == 1 ? (a.n_q_heads / a.n_kv_heads) * a.block_k : kRows;
-  switch ((rows + 15) / 16) {
+  switch (a.rows_per_block / 16) {
     case 1: launch_rt<T, DH, 1>(a, s); break;
     case 2: launch_rt<T, DH, 2>(a, s); break;
     case 3: launch_rt<T, DH, 3>(a, s); break;

@@ -66,6 +66,37 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   const int kq = 8 * (lane >> 4);
   const bool a_vec = (g.lda % 8) == 0;
 
+  // Loads the epilogue needs but the product does not (RMSNorm partial sums, the
+  // residual tile) are issued before the main loop so their latency overlaps it.
+  float ssq_part = 0.f;
+  {
+    const int r = tid >> 2, q = tid & 3, m = m0 + r;
+    if (g.ssq_in != nullptr && r < BM && m < g.M) {
+      const float* src = g.ssq_in + static_cast<size_t>(m) * g.np_in;
+      float v[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) v[t] = q + 4 * t < g.np_in ? src[q + 4 * t] : 0.f;
+      for (int p = q + 64; p < g.np_in; p += 4) ssq_part += src[p];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) ssq_part += v[t];
+    }
+  }
+  float hres[(EPI == EPI_RESID) ? (BM + 31) / 32 : 1][8];
+  if constexpr (EPI == EPI_RESID) {
+    const int c8 = tid & 7;
+#pragma unroll
+    for (int it = 0; it < (BM + 31) / 32; ++it) {
+      const int r = (tid >> 3) + 32 * it, m = m0 + r;
+      const int n0 = tile_n * kBN + c8 * 8;
+      if (r < BM && m < g.M && n0 < g.N) {
+        const float4* hp = reinterpret_cast<const float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
+        const float4 h0 = hp[0], h1 = hp[1];
+        hres[it][0] = h0.x; hres[it][1] = h0.y; hres[it][2] = h0.z; hres[it][3] = h0.w;
+        hres[it][4] = h1.x; hres[it][5] = h1.y; hres[it][6] = h1.z; hres[it][7] = h1.w;
+      }
+    }
+  }
+
   f32x4 acc[MT][4];
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi)
@@ -145,25 +176,37 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     }
     unsigned* counter = &g.counters[tile_m * g.n_tiles + tile_n];
     if (!arrive_last(counter, g.splits, &last_s)) return;
-    for (int idx = tid; idx < BM * kBN; idx += kThreads) {
-      const int r = idx / kBN, c = idx % kBN, m = m0 + r;
-      if (m >= g.M) continue;
+    // every partial of this thread's elements is requested before any is summed
+    constexpr int PER = BM * kBN / kThreads;  // elements per thread
+    constexpr int kMaxSplits = 16 / MT;  // the plan never splits further
+    float pv[PER][kMaxSplits];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = tid + e * kThreads, r = idx / kBN, c = idx % kBN, m = min(m0 + r, g.M - 1);
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp)
+        if (sp < g.splits)
+          pv[e][sp] = coherent_load(&g.partials[(static_cast<size_t>(sp) * g.M + m) * np + tile_n * kBN + c]);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = tid + e * kThreads, r = idx / kBN, c = idx % kBN;
       float s = 0.f;
-      for (int sp = 0; sp < g.splits; ++sp)
-        s += coherent_load(&g.partials[(static_cast<size_t>(sp) * g.M + m) * np + tile_n * kBN + c]);
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp)
+        if (sp < g.splits) s += pv[e][sp];
       tile[r][c] = s;
     }
     if (tid == 0) reset_counter(counter);
   }
 
-  // per-row RMSNorm factor of the A rows: 4 threads per row sum the partials
+  // per-row RMSNorm factor of the A rows: 4 threads per row combine the partials
   {
     const int r = tid >> 2, q = tid & 3;
-    float s = 0.f;
+    float s = ssq_part;
     const int m = m0 + r;
     const bool have = g.ssq_in != nullptr && r < BM && m < g.M;
-    if (have)
-      for (int p = q; p < g.np_in; p += 4) s += g.ssq_in[static_cast<size_t>(m) * g.np_in + p];
+    (void)q;
     s += __shfl_xor(s, 1, kWave);
     s += __shfl_xor(s, 2, kWave);
     if (q == 0 && r < BM) rs_s[r] = have ? 1.f / sqrtf(s / static_cast<float>(g.norm_dim) + g.eps) : 1.f;
@@ -175,22 +218,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     TA* out = static_cast<TA*>(g.out);
     const TIN* gain = static_cast<const TIN*>(g.gain);
     const int c8 = tid & 7;
-    for (int r = tid >> 3; r < BM; r += kThreads / 8) {
+#pragma unroll
+    for (int it = 0; it < (BM + 31) / 32; ++it) {
+      const int r = (tid >> 3) + 32 * it;
       const int m = m0 + r;
       const int n0 = tile_n * kBN + c8 * 8;
       float ss = 0.f;
-      if (m < g.M && n0 < g.N) {
+      if (r < BM && m < g.M && n0 < g.N) {
         TA* dst = out + pa_index(m, n0, g.out_steps);
+        float x[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          float x = tile[r][c8 * 8 + j] * rs_s[r];
-          if constexpr (EPI == EPI_RESID) {
-            float* hp = g.h + static_cast<size_t>(m) * g.N + n0 + j;
-            x += *hp;
-            *hp = x;
-          }
-          ss += x * x;
-          dst[j] = from_f32<TA>(x * to_f32(gain[n0 + j]));
+          x[j] = tile[r][c8 * 8 + j] * rs_s[r];
+          if constexpr (EPI == EPI_RESID) x[j] += hres[it][j];
+          ss += x[j] * x[j];
+          dst[j] = from_f32<TA>(x[j] * to_f32(gain[n0 + j]));
+        }
+        if constexpr (EPI == EPI_RESID) {
+          float4* hp = reinterpret_cast<float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
+          hp[0] = make_float4(x[0], x[1], x[2], x[3]);
+          hp[1] = make_float4(x[4], x[5], x[6], x[7]);
         }
       }
       ss += __shfl_xor(ss, 1, kWave);
@@ -271,14 +318,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         if (g.logits != nullptr) g.logits[static_cast<size_t>(m) * g.N + n] = v;
       }
       wave_argmax(v, idx);
-      if (lane == 0) atomicMax(&g.keys[m], argmax_key(v, idx));
+      if (lane == 0) atomicMax(&g.keys[static_cast<size_t>(m) * kKeyStride], argmax_key(v, idx));
     }
     if (!arrive_last(&g.counters[tile_m], g.n_tiles, &last_s)) return;
     for (int r = tid; r < BM; r += kThreads) {
       const int m = m0 + r;
       if (m >= g.M) continue;
       const unsigned long long key =
-          __hip_atomic_exchange(&g.keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_exchange(&g.keys[static_cast<size_t>(m) * kKeyStride], 0ull, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
       g.draft[m] = argmax_key_index(key);
     }
     if (tid == 0) reset_counter(&g.counters[tile_m]);

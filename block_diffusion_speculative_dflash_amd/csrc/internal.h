@@ -25,6 +25,7 @@ enum Epi : int {
 };
 
 constexpr int kBN = 64;           // output columns per workgroup tile (4 MFMA column blocks)
+constexpr int kKeyStride = 16;    // argmax keys one 128-byte line apart (u64 elements)
 constexpr int kKStep = 32;        // reduction elements per MFMA step
 constexpr int kTileStepElems = 4 * 512;  // one packed weight tile step: 4 fragments x 64 lanes x 8
 
@@ -64,7 +65,7 @@ struct GemmArgs {
   float theta;
   void* cache_k;  // [L, B, Hkv, C, dh]
   void* cache_v;
-  unsigned long long* keys;  // [M] zero-initialised argmax keys (ARGMAX)
+  unsigned long long* keys;  // [M * kKeyStride] zero-initialised argmax keys (ARGMAX)
   int32_t* draft;            // [M]
   float* logits;             // [M, N] or nullptr
   uint32_t* dev_error;
@@ -125,7 +126,7 @@ struct AttnArgs {
   float* part_ml;  // [B, Hkv, n_rb, max_splits, 64, 2]
   unsigned* counters;  // [B, Hkv, n_rb]
   int batch, block_k, n_q_heads, n_kv_heads, head_dim, cache_slots, window;
-  int keys_per_split, max_splits, n_rb;
+  int keys_per_split, max_splits, n_rb, rows_per_block;  // rows_per_block: 16, 32, 48 or 64
 };
 hipError_t launch_attention(bool f32, const AttnArgs& a, hipStream_t stream);
 

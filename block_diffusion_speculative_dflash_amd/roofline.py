@@ -49,3 +49,34 @@ def step_cost(d: Dims, mean_ctx: float) -> StepCost:
     head_bytes = p_head * e + rows_d * D * e + rows_d * 4 * ((D + 63) // 64) + rows_d * 4
     return StepCost(weights + kv_read + kv_write + taps + tokens, flops, weights, kv_read,
                     kv_write, taps, head_bytes, 2.0 * rows_d * p_head)
+
+
+# HBM traffic of the LM-head kernel measured with hardware counters (FETCH_SIZE and
+# WRITE_SIZE per dispatch, each scaled by what the counter reads for a device copy of
+# 1 GiB: fetch x2.000, write x1.000), keyed by workload name.  A figure holds only for
+# the kernel sources it was taken with; `measured_head_traffic` returns None otherwise.
+HEAD_TRAFFIC = {
+    "qwen3_8b_b1_k16_ctx4096": {
+        "source_sha256": "9da171d919b37690af8ce10317d32358d34644eadbaeb2f9fa0a4723b79016e3",
+        "bytes": 1256145512,
+    },
+}
+_KERNEL_SOURCES = ("gemm.hip", "common.h", "internal.h")
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+    import os
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    for f in _KERNEL_SOURCES:
+        with open(os.path.join(base, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_head_traffic(workload: str):
+    rec = HEAD_TRAFFIC.get(workload)
+    if rec is None or rec["source_sha256"] != kernel_source_sha256():
+        return None
+    return rec["bytes"]
