@@ -11,9 +11,12 @@ using namespace dflash;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr size_t kPartialCap = size_t(32) << 20;  // split-K partial tiles
+constexpr size_t kPartialCap = size_t(32) << 20;   // split-K partial tiles of the streaming GEMM
+constexpr size_t kPartialMax = size_t(512) << 20;  // upper bound with the tiled GEMM
 constexpr int kGemmCounters = 1 << 16;
-constexpr int kTargetWorkgroups = 256;            // one per CU
+constexpr int kTargetWorkgroups = 256;             // one per CU
+constexpr int kCUs = 256;
+constexpr int kTiledMinRows = 128;                 // bf16 GEMMs with at least this many rows go tiled
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -106,6 +109,8 @@ AttnPlan attn_plan(const dflash_dims& d) {
   return p;
 }
 
+size_t partial_bytes(const dflash_dims& d);
+
 struct Layout {
   size_t h, xa, ssq, q, kb, vb, o, act, cu, ssq_c, partials, counters, keys, attn_cnt, attn_o,
       attn_ml, total;
@@ -136,7 +141,7 @@ Layout layout(const dflash_dims& d) {
   L.act = take(Mb64 * L.S_f * 32 * e);
   L.cu = take(Mi64 * L.S_d * 32 * e);
   L.ssq_c = take(Mi * L.np_d * 4);
-  L.partials = take(kPartialCap);
+  L.partials = take(partial_bytes(d));
   L.counters = take(size_t(kGemmCounters) * 4);
   L.keys = take(Mb * 8 * kKeyStride);
   const size_t groups = size_t(d.batch) * d.n_kv_heads * L.ap.n_rb;
@@ -147,10 +152,10 @@ Layout layout(const dflash_dims& d) {
   return L;
 }
 
-// Tile plan of one GEMM.  Split K only while the grid is below the target size,
-// every split keeps >= 8 steps, the partial tiles fit their region, and their
-// traffic stays below a quarter of the weight bytes.
-GemmPlan gemm_plan(int M, int n_tiles, int S, bool allow_split) {
+// Tile plan of one weight-streaming GEMM.  Split K only while the grid is below the
+// target size, every split keeps >= 8 steps, the partial tiles fit their region, and
+// their traffic stays below a quarter of the weight bytes.
+GemmPlan stream_plan(int M, int n_tiles, int S, bool allow_split, size_t partial_cap) {
   GemmPlan p{};
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.depth = p.mt == 4 ? 2 : 4;
@@ -164,7 +169,7 @@ GemmPlan gemm_plan(int M, int n_tiles, int S, bool allow_split) {
       const int s2 = splits * 2;
       if (n_tiles * p.m_tiles * splits >= kTargetWorkgroups) break;
       if (cdiv(S, s2) < 8) break;
-      if (double(s2) * M * n_tiles * kBN * 4 > double(kPartialCap)) break;
+      if (double(s2) * M * n_tiles * kBN * 4 > double(std::min(partial_cap, kPartialCap))) break;
       if (s2 > std::max(1, K / (16 * m_pad))) break;
       if (s2 > 16 / p.mt) break;  // partial sums of one thread stay in registers
       if (size_t(p.m_tiles) * n_tiles > size_t(kGemmCounters)) break;
@@ -174,6 +179,76 @@ GemmPlan gemm_plan(int M, int n_tiles, int S, bool allow_split) {
   p.steps_per_split = cdiv(S, splits);
   p.splits = cdiv(S, p.steps_per_split);
   return p;
+}
+
+// Tile plan of one tiled GEMM: 256 x 256 tiles (one workgroup per CU) or 128 x 128
+// (two per CU), K split 1..8 ways.  Cost model: the grid runs in rounds of one
+// workgroup per CU slot; a round takes the time of one workgroup's multiply at the
+// per-CU MFMA rate, doubled when two workgroups share a CU; split K adds the fp32
+// partial-tile traffic.  partial_cap = 0 disables splitting.
+GemmPlan tiled_plan(int M, int n_tiles, int S, bool allow_split, size_t partial_cap) {
+  const double cu_flops = 1.0e15 / kCUs, hbm = 5.0e12;
+  GemmPlan best{};
+  double best_t = 1e30;
+  for (int cfg : {kTile256, kTile128}) {
+    const int slots = cfg == kTile256 ? kCUs : 2 * kCUs;
+    const int m_tiles = cdiv(M, cfg), n_big = cdiv(n_tiles, cfg / kBN);
+    for (int want = 1; want <= (allow_split ? 8 : 1); ++want) {
+      const int sps = cdiv(S, want);
+      const int splits = cdiv(S, sps);
+      if (splits != want) continue;
+      if (splits > 1) {
+        if (sps < 16) continue;
+        if (double(splits) * M * n_tiles * kBN * 4 > double(partial_cap)) continue;
+        if (size_t(m_tiles) * n_big > size_t(kGemmCounters)) continue;
+      }
+      const double rounds = cdiv(m_tiles * n_big * splits, slots);
+      const double round_t = 2.0 * cfg * cfg * kKStep * sps / cu_flops * (slots / kCUs);
+      const double t = rounds * round_t + (splits > 1 ? 2.0 * splits * M * n_tiles * kBN * 4 / hbm : 0.0);
+      if (t < best_t * 0.999) {
+        best_t = t;
+        best.tiled = 1;
+        best.mt = cfg;
+        best.m_tiles = m_tiles;
+        best.n_tiles = n_tiles;
+        best.splits = splits;
+        best.steps_per_split = sps;
+        best.depth = 0;
+      }
+    }
+  }
+  return best;
+}
+
+bool use_tiled(const dflash_dims& d, int M) { return !is_f32(d) && M >= kTiledMinRows; }
+
+GemmPlan gemm_plan(const dflash_dims& d, int epi, int M, int n_tiles, int S, bool allow_split,
+                   size_t partial_cap) {
+  if (use_tiled(d, M)) return tiled_plan(M, n_tiles, S, allow_split && epi != EPI_ARGMAX, partial_cap);
+  return stream_plan(M, n_tiles, S, allow_split, partial_cap);
+}
+
+// Bytes of split-K partial tiles the GEMMs of this drafter may use: the streaming
+// GEMM's fixed cap, or what the tiled plans at the largest row counts ask for.
+size_t partial_bytes(const dflash_dims& d) {
+  size_t need = kPartialCap;
+  const int tph = d.head_dim / kBN;
+  const int qkv_tiles = (d.n_q_heads + 2 * d.n_kv_heads) * tph;
+  const int D = d.hidden, Sd = ksteps(D);
+  struct G { int M, n_tiles, S; };
+  const int Mb = d.batch * d.block_k, Mi = d.batch * d.max_inject_rows;
+  const G gs[] = {{Mi, cdiv(D, kBN), ksteps(d.n_taps * d.tap_dim)},
+                  {Mi, d.n_layers * 2 * d.n_kv_heads * tph, Sd},
+                  {Mb, qkv_tiles, Sd},
+                  {Mb, cdiv(D, kBN), ksteps(d.n_q_heads * d.head_dim)},
+                  {Mb, cdiv(d.ffn, kBN / 2), Sd},
+                  {Mb, cdiv(D, kBN), ksteps(d.ffn)}};
+  for (const G& g : gs) {
+    if (!use_tiled(d, g.M)) continue;
+    const GemmPlan p = tiled_plan(g.M, g.n_tiles, g.S, true, kPartialMax);
+    if (p.splits > 1) need = std::max(need, size_t(p.splits) * g.M * g.n_tiles * kBN * 4);
+  }
+  return need;
 }
 
 struct Ctx {
@@ -210,11 +285,16 @@ GemmArgs base_args(const Ctx& c) {
   } while (0)
 
 int run_gemm(int epi, const Ctx& c, GemmArgs a, bool allow_split, hipStream_t s) {
-  const GemmPlan p = gemm_plan(a.M, a.n_tiles, a.S, allow_split);
+  const size_t cap = partial_bytes(c.d);
+  // the tiled fusion GEMM gathers whole 16-byte pieces of tap rows
+  const bool fuse_ok = epi != EPI_FUSE || (a.K == a.S * kKStep && a.lda % 8 == 0);
+  const GemmPlan p = fuse_ok ? gemm_plan(c.d, epi, a.M, a.n_tiles, a.S, allow_split, cap)
+                             : stream_plan(a.M, a.n_tiles, a.S, allow_split, cap);
   a.splits = p.splits;
   a.steps_per_split = p.steps_per_split;
   a.m_tiles = p.m_tiles;
-  DF_CHECK(launch_gemm(epi, is_f32(c.d), p, a, s));
+  if (p.tiled) DF_CHECK(launch_gemm_tiled(epi, p, a, s));
+  else DF_CHECK(launch_gemm(epi, is_f32(c.d), p, a, s));
   return DFLASH_OK;
 }
 

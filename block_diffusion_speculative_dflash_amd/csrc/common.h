@@ -153,6 +153,12 @@ __device__ __forceinline__ void coherent_store(float* p, float v) {
 __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Two consecutive floats (8-byte aligned) in one device-coherent load.
+__device__ __forceinline__ float2 coherent_load2(const float* p) {
+  const unsigned long long u = __hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<float*>(p)),
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(u)), __uint_as_float(static_cast<uint32_t>(u >> 32)));
+}
 // All of this thread's memory operations have completed.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 // Arrival counter: returns true in exactly one thread block, the last of `expected`.

@@ -1,0 +1,149 @@
+// Fused GEMM epilogues shared by the weight-streaming and the tiled GEMM.
+//
+// Input: one 64-column output tile in LDS, tile[r][c] = sum_k A[m0 + r, k] *
+// W[64 * tile_n + c, k] for r < BM, and rs[r], the RMSNorm factor of A row m0 + r
+// (1 when the rows are not normalised).  The epilogue applies what the method does
+// next and writes the next GEMM's operand already fragment-packed:
+//   FUSE    u * rs * fuse_norm gain (packed) + per-tile sum of (u * rs)^2
+//   RESID   h += tile * rs, next RMSNorm input h * gain (packed) + per-tile sum of h^2
+//   SWIGLU  silu(gate) * up, both scaled by rs (tile columns: 32 gate, 32 up)
+//   QKV     q / k / v rows with RoPE on q and k (tile columns: 32 rotation pairs)
+//   INJECT  RoPE on K, scatter of K and V rows into the ring slots pos mod C
+// The split-vocab argmax differs between the two GEMMs and lives with each.
+#pragma once
+
+#include "common.h"
+#include "internal.h"
+
+namespace dflash {
+
+// hres: RESID only, the residual tile prefetched by the caller (row pass `it` of
+// this thread, 8 columns), or nullptr to read it here.
+template <typename TIN, int EPI, int BM, int NT>
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*tile)[kBN + 4], const float* rs,
+                                              int tile_n, int m0, const float (*hres)[8]) {
+  typedef typename ActOf<TIN>::type TA;
+  const int tid = threadIdx.x;
+  if constexpr (EPI == EPI_FUSE || EPI == EPI_RESID) {
+    // 8 threads per row, 8 consecutive columns each: one packed 8-element store
+    constexpr int RPP = NT / 8;  // rows per pass
+    TA* out = static_cast<TA*>(g.out);
+    const TIN* gain = static_cast<const TIN*>(g.gain);
+    const int c8 = tid & 7;
+#pragma unroll
+    for (int it = 0; it < (BM + RPP - 1) / RPP; ++it) {
+      const int r = (tid >> 3) + RPP * it;
+      const int m = m0 + r;
+      const int n0 = tile_n * kBN + c8 * 8;
+      float ss = 0.f;
+      if (r < BM && m < g.M && n0 < g.N) {
+        TA* dst = out + pa_index(m, n0, g.out_steps);
+        float x[8];
+        float hv[8];
+        if constexpr (EPI == EPI_RESID) {
+          if (hres != nullptr) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hv[j] = hres[it][j];
+          } else {
+            const float4* hp = reinterpret_cast<const float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
+            const float4 h0 = hp[0], h1 = hp[1];
+            hv[0] = h0.x; hv[1] = h0.y; hv[2] = h0.z; hv[3] = h0.w;
+            hv[4] = h1.x; hv[5] = h1.y; hv[6] = h1.z; hv[7] = h1.w;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x[j] = tile[r][c8 * 8 + j] * rs[r];
+          if constexpr (EPI == EPI_RESID) x[j] += hv[j];
+          ss += x[j] * x[j];
+          dst[j] = from_f32<TA>(x[j] * to_f32(gain[n0 + j]));
+        }
+        if constexpr (EPI == EPI_RESID) {
+          float4* hp = reinterpret_cast<float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
+          hp[0] = make_float4(x[0], x[1], x[2], x[3]);
+          hp[1] = make_float4(x[4], x[5], x[6], x[7]);
+        }
+      }
+      ss += __shfl_xor(ss, 1, kWave);
+      ss += __shfl_xor(ss, 2, kWave);
+      ss += __shfl_xor(ss, 4, kWave);
+      if (c8 == 0 && r < BM && m < g.M) g.ssq_out[static_cast<size_t>(m) * g.np_out + tile_n] = ss;
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    TA* act = static_cast<TA*>(g.out);
+    for (int idx = tid; idx < BM * 32; idx += NT) {
+      const int r = idx >> 5, p = idx & 31, m = m0 + r;
+      const int j = tile_n * 32 + p;
+      if (m >= g.M || j >= g.ffn) continue;
+      const float gv = tile[r][p] * rs[r];
+      const float uv = tile[r][p + 32] * rs[r];
+      act[pa_index(m, j, g.out_steps)] = from_f32<TA>(gv / (1.f + expf(-gv)) * uv);
+    }
+  } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
+    const int dh = g.head_dim, half = dh / 2;
+    const int tph = dh / kBN;
+    const int sub = tile_n % tph;
+    const int p = tid & 31;  // constant per thread: NT is a multiple of 32
+    const int d1 = sub * 32 + p;
+    const double inv_freq = rope_inv_freq(d1, dh, g.theta);
+    int kind, head, layer = 0;  // kind 0 = q, 1 = k, 2 = v
+    if constexpr (EPI == EPI_QKV) {
+      const int hd = tile_n / tph;
+      kind = hd < g.n_q_heads ? 0 : (hd < g.n_q_heads + g.n_kv_heads ? 1 : 2);
+      head = kind == 0 ? hd : (kind == 1 ? hd - g.n_q_heads : hd - g.n_q_heads - g.n_kv_heads);
+    } else {
+      layer = tile_n / g.inj_tiles;
+      const int hd = (tile_n % g.inj_tiles) / tph;
+      kind = hd < g.n_kv_heads ? 1 : 2;
+      head = kind == 1 ? hd : hd - g.n_kv_heads;
+    }
+    for (int idx = tid; idx < BM * 32; idx += NT) {
+      const int r = idx >> 5, m = m0 + r;
+      if (m >= g.M) continue;
+      const int b = m / g.rows_per_seq, i = m % g.rows_per_seq;
+      int n_valid = g.rows_per_seq;
+      if constexpr (EPI == EPI_INJECT) {
+        const int nr = g.n_rows[b];
+        if ((nr < 0 || nr > g.rows_per_seq) && i == 0 && p == 0) atomicOr(g.dev_error, 2u);
+        n_valid = min(max(nr, 0), g.rows_per_seq);
+      }
+      if (i >= n_valid) continue;
+      const int pos = max(g.ctx_len[b], 0) + i;
+      const float x1 = tile[r][p] * rs[r], x2 = tile[r][p + 32] * rs[r];
+      float y1 = x1, y2 = x2;
+      if (kind != 2) {
+        float sn, cs;
+        rope_sincos(pos, inv_freq, &sn, &cs);
+        y1 = x1 * cs - x2 * sn;
+        y2 = x2 * cs + x1 * sn;
+      }
+      TA* dst;
+      if constexpr (EPI == EPI_QKV) {
+        if (kind == 0) dst = static_cast<TA*>(g.out) + (static_cast<size_t>(m) * g.n_q_heads + head) * dh;
+        else dst = static_cast<TA*>(kind == 1 ? g.out2 : g.out3) + (static_cast<size_t>(m) * g.n_kv_heads + head) * dh;
+      } else {
+        const int slot = pos % g.cache_slots;
+        dst = static_cast<TA*>(kind == 1 ? g.cache_k : g.cache_v) +
+              (((static_cast<size_t>(layer) * g.batch + b) * g.n_kv_heads + head) * g.cache_slots + slot) * dh;
+      }
+      dst[d1] = from_f32<TA>(y1);
+      dst[d1 + half] = from_f32<TA>(y2);
+    }
+  }
+}
+
+// RMSNorm factor of A row m from the producer's per-tile partial sums of squares.
+__device__ __forceinline__ float rms_factor(const GemmArgs& g, int m) {
+  if (g.ssq_in == nullptr || m >= g.M) return 1.f;
+  const float* src = g.ssq_in + static_cast<size_t>(m) * g.np_in;
+  float v[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) v[t] = t < g.np_in ? src[t] : 0.f;
+  float s = 0.f;
+  for (int p = 16; p < g.np_in; ++p) s += src[p];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) s += v[t];
+  return 1.f / sqrtf(s / static_cast<float>(g.norm_dim) + g.eps);
+}
+
+}  // namespace dflash

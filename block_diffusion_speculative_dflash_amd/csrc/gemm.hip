@@ -22,6 +22,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "epilogue.h"
 #include "internal.h"
 
 namespace dflash {
@@ -213,98 +214,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   }
   __syncthreads();
 
-  if constexpr (EPI == EPI_FUSE || EPI == EPI_RESID) {
-    // 8 threads per row, 8 consecutive columns each: one packed 8-element store
-    TA* out = static_cast<TA*>(g.out);
-    const TIN* gain = static_cast<const TIN*>(g.gain);
-    const int c8 = tid & 7;
-#pragma unroll
-    for (int it = 0; it < (BM + 31) / 32; ++it) {
-      const int r = (tid >> 3) + 32 * it;
-      const int m = m0 + r;
-      const int n0 = tile_n * kBN + c8 * 8;
-      float ss = 0.f;
-      if (r < BM && m < g.M && n0 < g.N) {
-        TA* dst = out + pa_index(m, n0, g.out_steps);
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          x[j] = tile[r][c8 * 8 + j] * rs_s[r];
-          if constexpr (EPI == EPI_RESID) x[j] += hres[it][j];
-          ss += x[j] * x[j];
-          dst[j] = from_f32<TA>(x[j] * to_f32(gain[n0 + j]));
-        }
-        if constexpr (EPI == EPI_RESID) {
-          float4* hp = reinterpret_cast<float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
-          hp[0] = make_float4(x[0], x[1], x[2], x[3]);
-          hp[1] = make_float4(x[4], x[5], x[6], x[7]);
-        }
-      }
-      ss += __shfl_xor(ss, 1, kWave);
-      ss += __shfl_xor(ss, 2, kWave);
-      ss += __shfl_xor(ss, 4, kWave);
-      if (c8 == 0 && m < g.M) g.ssq_out[static_cast<size_t>(m) * g.np_out + tile_n] = ss;
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    TA* act = static_cast<TA*>(g.out);
-    for (int idx = tid; idx < BM * 32; idx += kThreads) {
-      const int r = idx >> 5, p = idx & 31, m = m0 + r;
-      const int j = tile_n * 32 + p;
-      if (m >= g.M || j >= g.ffn) continue;
-      const float gv = tile[r][p] * rs_s[r];
-      const float uv = tile[r][p + 32] * rs_s[r];
-      act[pa_index(m, j, g.out_steps)] = from_f32<TA>(gv / (1.f + expf(-gv)) * uv);
-    }
-  } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
-    const int dh = g.head_dim, half = dh / 2;
-    const int tph = dh / kBN;
-    const int sub = tile_n % tph;
-    const int p = tid & 31;  // constant per thread: kThreads is a multiple of 32
-    const int d1 = sub * 32 + p;
-    const double inv_freq = rope_inv_freq(d1, dh, g.theta);
-    int kind, head, layer = 0;  // kind 0 = q, 1 = k, 2 = v
-    if constexpr (EPI == EPI_QKV) {
-      const int hd = tile_n / tph;
-      kind = hd < g.n_q_heads ? 0 : (hd < g.n_q_heads + g.n_kv_heads ? 1 : 2);
-      head = kind == 0 ? hd : (kind == 1 ? hd - g.n_q_heads : hd - g.n_q_heads - g.n_kv_heads);
-    } else {
-      layer = tile_n / g.inj_tiles;
-      const int hd = (tile_n % g.inj_tiles) / tph;
-      kind = hd < g.n_kv_heads ? 1 : 2;
-      head = kind == 1 ? hd : hd - g.n_kv_heads;
-    }
-    for (int idx = tid; idx < BM * 32; idx += kThreads) {
-      const int r = idx >> 5, m = m0 + r;
-      if (m >= g.M) continue;
-      const int b = m / g.rows_per_seq, i = m % g.rows_per_seq;
-      int n_valid = g.rows_per_seq;
-      if constexpr (EPI == EPI_INJECT) {
-        const int nr = g.n_rows[b];
-        if ((nr < 0 || nr > g.rows_per_seq) && i == 0 && p == 0) atomicOr(g.dev_error, 2u);
-        n_valid = min(max(nr, 0), g.rows_per_seq);
-      }
-      if (i >= n_valid) continue;
-      const int pos = max(g.ctx_len[b], 0) + i;
-      const float x1 = tile[r][p] * rs_s[r], x2 = tile[r][p + 32] * rs_s[r];
-      float y1 = x1, y2 = x2;
-      if (kind != 2) {
-        float sn, cs;
-        rope_sincos(pos, inv_freq, &sn, &cs);
-        y1 = x1 * cs - x2 * sn;
-        y2 = x2 * cs + x1 * sn;
-      }
-      TA* dst;
-      if constexpr (EPI == EPI_QKV) {
-        if (kind == 0) dst = static_cast<TA*>(g.out) + (static_cast<size_t>(m) * g.n_q_heads + head) * dh;
-        else dst = static_cast<TA*>(kind == 1 ? g.out2 : g.out3) + (static_cast<size_t>(m) * g.n_kv_heads + head) * dh;
-      } else {
-        const int slot = pos % g.cache_slots;
-        dst = static_cast<TA*>(kind == 1 ? g.cache_k : g.cache_v) +
-              (((static_cast<size_t>(layer) * g.batch + b) * g.n_kv_heads + head) * g.cache_slots + slot) * dh;
-      }
-      dst[d1] = from_f32<TA>(y1);
-      dst[d1 + half] = from_f32<TA>(y2);
-    }
+  if constexpr (EPI != EPI_ARGMAX) {
+    epilogue_tile<TIN, EPI, BM, kThreads>(g, tile, rs_s, tile_n, m0, hres);
   } else {  // EPI_ARGMAX
     for (int r = wave; r < BM; r += 4) {
       const int m = m0 + r;

@@ -1,0 +1,381 @@
+// Tiled MFMA GEMM for many rows (batch x block >= 128): out[m, n] = sum_k A[m, k] W[n, k].
+//
+// Once the draft batch has hundreds of rows the projections are compute-bound, and a
+// kernel that streams W once per 64-row block (the weight-streaming GEMM) would read
+// every weight matrix M/64 times.  Here one workgroup owns a BM x BN output tile
+// (256 x 256 with 8 wavefronts, or 128 x 128 with 4) and walks K in 32-wide steps:
+//
+//  * Both operands are fragment-packed (weights by dflash_pack_weights, activations
+//    by the producing epilogue), so one K step of a 16-row (or 16-column) block is
+//    one contiguous 1 KB chunk, exactly one wavefront MFMA operand.  Chunks go from
+//    HBM/L2 straight into LDS with the gfx950 16-byte LDS-DMA load (64 lanes x 16 B
+//    = 1 KB per instruction, no staging registers), four stages deep: the loads of
+//    step s+3 are in flight while step s is multiplied.  The fusion GEMM's A operand
+//    is the caller's row-major taps; there each lane supplies its own row address and
+//    the DMA gathers the same fragment layout.
+//  * Wavefront (wm, wn) owns WM x WN blocks of 16 x 16; its fragments for step s+1
+//    are read from LDS while the MFMAs of step s issue (two register sets, reads
+//    interleaved one per WM*WN/(WM+WN) MFMAs).
+//  * One barrier per step.  The DMA is issued from inline assembly so the compiler's
+//    wait-count pass does not drain it before every LDS read; the kernel waits with
+//    explicit vmcnt counts instead (every wavefront issues the same number of DMA
+//    loads per stage; rows/columns past the end re-load a valid chunk).
+//  * K may be split over workgroups (fp32 partial tiles, last arriver reduces in
+//    split order); the output tile then goes through LDS 64 columns at a time into
+//    the same fused epilogues as the weight-streaming GEMM.
+//  * Workgroup x runs on XCD x mod 8; tiles are renumbered so each XCD works on a
+//    contiguous run of tiles, m fastest, so the workgroups that share a weight tile
+//    share that XCD's L2.
+#include <type_traits>
+
+#include "common.h"
+#include "epilogue.h"
+#include "internal.h"
+
+namespace dflash {
+
+template <int NWM, int NWN, int WM, int WN>
+struct TileCfg {
+  static constexpr int NW = NWM * NWN, NT = 64 * NW;
+  static constexpr int AFR = NWM * WM, BFR = NWN * WN, FR = AFR + BFR;
+  static constexpr int BM = 16 * AFR, BN = 16 * BFR, SUB = BFR / 4;
+  static constexpr int LPW = FR / NW;      // DMA loads per wavefront per stage
+  static constexpr int STAGE = FR * 1024;  // bytes per stage
+  static constexpr int NST = 4;
+  static constexpr int MAIN = NST * STAGE;
+  static constexpr int TILE = BM * (kBN + 4) * 4;
+  static constexpr int BYTES = MAIN > TILE ? MAIN : TILE;
+  static_assert(FR % NW == 0, "chunks split evenly over the wavefronts");
+  static_assert(WN % 4 == 0 || 4 % WN == 0, "wavefront column blocks align with 64-column subtiles");
+  static_assert(BFR % 4 == 0, "whole 64-column subtiles");
+};
+
+constexpr int vmcnt_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// 1 KB DMA: lane l's 16 bytes at gp land at LDS byte lds + 16 * l.  m0 (the LDS
+// base of the DMA) is declared clobbered; no other code in these kernels uses m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_1k(const void* gp, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(lds) : "m0");
+}
+#pragma clang diagnostic pop
+
+template <int EPI, int NWM, int NWN, int WM, int WN>
+__global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) {
+  using C = TileCfg<NWM, NWN, WM, WN>;
+  constexpr int AFR = C::AFR, BFR = C::BFR, BM = C::BM, SUB = C::SUB, LPW = C::LPW, NW = C::NW, NT = C::NT;
+  constexpr bool APK = EPI != EPI_FUSE;  // packed activations; the fusion GEMM reads row-major taps
+  typedef typename std::conditional<EPI == EPI_FUSE, bf16, f16>::type E;
+  typedef typename std::conditional<EPI == EPI_FUSE, bf16x8, f16x8>::type E8;
+
+  __shared__ __attribute__((aligned(1024))) char smem[C::BYTES];
+  __shared__ float rs_s[BM];
+  __shared__ unsigned long long best_s[BM];
+  __shared__ int last_s;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % NWM, wn = wave / NWM;
+  // XCD-contiguous renumbering, then (split, n tile, m tile) with m fastest
+  const int nwg = gridDim.x, x = blockIdx.x, xcd = x & 7, q = nwg >> 3, r8 = nwg & 7;
+  const int L = xcd * q + min(xcd, r8) + (x >> 3);
+  const int n_big = (g.n_tiles + SUB - 1) / SUB;
+  const int tm = L % g.m_tiles, rest = L / g.m_tiles;
+  const int tn = rest % n_big, split = rest / n_big;
+  const int m0 = tm * BM;
+  const int s_lo = split * g.steps_per_split;
+  const int S = min(g.S, s_lo + g.steps_per_split) - s_lo;  // steps of this split (>= 1)
+  const int m_blocks = (g.M + 15) >> 4;
+
+  // per-chunk source addresses (at step s_lo) and per-step strides, LDS offsets
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+  const char* src[LPW];
+  uint32_t stride[LPW], ldsoff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int c = wave + NW * j;
+    if (c < AFR) {
+      if constexpr (APK) {
+        const int mb = min(tm * AFR + c, m_blocks - 1);
+        src[j] = static_cast<const char*>(g.A) + ((static_cast<size_t>(mb) * g.S + s_lo) * 512 + lane * 8) * 2;
+        stride[j] = 1024;
+      } else {
+        const int row = min(tm * BM + c * 16 + (lane & 15), g.M - 1);
+        src[j] = static_cast<const char*>(g.A) +
+                 (static_cast<size_t>(row) * g.lda + static_cast<size_t>(s_lo) * kKStep + (lane >> 4) * 8) * 2;
+        stride[j] = kKStep * 2;
+      }
+    } else {
+      const int cb = c - AFR;
+      const int t = min(tn * SUB + cb / 4, g.n_tiles - 1);
+      size_t wt = t;
+      if constexpr (EPI == EPI_INJECT) wt = static_cast<size_t>(t / g.inj_tiles) * g.layer_tiles + g.inj_tile0 + t % g.inj_tiles;
+      src[j] = static_cast<const char*>(g.W) + (((wt * g.S + s_lo) * 4 + (cb & 3)) * 512 + lane * 8) * 2;
+      stride[j] = 4096;
+    }
+    ldsoff[j] = __builtin_amdgcn_readfirstlane(lds0 + c * 1024);
+  }
+  auto issue = [&](int s, int buf) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) dma_1k(src[j] + static_cast<size_t>(s) * stride[j], ldsoff[j] + buf * C::STAGE);
+  };
+
+  f32x4 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  E8 fa0[WM], fb0[WN], fa1[WM], fb1[WN];
+  auto read = [&](int buf, E8* fa, E8* fb) {
+    const E* st = reinterpret_cast<const E*>(smem + buf * C::STAGE);
+#pragma unroll
+    for (int j = 0; j < WN; ++j) fb[j] = *reinterpret_cast<const E8*>(st + (AFR + wn * WN + j) * 512 + lane * 8);
+#pragma unroll
+    for (int i = 0; i < WM; ++i) fa[i] = *reinterpret_cast<const E8*>(st + (wm * WM + i) * 512 + lane * 8);
+  };
+  auto mma = [&](const E8* fa, const E8* fb) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        if constexpr (EPI == EPI_FUSE) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        else acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+  };
+  auto interleave = [&]() {
+    constexpr int NR = WM + WN, PER = (WM * WN) / NR;
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, WM * WN - PER * NR, 0);
+  };
+
+  // RMSNorm factor of this tile's A rows (thread r < BM: row m0 + r).  The partial
+  // sums are loaded before the first DMA so their latency overlaps the prologue's.
+  float ssq_v[16];
+  const int r_own = tid < BM ? tid : BM - 1;
+  const bool rs_vec = g.ssq_in != nullptr && (g.np_in & 3) == 0 && g.np_in <= 64;
+  const float* ssq_row =
+      g.ssq_in != nullptr ? g.ssq_in + static_cast<size_t>(min(m0 + r_own, g.M - 1)) * g.np_in : nullptr;
+  if (rs_vec) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (4 * t < g.np_in) v = reinterpret_cast<const float4*>(ssq_row)[t];
+      ssq_v[t] = (v.x + v.y) + (v.z + v.w);
+    }
+  }
+
+  // prologue: stages 0..2 in flight, wait for 0 and 1
+  issue(0, 0);
+  if (1 < S) issue(1, 1);
+  if (2 < S) issue(2, 2);
+  if (2 < S) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LPW));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  if (tid < BM) {
+    float f = 1.f;
+    if (g.ssq_in != nullptr && m0 + tid < g.M) {
+      float sum = 0.f;
+      if (rs_vec) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) sum += ssq_v[t];
+      } else {
+        for (int t = 0; t < g.np_in; ++t) sum += ssq_row[t];
+      }
+      f = 1.f / sqrtf(sum / static_cast<float>(g.norm_dim) + g.eps);
+    }
+    rs_s[tid] = f;
+    if constexpr (EPI == EPI_ARGMAX) best_s[tid] = 0ull;
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read(0, fa0, fb0);
+  // Step t multiplies the fragments read during step t-1 and reads those of step
+  // t+1 (stage t+1 landed at the end of step t-1).  The DMA of step t+3 reuses the
+  // buffer of step t-1, whose last reads completed before the barrier ending t-1.
+  for (int s = 0; s < S; s += 4) {
+#define DFLASH_STEP(u, fac, fbc, fan, fbn)                                    \
+  if (s + u < S) {                                                            \
+    if (s + u + 3 < S) issue(s + u + 3, (u + 3) & 3);                         \
+    read((u + 1) & 3, fan, fbn);                                              \
+    mma(fac, fbc);                                                            \
+    interleave();                                                             \
+    if (s + u + 2 < S) {                                                      \
+      if (s + u + 3 < S) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LPW));         \
+      else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));                         \
+      __builtin_amdgcn_s_barrier();                                           \
+      asm volatile("" ::: "memory");                                          \
+    }                                                                         \
+  }
+    DFLASH_STEP(0, fa0, fb0, fa1, fb1)
+    DFLASH_STEP(1, fa1, fb1, fa0, fb0)
+    DFLASH_STEP(2, fa0, fb0, fa1, fb1)
+    DFLASH_STEP(3, fa1, fb1, fa0, fb0)
+#undef DFLASH_STEP
+  }
+  __syncthreads();  // every wavefront is done with the stage buffers
+
+  float(*tile)[kBN + 4] = reinterpret_cast<float(*)[kBN + 4]>(smem);
+  const size_t np = static_cast<size_t>(g.n_tiles) * kBN;
+
+  if (g.splits > 1) {
+    // partial tile straight from the accumulators (MFMA layout: lane l, register r
+    // holds row 4 * (l / 16) + r, column l % 16 of each 16 x 16 block)
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int m = m0 + (wm * WM + i) * 16 + 4 * (lane >> 4) + rr;
+          const size_t n = static_cast<size_t>(tn * BFR + wn * WN + j) * 16 + (lane & 15);
+          if (m < g.M && n < np) coherent_store(&g.partials[(static_cast<size_t>(split) * g.M + m) * np + n], acc[i][j][rr]);
+        }
+    unsigned* counter = &g.counters[tm * n_big + tn];
+    if (!arrive_last(counter, g.splits, &last_s)) return;
+    if (tid == 0) reset_counter(counter);
+  }
+
+  if constexpr (EPI == EPI_ARGMAX) {
+    // split-vocab argmax straight from the accumulators: per lane, the best of its
+    // WN columns for each of its rows, then across the 16 lanes that share those rows
+    // (xor 1, 2, 4, 8), then across the NWN column wavefronts through an LDS max
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = (wm * WM + i) * 16 + 4 * (lane >> 4) + rr;
+        const int m = m0 + r;
+        const float f = rs_s[r];
+        unsigned long long key = 0ull;
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const int n = (tn * BFR + wn * WN + j) * 16 + (lane & 15);
+          const float v = acc[i][j][rr] * f;
+          if (n < g.N) {
+            const unsigned long long kj = argmax_key(v, n);
+            key = kj > key ? kj : key;
+            if (g.logits != nullptr && m < g.M) g.logits[static_cast<size_t>(m) * g.N + n] = v;
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const unsigned long long other = __shfl_xor(key, o, kWave);
+          key = other > key ? other : key;
+        }
+        if ((lane & 15) == 0 && key != 0ull) atomicMax(&best_s[r], key);
+      }
+  } else if (g.splits > 1) {
+    // the accumulators are dead here: this workgroup's partials are in memory
+#pragma unroll 1
+    for (int sub = 0; sub < SUB; ++sub) {
+      const int tile_n = tn * SUB + sub;
+      __syncthreads();
+      // every thread requests all split partials of 4 element pairs before summing
+      // them in split order (8-byte device-coherent loads)
+      constexpr int kMaxSplits = 8;
+      constexpr int PAIRS = BM * kBN / 2 / NT;
+      static_assert(PAIRS % 4 == 0, "pairs per thread");
+#pragma unroll 1
+      for (int e0 = 0; e0 < PAIRS; e0 += 4) {
+        float2 pv[4][kMaxSplits];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = tid + (e0 + e) * NT, r = idx / (kBN / 2), c = 2 * (idx % (kBN / 2));
+          const int m = min(m0 + r, g.M - 1);
+#pragma unroll
+          for (int sp = 0; sp < kMaxSplits; ++sp)
+            if (sp < g.splits)
+              pv[e][sp] = coherent_load2(&g.partials[(static_cast<size_t>(sp) * g.M + m) * np + tile_n * kBN + c]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = tid + (e0 + e) * NT, r = idx / (kBN / 2), c = 2 * (idx % (kBN / 2));
+          float2 v = make_float2(0.f, 0.f);
+#pragma unroll
+          for (int sp = 0; sp < kMaxSplits; ++sp)
+            if (sp < g.splits) {
+              v.x += pv[e][sp].x;
+              v.y += pv[e][sp].y;
+            }
+          tile[r][c] = v.x;
+          tile[r][c + 1] = v.y;
+        }
+      }
+      __syncthreads();
+      if (tile_n < g.n_tiles) epilogue_tile<bf16, EPI, BM, NT>(g, tile, rs_s, tile_n, m0, nullptr);
+    }
+  } else {
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub) {
+      const int tile_n = tn * SUB + sub;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int cb = wn * WN + j;  // column block of the workgroup tile
+        if (cb / 4 != sub) continue;
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            tile[(wm * WM + i) * 16 + 4 * (lane >> 4) + rr][(cb & 3) * 16 + (lane & 15)] = acc[i][j][rr];
+      }
+      __syncthreads();
+      if (tile_n < g.n_tiles) epilogue_tile<bf16, EPI, BM, NT>(g, tile, rs_s, tile_n, m0, nullptr);
+    }
+  }
+
+  if constexpr (EPI == EPI_ARGMAX) {
+    __syncthreads();
+    for (int r = tid; r < BM; r += NT)
+      if (m0 + r < g.M) atomicMax(&g.keys[static_cast<size_t>(m0 + r) * kKeyStride], best_s[r]);
+    unsigned* counter = &g.counters[tm];
+    if (!arrive_last(counter, n_big, &last_s)) return;
+    for (int r = tid; r < BM; r += NT) {
+      const int m = m0 + r;
+      if (m >= g.M) continue;
+      const unsigned long long key =
+          __hip_atomic_exchange(&g.keys[static_cast<size_t>(m) * kKeyStride], 0ull, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+      g.draft[m] = argmax_key_index(key);
+    }
+    if (tid == 0) reset_counter(counter);
+  }
+}
+
+template <int EPI, int NWM, int NWN, int WM, int WN>
+static hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+  using C = TileCfg<NWM, NWN, WM, WN>;
+  const int n_big = (p.n_tiles + C::SUB - 1) / C::SUB;
+  const long long grid = static_cast<long long>(p.m_tiles) * n_big * p.splits;
+  if (p.m_tiles != (a.M + C::BM - 1) / C::BM || grid <= 0 || grid > (1ll << 31) - 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_tiled_kernel<EPI, NWM, NWN, WM, WN>), dim3(static_cast<unsigned>(grid)), dim3(C::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch_tile(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+  switch (p.mt) {
+    case kTile256: return launch_cfg<EPI, 2, 4, 8, 4>(p, a, s);
+    case kTile128: return launch_cfg<EPI, 2, 2, 4, 4>(p, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_tiled(int epi, const GemmPlan& plan, const GemmArgs& a, hipStream_t stream) {
+  if (plan.n_tiles <= 0 || plan.m_tiles <= 0 || plan.splits <= 0 || a.S <= 0) return hipErrorInvalidValue;
+  if (a.steps_per_split * (plan.splits - 1) >= a.S) return hipErrorInvalidValue;  // every split has a step
+  switch (epi) {
+    case EPI_FUSE: return launch_tile<EPI_FUSE>(plan, a, stream);
+    case EPI_INJECT: return launch_tile<EPI_INJECT>(plan, a, stream);
+    case EPI_QKV: return launch_tile<EPI_QKV>(plan, a, stream);
+    case EPI_RESID: return launch_tile<EPI_RESID>(plan, a, stream);
+    case EPI_SWIGLU: return launch_tile<EPI_SWIGLU>(plan, a, stream);
+    case EPI_ARGMAX: return plan.splits == 1 ? launch_tile<EPI_ARGMAX>(plan, a, stream) : hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dflash

@@ -72,13 +72,20 @@ struct GemmArgs {
 };
 
 struct GemmPlan {
-  int mt;       // 16-row MFMA blocks per workgroup (1, 2 or 4)
+  int tiled;    // 0: weight-streaming GEMM, 1: tiled MFMA GEMM
+  int mt;       // streaming: 16-row MFMA blocks per workgroup (1, 2 or 4); tiled: kTile128 / kTile256
   int m_tiles, n_tiles, splits, steps_per_split, depth;
 };
+
+constexpr int kTile128 = 128;  // tiled GEMM: 128 x 128 tiles, 4 wavefronts, two workgroups per CU
+constexpr int kTile256 = 256;  // tiled GEMM: 256 x 256 tiles, 8 wavefronts
 
 // f32: true for an fp32 drafter, false for a bf16 drafter (fp16 compute)
 hipError_t launch_gemm(int epi, bool f32, const GemmPlan& plan, const GemmArgs& args,
                        hipStream_t stream);
+// bf16 drafters only; m_tiles counts plan.mt-row tiles, n_tiles 64-column tiles.
+// The fusion GEMM needs K % 32 == 0 and a row stride that is a multiple of 8.
+hipError_t launch_gemm_tiled(int epi, const GemmPlan& plan, const GemmArgs& args, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // weight packing

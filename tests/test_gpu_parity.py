@@ -80,6 +80,20 @@ def test_head_dim_128_bf16():
     _assert_ok(_run(d, [70, 64], [64, 64], [[8, 1], [2, 7], [4, 4]]))
 
 
+def test_tiled_gemm_path_bf16():
+    """Batch x block >= 128 rows takes the tiled MFMA GEMM for every projection: row
+    tails (160 draft rows, 180 and 320 injected rows), ragged SwiGLU width and
+    vocabulary, K split over workgroups in the fusion and down projections, and a
+    vocabulary large enough that the 256 x 256 tile wins the plan."""
+    d = replace(configs.C1.dims, batch=20, block_k=8, n_layers=2, n_q_heads=4, n_kv_heads=2,
+                ffn=1100, vocab=40003, window=32, cache_slots=40, dtype=BF16, max_inject_rows=16)
+    say(f"[test] tiled GEMM path {d}")
+    ctx = [40 + (7 * b) % 23 for b in range(d.batch)]
+    pre = [min(c, d.window) for c in ctx]
+    steps = [[(3 * b + s) % 9 for b in range(d.batch)] for s in range(3)]
+    _assert_ok(_run(d, ctx, pre, steps))
+
+
 def test_block_of_one_and_empty_context():
     d = replace(configs.C1.dims, batch=2, block_k=1, window=32, cache_slots=33, max_inject_rows=8)
     say(f"[test] k=1, empty context {d}")
