@@ -93,17 +93,16 @@ AttnPlan attn_plan(const dflash_dims& d) {
   AttnPlan p;
   const int G = d.n_q_heads / d.n_kv_heads;
   const int row_tiles = cdiv(G * d.block_k, 16);
-  // few (sequence, kv head) groups: one 16-row tile per workgroup for parallelism;
-  // many: up to four tiles, so the group's keys are read once
-  const int groups = d.batch * d.n_kv_heads;
-  const int rt = groups >= 256 ? std::min(4, row_tiles) : 1;
+  // one wavefront per (sequence, kv head, row tile of 16, key split)
+  const int rt = 1;
   p.rows = 16 * rt;
   p.n_rb = cdiv(row_tiles, rt);
-  // Split a group's keys over workgroups only when the groups alone leave the
-  // CUs idle and each split keeps >= 512 keys; splits need a merge launch.
+  // Split a row block's keys only while the items alone leave SIMDs idle (about
+  // one wavefront per SIMD), keeping >= 128 keys per split; splits need a merge.
   const int max_keys = d.window + d.block_k;
-  const double per_wg = double(max_keys) * d.batch * d.n_kv_heads * p.n_rb / 256.0;
-  const int kps = round_up(std::max(512, int(per_wg + 0.999)), 32);
+  const long long base = static_cast<long long>(d.batch) * d.n_kv_heads * p.n_rb;
+  const int want = static_cast<int>(std::max(1ll, (1024 + base - 1) / base));
+  const int kps = std::max(128, round_up(cdiv(max_keys, want), 32));
   p.kps = std::min(kps, round_up(max_keys, 32));
   p.max_splits = cdiv(max_keys, p.kps);
   return p;

@@ -4,25 +4,35 @@
 // masked block, all-SWA drafter with window W; zhihu answer §4: parallel decoding
 // inside a block).
 //
-// Workgroup = (key split, kv head g, sequence b, row block).  Its query rows are
-// the G = Hq/Hkv query heads of group g times the k block rows (up to 64, RT tiles
-// of 16).  The four wavefronts take interleaved chunks of 32 keys; per chunk a
-// wavefront computes S = Q K^T with 16x16x32 MFMA (K fragments load straight from
-// the key rows), updates an online softmax (row max / sum across the 16 lanes that
-// share a row), stages P and the chunk's V (transposed) in its own LDS, and adds
-// P V with MFMA.  The four wavefronts' (max, sum, O) are merged in a fixed order.
-// When one sequence's keys are split over several workgroups (long full-attention
-// contexts at small batch), each writes its unnormalised partial and a second
-// kernel merges them in split order; either way the result does not depend on
-// scheduling.
+// Work item = one wavefront = (sequence b, kv head g, row block, key split).  The
+// rows of kv head g are its G = Hq/Hkv query heads times the k block rows; a row
+// block is up to RT tiles of 16 of them.  The four wavefronts of a workgroup are
+// independent items; there is no workgroup barrier.
+//
+// Everything is computed transposed so that one query row lives in one lane:
+//   S^T = K Q^T     A = 16 keys x 32 head dims (straight from the key rows),
+//                   B = Q^T; lane l gets the scores of row l%16 for keys 4*(l/16)+r
+//   softmax         running max / sum per lane; across keys: in-lane, then the four
+//                   lanes of a row (xor 16, 32)
+//   O^T += V^T P^T  B = P^T straight from the score registers: its 32 reduction
+//                   slots are keys {4q..4q+3, 16+4q..16+4q+3} for lane group q, and
+//                   A = V^T uses the same key order, gathered from the chunk's V rows
+//                   staged in this wavefront's LDS
+// so the row statistics scale the output accumulators without any data exchange.
+// When one sequence's keys are split over several items (long full-attention
+// contexts at small batch), each writes its unnormalised partial and a second kernel
+// merges them in split order; either way the result does not depend on scheduling.
 #include "common.h"
 #include "internal.h"
 
 namespace dflash {
 
-constexpr int kRows = 64;  // row stride of the split partials (RT <= 4 tiles of 16 per workgroup)
-constexpr int kKC = 32;    // keys per wavefront chunk (one MFMA K step for P V)
-constexpr int kPad = 8;    // LDS row padding (elements)
+constexpr int kRows = 64;  // row stride of the split partials
+constexpr int kKC = 32;    // keys per chunk (one MFMA reduction step of P V)
+
+template <typename T> struct VPad;
+template <> struct VPad<f16> { static constexpr int value = 8; };    // 16-byte rows
+template <> struct VPad<float> { static constexpr int value = 4; };  // 16-byte rows
 
 // lgkmcnt(0) only (gfx9 s_waitcnt encoding, vmcnt and expcnt left at their maxima):
 // this wavefront's LDS writes are complete before its other lanes read them.
@@ -32,25 +42,21 @@ __device__ __forceinline__ void lds_written() {
 }
 
 template <typename T, int DH, int RT>
-struct __attribute__((aligned(16))) AttnSmem {
-  union {
-    struct {
-      T vt[4][DH][kKC + kPad];      // per wavefront: V chunk transposed [dh][key]
-      T p[4][RT * 16][kKC + kPad];  // per wavefront: probabilities [row][key]
-    } loop;
-    float o[RT * 16][DH + 4];       // merge of the four wavefronts
-  } u;
-  float ml[4][RT * 16][2];          // per wavefront (row max, row sum)
-};
+__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
+  constexpr int KS = DH / 32;  // MFMA reduction steps over the head dimension (S^T)
+  constexpr int DT = DH / 16;  // 16-dim output tiles (O^T)
+  constexpr int VS = DH + VPad<T>::value;
+  __shared__ __attribute__((aligned(16))) T vl[4][kKC][VS];
 
-template <typename T, int DH, int RT>
-__global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
-  constexpr int KS = DH / 32;  // MFMA K steps over the head dimension (Q K^T)
-  constexpr int DT = DH / 16;  // 16-wide output column tiles (P V)
-  __shared__ AttnSmem<T, DH, RT> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x, g = blockIdx.y;
-  const int b = blockIdx.z / a.n_rb, rb = blockIdx.z % a.n_rb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q4 = lane >> 4, l16 = lane & 15;
+  int item = blockIdx.x * 4 + wave;
+  const int split = item % a.max_splits;
+  item /= a.max_splits;
+  const int rb = item % a.n_rb;
+  item /= a.n_rb;
+  const int g = item % a.n_kv_heads, b = item / a.n_kv_heads;
+  if (b >= a.batch) return;
   const int k = a.block_k, G = a.n_q_heads / a.n_kv_heads;
   const int P = max(a.ctx_len[b], 0);
   const int n_ctx = min(P, a.window);
@@ -68,242 +74,232 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   const size_t seq_base = (static_cast<size_t>(b) * a.n_kv_heads + g) * a.cache_slots;
   const T* ck = static_cast<const T*>(a.cache_k) + seq_base * DH;
   const T* cv = static_cast<const T*>(a.cache_v) + seq_base * DH;
-  // row j of this sequence's key list: the window (ring slots), then the block
-  auto key_row = [&](int j, const T* ring, const T* blk) -> const T* {
-    if (j < n_ctx) return ring + static_cast<size_t>((P - n_ctx + j) % a.cache_slots) * DH;
-    return blk + ((static_cast<size_t>(b) * k + (j - n_ctx)) * a.n_kv_heads + g) * DH;
+  const int C = a.cache_slots;
+  const int slot0 = (P - n_ctx) % C;  // ring slot of key 0 (n_ctx < C)
+  const int blk_stride = a.n_kv_heads * DH;
+  const T* kblk = kbg + (static_cast<size_t>(b) * k * a.n_kv_heads + g) * DH;
+  const T* vblk = vbg + (static_cast<size_t>(b) * k * a.n_kv_heads + g) * DH;
+  // key j's row: ring slot slot0 + j (mod C) of the window, then block row j - n_ctx;
+  // selects only (no branch), so the unrolled loads stay in flight together
+  auto key_ptr = [&](int j, const T* ring, const T* blk) -> const T* {
+    const int sl = slot0 + j;
+    const uintptr_t pr = reinterpret_cast<uintptr_t>(ring + (sl >= C ? sl - C : sl) * DH);
+    const uintptr_t pb = reinterpret_cast<uintptr_t>(blk + (j - n_ctx) * blk_stride);
+    const uintptr_t m = uintptr_t(0) - static_cast<uintptr_t>(j < n_ctx);
+    return reinterpret_cast<const T*>((pr & m) | (pb & ~m));
   };
 
-  // Q fragments, resident for the whole key loop: row rt*16 + lane%16
+  // Q^T fragments (B operand), resident for the whole key loop: row rt*16 + l16
   Frag<T> qf[RT][KS];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int rr = rt * 16 + (lane & 15);
-    const bool ok = rr < nr;
-    const int r = r0 + (ok ? rr : 0);
+    const int rr = rt * 16 + l16;
+    const int r = r0 + (rr < nr ? rr : 0);
     const T* qrow = qg + ((static_cast<size_t>(b) * k + r % k) * a.n_q_heads + g * G + r / k) * DH;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[rt][ks].load(qrow + ks * 32 + 8 * (lane >> 4));
-      if (!ok) qf[rt][ks].zero();
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[rt][ks].load(qrow + ks * 32 + 8 * q4);
   }
 
   const float scale = 1.f / sqrtf(static_cast<float>(DH));
-  f32x4 o[RT][DT];
-  float m_run[RT][4], l_run[RT][4];
+  f32x4 o[RT][DT];  // O^T: lane holds dims dt*16 + 4*q4 + r of row rt*16 + l16
+  float m_run[RT], l_run[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) { m_run[rt][r] = -INFINITY; l_run[rt][r] = 0.f; }
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
   }
 
-  T(*vt)[kKC + kPad] = sm.u.loop.vt[wave];
-  T(*pp)[kKC + kPad] = sm.u.loop.p[wave];
-  // K fragments of keys c + kt*16 + lane%16 and this lane's V slice (key c + lane/2,
-  // half the head dim); past j1 a valid row is loaded and masked later.
-  constexpr int VE = DH / 2 / 8;  // V fragments per lane
-  Frag<T> kf[2][KS], vr[VE], kf_n[2][KS], vr_n[VE];
-  auto load_chunk = [&](int c, Frag<T>(&kk)[2][KS], Frag<T>(&vv)[VE]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const T* krow = key_row(min(c + kt * 16 + (lane & 15), j1 - 1), ck, kbg);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kk[kt][ks].load(krow + ks * 32 + 8 * (lane >> 4));
-    }
-    const T* vrow = key_row(min(c + (lane >> 1), j1 - 1), cv, vbg) + (lane & 1) * (DH / 2);
-#pragma unroll
-    for (int e = 0; e < VE; ++e) vv[e].load(vrow + 8 * e);
-  };
-  int c0 = j0 + wave * kKC;
-  if (c0 < j1) load_chunk(c0, kf, vr);
-  for (; c0 < j1; c0 += 4 * kKC) {
-    const int cn = c0 + 4 * kKC;
-    if (cn < j1) load_chunk(cn, kf_n, vr_n);  // next chunk in flight during this one
-    // V chunk -> LDS, transposed: [dh][key]
-    {
-      const int jj = lane >> 1, h0 = (lane & 1) * (DH / 2);
-      const bool ok = c0 + jj < j1;
-#pragma unroll
-      for (int e = 0; e < VE; ++e)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vt[h0 + 8 * e + i][jj] = ok ? vr[e].v[i] : from_f32<T>(0.f);
-    }
-    // S = Q K^T, scaled, masked
-    f32x4 s[RT][2];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Frag<T>::mma(s[rt][kt], qf[rt][ks], kf[kt][ks]);
-      }
-    const bool kv0 = c0 + (lane & 15) < j1, kv1 = c0 + 16 + (lane & 15) < j1;
-    // online softmax; this lane holds rows rt*16 + 4*(lane/16) + r, key column lane%16
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x0 = kv0 ? s[rt][0][r] * scale : -INFINITY;
-        const float x1 = kv1 ? s[rt][1][r] * scale : -INFINITY;
-        float mx = fmaxf(x0, x1);
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
-        const float m_new = fmaxf(m_run[rt][r], mx);
-        const float corr = expf(m_run[rt][r] - m_new);  // 0 on the first chunk
-        const float p0 = expf(x0 - m_new), p1 = expf(x1 - m_new);
-        float ps = p0 + p1;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off, kWave);
-        l_run[rt][r] = l_run[rt][r] * corr + ps;
-        m_run[rt][r] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[rt][dt][r] *= corr;
-        const int row = rt * 16 + 4 * (lane >> 4) + r;
-        pp[row][lane & 15] = from_f32<T>(p0);
-        pp[row][16 + (lane & 15)] = from_f32<T>(p1);
-      }
-    lds_written();
-    // O += P V: A = P rows (lane%16), keys 8*(lane/16)..; B = V^T dims (lane%16)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      Frag<T> vf;
-      vf.load(&vt[dt * 16 + (lane & 15)][8 * (lane >> 4)]);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        Frag<T> pf;
-        pf.load(&pp[rt * 16 + (lane & 15)][8 * (lane >> 4)]);
-        Frag<T>::mma(o[rt][dt], pf, vf);
-      }
-    }
-    lds_written();
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = kf_n[kt][ks];
-#pragma unroll
-    for (int e = 0; e < VE; ++e) vr[e] = vr_n[e];
+  T(*vw)[VS] = vl[wave];
+  // K fragments of keys c + kt*16 + l16; V pieces: VPR lanes per row, RPL rows per
+  // load (1 KB contiguous).  Past j1 the last valid row is loaded and masked later.
+  constexpr int VR = kKC * DH * static_cast<int>(sizeof(T)) / (64 * 16);  // 16-byte pieces per lane
+  constexpr int VPR = DH * static_cast<int>(sizeof(T)) / 16;               // 16-byte pieces per row
+  constexpr int RPL = 64 / VPR;                                            // rows per load
+  const int vrow0 = lane / VPR, vpiece = lane % VPR;
+  Frag<T> kfa[2][KS], kfb[2][KS];
+  f32x4 va[VR], vb[VR];  // raw 16-byte pieces (any element type)
+
+#define DFLASH_LOAD_CHUNK(c, KF, VV)                                                          \
+  {                                                                                           \
+    _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                        \
+      const int j_ = min((c) + kt * 16 + l16, j1 - 1);                                        \
+      const T* krow_ = key_ptr(j_, ck, kblk);                                                 \
+      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) KF[kt][ks].load(krow_ + ks * 32 + 8 * q4); \
+    }                                                                                         \
+    _Pragma("unroll") for (int e = 0; e < VR; ++e) {                                          \
+      const int j_ = min((c) + e * RPL + vrow0, j1 - 1);                                      \
+      const T* vrow_ = key_ptr(j_, cv, vblk);                                                 \
+      VV[e] = reinterpret_cast<const f32x4*>(vrow_)[vpiece];                                  \
+    }                                                                                         \
   }
 
-  // merge the four wavefronts: global row max M, weights exp(m_w - M)
-  if ((lane & 15) == 0) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rt * 16 + 4 * (lane >> 4) + r;
-        sm.ml[wave][row][0] = m_run[rt][r];
-        sm.ml[wave][row][1] = l_run[rt][r];
-      }
-  }
-  __syncthreads();
-  float wf[RT][4];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = rt * 16 + 4 * (lane >> 4) + r;
-      float M = -INFINITY;
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.ml[w][row][0]);
-      wf[rt][r] = m_run[rt][r] == -INFINITY ? 0.f : expf(m_run[rt][r] - M);
-    }
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rt * 16 + 4 * (lane >> 4) + r, col = dt * 16 + (lane & 15);
-            const float v = o[rt][dt][r] * wf[rt][r];
-            sm.u.o[row][col] = (w == 0 ? 0.f : sm.u.o[row][col]) + v;
-          }
-    }
-    __syncthreads();
+#define DFLASH_PROCESS_CHUNK(c, KF, VV)                                                       \
+  {                                                                                           \
+    _Pragma("unroll") for (int e = 0; e < VR; ++e)                                            \
+      reinterpret_cast<f32x4*>(&vw[e * RPL + vrow0][0])[vpiece] = VV[e];                      \
+    f32x4 s_[2][RT];                                                                          \
+    _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                          \
+      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                     \
+        s_[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};                                               \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) Frag<T>::mma(s_[kt][rt], KF[kt][ks], qf[rt][ks]); \
+      }                                                                                       \
+    Frag<T> pf_[RT];                                                                          \
+    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                       \
+      float x_[2][4];                                                                         \
+      float mx_ = -INFINITY;                                                                  \
+      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                        \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                       \
+          const bool valid_ = (c) + kt * 16 + 4 * q4 + r < j1;                                \
+          x_[kt][r] = valid_ ? s_[kt][rt][r] * scale : -INFINITY;                             \
+          mx_ = fmaxf(mx_, x_[kt][r]);                                                        \
+        }                                                                                     \
+      mx_ = fmaxf(mx_, __shfl_xor(mx_, 16, kWave));                                           \
+      mx_ = fmaxf(mx_, __shfl_xor(mx_, 32, kWave));                                           \
+      const float m_new_ = fmaxf(m_run[rt], mx_);                                             \
+      const float corr_ = expf(m_run[rt] - m_new_);                                           \
+      float ps_ = 0.f;                                                                        \
+      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                        \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                       \
+          const float p_ = expf(x_[kt][r] - m_new_);                                          \
+          ps_ += p_;                                                                          \
+          pf_[rt].v[4 * kt + r] = from_f32<T>(p_);                                            \
+        }                                                                                     \
+      ps_ += __shfl_xor(ps_, 16, kWave);                                                      \
+      ps_ += __shfl_xor(ps_, 32, kWave);                                                      \
+      l_run[rt] = l_run[rt] * corr_ + ps_;                                                    \
+      m_run[rt] = m_new_;                                                                     \
+      _Pragma("unroll") for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= corr_;                   \
+    }                                                                                         \
+    lds_written();                                                                            \
+    _Pragma("unroll") for (int dt = 0; dt < DT; ++dt) {                                       \
+      Frag<T> vf_;                                                                            \
+      _Pragma("unroll") for (int t = 0; t < 8; ++t)                                           \
+        vf_.v[t] = vw[(t < 4 ? 0 : 12) + 4 * q4 + t][dt * 16 + l16];                          \
+      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) Frag<T>::mma(o[rt][dt], vf_, pf_[rt]); \
+    }                                                                                         \
+    lds_written();                                                                            \
   }
 
-  // rows: thread -> row tid/4, a quarter of the head dimension
-  const int rr = tid >> 2, qd = tid & 3;
-  constexpr int DQ = DH / 4;
-  if (rr >= nr) return;
-  float M = -INFINITY, L = 0.f;
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.ml[w][rr][0]);
-  for (int w = 0; w < 4; ++w) {
-    const float mw = sm.ml[w][rr][0];
-    if (mw != -INFINITY) L += sm.ml[w][rr][1] * expf(mw - M);
+  // Two register sets in turn: the loads of the next chunk are in flight while this
+  // one is processed, and nothing is copied between the sets.  Per chunk: S^T = K Q^T,
+  // online softmax of row rt*16 + l16 over this lane's 8 keys and its 3 partner lanes
+  // (the running max stays finite: key c < j1 is valid for every row), then
+  // O^T += V^T P^T with V^T gathered as dim dt*16 + l16, keys {4*q4 + t, 16 + 4*q4 + t}.
+  DFLASH_LOAD_CHUNK(j0, kfa, va)
+  for (int c = j0; c < j1; c += 2 * kKC) {
+    if (c + kKC < j1) DFLASH_LOAD_CHUNK(c + kKC, kfb, vb)
+    DFLASH_PROCESS_CHUNK(c, kfa, va)
+    if (c + kKC >= j1) break;
+    if (c + 2 * kKC < j1) DFLASH_LOAD_CHUNK(c + 2 * kKC, kfa, va)
+    DFLASH_PROCESS_CHUNK(c + kKC, kfb, vb)
   }
-  const int r = r0 + rr, hl = r / k, i = r % k;
-  if (n_split_b == 1) {
-    T* out = static_cast<T*>(a.out);
-    const int m = b * k + i;
-    const int col0 = (g * G + hl) * DH + qd * DQ;
-    const float inv = 1.f / L;
+#undef DFLASH_LOAD_CHUNK
+#undef DFLASH_PROCESS_CHUNK
+
+  // output: lane -> row rt*16 + l16, dims dt*16 + 4*q4 .. +3
+  const size_t grp = (static_cast<size_t>(b) * a.n_kv_heads + g) * a.n_rb + rb;
 #pragma unroll
-    for (int c = 0; c < DQ; c += 8) {
-      T* dst = out + pa_index(m, col0 + c, a.out_steps);
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rr = rt * 16 + l16;
+    if (rr >= nr) continue;
+    const int r = r0 + rr, hl = r / k, i = r % k;
+    if (n_split_b == 1) {
+      T* out = static_cast<T*>(a.out);
+      const float inv = 1.f / l_run[rt];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = from_f32<T>(sm.u.o[rr][qd * DQ + c + j] * inv);
-    }
-  } else {
-    const size_t grp = (static_cast<size_t>(b) * a.n_kv_heads + g) * a.n_rb + rb;
-    float* po = a.part_o + ((grp * a.max_splits + split) * kRows + rr) * DH + qd * DQ;
+      for (int dt = 0; dt < DT; ++dt) {
+        T* dst = out + pa_index(b * k + i, (g * G + hl) * DH + dt * 16 + 4 * q4, a.out_steps);
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) po[d] = sm.u.o[rr][qd * DQ + d];
-    if (qd == 0) {
-      float* pml = a.part_ml + ((grp * a.max_splits + split) * kRows + rr) * 2;
-      pml[0] = M;
-      pml[1] = L;
+        for (int j = 0; j < 4; ++j) dst[j] = from_f32<T>(o[rt][dt][j] * inv);
+      }
+    } else {
+      float* po = a.part_o + ((grp * a.max_splits + split) * kRows + rr) * DH;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(po + dt * 16 + 4 * q4) =
+            make_float4(o[rt][dt][0], o[rt][dt][1], o[rt][dt][2], o[rt][dt][3]);
+      if (q4 == 0) {
+        float* pml = a.part_ml + ((grp * a.max_splits + split) * kRows + rr) * 2;
+        pml[0] = m_run[rt];
+        pml[1] = l_run[rt];
+      }
     }
   }
 }
 
 // Merge of the key splits of every (sequence, kv head, row block) whose keys were
-// split, in split order; sequences with one split were finished by the attention
-// kernel itself.
+// split; sequences with one split were finished by the attention kernel itself.
+// One workgroup per row: thread t takes 4 head dims ((t % (DH/4)) * 4) and the
+// splits s = t / (DH/4) (mod NSUB); the NSUB subsets combine in a fixed order, so
+// the result does not depend on scheduling.
 template <typename T, int DH>
 __global__ __launch_bounds__(kThreads) void attention_merge_kernel(AttnArgs a) {
-  // blockIdx.x picks 32 head dims; thread -> row tid/4, 8 of those dims
-  const int g = blockIdx.y, b = blockIdx.z / a.n_rb, rb = blockIdx.z % a.n_rb;
+  constexpr int TPR = DH / 4, NSUB = kThreads / TPR;
+  __shared__ float red_m[NSUB];
+  __shared__ float4 red_o[NSUB][TPR];
+  __shared__ float red_l[NSUB];
+  const int rows = a.rows_per_block;
+  const int rr = blockIdx.x % rows, grp_i = blockIdx.x / rows;
+  const int rb = grp_i % a.n_rb, g = (grp_i / a.n_rb) % a.n_kv_heads, b = grp_i / (a.n_rb * a.n_kv_heads);
   const int k = a.block_k, G = a.n_q_heads / a.n_kv_heads;
   const int P = max(a.ctx_len[b], 0);
   const int n_keys = min(P, a.window) + k;
   const int n_split_b = (n_keys + a.keys_per_split - 1) / a.keys_per_split;
-  if (n_split_b == 1) return;
-  const int rr = threadIdx.x >> 2;
-  const int d0 = blockIdx.x * 32 + (threadIdx.x & 3) * 8;
-  const int rows = a.rows_per_block;
   const int r0 = rb * rows;
-  if (rr >= min(rows, G * k - r0)) return;
+  if (n_split_b == 1 || rr >= min(rows, G * k - r0)) return;  // uniform per workgroup
+  const int t = threadIdx.x, dq = t % TPR, sub = t / TPR;
   const size_t grp = (static_cast<size_t>(b) * a.n_kv_heads + g) * a.n_rb + rb;
+  auto ml = [&](int s) { return a.part_ml + ((grp * a.max_splits + s) * kRows + rr) * 2; };
+  float mloc = -INFINITY;
+  for (int s = sub; s < n_split_b; s += NSUB) mloc = fmaxf(mloc, ml(s)[0]);
+  if (dq == 0) red_m[sub] = mloc;
+  __syncthreads();
   float M = -INFINITY;
-  for (int s = 0; s < n_split_b; ++s) M = fmaxf(M, a.part_ml[((grp * a.max_splits + s) * kRows + rr) * 2]);
-  float acc[8];
 #pragma unroll
-  for (int d = 0; d < 8; ++d) acc[d] = 0.f;
+  for (int i = 0; i < NSUB; ++i) M = fmaxf(M, red_m[i]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.f;
-  for (int s = 0; s < n_split_b; ++s) {
-    const float* pml = a.part_ml + ((grp * a.max_splits + s) * kRows + rr) * 2;
-    const float w = expf(pml[0] - M);
-    L += pml[1] * w;
-    const float* po = a.part_o + ((grp * a.max_splits + s) * kRows + rr) * DH + d0;
+  for (int s = sub; s < n_split_b; s += NSUB) {
+    const float* pm = ml(s);
+    const float w = expf(pm[0] - M);
+    L += pm[1] * w;
+    const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((grp * a.max_splits + s) * kRows + rr) * DH + 4 * dq);
+    acc.x += v.x * w;
+    acc.y += v.y * w;
+    acc.z += v.z * w;
+    acc.w += v.w * w;
+  }
+  red_o[sub][dq] = acc;
+  if (dq == 0) red_l[sub] = L;
+  __syncthreads();
+  if (sub != 0) return;
+  float4 o = red_o[0][dq];
+  float Lt = red_l[0];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[d] += po[d] * w;
+  for (int i = 1; i < NSUB; ++i) {
+    const float4 v = red_o[i][dq];
+    o.x += v.x;
+    o.y += v.y;
+    o.z += v.z;
+    o.w += v.w;
+    Lt += red_l[i];
   }
   const int r = r0 + rr, hl = r / k, i = r % k;
-  T* dst = static_cast<T*>(a.out) + pa_index(b * k + i, (g * G + hl) * DH + d0, a.out_steps);
-  const float inv = 1.f / L;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) dst[j] = from_f32<T>(acc[j] * inv);
+  T* dst = static_cast<T*>(a.out) + pa_index(b * k + i, (g * G + hl) * DH + 4 * dq, a.out_steps);
+  const float inv = 1.f / Lt;
+  dst[0] = from_f32<T>(o.x * inv);
+  dst[1] = from_f32<T>(o.y * inv);
+  dst[2] = from_f32<T>(o.z * inv);
+  dst[3] = from_f32<T>(o.w * inv);
 }
 
 template <typename T, int DH, int RT>
 static void launch_rt(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.max_splits, a.n_kv_heads, a.batch * a.n_rb);
-  hipLaunchKernelGGL((attention_kernel<T, DH, RT>), grid, dim3(kThreads), 0, s, a);
+  const long long items = static_cast<long long>(a.batch) * a.n_kv_heads * a.n_rb * a.max_splits;
+  hipLaunchKernelGGL((attention_kernel<T, DH, RT>), dim3(static_cast<unsigned>((items + 3) / 4)), dim3(kThreads), 0,
+                     s, a);
 }
 
 template <typename T, int DH>
@@ -311,13 +307,12 @@ static hipError_t launch_dh(const AttnArgs& a, hipStream_t s) {
   switch (a.rows_per_block / 16) {
     case 1: launch_rt<T, DH, 1>(a, s); break;
     case 2: launch_rt<T, DH, 2>(a, s); break;
-    case 3: launch_rt<T, DH, 3>(a, s); break;
-    default: launch_rt<T, DH, 4>(a, s); break;
+    default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
-  const dim3 grid(DH / 32, a.n_kv_heads, a.batch * a.n_rb);
-  hipLaunchKernelGGL((attention_merge_kernel<T, DH>), grid, dim3(kThreads), 0, s, a);
+  const long long wgs = static_cast<long long>(a.batch) * a.n_kv_heads * a.n_rb * a.rows_per_block;
+  hipLaunchKernelGGL((attention_merge_kernel<T, DH>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
