@@ -93,12 +93,13 @@ AttnPlan attn_plan(const dflash_dims& d) {
   AttnPlan p;
   const int G = d.n_q_heads / d.n_kv_heads;
   const int row_tiles = cdiv(G * d.block_k, 16);
-  // one wavefront per (sequence, kv head, row tile of 16, key split)
-  const int rt = 1;
-  p.rows = 16 * rt;
-  p.n_rb = cdiv(row_tiles, rt);
-  // Split a row block's keys only while the items alone leave SIMDs idle (about
-  // one wavefront per SIMD), keeping >= 128 keys per split; splits need a merge.
+  // one workgroup per (sequence, kv head, row block of <= 4 tiles, key split); its
+  // wavefronts are the row tiles and share every K/V chunk through LDS
+  const int nw = std::min(4, row_tiles);
+  p.n_rb = cdiv(row_tiles, nw);
+  p.rows = 16 * nw;
+  // Split keys only while the workgroups alone leave CUs idle (about four per CU),
+  // keeping >= 128 keys per split; splits need a merge.
   const int max_keys = d.window + d.block_k;
   const long long base = static_cast<long long>(d.batch) * d.n_kv_heads * p.n_rb;
   const int want = static_cast<int>(std::max(1ll, (1024 + base - 1) / base));

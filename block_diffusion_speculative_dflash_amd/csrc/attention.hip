@@ -4,20 +4,24 @@
 // masked block, all-SWA drafter with window W; zhihu answer §4: parallel decoding
 // inside a block).
 //
-// Work item = one wavefront = (sequence b, kv head g, row block, key split).  The
-// rows of kv head g are its G = Hq/Hkv query heads times the k block rows; a row
-// block is up to RT tiles of 16 of them.  The four wavefronts of a workgroup are
-// independent items; there is no workgroup barrier.
+// Workgroup = (sequence b, kv head g, row block, key split).  The rows of kv head g
+// are its G = Hq/Hkv query heads times the k block rows; a row block is up to four
+// tiles of 16 of them, one per wavefront.  The workgroup streams its keys in chunks
+// of 32: every chunk's K and V rows are loaded from HBM once, cooperatively, into a
+// double-buffered LDS stage (the next chunk's loads are in flight while this one is
+// used), and every wavefront reads its operands from there.
 //
 // Everything is computed transposed so that one query row lives in one lane:
 //   S^T = K Q^T     A = 16 keys x 32 head dims (straight from the key rows),
 //                   B = Q^T; lane l gets the scores of row l%16 for keys 4*(l/16)+r
-//   softmax         running max / sum per lane; across keys: in-lane, then the four
-//                   lanes of a row (xor 16, 32)
+//   softmax         running max / sum per lane in log2 units (native exp2); across
+//                   keys: in-lane, then the four lanes of a row (xor 16, 32); the
+//                   output rescale is skipped when no row maximum moved
 //   O^T += V^T P^T  B = P^T straight from the score registers: its 32 reduction
 //                   slots are keys {4q..4q+3, 16+4q..16+4q+3} for lane group q, and
-//                   A = V^T uses the same key order, gathered from the chunk's V rows
-//                   staged in this wavefront's LDS
+//                   A = V^T uses the same key order, read from the chunk's V rows
+//                   in LDS with the gfx950 transposing LDS read (two 8-byte reads
+//                   per 16 x 32 operand)
 // so the row statistics scale the output accumulators without any data exchange.
 // When one sequence's keys are split over several items (long full-attention
 // contexts at small batch), each writes its unnormalised partial and a second kernel
@@ -31,7 +35,7 @@ constexpr int kRows = 64;  // row stride of the split partials
 constexpr int kKC = 32;    // keys per chunk (one MFMA reduction step of P V)
 
 template <typename T> struct VPad;
-template <> struct VPad<f16> { static constexpr int value = 8; };    // 16-byte rows
+template <> struct VPad<f16> { static constexpr int value = 16; };   // 288-byte rows: 8 rows on disjoint banks
 template <> struct VPad<float> { static constexpr int value = 4; };  // 16-byte rows
 
 // lgkmcnt(0) only (gfx9 s_waitcnt encoding, vmcnt and expcnt left at their maxima):
@@ -41,32 +45,37 @@ __device__ __forceinline__ void lds_written() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <typename T, int DH, int RT>
-__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
+template <typename T, int DH, int NW>
+__global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs a) {
   constexpr int KS = DH / 32;  // MFMA reduction steps over the head dimension (S^T)
   constexpr int DT = DH / 16;  // 16-dim output tiles (O^T)
   constexpr int VS = DH + VPad<T>::value;
-  __shared__ __attribute__((aligned(16))) T vl[4][kKC][VS];
+  constexpr int NT = 64 * NW;
+  constexpr int VPR = DH * static_cast<int>(sizeof(T)) / 16;  // 16-byte pieces per row
+  constexpr int HALF = kKC * VPR;                             // pieces of K (or V) per chunk
+  constexpr int PPL = (2 * HALF + NT - 1) / NT;               // pieces per thread per chunk
+  __shared__ __attribute__((aligned(16))) T kv[2][2][kKC][VS];  // [stage][K, V][key][dim]
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int q4 = lane >> 4, l16 = lane & 15;
-  int item = blockIdx.x * 4 + wave;
+  int item = blockIdx.x;
   const int split = item % a.max_splits;
   item /= a.max_splits;
   const int rb = item % a.n_rb;
   item /= a.n_rb;
   const int g = item % a.n_kv_heads, b = item / a.n_kv_heads;
-  if (b >= a.batch) return;
   const int k = a.block_k, G = a.n_q_heads / a.n_kv_heads;
   const int P = max(a.ctx_len[b], 0);
   const int n_ctx = min(P, a.window);
   const int n_keys = n_ctx + k;
   const int n_split_b = (n_keys + a.keys_per_split - 1) / a.keys_per_split;
-  if (split >= n_split_b) return;
+  if (split >= n_split_b) return;  // uniform per workgroup
   const int j0 = split * a.keys_per_split;
   const int j1 = min(n_keys, j0 + a.keys_per_split);
-  const int r0 = rb * RT * 16;
-  const int nr = min(RT * 16, G * k - r0);
+  const int rr0 = wave * 16;                 // this wavefront's rows within the row block
+  const int r0 = rb * a.rows_per_block;      // first row of the row block
+  const int nr = min(a.rows_per_block, G * k - r0);  // rows of the row block
 
   const T* qg = static_cast<const T*>(a.q);
   const T* kbg = static_cast<const T*>(a.kb);
@@ -89,202 +98,222 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
     return reinterpret_cast<const T*>((pr & m) | (pb & ~m));
   };
 
-  // Q^T fragments (B operand), resident for the whole key loop: row rt*16 + l16
-  Frag<T> qf[RT][KS];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int rr = rt * 16 + l16;
+  // Q^T fragments (B operand), resident for the whole key loop: row rr0 + l16
+  Frag<T> qf[KS];
+  {
+    const int rr = rr0 + l16;
     const int r = r0 + (rr < nr ? rr : 0);
     const T* qrow = qg + ((static_cast<size_t>(b) * k + r % k) * a.n_q_heads + g * G + r / k) * DH;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[rt][ks].load(qrow + ks * 32 + 8 * q4);
+    for (int ks = 0; ks < KS; ++ks) qf[ks].load(qrow + ks * 32 + 8 * q4);
   }
 
-  const float scale = 1.f / sqrtf(static_cast<float>(DH));
-  f32x4 o[RT][DT];  // O^T: lane holds dims dt*16 + 4*q4 + r of row rt*16 + l16
-  float m_run[RT], l_run[RT];
+  // scores in log2 units: softmax(s / sqrt(dh)) = 2^(s * log2(e) / sqrt(dh) - max)
+  const float scale2 = 1.4426950408889634f / sqrtf(static_cast<float>(DH));
+  f32x4 o[DT];  // O^T: lane holds dims dt*16 + 4*q4 + r of row rr0 + l16
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // cooperative chunk load: piece p < HALF is K, else V; key (p % HALF) / VPR, 16-byte
+  // piece p % VPR of that row.  Past j1 (and past the last piece) valid rows are
+  // re-loaded, and the stores of pieces past the last are skipped.
+  f32x4 st[PPL];
+  auto load = [&](int c) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
+    for (int i = 0; i < PPL; ++i) {
+      const int p = min(tid + NT * i, 2 * HALF - 1);
+      const int h = p / HALF, pp = p % HALF;
+      const int j = min(c + pp / VPR, j1 - 1);
+      const T* row = h == 0 ? key_ptr(j, ck, kblk) : key_ptr(j, cv, vblk);
+      st[i] = reinterpret_cast<const f32x4*>(row)[pp % VPR];
+    }
+  };
+  auto store = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int p = tid + NT * i;
+      if (2 * HALF % NT == 0 || p < 2 * HALF) {
+        const int h = p / HALF, pp = p % HALF;
+        reinterpret_cast<f32x4*>(&kv[stage][h][pp / VPR][0])[pp % VPR] = st[i];
+      }
+    }
+  };
+
+  load(j0);
+  store(0);
+  __syncthreads();
+  int stage = 0;
+  for (int c = j0; c < j1; c += kKC, stage ^= 1) {
+    load(c + kKC);  // unconditional (clamped): a branch here would drain every load
+    // S^T = K Q^T from the stage's K rows
+    f32x4 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Frag<T> kf;
+        kf.load(&kv[stage][0][kt * 16 + l16][ks * 32 + 8 * q4]);
+        Frag<T>::mma(s[kt], kf, qf[ks]);
+      }
+    }
+    // online softmax of row rr0 + l16 over this lane's 8 keys and its 3 partner lanes
+    float x[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[kt][r] = s[kt][r] * scale2;
+    if (c + kKC > j1) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (c + kt * 16 + 4 * q4 + r >= j1) x[kt][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[kt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);  // finite: key c < j1 is valid for every row
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first chunk
+    Frag<T> pf;
+    float ps = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(x[kt][r] - m_new);
+        ps += p;
+        pf.v[4 * kt + r] = from_f32<T>(p);
+      }
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    l_run = l_run * corr + ps;
+    m_run = m_new;
+    if (__any(corr != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+    }
+    // O^T += V^T P^T; V^T operand: dim dt*16 + l16, keys {4*q4 + t, 16 + 4*q4 + t}
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      Frag<T> vf;
+      if constexpr (sizeof(T) == 2) {
+        // transposing LDS reads: in each 16-lane group, result lane i, slot j takes
+        // element i % 4 of the 8 bytes source lane 4j + i/4 points at, so lane (q4, m)
+        // points at row 4*q4 + m/4 (then + 16), dims dt*16 + 4*(m % 4)
+        typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+        const h4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (__attribute__((address_space(3))) h4*)&kv[stage][1][4 * q4 + (l16 >> 2)][dt * 16 + 4 * (l16 & 3)]);
+        const h4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (__attribute__((address_space(3))) h4*)&kv[stage][1][16 + 4 * q4 + (l16 >> 2)][dt * 16 + 4 * (l16 & 3)]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          vf.v[t] = static_cast<T>(lo[t]);
+          vf.v[4 + t] = static_cast<T>(hi[t]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vf.v[t] = kv[stage][1][(t < 4 ? 0 : 12) + 4 * q4 + t][dt * 16 + l16];
+      }
+      Frag<T>::mma(o[dt], vf, pf);
+    }
+    store(stage ^ 1);  // the next chunk into the other stage
+    __syncthreads();   // its rows are visible; this stage's reads are done
   }
 
-  T(*vw)[VS] = vl[wave];
-  // K fragments of keys c + kt*16 + l16; V pieces: VPR lanes per row, RPL rows per
-  // load (1 KB contiguous).  Past j1 the last valid row is loaded and masked later.
-  constexpr int VR = kKC * DH * static_cast<int>(sizeof(T)) / (64 * 16);  // 16-byte pieces per lane
-  constexpr int VPR = DH * static_cast<int>(sizeof(T)) / 16;               // 16-byte pieces per row
-  constexpr int RPL = 64 / VPR;                                            // rows per load
-  const int vrow0 = lane / VPR, vpiece = lane % VPR;
-  Frag<T> kfa[2][KS], kfb[2][KS];
-  f32x4 va[VR], vb[VR];  // raw 16-byte pieces (any element type)
-
-#define DFLASH_LOAD_CHUNK(c, KF, VV)                                                          \
-  {                                                                                           \
-    _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                        \
-      const int j_ = min((c) + kt * 16 + l16, j1 - 1);                                        \
-      const T* krow_ = key_ptr(j_, ck, kblk);                                                 \
-      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) KF[kt][ks].load(krow_ + ks * 32 + 8 * q4); \
-    }                                                                                         \
-    _Pragma("unroll") for (int e = 0; e < VR; ++e) {                                          \
-      const int j_ = min((c) + e * RPL + vrow0, j1 - 1);                                      \
-      const T* vrow_ = key_ptr(j_, cv, vblk);                                                 \
-      VV[e] = reinterpret_cast<const f32x4*>(vrow_)[vpiece];                                  \
-    }                                                                                         \
-  }
-
-#define DFLASH_PROCESS_CHUNK(c, KF, VV)                                                       \
-  {                                                                                           \
-    _Pragma("unroll") for (int e = 0; e < VR; ++e)                                            \
-      reinterpret_cast<f32x4*>(&vw[e * RPL + vrow0][0])[vpiece] = VV[e];                      \
-    f32x4 s_[2][RT];                                                                          \
-    _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                          \
-      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                     \
-        s_[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};                                               \
-        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) Frag<T>::mma(s_[kt][rt], KF[kt][ks], qf[rt][ks]); \
-      }                                                                                       \
-    Frag<T> pf_[RT];                                                                          \
-    _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                       \
-      float x_[2][4];                                                                         \
-      float mx_ = -INFINITY;                                                                  \
-      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                        \
-        _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                       \
-          const bool valid_ = (c) + kt * 16 + 4 * q4 + r < j1;                                \
-          x_[kt][r] = valid_ ? s_[kt][rt][r] * scale : -INFINITY;                             \
-          mx_ = fmaxf(mx_, x_[kt][r]);                                                        \
-        }                                                                                     \
-      mx_ = fmaxf(mx_, __shfl_xor(mx_, 16, kWave));                                           \
-      mx_ = fmaxf(mx_, __shfl_xor(mx_, 32, kWave));                                           \
-      const float m_new_ = fmaxf(m_run[rt], mx_);                                             \
-      const float corr_ = expf(m_run[rt] - m_new_);                                           \
-      float ps_ = 0.f;                                                                        \
-      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                        \
-        _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                       \
-          const float p_ = expf(x_[kt][r] - m_new_);                                          \
-          ps_ += p_;                                                                          \
-          pf_[rt].v[4 * kt + r] = from_f32<T>(p_);                                            \
-        }                                                                                     \
-      ps_ += __shfl_xor(ps_, 16, kWave);                                                      \
-      ps_ += __shfl_xor(ps_, 32, kWave);                                                      \
-      l_run[rt] = l_run[rt] * corr_ + ps_;                                                    \
-      m_run[rt] = m_new_;                                                                     \
-      _Pragma("unroll") for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= corr_;                   \
-    }                                                                                         \
-    lds_written();                                                                            \
-    _Pragma("unroll") for (int dt = 0; dt < DT; ++dt) {                                       \
-      Frag<T> vf_;                                                                            \
-      _Pragma("unroll") for (int t = 0; t < 8; ++t)                                           \
-        vf_.v[t] = vw[(t < 4 ? 0 : 12) + 4 * q4 + t][dt * 16 + l16];                          \
-      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) Frag<T>::mma(o[rt][dt], vf_, pf_[rt]); \
-    }                                                                                         \
-    lds_written();                                                                            \
-  }
-
-  // Two register sets in turn: the loads of the next chunk are in flight while this
-  // one is processed, and nothing is copied between the sets.  Per chunk: S^T = K Q^T,
-  // online softmax of row rt*16 + l16 over this lane's 8 keys and its 3 partner lanes
-  // (the running max stays finite: key c < j1 is valid for every row), then
-  // O^T += V^T P^T with V^T gathered as dim dt*16 + l16, keys {4*q4 + t, 16 + 4*q4 + t}.
-  DFLASH_LOAD_CHUNK(j0, kfa, va)
-  for (int c = j0; c < j1; c += 2 * kKC) {
-    if (c + kKC < j1) DFLASH_LOAD_CHUNK(c + kKC, kfb, vb)
-    DFLASH_PROCESS_CHUNK(c, kfa, va)
-    if (c + kKC >= j1) break;
-    if (c + 2 * kKC < j1) DFLASH_LOAD_CHUNK(c + 2 * kKC, kfa, va)
-    DFLASH_PROCESS_CHUNK(c + kKC, kfb, vb)
-  }
-#undef DFLASH_LOAD_CHUNK
-#undef DFLASH_PROCESS_CHUNK
-
-  // output: lane -> row rt*16 + l16, dims dt*16 + 4*q4 .. +3
+  // output: lane -> row rr0 + l16, dims dt*16 + 4*q4 .. +3
+  const int rr = rr0 + l16;
+  if (rr >= nr) return;
   const size_t grp = (static_cast<size_t>(b) * a.n_kv_heads + g) * a.n_rb + rb;
+  const int r = r0 + rr, hl = r / k, i = r % k;
+  if (n_split_b == 1) {
+    T* out = static_cast<T*>(a.out);
+    const float inv = 1.f / l_run;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int rr = rt * 16 + l16;
-    if (rr >= nr) continue;
-    const int r = r0 + rr, hl = r / k, i = r % k;
-    if (n_split_b == 1) {
-      T* out = static_cast<T*>(a.out);
-      const float inv = 1.f / l_run[rt];
+    for (int dt = 0; dt < DT; ++dt) {
+      T* dst = out + pa_index(b * k + i, (g * G + hl) * DH + dt * 16 + 4 * q4, a.out_steps);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        T* dst = out + pa_index(b * k + i, (g * G + hl) * DH + dt * 16 + 4 * q4, a.out_steps);
+      for (int j = 0; j < 4; ++j) dst[j] = from_f32<T>(o[dt][j] * inv);
+    }
+  } else {
+    float* po = a.part_o + ((grp * a.max_splits + split) * kRows + rr) * DH;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = from_f32<T>(o[rt][dt][j] * inv);
-      }
-    } else {
-      float* po = a.part_o + ((grp * a.max_splits + split) * kRows + rr) * DH;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(po + dt * 16 + 4 * q4) =
-            make_float4(o[rt][dt][0], o[rt][dt][1], o[rt][dt][2], o[rt][dt][3]);
-      if (q4 == 0) {
-        float* pml = a.part_ml + ((grp * a.max_splits + split) * kRows + rr) * 2;
-        pml[0] = m_run[rt];
-        pml[1] = l_run[rt];
-      }
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + dt * 16 + 4 * q4) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (q4 == 0) {
+      float* pml = a.part_ml + ((grp * a.max_splits + split) * kRows + rr) * 2;
+      pml[0] = m_run;
+      pml[1] = l_run;
     }
   }
 }
 
 // Merge of the key splits of every (sequence, kv head, row block) whose keys were
 // split; sequences with one split were finished by the attention kernel itself.
-// One workgroup per row: thread t takes 4 head dims ((t % (DH/4)) * 4) and the
-// splits s = t / (DH/4) (mod NSUB); the NSUB subsets combine in a fixed order, so
-// the result does not depend on scheduling.
-template <typename T, int DH>
+// Thread t of a workgroup takes 4 head dims ((t % (DH/4)) * 4) of row
+// (t / (DH/4)) / NSUB of the workgroup's rows, and the splits s = (t / (DH/4)) % NSUB
+// (mod NSUB); the NSUB subsets combine in a fixed order, so the result does not
+// depend on scheduling.
+template <typename T, int DH, int NSUB>
 __global__ __launch_bounds__(kThreads) void attention_merge_kernel(AttnArgs a) {
-  constexpr int TPR = DH / 4, NSUB = kThreads / TPR;
-  __shared__ float red_m[NSUB];
-  __shared__ float4 red_o[NSUB][TPR];
-  __shared__ float red_l[NSUB];
+  constexpr int TPR = DH / 4, RPW = kThreads / (TPR * NSUB);  // threads per row-subset, rows per workgroup
+  __shared__ float red_m[RPW][NSUB];
+  __shared__ float4 red_o[RPW][NSUB][TPR];
+  __shared__ float red_l[RPW][NSUB];
   const int rows = a.rows_per_block;
-  const int rr = blockIdx.x % rows, grp_i = blockIdx.x / rows;
+  const int wg_per_grp = (rows + RPW - 1) / RPW;
+  const int grp_i = blockIdx.x / wg_per_grp;
   const int rb = grp_i % a.n_rb, g = (grp_i / a.n_rb) % a.n_kv_heads, b = grp_i / (a.n_rb * a.n_kv_heads);
   const int k = a.block_k, G = a.n_q_heads / a.n_kv_heads;
   const int P = max(a.ctx_len[b], 0);
   const int n_keys = min(P, a.window) + k;
   const int n_split_b = (n_keys + a.keys_per_split - 1) / a.keys_per_split;
+  if (n_split_b == 1) return;  // uniform per workgroup
+  const int t = threadIdx.x, dq = t % TPR, sub = (t / TPR) % NSUB, rw = t / (TPR * NSUB);
   const int r0 = rb * rows;
-  if (n_split_b == 1 || rr >= min(rows, G * k - r0)) return;  // uniform per workgroup
-  const int t = threadIdx.x, dq = t % TPR, sub = t / TPR;
+  const int rr = (blockIdx.x % wg_per_grp) * RPW + rw;
+  const bool valid = rr < min(rows, G * k - r0);
+  const int rrc = valid ? rr : 0;
   const size_t grp = (static_cast<size_t>(b) * a.n_kv_heads + g) * a.n_rb + rb;
-  auto ml = [&](int s) { return a.part_ml + ((grp * a.max_splits + s) * kRows + rr) * 2; };
+  auto ml = [&](int s) { return a.part_ml + ((grp * a.max_splits + s) * kRows + rrc) * 2; };
   float mloc = -INFINITY;
   for (int s = sub; s < n_split_b; s += NSUB) mloc = fmaxf(mloc, ml(s)[0]);
-  if (dq == 0) red_m[sub] = mloc;
+  if (dq == 0) red_m[rw][sub] = mloc;
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < NSUB; ++i) M = fmaxf(M, red_m[i]);
+  for (int i = 0; i < NSUB; ++i) M = fmaxf(M, red_m[rw][i]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.f;
   for (int s = sub; s < n_split_b; s += NSUB) {
     const float* pm = ml(s);
-    const float w = expf(pm[0] - M);
+    const float w = __builtin_amdgcn_exp2f(pm[0] - M);  // maxima are in log2 units
     L += pm[1] * w;
-    const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((grp * a.max_splits + s) * kRows + rr) * DH + 4 * dq);
+    const float4 v = *reinterpret_cast<const float4*>(a.part_o + ((grp * a.max_splits + s) * kRows + rrc) * DH + 4 * dq);
     acc.x += v.x * w;
     acc.y += v.y * w;
     acc.z += v.z * w;
     acc.w += v.w * w;
   }
-  red_o[sub][dq] = acc;
-  if (dq == 0) red_l[sub] = L;
+  red_o[rw][sub][dq] = acc;
+  if (dq == 0) red_l[rw][sub] = L;
   __syncthreads();
-  if (sub != 0) return;
-  float4 o = red_o[0][dq];
-  float Lt = red_l[0];
+  if (sub != 0 || !valid) return;
+  float4 o = red_o[rw][0][dq];
+  float Lt = red_l[rw][0];
 #pragma unroll
   for (int i = 1; i < NSUB; ++i) {
-    const float4 v = red_o[i][dq];
+    const float4 v = red_o[rw][i][dq];
     o.x += v.x;
     o.y += v.y;
     o.z += v.z;
     o.w += v.w;
-    Lt += red_l[i];
+    Lt += red_l[rw][i];
   }
   const int r = r0 + rr, hl = r / k, i = r % k;
   T* dst = static_cast<T*>(a.out) + pa_index(b * k + i, (g * G + hl) * DH + 4 * dq, a.out_steps);
@@ -295,24 +324,35 @@ __global__ __launch_bounds__(kThreads) void attention_merge_kernel(AttnArgs a) {
   dst[3] = from_f32<T>(o.w * inv);
 }
 
-template <typename T, int DH, int RT>
-static void launch_rt(const AttnArgs& a, hipStream_t s) {
-  const long long items = static_cast<long long>(a.batch) * a.n_kv_heads * a.n_rb * a.max_splits;
-  hipLaunchKernelGGL((attention_kernel<T, DH, RT>), dim3(static_cast<unsigned>((items + 3) / 4)), dim3(kThreads), 0,
-                     s, a);
+template <typename T, int DH, int NW>
+static void launch_nw(const AttnArgs& a, hipStream_t s) {
+  const long long wgs = static_cast<long long>(a.batch) * a.n_kv_heads * a.n_rb * a.max_splits;
+  hipLaunchKernelGGL((attention_kernel<T, DH, NW>), dim3(static_cast<unsigned>(wgs)), dim3(64 * NW), 0, s, a);
+}
+
+template <typename T, int DH, int NSUB>
+static void launch_merge(const AttnArgs& a, hipStream_t s) {
+  constexpr int RPW = kThreads / (DH / 4 * NSUB);
+  const long long wgs = static_cast<long long>(a.batch) * a.n_kv_heads * a.n_rb * ((a.rows_per_block + RPW - 1) / RPW);
+  hipLaunchKernelGGL((attention_merge_kernel<T, DH, NSUB>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s, a);
 }
 
 template <typename T, int DH>
 static hipError_t launch_dh(const AttnArgs& a, hipStream_t s) {
   switch (a.rows_per_block / 16) {
-    case 1: launch_rt<T, DH, 1>(a, s); break;
-    case 2: launch_rt<T, DH, 2>(a, s); break;
+    case 1: launch_nw<T, DH, 1>(a, s); break;
+    case 2: launch_nw<T, DH, 2>(a, s); break;
+    case 3: launch_nw<T, DH, 3>(a, s); break;
+    case 4: launch_nw<T, DH, 4>(a, s); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
-  const long long wgs = static_cast<long long>(a.batch) * a.n_kv_heads * a.n_rb * a.rows_per_block;
-  hipLaunchKernelGGL((attention_merge_kernel<T, DH>), dim3(static_cast<unsigned>(wgs)), dim3(kThreads), 0, s, a);
+  // split subsets per row: about as many as there are splits (DH = 128: 8 rows per
+  // workgroup with 1 subset, down to 1 row with 8)
+  if (a.max_splits >= 8) launch_merge<T, DH, 8>(a, s);
+  else if (a.max_splits >= 4) launch_merge<T, DH, 4>(a, s);
+  else if (a.max_splits >= 2) launch_merge<T, DH, 2>(a, s);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   __shared__ int last_s;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int tile_n = blockIdx.x, tile_m = blockIdx.y, split = blockIdx.z;
   const int m0 = tile_m * BM;
 

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   __shared__ unsigned long long best_s[BM];
   __shared__ int last_s;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % NWM, wn = wave / NWM;
   // XCD-contiguous renumbering, then (split, n tile, m tile) with m fastest
   const int nwg = gridDim.x, x = blockIdx.x, xcd = x & 7, q = nwg >> 3, r8 = nwg & 7;
