@@ -86,8 +86,8 @@ def main() -> int:
     import torch
     from block_diffusion_speculative_dflash_amd import binding as bd
     from block_diffusion_speculative_dflash_amd import configs, harness, synth
-    from block_diffusion_speculative_dflash_amd.roofline import (HBM_PEAK_GBS, measured_head_traffic,
-                                                                  step_cost)
+    from block_diffusion_speculative_dflash_amd.roofline import (HBM_PEAK_GBS, MFMA_BF16_PEAK_TFLOPS,
+                                                                  measured_head_traffic, step_cost)
 
     wl = configs.WORKLOADS[args.workload]
     d = wl.dims
@@ -206,8 +206,31 @@ def main() -> int:
     cost = step_cost(d, float(ctx.mean()))
     head_gbs = cost.head_bytes / (head_ms * 1e-3) / 1e9
     step_gbs = cost.bytes_total * steps_per_s / 1e9
-    log(f"[bench] head kernel {head_ms * 1e3:.1f} us = {head_gbs:.0f} GB/s; step {step_gbs:.0f} GB/s "
-        f"({cost.bytes_total / 1e9:.3f} GB/step)")
+    head_tfs = cost.head_flops / (head_ms * 1e-3) / 1e12
+    step_tfs = cost.flops_total * steps_per_s / 1e12
+    log(f"[bench] head kernel {head_ms * 1e3:.1f} us = {head_gbs:.0f} GB/s, {head_tfs:.1f} TFLOP/s; "
+        f"step {step_gbs:.0f} GB/s, {step_tfs:.1f} TFLOP/s ({cost.bytes_total / 1e9:.3f} GB/step)")
+    # batch x block >= 128 rows: the projections run on the tiled MFMA GEMM and the
+    # step is compute-bound (bf16-class MFMA peak); below that it streams weights
+    mfma_bound = d.dtype == configs.BF16 and B * k >= 128
+    if mfma_bound:
+        step_roof = {"bound": "mfma", "flops_per_step": cost.flops_total,
+                     "achieved_TFLOPs": round(step_tfs, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                     "frac": round(step_tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
+        head_roof = {"kernel": "gemm_tiled_kernel<EPI_ARGMAX> (final norm + LM head + argmax)",
+                     "bound": "mfma", "achieved": round(head_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(head_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_head_traffic(wl.name),
+                     "avg_us": round(head_ms * 1e3, 2), "flops_per_launch": cost.head_flops}
+    else:
+        step_roof = {"bound": "hbm", "bytes_per_step": cost.bytes_total,
+                     "achieved_GBs": round(step_gbs, 1), "peak_GBs": HBM_PEAK_GBS,
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4)}
+        head_roof = {"kernel": "gemm_kernel<EPI_ARGMAX> (final norm + LM head + argmax)",
+                     "bound": "hbm", "achieved": round(head_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(head_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_head_traffic(wl.name),
+                     "avg_us": round(head_ms * 1e3, 2), "bytes_per_launch": cost.head_bytes}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -233,14 +256,8 @@ def main() -> int:
         "committed_tok_s": round(committed / elapsed, 1),
         "mean_accept": round(accepted / (args.steps * B), 4),
         "planted_accept_matches": accepted == planted,
-        "step_roofline": {"bound": "hbm", "bytes_per_step": cost.bytes_total,
-                          "achieved_GBs": round(step_gbs, 1), "peak_GBs": HBM_PEAK_GBS,
-                          "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "gemm_kernel<bf16,*,EPI_ARGMAX> (final norm + LM head + argmax)",
-                     "bound": "hbm", "achieved": round(head_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(head_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_head_traffic(wl.name),
-                     "avg_us": round(head_ms * 1e3, 2), "bytes_per_launch": cost.head_bytes},
+        "step_roofline": step_roof,
+        "roofline": head_roof,
         "cpu_baseline": cpu,
         "dev_error": err,
     }

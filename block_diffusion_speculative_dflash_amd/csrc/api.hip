@@ -14,7 +14,7 @@ constexpr size_t kAlign = 256;
 constexpr size_t kPartialCap = size_t(32) << 20;   // split-K partial tiles of the streaming GEMM
 constexpr size_t kPartialMax = size_t(512) << 20;  // upper bound with the tiled GEMM
 constexpr int kGemmCounters = 1 << 16;
-constexpr int kTargetWorkgroups = 256;             // one per CU
+constexpr int kSplitBelow = 256;                   // streaming GEMM: split K only below this many tiles (one per CU)
 constexpr int kCUs = 256;
 constexpr int kTiledMinRows = 128;                 // bf16 GEMMs with at least this many rows go tiled
 
@@ -152,13 +152,15 @@ Layout layout(const dflash_dims& d) {
   return L;
 }
 
-// Tile plan of one weight-streaming GEMM.  Split K only while the grid is below the
-// target size, every split keeps >= 8 steps, the partial tiles fit their region, and
-// their traffic stays below a quarter of the weight bytes.
+// Tile plan of one weight-streaming GEMM.  Split K while the grid has fewer than
+// kSplitBelow tiles (measured on the batch-1 projections with weights cold in HBM:
+// fewer splits leave loads idle, more add reduction cost), every split keeps >= 8
+// steps, the partial tiles fit their region, and their traffic stays below a quarter
+// of the weight bytes.
 GemmPlan stream_plan(int M, int n_tiles, int S, bool allow_split, size_t partial_cap) {
   GemmPlan p{};
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  p.depth = p.mt == 4 ? 2 : 4;
+  p.depth = p.mt == 4 ? 2 : (p.mt == 1 ? 8 : 4);
   p.m_tiles = cdiv(M, 16 * p.mt);
   p.n_tiles = n_tiles;
   int splits = 1;
@@ -167,7 +169,7 @@ GemmPlan stream_plan(int M, int n_tiles, int S, bool allow_split, size_t partial
     const int K = S * kKStep;
     while (true) {
       const int s2 = splits * 2;
-      if (n_tiles * p.m_tiles * splits >= kTargetWorkgroups) break;
+      if (n_tiles * p.m_tiles * splits >= kSplitBelow) break;
       if (cdiv(S, s2) < 8) break;
       if (double(s2) * M * n_tiles * kBN * 4 > double(std::min(partial_cap, kPartialCap))) break;
       if (s2 > std::max(1, K / (16 * m_pad))) break;

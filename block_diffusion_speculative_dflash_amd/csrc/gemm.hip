@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 template <typename TIN, int MT, int EPI>
 static hipError_t launch_t(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
   const dim3 grid(p.n_tiles, p.m_tiles, p.splits);
-  constexpr int D = MT == 4 ? 2 : 4;
+  constexpr int D = MT == 4 ? 2 : (MT == 1 ? 8 : 4);
   if (p.depth != D) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_kernel<TIN, MT, EPI, D>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
