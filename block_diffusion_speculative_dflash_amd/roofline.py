@@ -57,8 +57,8 @@ def step_cost(d: Dims, mean_ctx: float) -> StepCost:
 # the kernel sources it was taken with; `measured_head_traffic` returns None otherwise.
 HEAD_TRAFFIC = {
     "qwen3_8b_b1_k16_ctx4096": {
-        "source_sha256": "9da171d919b37690af8ce10317d32358d34644eadbaeb2f9fa0a4723b79016e3",
-        "bytes": 1256145512,
+        "source_sha256": "954b4d3bd477012318d6648c73d51d4d11444d08ad96a0ea3287bb19016fcff1",
+        "bytes": 1256499476,
     },
 }
 _KERNEL_SOURCES = ("gemm.hip", "common.h", "internal.h")
