@@ -25,9 +25,11 @@ class Dims:
     """Static shapes of one drafter instance (mirrors ``dflash_dims`` in dflash.h).
 
     window      W: how many committed positions before the block each query sees.
-    cache_slots C: ring slots per (layer, sequence, kv head); C >= W + k so the
-                k+1 tentative rows of one round never overwrite a row that the
-                next round's window still needs.
+    sink        s: the first s positions stay visible to every query after they
+                leave the window (attention sink; 0 = plain sliding window).
+    cache_slots C: slots per (layer, sequence, kv head): s sink slots, then a ring
+                of C - s >= W + k slots, so the k+1 tentative rows of one round
+                never overwrite a row that the next round's window still needs.
     max_inject_rows: the largest per-sequence row count one fuse_inject call may
                 carry (sizes the workspace); at least k + 1.
     """
@@ -49,6 +51,7 @@ class Dims:
     max_inject_rows: int
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
+    sink: int = 0
 
     @property
     def group(self) -> int:

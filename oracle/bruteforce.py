@@ -68,12 +68,14 @@ def block_logits(dims, W, history: Dict[int, Sequence], P: int, anchor: int,
     """Logits [k][V] of the block at position P whose committed context is history.
 
     history maps every committed position p < P to its taps [n_taps][tap_dim];
-    only the last W of them are used.
+    the block sees the last W of them and, with an attention sink of s, also
+    positions 0..s-1.
     """
     k, D = dims.block_k, dims.hidden
     Hq, Hkv, dh, F = dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn
     eps, th = dims.rms_eps, dims.rope_theta
-    ctx_pos = [p for p in range(P - dims.window, P) if p >= 0]
+    sink = int(getattr(dims, "sink", 0))
+    ctx_pos = [p for p in range(P) if p < sink or P - p <= dims.window]
     n_ctx = len(ctx_pos)
     feats = {p: fused_feature(dims, W, history[p]) for p in ctx_pos}
 

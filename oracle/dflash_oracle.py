@@ -117,7 +117,7 @@ def attend(q, keys, vals) -> np.ndarray:
 class State:
     """Per-sequence decode state: K/V rings, committed length P and anchor token.
 
-    k_ring / v_ring: [L, B, Hkv, C, dh] float64; slot p % C holds position p.
+    k_ring / v_ring: [L, B, Hkv, C, dh] float64; slot_of(dims, p) holds position p.
     Slots that hold no committed position are NaN, so reading one poisons logits.
     """
     k_ring: np.ndarray
@@ -186,16 +186,30 @@ def fuse_inject(dims, W, st: State, taps, n_rows, commit: bool) -> None:
         for l in range(dims.n_layers):
             K, V = inject_kv(dims, W, l, c[b, :n], pos)     # [n, Hkv, dh]
             for r in range(n):                               # in position order
-                slot = int(pos[r]) % dims.cache_slots
+                slot = slot_of(dims, int(pos[r]))
                 st.k_ring[l, b, :, slot, :] = K[r]
                 st.v_ring[l, b, :, slot, :] = V[r]
         if commit:
             st.ctx_len[b] += n
 
 
+def slot_of(dims, p: int) -> int:
+    """Cache slot of position p: the first s positions (the attention sink) keep
+    slots 0..s-1; later positions share a ring of C - s slots after them.  With
+    s = 0 this is p mod C (hotdry blog, SWA section: sliding-window cache; aufer
+    article, micro-op section, names the attention sink as this drafter's knob)."""
+    s = int(getattr(dims, "sink", 0))
+    if p < s:
+        return int(p)
+    return s + (int(p) - s) % (dims.cache_slots - s)
+
+
 def window_positions(dims, P: int) -> np.ndarray:
-    """Committed positions every block query sees: the last min(P, W) before P."""
-    return np.arange(max(0, P - dims.window), P)
+    """Committed positions every block query sees: the sink positions 0..s-1 that
+    exist, then the last W positions before P that are not sink positions (no
+    position is listed twice)."""
+    s = min(int(getattr(dims, "sink", 0)), P)
+    return np.concatenate([np.arange(0, s), np.arange(max(s, P - dims.window), P)]).astype(np.int64)
 
 
 # ----------------------------------------------------------------------------
@@ -229,7 +243,8 @@ def draft_step(dims, W, st: State, want_logits: bool = True) -> Dict[str, np.nda
 
         o = np.empty((B, k, Hq, dh), dtype=np.float64)
         for b in range(B):
-            slots = window_positions(dims, int(st.ctx_len[b])) % dims.cache_slots
+            slots = np.array([slot_of(dims, int(p)) for p in window_positions(dims, int(st.ctx_len[b]))],
+                             dtype=np.int64)
             for hq in range(Hq):
                 g = kv_head_of(hq, Hq, Hkv)
                 keys = np.concatenate([st.k_ring[l, b, g, slots], kb[b, :, g]], axis=0)
@@ -281,7 +296,7 @@ def verify_commit(dims, st: State, draft, target) -> Dict[str, np.ndarray]:
         acc[b] = a
         out[b, :a + 1] = target[b, :a + 1]
         P = int(st.ctx_len[b])
-        dead = np.arange(P + a + 1, P + k + 1) % dims.cache_slots
+        dead = np.array([slot_of(dims, p) for p in range(P + a + 1, P + k + 1)], dtype=np.int64)
         st.k_ring[:, b][:, :, dead, :] = np.nan
         st.v_ring[:, b][:, :, dead, :] = np.nan
         st.ctx_len[b] = P + a + 1
@@ -295,7 +310,8 @@ def verify_commit(dims, st: State, draft, target) -> Dict[str, np.ndarray]:
 
 def decode_step(dims, W, st: State) -> np.ndarray:
     """Textbook one-token decode of the anchor at position P: causal attention over
-    the last W committed positions and the token itself.  Returns logits [B, V]."""
+    the sink positions, the last W committed positions and the token itself.
+    Returns logits [B, V]."""
     B = st.ctx_len.shape[0]
     Hq, Hkv, dh = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
     logits = np.empty((B, dims.vocab))
@@ -310,12 +326,13 @@ def decode_step(dims, W, st: State) -> np.ndarray:
             own_v = proj[(Hq + Hkv) * dh:].reshape(Hkv, dh)
             heads_q = rope(heads_q, np.full(Hq, P), dims.rope_theta)
             own_k = rope(own_k, np.full(Hkv, P), dims.rope_theta)
-            past = [p for p in range(P - dims.window, P) if p >= 0]
+            sink = int(getattr(dims, "sink", 0))
+            past = [p for p in range(P) if p < sink or p >= P - dims.window]
             ctx = np.zeros(Hq * dh)
             for hq in range(Hq):
                 g = (hq * Hkv) // Hq
-                ks = [st.k_ring[l, b, g, p % dims.cache_slots] for p in past] + [own_k[g]]
-                vs = [st.v_ring[l, b, g, p % dims.cache_slots] for p in past] + [own_v[g]]
+                ks = [st.k_ring[l, b, g, slot_of(dims, p)] for p in past] + [own_k[g]]
+                vs = [st.v_ring[l, b, g, slot_of(dims, p)] for p in past] + [own_v[g]]
                 sc = np.array([heads_q[hq] @ kk for kk in ks]) / np.sqrt(dh)
                 wts = np.exp(sc - sc.max())
                 wts /= wts.sum()

@@ -69,3 +69,9 @@ def prefilled(d: Dims, W, ctx_lens, seed: int = 1, anchors=None, offset: int = 0
 
 def with_window(d: Dims, window: int, extra_slots: int = 0) -> Dims:
     return replace(d, window=window, cache_slots=window + d.block_k + extra_slots)
+
+
+def with_sink(d: Dims, sink: int, window: int, extra_slots: int = 0) -> Dims:
+    """Attention sink of `sink` positions plus a window of `window`: sink slots, then
+    a ring of window + k (+ extra) slots."""
+    return replace(d, sink=sink, window=window, cache_slots=sink + window + d.block_k + extra_slots)

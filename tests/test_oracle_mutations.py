@@ -10,17 +10,18 @@ import pytest
 
 from oracle import bruteforce as bf
 from oracle import dflash_oracle as orc
-from tests.helpers import prefilled, tiny_dims, tiny_weights, with_window
+from tests.helpers import prefilled, tiny_dims, tiny_weights, with_sink, with_window
 
 _rope, _rms, _attend, _silu, _linear = orc.rope, orc.rms_norm, orc.attend, orc.silu, orc.linear
-_window, _accepted = orc.window_positions, orc.accepted_length
+_window, _accepted, _slot = orc.window_positions, orc.accepted_length, orc.slot_of
 
 
 def battery() -> bool:
     """True iff the oracle agrees with the brute force and the verify definition."""
     try:
-        for ctx, window, k in [([9, 3], 6, 4), ([4, 12], 5, 3)]:
-            d = with_window(tiny_dims(block_k=k, batch=2), window)
+        for ctx, window, k, sink in [([9, 3], 6, 4, 0), ([4, 12], 5, 3, 0), ([15, 4], 4, 3, 2)]:
+            d = with_window(tiny_dims(block_k=k, batch=2), window) if sink == 0 else \
+                with_sink(tiny_dims(block_k=k, batch=2), sink, window)
             W = tiny_weights(d, seed=21)
             st, hist = prefilled(d, W, ctx, seed=22, anchors=[2, 17])
             z = orc.draft_step(d, W, st)["logits"]
@@ -99,6 +100,19 @@ def _window_long(dims, P):
     return np.arange(max(0, P - dims.window - 1), P)
 
 
+def _window_sink_twice(dims, P):
+    s = min(dims.sink, P)
+    return np.concatenate([np.arange(0, s), np.arange(max(0, P - dims.window), P)])
+
+
+def _window_sink_ignored(dims, P):
+    return np.arange(max(0, P - dims.window), P)
+
+
+def _slot_sink_in_ring(dims, p):
+    return int(p) % dims.cache_slots
+
+
 def _accept_count_all(draft_row, target_row, k):
     return int(sum(int(draft_row[i]) == int(target_row[i]) for i in range(k)))
 
@@ -117,6 +131,9 @@ MUTATIONS = {
     "window_one_short": ("window_positions", _window_short),
     "window_one_long": ("window_positions", _window_long),
     "accept_counts_all_matches": ("accepted_length", _accept_count_all),
+    "sink_counted_twice": ("window_positions", _window_sink_twice),
+    "sink_ignored": ("window_positions", _window_sink_ignored),
+    "sink_slots_in_the_ring": ("slot_of", _slot_sink_in_ring),
 }
 
 

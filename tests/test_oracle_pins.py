@@ -6,7 +6,10 @@
 * invariants: window >= context is full attention, block of 1 is a decode step,
   a global position shift leaves logits unchanged, ring rotation leaves logits
   unchanged, the block is bidirectional, tentative rows + rollback equal
-  injecting only the committed rows, exhaustive greedy verification.
+  injecting only the committed rows, exhaustive greedy verification;
+* the attention sink (first s positions stay visible): brute force with its own
+  visibility rule, over steps with rollback; a sink inside the window changes
+  nothing; a block of one with a sink is a decode step.
 """
 import itertools
 from dataclasses import replace
@@ -18,7 +21,7 @@ import torch
 from block_diffusion_speculative_dflash_amd import synth
 from oracle import bruteforce as bf
 from oracle import dflash_oracle as orc
-from tests.helpers import prefilled, random_taps, tiny_dims, tiny_weights, with_window
+from tests.helpers import prefilled, random_taps, tiny_dims, tiny_weights, with_sink, with_window
 
 RNG = np.random.default_rng(1234)
 
@@ -233,3 +236,68 @@ def test_oracle_is_deterministic():
         st, _ = prefilled(d, W, [9, 5], seed=20)
         z.append(orc.draft_step(d, W, st)["logits"])
     assert np.array_equal(z[0], z[1])
+
+
+# ---------------------------------------------------------------- attention sink
+SINK_SCENARIOS = [
+    dict(ctx=[1, 5], sink=2, window=4, k=3),     # fewer committed positions than the sink; inside the window
+    dict(ctx=[6, 7], sink=2, window=4, k=3),     # window about to leave the sink behind
+    dict(ctx=[15, 23], sink=2, window=4, k=3),   # ring wrapped several times, sink kept
+    dict(ctx=[12, 9], sink=3, window=2, k=4),    # window smaller than the block and the sink
+]
+
+
+@pytest.mark.parametrize("sc", SINK_SCENARIOS, ids=lambda s: f"ctx{s['ctx']}_s{s['sink']}_w{s['window']}_k{s['k']}")
+def test_sink_draft_step_matches_bruteforce(sc):
+    d = with_sink(tiny_dims(block_k=sc["k"], batch=2), sc["sink"], sc["window"], extra_slots=1)
+    W = tiny_weights(d, seed=31)
+    st, hist = prefilled(d, W, sc["ctx"], seed=32, anchors=[5, 21])
+    out = orc.draft_step(d, W, st)
+    for b, P in enumerate(sc["ctx"]):
+        ref = np.array(bf.block_logits(d, W, hist[b], P, int(st.anchor[b])))
+        np.testing.assert_allclose(out["logits"][b], ref, rtol=1e-10, atol=1e-10)
+        assert np.all(np.isfinite(out["logits"][b]))
+
+
+def test_sink_rows_survive_rounds_and_rollbacks():
+    d = with_sink(tiny_dims(batch=2, block_k=4), 2, 5)
+    W = tiny_weights(d, seed=33)
+    st, hist = prefilled(d, W, [3, 8], seed=34, anchors=[6, 11])
+    planted = [[4, 0], [1, 4], [3, 2], [0, 3], [4, 4], [2, 1], [0, 0]]
+    for step, a_star in enumerate(planted):
+        out = orc.draft_step(d, W, st)
+        for b in range(2):
+            ref = np.array(bf.block_logits(d, W, hist[b], int(st.ctx_len[b]), int(st.anchor[b])))
+            np.testing.assert_allclose(out["logits"][b], ref, rtol=1e-10, atol=1e-10)
+        fill = synth.target_fill(d.block_k, 1, 2, seed=300 + step)[0]
+        T = synth.plant_targets(out["draft"], np.array(a_star), fill, d.vocab)
+        taps = random_taps(d, 2, d.block_k + 1, seed=400 + step)
+        P = st.ctx_len.copy()
+        orc.fuse_inject(d, W, st, taps, np.full(2, d.block_k + 1), commit=False)
+        r = orc.verify_commit(d, st, out["draft"], T)
+        for b in range(2):
+            a = int(r["accept_len"][b])
+            for j in range(a + 1):
+                hist[b][int(P[b]) + j] = taps[b, j]
+    assert min(st.ctx_len) > d.sink + d.window + d.block_k   # the ring wrapped past the sink
+
+
+def test_sink_inside_the_window_changes_nothing():
+    base = tiny_dims(batch=2)
+    W = tiny_weights(base, seed=35)
+    ctx = [6, 4]
+    z0 = orc.draft_step(with_window(base, 6), W, prefilled(with_window(base, 6), W, ctx, seed=36)[0])["logits"]
+    d = with_sink(base, 3, 6)
+    z1 = orc.draft_step(d, W, prefilled(d, W, ctx, seed=36)[0])["logits"]
+    np.testing.assert_allclose(z1, z0, rtol=0, atol=1e-12)
+    d2 = with_sink(base, 3, 3)                         # window alone would drop positions 0..2
+    z2 = orc.draft_step(d2, W, prefilled(d2, W, ctx, seed=36)[0])["logits"]
+    np.testing.assert_allclose(z2[0], z0[0], rtol=0, atol=1e-12)   # sink + window = all 6
+
+
+def test_sink_block_of_one_is_a_decode_step():
+    d = with_sink(tiny_dims(block_k=1, batch=2), 2, 4)
+    W = tiny_weights(d, seed=37)
+    st, _ = prefilled(d, W, [11, 5], seed=38, anchors=[2, 19])
+    z = orc.draft_step(d, W, st)["logits"][:, 0]
+    np.testing.assert_allclose(z, orc.decode_step(d, W, st), rtol=1e-11, atol=1e-11)
