@@ -47,6 +47,9 @@ def parse():
                    help="for hardware-counter runs: 5 draft steps, then 5 copies of 1 GiB "
                         "(the copy calibrates FETCH_SIZE / WRITE_SIZE against known bytes)")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--sink", type=int, default=0,
+                   help="attention sink: positions 0..S-1 stay visible beside the window "
+                        "(adds S cache slots; the sink rows are injected before the prefill)")
     return p.parse_args()
 
 
@@ -91,6 +94,9 @@ def main() -> int:
 
     wl = configs.WORKLOADS[args.workload]
     d = wl.dims
+    if args.sink:
+        from dataclasses import replace
+        d = replace(d, sink=args.sink, cache_slots=d.cache_slots + args.sink)
     B, k, V = d.batch, d.block_k, d.vocab
     dev = "cuda"
     torch.cuda.init()
@@ -102,8 +108,14 @@ def main() -> int:
     cache = bd.alloc_cache(d, device=dev, ctx_len=ctx - pre, anchor=anchors)
     ws = bd.alloc_workspace(d, device=dev)
 
-    # prefill: inject the committed context (all of it, or the last W for SWA)
+    # prefill: inject the committed context (all of it, or the last W for SWA); with
+    # an attention sink, positions 0..S-1 first when the prefill starts past them
     n_max = d.max_inject_rows
+    if d.sink and int((ctx - pre).min()) >= d.sink:
+        cache["ctx_len"].zero_()
+        sr = torch.full((B,), d.sink, dtype=torch.int32, device=dev)
+        bd.dflash_fuse_inject(d, W, sink_taps(d, args.seed), sr, d.sink, True, cache, ws)
+        cache["ctx_len"].copy_(torch.as_tensor(ctx - pre, dtype=torch.int32))
     n_pre = int(pre.max())
     for r0 in range(0, n_pre, n_max):
         taps = prefill_taps(d, n_pre, r0, args.seed)
@@ -234,7 +246,7 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, wl, W, ctx, pre, anchors, a_tab)
+        cpu = cpu_baseline(args, d, W, ctx, pre, anchors, a_tab)
 
     res = {
         "metric": "draft+verify block steps/s & accepted tok/s at batch B; % of HBM/MFMA roofline",
@@ -250,8 +262,8 @@ def main() -> int:
         "dtype": "bf16" if d.dtype == configs.BF16 else "f32",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps, planted targets)",
         "config": {"workload": wl.name, "batch": B, "block_k": k, "context": int(ctx.max()),
-                   "window": d.window, "layers": d.n_layers, "hidden": d.hidden, "ffn": d.ffn,
-                   "vocab": V, "accept": [kind, q]},
+                   "window": d.window, "sink": d.sink, "layers": d.n_layers, "hidden": d.hidden,
+                   "ffn": d.ffn, "vocab": V, "accept": [kind, q]},
         "accepted_tok_s": round(accepted / elapsed, 1),
         "committed_tok_s": round(committed / elapsed, 1),
         "mean_accept": round(accepted / (args.steps * B), 4),
@@ -272,7 +284,13 @@ def prefill_taps(d, n_pre: int, r0: int, seed: int):
                            device="cuda")
 
 
-def cpu_baseline(args, wl, W, ctx, pre, anchors, a_tab):
+def sink_taps(d, seed: int):
+    """Taps of the attention-sink positions 0..S-1 of every sequence."""
+    from block_diffusion_speculative_dflash_amd import synth
+    return synth.make_taps(d, d.sink, seed=seed, stream=9_999, device="cuda")
+
+
+def cpu_baseline(args, d, W, ctx, pre, anchors, a_tab):
     """The fp64 oracle, as it stands, on this host: a bounded sample of the same
     workload (sequence 0's block steps; at batch 1 that is the whole batch)."""
     import torch
@@ -283,13 +301,16 @@ def cpu_baseline(args, wl, W, ctx, pre, anchors, a_tab):
         threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = None
-    d = wl.dims
     k = d.block_k
     cores = len(os.sched_getaffinity(0))
     log(f"[bench] cpu baseline: oracle on sequence 0, {args.cpu_steps} block steps, {cores} cores")
     Wn = {n: t.float().cpu().numpy() for n, t in W.items() if n != "packed"}
     st = orc.new_state(d, batch=1, ctx_len=[int(ctx[0] - pre[0])], anchor=[int(anchors[0])])
     n_pre, n_all = int(pre[0]), int(pre.max())
+    if d.sink and int((ctx - pre).min()) >= d.sink:
+        st.ctx_len[0] = 0
+        orc.fuse_inject(d, Wn, st, sink_taps(d, args.seed)[:1].float().cpu().numpy(), [d.sink], commit=True)
+        st.ctx_len[0] = int(ctx[0] - pre[0])
     if n_pre:
         rows = [prefill_taps(d, n_all, r0, args.seed)[:1] for r0 in range(0, n_all, d.max_inject_rows)]
         taps = torch.cat(rows, dim=1)[:, :n_pre].float().cpu().numpy()

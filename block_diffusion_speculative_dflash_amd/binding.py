@@ -29,7 +29,8 @@ WEIGHT_FIELDS = ("fuse_w", "fuse_norm", "embed", "mask_embed", "attn_norm", "w_q
 
 class DflashDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in _INT_FIELDS] + [("rms_eps", ctypes.c_float),
-                                                            ("rope_theta", ctypes.c_float)]
+                                                            ("rope_theta", ctypes.c_float),
+                                                            ("sink", ctypes.c_int32)]
 
 
 class DflashWeights(ctypes.Structure):
@@ -96,7 +97,7 @@ def status_string(status: int) -> str:
 def dims_struct(d: Dims) -> DflashDims:
     vals = {n: getattr(d, n) for n in _INT_FIELDS if n != "dtype"}
     vals["dtype"] = 1 if d.dtype == BF16 else 0
-    return DflashDims(**vals, rms_eps=d.rms_eps, rope_theta=d.rope_theta)
+    return DflashDims(**vals, rms_eps=d.rms_eps, rope_theta=d.rope_theta, sink=d.sink)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

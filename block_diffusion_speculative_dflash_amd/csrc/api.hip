@@ -35,7 +35,7 @@ bool dims_ok(const dflash_dims* d) {
   if (d->n_q_heads % d->n_kv_heads != 0) return false;
   if (d->head_dim != 64 && d->head_dim != 128) return false;
   if (d->ffn < 1 || d->vocab < 2 || d->n_taps < 1 || d->tap_dim < 1) return false;
-  if (d->window < 1 || d->cache_slots < d->window + d->block_k) return false;
+  if (d->window < 1 || d->sink < 0 || d->cache_slots < d->sink + d->window + d->block_k) return false;
   if (d->dtype != DFLASH_F32 && d->dtype != DFLASH_BF16) return false;
   if (d->max_inject_rows < d->block_k + 1) return false;
   if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.f)) return false;
@@ -100,7 +100,7 @@ AttnPlan attn_plan(const dflash_dims& d) {
   p.rows = 16 * nw;
   // Split keys only while the workgroups alone leave CUs idle (about four per CU),
   // keeping >= 128 keys per split; splits need a merge.
-  const int max_keys = d.window + d.block_k;
+  const int max_keys = d.sink + d.window + d.block_k;
   const long long base = static_cast<long long>(d.batch) * d.n_kv_heads * p.n_rb;
   const int want = static_cast<int>(std::max(1ll, (1024 + base - 1) / base));
   const int kps = std::max(128, round_up(cdiv(max_keys, want), 32));
@@ -276,6 +276,7 @@ GemmArgs base_args(const Ctx& c) {
   a.n_layers = c.d.n_layers;
   a.batch = c.d.batch;
   a.cache_slots = c.d.cache_slots;
+  a.sink = c.d.sink;
   a.ffn = c.d.ffn;
   a.theta = c.d.rope_theta;
   return a;
@@ -380,6 +381,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     at.head_dim = d.head_dim;
     at.cache_slots = d.cache_slots;
     at.window = d.window;
+    at.sink = d.sink;
     at.keys_per_split = L.ap.kps;
     at.max_splits = L.ap.max_splits;
     at.n_rb = L.ap.n_rb;

@@ -1,5 +1,6 @@
-// Block attention on MFMA: every query row of the block attends to the last
-// min(P, W) committed positions (the layer's K/V ring) and to all k block rows,
+// Block attention on MFMA: every query row of the block attends to the sink
+// positions 0..min(s, P)-1, the last W committed positions that are not sink
+// positions (the layer's K/V ring), and all k block rows,
 // with no causal mask inside the block (hotdry blog: one forward fills the whole
 // masked block, all-SWA drafter with window W; zhihu answer §4: parallel decoding
 // inside a block).
@@ -66,8 +67,11 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs a) {
   item /= a.n_rb;
   const int g = item % a.n_kv_heads, b = item / a.n_kv_heads;
   const int k = a.block_k, G = a.n_q_heads / a.n_kv_heads;
+  // key list: the sink positions 0..n_sink-1, the window positions ws..P-1, the block
   const int P = max(a.ctx_len[b], 0);
-  const int n_ctx = min(P, a.window);
+  const int n_sink = min(a.sink, P);
+  const int ws = max(n_sink, P - a.window);
+  const int n_ctx = n_sink + (P - ws);
   const int n_keys = n_ctx + k;
   const int n_split_b = (n_keys + a.keys_per_split - 1) / a.keys_per_split;
   if (split >= n_split_b) return;  // uniform per workgroup
@@ -83,17 +87,19 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs a) {
   const size_t seq_base = (static_cast<size_t>(b) * a.n_kv_heads + g) * a.cache_slots;
   const T* ck = static_cast<const T*>(a.cache_k) + seq_base * DH;
   const T* cv = static_cast<const T*>(a.cache_v) + seq_base * DH;
-  const int C = a.cache_slots;
-  const int slot0 = (P - n_ctx) % C;  // ring slot of key 0 (n_ctx < C)
+  // slots: sink position p in slot p; later positions p in slot s + (p - s) mod R
+  const int sk = a.sink, R = a.cache_slots - a.sink;
+  const int wrel0 = P > sk ? (ws - sk) % R : 0;  // ring offset of the first window position
   const int blk_stride = a.n_kv_heads * DH;
   const T* kblk = kbg + (static_cast<size_t>(b) * k * a.n_kv_heads + g) * DH;
   const T* vblk = vbg + (static_cast<size_t>(b) * k * a.n_kv_heads + g) * DH;
-  // key j's row: ring slot slot0 + j (mod C) of the window, then block row j - n_ctx;
+  // key j's row: sink slot j, ring slot of window key j, or block row j - n_ctx;
   // selects only (no branch), so the unrolled loads stay in flight together
   auto key_ptr = [&](int j, const T* ring, const T* blk) -> const T* {
-    const int sl = slot0 + j;
-    const uintptr_t pr = reinterpret_cast<uintptr_t>(ring + (sl >= C ? sl - C : sl) * DH);
-    const uintptr_t pb = reinterpret_cast<uintptr_t>(blk + (j - n_ctx) * blk_stride);
+    const int t = max(wrel0 + j - n_sink, 0);  // window keys: < 2R
+    const int sl = j < n_sink ? j : sk + (t >= R ? t - R : t);
+    const uintptr_t pr = reinterpret_cast<uintptr_t>(ring + sl * DH);
+    const uintptr_t pb = reinterpret_cast<uintptr_t>(blk + max(j - n_ctx, 0) * blk_stride);
     const uintptr_t m = uintptr_t(0) - static_cast<uintptr_t>(j < n_ctx);
     return reinterpret_cast<const T*>((pr & m) | (pb & ~m));
   };
@@ -271,7 +277,8 @@ __global__ __launch_bounds__(kThreads) void attention_merge_kernel(AttnArgs a) {
   const int rb = grp_i % a.n_rb, g = (grp_i / a.n_rb) % a.n_kv_heads, b = grp_i / (a.n_rb * a.n_kv_heads);
   const int k = a.block_k, G = a.n_q_heads / a.n_kv_heads;
   const int P = max(a.ctx_len[b], 0);
-  const int n_keys = min(P, a.window) + k;
+  const int n_sink = min(a.sink, P);
+  const int n_keys = n_sink + (P - max(n_sink, P - a.window)) + k;
   const int n_split_b = (n_keys + a.keys_per_split - 1) / a.keys_per_split;
   if (n_split_b == 1) return;  // uniform per workgroup
   const int t = threadIdx.x, dq = t % TPR, sub = (t / TPR) % NSUB, rw = t / (TPR * NSUB);

@@ -8,7 +8,8 @@
 //   RESID   h += tile * rs, next RMSNorm input h * gain (packed) + per-tile sum of h^2
 //   SWIGLU  silu(gate) * up, both scaled by rs (tile columns: 32 gate, 32 up)
 //   QKV     q / k / v rows with RoPE on q and k (tile columns: 32 rotation pairs)
-//   INJECT  RoPE on K, scatter of K and V rows into the ring slots pos mod C
+//   INJECT  RoPE on K, scatter of K and V rows into their cache slots (positions
+//           below the sink keep slot = position, the rest ring over C - sink)
 // The split-vocab argmax differs between the two GEMMs and lives with each.
 #pragma once
 
@@ -122,7 +123,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
         if (kind == 0) dst = static_cast<TA*>(g.out) + (static_cast<size_t>(m) * g.n_q_heads + head) * dh;
         else dst = static_cast<TA*>(kind == 1 ? g.out2 : g.out3) + (static_cast<size_t>(m) * g.n_kv_heads + head) * dh;
       } else {
-        const int slot = pos % g.cache_slots;
+        const int slot = pos < g.sink ? pos : g.sink + (pos - g.sink) % (g.cache_slots - g.sink);
         dst = static_cast<TA*>(kind == 1 ? g.cache_k : g.cache_v) +
               (((static_cast<size_t>(layer) * g.batch + b) * g.n_kv_heads + head) * g.cache_slots + slot) * dh;
       }

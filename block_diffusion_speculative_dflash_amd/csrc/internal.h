@@ -62,6 +62,7 @@ struct GemmArgs {
   const int32_t* ctx_len;  // [B]
   const int32_t* n_rows;   // [B] (INJECT)
   int n_q_heads, n_kv_heads, head_dim, n_layers, batch, cache_slots, ffn;
+  int sink;  // INJECT: positions < sink keep slot = position; the rest ring over cache_slots - sink
   float theta;
   void* cache_k;  // [L, B, Hkv, C, dh]
   void* cache_v;
@@ -132,7 +133,7 @@ struct AttnArgs {
   float* part_o;   // [B, Hkv, n_rb, max_splits, 64, dh]
   float* part_ml;  // [B, Hkv, n_rb, max_splits, 64, 2]
   unsigned* counters;  // [B, Hkv, n_rb]
-  int batch, block_k, n_q_heads, n_kv_heads, head_dim, cache_slots, window;
+  int batch, block_k, n_q_heads, n_kv_heads, head_dim, cache_slots, window, sink;
   int keys_per_split, max_splits, n_rb, rows_per_block;  // rows_per_block: 16, 32, 48 or 64
 };
 hipError_t launch_attention(bool f32, const AttnArgs& a, hipStream_t stream);

@@ -77,13 +77,17 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
  *   batch B, block_k k (1..63), n_layers L, hidden d, n_q_heads Hq, n_kv_heads Hkv
  *   (Hq % Hkv == 0), head_dim dh (64 or 128), ffn F (SwiGLU width), vocab V,
  *   n_taps (the pages fix 5), tap_dim d_t, window W (committed positions each block
- *   query sees), cache_slots C (ring slots per layer/sequence/kv head, C >= W + k),
+ *   query sees), cache_slots C (slots per layer/sequence/kv head, C >= s + W + k),
  *   dtype (dflash_dtype), max_inject_rows (largest n_max a fuse_inject call may
- *   use, >= k + 1; sizes the workspace), rms_eps, rope_theta (RoPE base). */
+ *   use, >= k + 1; sizes the workspace), rms_eps, rope_theta (RoPE base), sink s
+ *   (attention sink: positions 0..s-1 stay visible to every block query after they
+ *   leave the window, as the aufer article's micro-op section names it for this
+ *   drafter; 0 = plain sliding window). */
 typedef struct {
   int32_t batch, block_k, n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn,
       vocab, n_taps, tap_dim, window, cache_slots, dtype, max_inject_rows;
   float rms_eps, rope_theta;
+  int32_t sink;
 } dflash_dims;
 
 /* (host) Device pointers to the drafter weights, all in dims->dtype, all
@@ -114,8 +118,9 @@ typedef struct {
 
 /* (host) The whole decode state, caller-owned device memory:
  *   k, v       [L, B, Hkv, C, dh], fp16 for a bf16 drafter and float for an fp32
- *              drafter (16-byte aligned); logical position p of sequence b
- *              lives in slot p % C; k rows carry RoPE at position p
+ *              drafter (16-byte aligned); logical position p of sequence b lives
+ *              in slot p if p < s (the sink), else in slot s + (p - s) % (C - s);
+ *              k rows carry RoPE at position p
  *   ctx_len    [B] int32 committed length P_b (a logical position, may exceed C)
  *   anchor     [B] int32 token at position P_b (the visible first row of the block)
  *   dev_error  [1] uint32 sticky DFLASH_DEVERR_* bits */
@@ -155,7 +160,8 @@ int dflash_pack_weights(const dflash_dims *dims, const dflash_weights *w, void *
  *   commit   (host) 0: rows are tentative (the per-round path, n_rows = k+1);
  *            1: also advance ctx_len[b] by n_rows[b] (prefill)
  * For every row and layer l: c = RMSNorm(fuse_w . concat(taps)) * fuse_norm, then
- * K = RoPE(W_k^l c, position) and V = W_v^l c are written to slot position % C. */
+ * K = RoPE(W_k^l c, position) and V = W_v^l c are written to the position's slot
+ * (see dflash_cache). */
 int dflash_fuse_inject(const dflash_dims *dims, const dflash_weights *w,
                        const void *taps, const int32_t *n_rows, int32_t n_max,
                        int32_t commit, const dflash_cache *cache, void *workspace,
@@ -165,8 +171,9 @@ int dflash_fuse_inject(const dflash_dims *dims, const dflash_weights *w,
  * forward fills the whole block; zhihu §5.3, §5.4).  Row 0 of sequence b's block is
  * embed[anchor[b]] at position P_b = ctx_len[b]; rows 1..k-1 are mask_embed at
  * P_b+1 .. P_b+k-1.  Each of the L pre-norm layers applies RMSNorm, the fused QKV
- * projection with RoPE, attention of every block row over the last min(P_b, W)
- * committed positions plus all k block rows (bidirectional inside the block, GQA),
+ * projection with RoPE, attention of every block row over the sink positions
+ * 0..min(s, P_b)-1, the last W committed positions that are not sink positions,
+ * and all k block rows (bidirectional inside the block, GQA),
  * the output projection with residual, and a SwiGLU MLP with residual.  A final
  * RMSNorm and the LM head give logits; row i's argmax (lowest id on ties) is the
  * draft for position P_b+i+1.

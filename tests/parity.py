@@ -89,10 +89,26 @@ class ParityRun:
         pre = np.asarray(prefill_rows, np.int64)
         anchors = np.asarray(anchors, np.int64)
         p0 = ctx_start - pre
+        s = self.sample
         self.cache = bd.alloc_cache(dims, ctx_len=p0, anchor=anchors)
         self.ws = bd.alloc_workspace(dims)
-        n_pre = int(pre.max())
+        self.st = orc.new_state(dims, batch=len(s), ctx_len=p0[s], anchor=anchors[s])
         n_max = dims.max_inject_rows
+        if dims.sink > 0 and int(p0.min()) >= dims.sink:
+            # attention sink: positions 0..s-1 are injected first, then the prefill
+            # continues at p0 (both sides), as a long context would have left them
+            sink_taps = synth.make_taps(dims, dims.sink, seed=seed, stream=10_000, device="cuda")
+            say(f"[parity] sink rows 0..{dims.sink - 1} (B={B})")
+            self.cache["ctx_len"].zero_()
+            sr = torch.full((B,), dims.sink, dtype=torch.int32, device="cuda")
+            bd.dflash_fuse_inject(dims, W, sink_taps, sr, dims.sink, True, self.cache, self.ws)
+            self.cache["ctx_len"].copy_(torch.as_tensor(p0, dtype=torch.int32))
+            torch.cuda.synchronize()
+            self.st.ctx_len[:] = 0
+            orc.fuse_inject(dims, self.Wn, self.st, sink_taps[s].float().cpu().numpy(),
+                            np.full(len(s), dims.sink), commit=True)
+            self.st.ctx_len[:] = p0[s]
+        n_pre = int(pre.max())
         if n_pre > 0:
             taps = synth.make_taps(dims, n_pre, seed=seed, stream=0, device="cuda")
             say(f"[parity] prefill {n_pre} rows in chunks of {n_max} (B={B})")
@@ -101,8 +117,6 @@ class ParityRun:
                 n_rows = torch.as_tensor(np.clip(pre - r0, 0, chunk.shape[1]), dtype=torch.int32).cuda()
                 bd.dflash_fuse_inject(dims, W, chunk, n_rows, chunk.shape[1], True, self.cache, self.ws)
             torch.cuda.synchronize()
-        s = self.sample
-        self.st = orc.new_state(dims, batch=len(s), ctx_len=p0[s], anchor=anchors[s])
         if n_pre > 0:
             orc.fuse_inject(dims, self.Wn, self.st, taps[s].float().cpu().numpy(), pre[s], commit=True)
         self.step_idx = 0
@@ -168,7 +182,7 @@ class ParityRun:
             vc = self.cache["v"][:, s].float().cpu().numpy()
             for j in range(len(s)):
                 P = int(self.st.ctx_len[j])
-                slots = orc.window_positions(d, P) % d.cache_slots
+                slots = np.array([orc.slot_of(d, int(p)) for p in orc.window_positions(d, P)], dtype=np.int64)
                 for ring, cache_np in ((self.st.k_ring, kc), (self.st.v_ring, vc)):
                     ref = ring[:, j][:, :, slots]
                     got = cache_np[:, j][:, :, slots]

@@ -52,6 +52,13 @@ def test_status_strings_and_workspace_query():
     assert L.dflash_workspace_bytes(ctypes.byref(bad)) == 0
     bad = bd.dims_struct(replace(configs.C1.dims, cache_slots=configs.C1.dims.window))
     assert L.dflash_workspace_bytes(ctypes.byref(bad)) == 0
+    bad = bd.dims_struct(replace(configs.C1.dims, sink=-1))
+    assert L.dflash_workspace_bytes(ctypes.byref(bad)) == 0
+    d = configs.C1.dims                            # sink slots come on top of window + k
+    bad = bd.dims_struct(replace(d, sink=2, cache_slots=d.window + d.block_k + 1))
+    assert L.dflash_workspace_bytes(ctypes.byref(bad)) == 0
+    good = bd.dims_struct(replace(d, sink=2, cache_slots=d.window + d.block_k + 2))
+    assert L.dflash_workspace_bytes(ctypes.byref(good)) > 0
 
 
 FAKE = 0x10000  # 16-byte aligned host integer, never dereferenced: validation fails first

@@ -3,6 +3,8 @@ sequences (every sequence's computation is independent of the others, so the
 oracle runs only the sampled ones while the GPU runs the whole batch in the
 launch configuration the benchmark times).  Two block steps each, with planted
 acceptance drawn from the workload's distribution."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 
@@ -31,6 +33,28 @@ def test_fullsize_parity(name):
     kind, q = w.accept
     a_tab = synth.planted_accept(kind, q, d.block_k, 2, d.batch, seed=0)
     run = ParityRun(d, W, ctx, synth.make_anchors(d), pre, sample=CASES[name], seed=0)
+    for s in range(2):
+        r = run.step(a_tab[s])
+        assert r.logits_ok, f"step {s}: max |dz| {r.logit_err} > 0.05"
+        assert r.draft_mismatch == 0
+        assert r.state_mismatch == 0
+        assert r.kv_ok, f"step {s}: kv error {r.kv_err}"
+    assert run.dev_error() == 0
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_swa_with_attention_sink():
+    """The MiMo-shaped SWA workload (batch 8, window 128, logical position 65536) with
+    an attention sink of 4: positions 0..3 stay visible beside the window."""
+    w = configs.C3
+    d = replace(w.dims, sink=4, cache_slots=w.dims.cache_slots + 4)
+    say(f"[fullsize] sink: B={d.batch} k={d.block_k} sink={d.sink} W={d.window} C={d.cache_slots}")
+    W = synth.make_weights(d, seed=0, device="cuda")
+    ctx = synth.make_context_lengths(w, seed=0)
+    pre = np.minimum(ctx, w.prefill)
+    kind, q = w.accept
+    a_tab = synth.planted_accept(kind, q, d.block_k, 2, d.batch, seed=0)
+    run = ParityRun(d, W, ctx, synth.make_anchors(d), pre, sample=[0, 5], seed=0)
     for s in range(2):
         r = run.step(a_tab[s])
         assert r.logits_ok, f"step {s}: max |dz| {r.logit_err} > 0.05"

@@ -94,6 +94,21 @@ def test_tiled_gemm_path_bf16():
     _assert_ok(_run(d, ctx, pre, steps))
 
 
+def test_attention_sink_fp32_ring_wrap():
+    """Attention sink of 4 beside a window of 24: one sequence far past the sink
+    (ring wrapped), one still inside the window."""
+    d = replace(configs.C1.dims, batch=2, sink=4, window=24, cache_slots=4 + 24 + 8 + 3, max_inject_rows=16)
+    say(f"[test] sink fp32 {d}")
+    _assert_ok(_run(d, [60, 13], [60, 13], [[8, 3], [2, 8], [5, 0], [0, 4]]))
+
+
+def test_attention_sink_gqa_bf16():
+    d = replace(configs.C1.dims, batch=3, block_k=4, n_q_heads=4, n_kv_heads=2, sink=3, window=16,
+                cache_slots=3 + 16 + 4, dtype=BF16, max_inject_rows=16)
+    say(f"[test] sink gqa bf16 {d}")
+    _assert_ok(_run(d, [40, 17, 2], [40, 17, 2], [[4, 0, 2], [1, 4, 3], [2, 2, 4], [0, 1, 1], [3, 3, 0]]))
+
+
 def test_block_of_one_and_empty_context():
     d = replace(configs.C1.dims, batch=2, block_k=1, window=32, cache_slots=33, max_inject_rows=8)
     say(f"[test] k=1, empty context {d}")
