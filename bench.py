@@ -3,7 +3,10 @@
 
 One step = dflash_draft_step -> target stand-in (planted target tokens) ->
 dflash_fuse_inject(commit = 0) -> dflash_verify_commit over the whole batch, with
-synthetic seeded inputs already resident in HBM.  Steps are captured as HIP
+synthetic seeded inputs already resident in HBM.  With --temperature T > 0 the step
+samples instead: dflash_draft_step_sampled (Gumbel-max drafts, logits and
+log-sum-exps out) -> target stand-in (planted target logits) -> dflash_fuse_inject
+-> dflash_verify_sampled (rejection sampling over the full vocabulary).  Steps are captured as HIP
 graphs and replayed.  Prints one JSON line:
   value      block steps/s (all B sequences per step)
   roofline   the dominant kernel (fused final-norm + LM-head + argmax), timed with
@@ -47,6 +50,9 @@ def parse():
                    help="for hardware-counter runs: 5 draft steps, then 5 copies of 1 GiB "
                         "(the copy calibrates FETCH_SIZE / WRITE_SIZE against known bytes)")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--temperature", type=float, default=0.0,
+                   help="0: greedy drafting and verification; > 0: sampled drafting and "
+                        "rejection-sampling verification at this temperature")
     p.add_argument("--sink", type=int, default=0,
                    help="attention sink: positions 0..S-1 stay visible beside the window "
                         "(adds S cache slots; the sink rows are injected before the prefill)")
@@ -155,8 +161,25 @@ def main() -> int:
     n_rows_step = torch.full((B,), k + 1, dtype=torch.int32, device=dev)
     pool = [synth.make_taps(d, k + 1, seed=args.seed, stream=1 + i, device=dev) for i in range(4)]
     saved_ctx = cache["ctx_len"].clone()
+    sampled = args.temperature > 0
+    if sampled:
+        # sampled target stand-in: resident filler logits, planted per step from the drafts
+        tgt_logits = synth.make_logits((B, k + 1, V), seed=args.seed, stream=31_337, device=dev)
+        saved_idx = torch.full((B, k + 1), -1, dtype=torch.int32, device=dev)
+        saved_val = torch.zeros((B, k + 1), dtype=torch.float32, device=dev)
+        logits = torch.empty((B, k, V), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, k), dtype=torch.float32, device=dev)
+        rng_step = torch.zeros(1, dtype=torch.int64, device=dev)
+        smp = bd.sampling_struct(args.temperature, args.seed + 1, 0, step_dev=rng_step)
 
     def step(taps):
+        if sampled:
+            bd.dflash_draft_step_sampled(d, W, cache, smp, draft, logits, lse, ws)
+            harness.plant_logits(draft, tgt_logits, a_tab_d, step_ctr, saved_idx, saved_val, accept,
+                                 acc_total, rng_step)
+            bd.dflash_fuse_inject(d, W, taps, n_rows_step, k + 1, False, cache, ws)
+            bd.dflash_verify_sampled(d, smp, draft, logits, lse, tgt_logits, cache, accept, out_tok, ws)
+            return
         bd.dflash_draft_step(d, W, cache, draft, None, ws)
         harness.plant(draft, target, a_tab_d, fill_d, step_ctr, accept, acc_total, V)
         bd.dflash_fuse_inject(d, W, taps, n_rows_step, k + 1, False, cache, ws)
@@ -209,13 +232,19 @@ def main() -> int:
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.head_launches)]
     for e0, e1 in pairs:
-        bd.dflash_draft_step_timed(d, W, cache, draft, None, ws, e0, e1)
+        if sampled:
+            bd.dflash_draft_step_sampled_timed(d, W, cache, smp, draft, logits, lse, ws, e0, e1)
+        else:
+            bd.dflash_draft_step_timed(d, W, cache, draft, None, ws, e0, e1)
     torch.cuda.synchronize()
     head_ms = float(np.mean([ev.elapsed_ms(e0, e1) for e0, e1 in pairs]))
     for e0, e1 in pairs:
         ev.destroy(e0)
         ev.destroy(e1)
-    cost = step_cost(d, float(ctx.mean()))
+    cost = step_cost(d, float(ctx.mean()), sampled=sampled)
+    head_epi = "EPI_SAMPLE" if sampled else "EPI_ARGMAX"
+    head_what = "LM head + Gumbel-max draw + logits/lse out" if sampled else "LM head + argmax"
+    head_traffic = None if sampled else measured_head_traffic(wl.name)
     head_gbs = cost.head_bytes / (head_ms * 1e-3) / 1e9
     step_gbs = cost.bytes_total * steps_per_s / 1e9
     head_tfs = cost.head_flops / (head_ms * 1e-3) / 1e12
@@ -229,19 +258,19 @@ def main() -> int:
         step_roof = {"bound": "mfma", "flops_per_step": cost.flops_total,
                      "achieved_TFLOPs": round(step_tfs, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
                      "frac": round(step_tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
-        head_roof = {"kernel": "gemm_tiled_kernel<EPI_ARGMAX> (final norm + LM head + argmax)",
+        head_roof = {"kernel": f"gemm_tiled_kernel<{head_epi}> (final norm + {head_what})",
                      "bound": "mfma", "achieved": round(head_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(head_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_head_traffic(wl.name),
+                     "traffic": head_traffic,
                      "avg_us": round(head_ms * 1e3, 2), "flops_per_launch": cost.head_flops}
     else:
         step_roof = {"bound": "hbm", "bytes_per_step": cost.bytes_total,
                      "achieved_GBs": round(step_gbs, 1), "peak_GBs": HBM_PEAK_GBS,
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)}
-        head_roof = {"kernel": "gemm_kernel<EPI_ARGMAX> (final norm + LM head + argmax)",
+        head_roof = {"kernel": f"gemm_kernel<{head_epi}> (final norm + {head_what})",
                      "bound": "hbm", "achieved": round(head_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(head_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_head_traffic(wl.name),
+                     "traffic": head_traffic,
                      "avg_us": round(head_ms * 1e3, 2), "bytes_per_launch": cost.head_bytes}
 
     cpu = None
@@ -260,10 +289,11 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if d.dtype == configs.BF16 else "f32",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps, planted targets)",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps, planted targets"
+                + (", N(0,4) target logits with planted acceptance)" if sampled else ")"),
         "config": {"workload": wl.name, "batch": B, "block_k": k, "context": int(ctx.max()),
                    "window": d.window, "sink": d.sink, "layers": d.n_layers, "hidden": d.hidden,
-                   "ffn": d.ffn, "vocab": V, "accept": [kind, q]},
+                   "ffn": d.ffn, "vocab": V, "accept": [kind, q], "temperature": args.temperature},
         "accepted_tok_s": round(accepted / elapsed, 1),
         "committed_tok_s": round(committed / elapsed, 1),
         "mean_accept": round(accepted / (args.steps * B), 4),
@@ -317,13 +347,27 @@ def cpu_baseline(args, d, W, ctx, pre, anchors, a_tab):
         orc.fuse_inject(d, Wn, st, taps, [n_pre], commit=True)
     taps_step = synth.make_taps(d, k + 1, seed=args.seed, stream=1, device="cuda")[:1].float().cpu().numpy()
     fill = synth.target_fill(k, 1, 1, seed=args.seed + 1)[0]
+    temp = args.temperature
+    if temp > 0:
+        from oracle import sampling as sp
+        fill_logits = synth.make_logits((1, k + 1, d.vocab), seed=args.seed, stream=31_337)
     t0 = time.perf_counter()
     committed = 0
     for s in range(args.cpu_steps):
-        o = orc.draft_step(d, Wn, st, want_logits=False)
-        T = synth.plant_targets(o["draft"], a_tab[s, :1], fill, d.vocab)
-        orc.fuse_inject(d, Wn, st, taps_step, [k + 1], commit=False)
-        r = orc.verify_commit(d, st, o["draft"], T)
+        if temp > 0:
+            # sampled round: Gumbel-max drafts, planted target logits, rejection sampling
+            o = orc.draft_step(d, Wn, st, want_logits=True)
+            sd = sp.sample_drafts(o["logits"], temp, args.seed + 1, s)
+            tl = synth.plant_target_logits(torch.as_tensor(o["logits"], dtype=torch.float32), sd["draft"],
+                                           a_tab[s, :1], fill_logits)
+            orc.fuse_inject(d, Wn, st, taps_step, [k + 1], commit=False)
+            r = sp.verify_sampled(sd["draft"], o["logits"], tl.double().numpy(), temp, args.seed + 1, s)
+            sp.commit_sampled(d, st, r)
+        else:
+            o = orc.draft_step(d, Wn, st, want_logits=False)
+            T = synth.plant_targets(o["draft"], a_tab[s, :1], fill, d.vocab)
+            orc.fuse_inject(d, Wn, st, taps_step, [k + 1], commit=False)
+            r = orc.verify_commit(d, st, o["draft"], T)
         committed += int(r["accept_len"][0]) + 1
     dt = time.perf_counter() - t0
     per_seq_step = dt / args.cpu_steps
@@ -332,8 +376,9 @@ def cpu_baseline(args, d, W, ctx, pre, anchors, a_tab):
             "blas_threads": threads, "kind": "oracle",
             "committed_tok_s": round(committed / dt, 4),
             "seconds": round(dt, 2),
-            "sample": f"{args.cpu_steps} block steps of sequence 0 (of {d.batch}), fp64 numpy; "
-                      f"full-batch rate = per-sequence rate / {d.batch}"}
+            "sample": f"{args.cpu_steps} block steps of sequence 0 (of {d.batch}), fp64 numpy"
+                      + (f", sampled at T={temp}" if temp > 0 else "")
+                      + f"; full-batch rate = per-sequence rate / {d.batch}"}
 
 
 if __name__ == "__main__":

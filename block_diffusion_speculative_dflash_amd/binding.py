@@ -42,6 +42,11 @@ class DflashCache(ctypes.Structure):
                 ("anchor", ctypes.c_void_p), ("dev_error", ctypes.c_void_p)]
 
 
+class DflashSampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("reserved", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64), ("step", ctypes.c_uint64), ("step_dev", ctypes.c_void_p)]
+
+
 class DFlashError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {status_string(status)} ({status})")
@@ -52,7 +57,8 @@ _lib: Optional[ctypes.CDLL] = None
 
 EXPORTED = ("dflash_workspace_bytes", "dflash_status_string", "dflash_packed_bytes",
             "dflash_pack_weights", "dflash_fuse_inject", "dflash_draft_step",
-            "dflash_verify_commit", "dflash_draft_step_timed")
+            "dflash_verify_commit", "dflash_draft_step_timed", "dflash_draft_step_sampled",
+            "dflash_draft_step_sampled_timed", "dflash_verify_sampled")
 
 
 def lib() -> ctypes.CDLL:
@@ -85,6 +91,15 @@ def lib() -> ctypes.CDLL:
     L.dflash_verify_commit.argtypes = [ctypes.POINTER(DflashDims), P, P, ctypes.POINTER(DflashCache),
                                        P, P, P]
     L.dflash_verify_commit.restype = ctypes.c_int
+    L.dflash_draft_step_sampled.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashWeights),
+                                            ctypes.POINTER(DflashCache), ctypes.POINTER(DflashSampling),
+                                            P, P, P, P, S, P]
+    L.dflash_draft_step_sampled.restype = ctypes.c_int
+    L.dflash_draft_step_sampled_timed.argtypes = L.dflash_draft_step_sampled.argtypes + [P, P]
+    L.dflash_draft_step_sampled_timed.restype = ctypes.c_int
+    L.dflash_verify_sampled.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashSampling),
+                                        P, P, P, P, ctypes.POINTER(DflashCache), P, P, P, S, P]
+    L.dflash_verify_sampled.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -198,6 +213,49 @@ def dflash_verify_commit(dims: Dims, draft: torch.Tensor, target: torch.Tensor, 
     st = lib().dflash_verify_commit(ctypes.byref(ds), _ptr(draft), _ptr(target), ctypes.byref(cs),
                                     _ptr(accept_len), _ptr(out_tokens), _stream(stream))
     _check("dflash_verify_commit", st)
+
+
+def sampling_struct(temperature: float, seed: int, step: int,
+                    step_dev: Optional[torch.Tensor] = None) -> DflashSampling:
+    """Sampling parameters; step_dev (one int64 device word) makes the kernels read
+    the step at run time, for graph replays."""
+    return DflashSampling(temperature=float(temperature), reserved=0, seed=int(seed) & (2**64 - 1),
+                          step=int(step) & (2**64 - 1), step_dev=_ptr(step_dev))
+
+
+def dflash_draft_step_sampled(dims: Dims, weights, cache, sampling: DflashSampling, draft: torch.Tensor,
+                              logits_out: torch.Tensor, lse_out: torch.Tensor, workspace: torch.Tensor,
+                              stream=None) -> None:
+    ds, ws, cs = dims_struct(dims), weights_struct(weights), cache_struct(cache)
+    st = lib().dflash_draft_step_sampled(ctypes.byref(ds), ctypes.byref(ws), ctypes.byref(cs),
+                                         ctypes.byref(sampling), _ptr(draft), _ptr(logits_out), _ptr(lse_out),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(stream))
+    _check("dflash_draft_step_sampled", st)
+
+
+def dflash_draft_step_sampled_timed(dims: Dims, weights, cache, sampling: DflashSampling,
+                                    draft: torch.Tensor, logits_out: torch.Tensor, lse_out: torch.Tensor,
+                                    workspace: torch.Tensor, head_begin: int, head_end: int,
+                                    stream=None) -> None:
+    ds, ws, cs = dims_struct(dims), weights_struct(weights), cache_struct(cache)
+    st = lib().dflash_draft_step_sampled_timed(ctypes.byref(ds), ctypes.byref(ws), ctypes.byref(cs),
+                                               ctypes.byref(sampling), _ptr(draft), _ptr(logits_out),
+                                               _ptr(lse_out), _ptr(workspace),
+                                               workspace.numel() * workspace.element_size(),
+                                               _stream(stream), head_begin, head_end)
+    _check("dflash_draft_step_sampled_timed", st)
+
+
+def dflash_verify_sampled(dims: Dims, sampling: DflashSampling, draft: torch.Tensor, draft_logits: torch.Tensor,
+                          draft_lse: torch.Tensor, target_logits: torch.Tensor, cache, accept_len: torch.Tensor,
+                          out_tokens: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    ds, cs = dims_struct(dims), cache_struct(cache)
+    st = lib().dflash_verify_sampled(ctypes.byref(ds), ctypes.byref(sampling), _ptr(draft), _ptr(draft_logits),
+                                     _ptr(draft_lse), _ptr(target_logits), ctypes.byref(cs), _ptr(accept_len),
+                                     _ptr(out_tokens), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dflash_verify_sampled", st)
 
 
 # ----------------------------------------------------------------------------- buffers

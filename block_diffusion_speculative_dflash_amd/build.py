@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
 HARNESS_LIB = os.path.join(PKG, "libdflash_harness.so")
 
-LIB_SOURCES = ["api.hip", "gemm.hip", "gemm_tiled.hip", "attention.hip", "misc.hip", "pack.hip"]
+LIB_SOURCES = ["api.hip", "gemm.hip", "gemm_tiled.hip", "attention.hip", "misc.hip", "pack.hip", "sampling.hip"]
 HARNESS_SOURCES = ["harness_plant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,6 +1,7 @@
 // C ABI of libdflash: host-side validation, packed-weight and workspace layouts,
 // launch plans and the kernel sequence of each call.  See include/dflash.h.
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 
 #include "../../include/dflash.h"
@@ -24,6 +25,7 @@ int round_up(int a, int b) { return cdiv(a, b) * b; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 bool is_f32(const dflash_dims& d) { return d.dtype == DFLASH_F32; }
 size_t elem(const dflash_dims& d) { return is_f32(d) ? 4 : 2; }  // weights, activations, cache
@@ -113,7 +115,8 @@ size_t partial_bytes(const dflash_dims& d);
 
 struct Layout {
   size_t h, xa, ssq, q, kb, vb, o, act, cu, ssq_c, partials, counters, keys, attn_cnt, attn_o,
-      attn_ml, total;
+      attn_ml, lse_part, v_part, v_cnt, v_dec, v_keys, total;
+  int v_chunks;
   int np_d, S_d, S_o, S_f;
   AttnPlan ap;
 };
@@ -148,6 +151,13 @@ Layout layout(const dflash_dims& d) {
   L.attn_cnt = take(groups * 4);
   L.attn_o = take(groups * L.ap.max_splits * 64 * d.head_dim * 4);
   L.attn_ml = take(groups * L.ap.max_splits * 64 * 2 * 4);
+  // sampled drafting / verification
+  L.lse_part = take(Mb * size_t(cdiv(d.vocab, kBN)) * 8);
+  L.v_chunks = cdiv(d.vocab, kVerifyChunk);
+  L.v_part = take(size_t(d.batch) * (d.block_k + 1) * L.v_chunks * 8);
+  L.v_cnt = take(size_t(d.batch) * 2 * 4);
+  L.v_dec = take(size_t(d.batch) * 16);
+  L.v_keys = take(size_t(d.batch) * 2 * kKeyStride * 8);
   L.total = off;
   return L;
 }
@@ -301,10 +311,20 @@ int run_gemm(int epi, const Ctx& c, GemmArgs a, bool allow_split, hipStream_t s)
   return DFLASH_OK;
 }
 
+bool sampling_ok(const dflash_sampling* smp) {
+  return smp != nullptr && smp->temperature > 0.f && std::isfinite(smp->temperature) && smp->reserved == 0 &&
+         (smp->step_dev == nullptr || aligned8(smp->step_dev));
+}
+
+// smp == nullptr: greedy drafts (argmax); otherwise Gumbel-max draws at temperature
+// smp->temperature, raw logits to logits_out and row log-sum-exps of logits / T to lse_out.
 int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_cache* cache,
-               int32_t* draft, float* logits_out, void* workspace, size_t workspace_bytes,
-               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+               const dflash_sampling* smp, int32_t* draft, float* logits_out, float* lse_out,
+               void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t ev0,
+               hipEvent_t ev1) {
   if (!dims_ok(dims) || w == nullptr || cache == nullptr || draft == nullptr) return DFLASH_E_INVALID;
+  if (smp != nullptr && (!sampling_ok(smp) || logits_out == nullptr || lse_out == nullptr || !aligned4(lse_out)))
+    return DFLASH_E_INVALID;
   const dflash_dims& d = *dims;
   const void* wp[] = {w->embed, w->mask_embed, w->attn_norm, w->mlp_norm, w->final_norm, w->packed};
   for (const void* p : wp)
@@ -452,9 +472,20 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   a.keys = c.at<unsigned long long>(L.keys);
   a.draft = draft;
   a.logits = logits_out;
+  const int epi = smp != nullptr ? EPI_SAMPLE : EPI_ARGMAX;
+  if (smp != nullptr) {
+    const GemmPlan hp = gemm_plan(d, EPI_SAMPLE, a.M, a.n_tiles, a.S, false, partial_bytes(d));
+    a.inv_temp = 1.f / smp->temperature;
+    a.seed = smp->seed;
+    a.step = smp->step;
+    a.step_dev = reinterpret_cast<const unsigned long long*>(smp->step_dev);
+    a.lse_part = c.at<float2>(L.lse_part);
+    a.n_parts = hp.tiled ? cdiv(a.n_tiles, hp.mt / kBN) : a.n_tiles;
+  }
   if (ev0) DF_CHECK(hipEventRecord(ev0, stream));
-  if (int st = run_gemm(EPI_ARGMAX, c, a, false, stream)) return st;
+  if (int st = run_gemm(epi, c, a, false, stream)) return st;
   if (ev1) DF_CHECK(hipEventRecord(ev1, stream));
+  if (smp != nullptr) DF_CHECK(launch_lse_merge(a.lse_part, a.n_parts, a.M, lse_out, stream));
   return DFLASH_OK;
 }
 
@@ -595,15 +626,33 @@ int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const v
 int dflash_draft_step(const dflash_dims* dims, const dflash_weights* w, const dflash_cache* cache,
                       int32_t* draft, float* logits_out, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
-  return draft_impl(dims, w, cache, draft, logits_out, workspace, workspace_bytes, stream, nullptr,
-                    nullptr);
+  return draft_impl(dims, w, cache, nullptr, draft, logits_out, nullptr, workspace, workspace_bytes, stream,
+                    nullptr, nullptr);
+}
+
+int dflash_draft_step_sampled(const dflash_dims* dims, const dflash_weights* w, const dflash_cache* cache,
+                              const dflash_sampling* sampling, int32_t* draft, float* logits_out,
+                              float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (sampling == nullptr) return DFLASH_E_INVALID;
+  return draft_impl(dims, w, cache, sampling, draft, logits_out, lse_out, workspace, workspace_bytes, stream,
+                    nullptr, nullptr);
 }
 
 int dflash_draft_step_timed(const dflash_dims* dims, const dflash_weights* w,
                             const dflash_cache* cache, int32_t* draft, float* logits_out,
                             void* workspace, size_t workspace_bytes, hipStream_t stream,
                             hipEvent_t head_begin, hipEvent_t head_end) {
-  return draft_impl(dims, w, cache, draft, logits_out, workspace, workspace_bytes, stream,
+  return draft_impl(dims, w, cache, nullptr, draft, logits_out, nullptr, workspace, workspace_bytes, stream,
+                    head_begin, head_end);
+}
+
+int dflash_draft_step_sampled_timed(const dflash_dims* dims, const dflash_weights* w,
+                                    const dflash_cache* cache, const dflash_sampling* sampling,
+                                    int32_t* draft, float* logits_out, float* lse_out, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream, hipEvent_t head_begin,
+                                    hipEvent_t head_end) {
+  if (sampling == nullptr) return DFLASH_E_INVALID;
+  return draft_impl(dims, w, cache, sampling, draft, logits_out, lse_out, workspace, workspace_bytes, stream,
                     head_begin, head_end);
 }
 
@@ -628,6 +677,47 @@ int dflash_verify_commit(const dflash_dims* dims, const int32_t* draft, const in
   v.block_k = dims->block_k;
   v.vocab = dims->vocab;
   DF_CHECK(launch_verify(v, stream));
+  return DFLASH_OK;
+}
+
+int dflash_verify_sampled(const dflash_dims* dims, const dflash_sampling* sampling, const int32_t* draft,
+                          const float* draft_logits, const float* draft_lse, const float* target_logits,
+                          const dflash_cache* cache, int32_t* accept_len, int32_t* out_tokens,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dims_ok(dims) || cache == nullptr || !sampling_ok(sampling)) return DFLASH_E_INVALID;
+  if (!draft || !draft_logits || !draft_lse || !target_logits || !accept_len || !out_tokens ||
+      !cache->ctx_len || !cache->anchor || !cache->dev_error)
+    return DFLASH_E_INVALID;
+  if (!aligned4(draft) || !aligned16(draft_logits) || !aligned4(draft_lse) || !aligned16(target_logits) ||
+      !aligned4(accept_len) || !aligned4(out_tokens))
+    return DFLASH_E_INVALID;
+  const dflash_dims& d = *dims;
+  const Layout L = layout(d);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < L.total) return DFLASH_E_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  VerifySampledArgs v{};
+  v.draft = draft;
+  v.draft_logits = draft_logits;
+  v.draft_lse = draft_lse;
+  v.target_logits = target_logits;
+  v.ctx_len = cache->ctx_len;
+  v.anchor = cache->anchor;
+  v.accept_len = accept_len;
+  v.out_tokens = out_tokens;
+  v.dev_error = cache->dev_error;
+  v.part = reinterpret_cast<float2*>(ws + L.v_part);
+  v.counters = reinterpret_cast<unsigned*>(ws + L.v_cnt);
+  v.decision = reinterpret_cast<float4*>(ws + L.v_dec);
+  v.keys = reinterpret_cast<unsigned long long*>(ws + L.v_keys);
+  v.batch = d.batch;
+  v.block_k = d.block_k;
+  v.vocab = d.vocab;
+  v.n_chunks = L.v_chunks;
+  v.inv_temp = 1.f / sampling->temperature;
+  v.seed = sampling->seed;
+  v.step = sampling->step;
+  v.step_dev = reinterpret_cast<const unsigned long long*>(sampling->step_dev);
+  DF_CHECK(launch_verify_sampled(v, stream));
   return DFLASH_OK;
 }
 

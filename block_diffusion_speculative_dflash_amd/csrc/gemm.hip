@@ -24,8 +24,72 @@
 #include "common.h"
 #include "epilogue.h"
 #include "internal.h"
+#include "philox.h"
 
 namespace dflash {
+
+// Sampled drafts from the reduced tile in LDS (EPI_SAMPLE).  A work unit is a group
+// of 4 rows times the column pair (c, c + 16) of one 32-column half of the tile:
+// one Philox block holds the Gumbel noise of its 8 logits.  Per row the unit keeps
+// the best key of s + noise (s = logits / T) and the log-sum-exp pair of s; the 32
+// units of a row group are 32 consecutive lanes and reduce with xor shuffles.
+template <int BM>
+__device__ __forceinline__ void sample_tile(const GemmArgs& g, const float (*tile)[kBN + 4], const float* rs,
+                                            int tile_n, int m0) {
+  static_assert((BM * 8) % kWave == 0, "units fill whole wavefronts");
+  const unsigned long long step = g.step_dev != nullptr ? *g.step_dev : g.step;
+  for (int u = threadIdx.x; u < BM * 8; u += kThreads) {
+    const int rg = u >> 5, cp = u & 31;
+    const int col0 = (cp >> 4) * 32 + (cp & 15);
+    const int v0 = tile_n * kBN + col0;
+    uint32_t h[8];
+    philox_u32x8(16ull * static_cast<unsigned>(v0 >> 5) + static_cast<unsigned>(v0 & 15),
+                 static_cast<unsigned>((m0 >> 2) + rg), step, 0ull, g.seed, kStreamDraft, h);
+    unsigned long long key[4];
+    float mx[4], sm[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = 4 * rg + rr, m = m0 + r;
+      float sv[2];
+      key[rr] = 0ull;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = col0 + 16 * j, v = tile_n * kBN + col;
+        sv[j] = -INFINITY;
+        if (v < g.N && m < g.M) {
+          const float z = tile[r][col] * rs[r];
+          if (g.logits != nullptr) g.logits[static_cast<size_t>(m) * g.N + v] = z;
+          sv[j] = z * g.inv_temp;
+          const unsigned long long kj = argmax_key(sv[j] + gumbel_f32(h[2 * rr + j]), v);
+          key[rr] = kj > key[rr] ? kj : key[rr];
+        }
+      }
+      mx[rr] = fmaxf(sv[0], sv[1]);
+      sm[rr] = mx[rr] == -INFINITY ? 0.f
+                                   : __builtin_amdgcn_exp2f((sv[0] - mx[rr]) * kLog2e) +
+                                         __builtin_amdgcn_exp2f((sv[1] - mx[rr]) * kLog2e);
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const unsigned long long ok = __shfl_xor(key[rr], o, kWave);
+        key[rr] = ok > key[rr] ? ok : key[rr];
+        const float om = __shfl_xor(mx[rr], o, kWave), os = __shfl_xor(sm[rr], o, kWave);
+        lse_merge(mx[rr], sm[rr], om, os);
+      }
+    if (cp == 0) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int m = m0 + 4 * rg + rr;
+        if (m < g.M) {
+          if (key[rr] != 0ull) atomicMax(&g.keys[static_cast<size_t>(m) * kKeyStride], key[rr]);
+          g.lse_part[static_cast<size_t>(m) * g.n_parts + tile_n] = make_float2(mx[rr], sm[rr]);
+        }
+      }
+    }
+  }
+}
 
 template <typename TIN, int MT, int EPI, int D>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
@@ -214,10 +278,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   }
   __syncthreads();
 
-  if constexpr (EPI != EPI_ARGMAX) {
+  if constexpr (EPI != EPI_ARGMAX && EPI != EPI_SAMPLE) {
     epilogue_tile<TIN, EPI, BM, kThreads>(g, tile, rs_s, tile_n, m0, hres);
-  } else {  // EPI_ARGMAX
-    for (int r = wave; r < BM; r += 4) {
+  } else {  // EPI_ARGMAX, EPI_SAMPLE
+    if constexpr (EPI == EPI_SAMPLE) sample_tile<BM>(g, tile, rs_s, tile_n, m0);
+    else for (int r = wave; r < BM; r += 4) {
       const int m = m0 + r;
       if (m >= g.M) continue;
       const int n = tile_n * kBN + lane;
@@ -272,6 +337,7 @@ static hipError_t launch_epi(int epi, const GemmPlan& p, const GemmArgs& a, hipS
     case EPI_RESID: return launch_mt<TIN, EPI_RESID>(p, a, s);
     case EPI_SWIGLU: return launch_mt<TIN, EPI_SWIGLU>(p, a, s);
     case EPI_ARGMAX: return launch_mt<TIN, EPI_ARGMAX>(p, a, s);
+    case EPI_SAMPLE: return launch_mt<TIN, EPI_SAMPLE>(p, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -31,6 +31,7 @@
 #include "common.h"
 #include "epilogue.h"
 #include "internal.h"
+#include "philox.h"
 
 namespace dflash {
 
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
       f = 1.f / sqrtf(sum / static_cast<float>(g.norm_dim) + g.eps);
     }
     rs_s[tid] = f;
-    if constexpr (EPI == EPI_ARGMAX) best_s[tid] = 0ull;
+    if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) best_s[tid] = 0ull;
   }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -267,6 +268,61 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
         }
         if ((lane & 15) == 0 && key != 0ull) atomicMax(&best_s[r], key);
       }
+  } else if constexpr (EPI == EPI_SAMPLE) {
+    // sampled drafts straight from the accumulators: for each pair of adjacent 16 x 16
+    // column blocks (2p, 2p + 1) one Philox block gives the noise of the lane's 4 rows
+    // x 2 columns; per row the best key of s + noise (s = logits / T) and the
+    // log-sum-exp pair of s go across the 16 lanes sharing the row (xor 1, 2, 4, 8),
+    // then across the NWN column wavefronts through LDS (the stage buffers are dead)
+    float2* lse_s = reinterpret_cast<float2*>(smem);  // [BM][NWN]
+    const unsigned long long step = g.step_dev != nullptr ? *g.step_dev : g.step;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const int rb = (wm * WM + i) * 16 + 4 * (lane >> 4);
+      uint32_t h[WN / 2][8];
+#pragma unroll
+      for (int p = 0; p < WN / 2; ++p) {
+        const int cb = tn * BFR + wn * WN + 2 * p;  // even: BFR and WN are
+        philox_u32x8<true>(16ull * static_cast<unsigned>(cb >> 1) + static_cast<unsigned>(lane & 15),
+                     static_cast<unsigned>((m0 + rb) >> 2), step, 0ull, g.seed, kStreamDraft, h[p]);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = rb + rr, m = m0 + r;
+        const float f = rs_s[r];
+        unsigned long long key = 0ull;
+        float sv[WN], mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const int n = (tn * BFR + wn * WN + j) * 16 + (lane & 15);
+          sv[j] = -INFINITY;
+          if (n < g.N && m < g.M) {
+            const float z = acc[i][j][rr] * f;
+            if (g.logits != nullptr) g.logits[static_cast<size_t>(m) * g.N + n] = z;
+            sv[j] = z * g.inv_temp;
+            const unsigned long long kj = argmax_key(sv[j] + gumbel_f32(h[j >> 1][2 * rr + (j & 1)]), n);
+            key = kj > key ? kj : key;
+          }
+          mx = fmaxf(mx, sv[j]);
+        }
+        float sm = 0.f;
+        if (mx != -INFINITY) {
+#pragma unroll
+          for (int j = 0; j < WN; ++j) sm += __builtin_amdgcn_exp2f((sv[j] - mx) * kLog2e);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const unsigned long long other = __shfl_xor(key, o, kWave);
+          key = other > key ? other : key;
+          const float om = __shfl_xor(mx, o, kWave), os = __shfl_xor(sm, o, kWave);
+          lse_merge(mx, sm, om, os);
+        }
+        if ((lane & 15) == 0) {
+          if (key != 0ull) atomicMax(&best_s[r], key);
+          lse_s[r * NWN + wn] = make_float2(mx, sm);
+        }
+      }
+    }
   } else if (g.splits > 1) {
     // the accumulators are dead here: this workgroup's partials are in memory
 #pragma unroll 1
@@ -327,10 +383,20 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
     }
   }
 
-  if constexpr (EPI == EPI_ARGMAX) {
+  if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) {
     __syncthreads();
     for (int r = tid; r < BM; r += NT)
       if (m0 + r < g.M) atomicMax(&g.keys[static_cast<size_t>(m0 + r) * kKeyStride], best_s[r]);
+    if constexpr (EPI == EPI_SAMPLE) {
+      const float2* lse_s = reinterpret_cast<const float2*>(smem);
+      for (int r = tid; r < BM; r += NT) {
+        if (m0 + r >= g.M) continue;
+        float mx = -INFINITY, sm = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWN; ++w) lse_merge(mx, sm, lse_s[r * NWN + w].x, lse_s[r * NWN + w].y);
+        g.lse_part[static_cast<size_t>(m0 + r) * g.n_parts + tn] = make_float2(mx, sm);
+      }
+    }
     unsigned* counter = &g.counters[tm];
     if (!arrive_last(counter, n_big, &last_s)) return;
     for (int r = tid; r < BM; r += NT) {
@@ -374,6 +440,7 @@ hipError_t launch_gemm_tiled(int epi, const GemmPlan& plan, const GemmArgs& a, h
     case EPI_RESID: return launch_tile<EPI_RESID>(plan, a, stream);
     case EPI_SWIGLU: return launch_tile<EPI_SWIGLU>(plan, a, stream);
     case EPI_ARGMAX: return plan.splits == 1 ? launch_tile<EPI_ARGMAX>(plan, a, stream) : hipErrorInvalidValue;
+    case EPI_SAMPLE: return plan.splits == 1 ? launch_tile<EPI_SAMPLE>(plan, a, stream) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

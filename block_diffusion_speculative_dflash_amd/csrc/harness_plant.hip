@@ -37,6 +37,56 @@ __global__ void plant_kernel(const int32_t* draft, int32_t* target, const int32_
   }
 }
 
+// Stand-in for sampled verification: target [B, k+1, V] holds filler logits.  Each
+// step first restores the entries the previous step planted, then, per sequence,
+// sets t[i, draft[i]] = +1e4 for i < a* (the draft gets probability ~1: accepted)
+// and t[a*, draft[a*]] = -1e4 when a* < k (probability 0: rejected), so exactly a*
+// drafts are accepted at any temperature up to 100.  Advances *rng_step (the device
+// step word the sampled calls read) and accumulates accepted lengths like
+// plant_kernel.
+__global__ void plant_logits_kernel(const int32_t* draft, float* target, const int32_t* a_star_tab,
+                                    int32_t* step_counter, int n_tab_steps, int32_t* saved_idx,
+                                    float* saved_val, const int32_t* accept_len, long long* accept_total,
+                                    unsigned long long* rng_step, int batch, int k, int vocab) {
+  __shared__ int step_s;
+  if (threadIdx.x == 0) step_s = step_counter[0];
+  __syncthreads();
+  const int s = step_s % n_tab_steps;
+  for (int idx = threadIdx.x; idx < batch * (k + 1); idx += blockDim.x) {
+    const int b = idx / (k + 1), i = idx % (k + 1);
+    float* row = target + static_cast<size_t>(idx) * vocab;
+    const int old = saved_idx[idx];
+    if (old >= 0 && old < vocab) row[old] = saved_val[idx];
+    const int a = min(max(a_star_tab[s * batch + b], 0), k);
+    int x = -1;
+    if (i < k && i <= a) {
+      x = min(max(draft[b * k + i], 0), vocab - 1);
+      saved_val[idx] = row[x];
+      row[x] = i < a ? 1.0e4f : -1.0e4f;
+    }
+    saved_idx[idx] = x;
+  }
+  if (threadIdx.x == 0) {
+    long long add = 0;
+    for (int b = 0; b < batch; ++b) add += accept_len[b];
+    accept_total[0] += add;
+    step_counter[0] = step_s + 1;
+    if (rng_step != nullptr) rng_step[0] += 1ull;
+  }
+}
+
+int dflash_harness_plant_logits(const int32_t* draft, float* target, const int32_t* a_star_tab,
+                                int32_t* step_counter, int n_tab_steps, int32_t* saved_idx, float* saved_val,
+                                const int32_t* accept_len, long long* accept_total,
+                                unsigned long long* rng_step, int batch, int k, int vocab,
+                                hipStream_t stream) {
+  if (batch < 1 || k < 1 || vocab < 2 || n_tab_steps < 1) return -1;
+  hipLaunchKernelGGL(plant_logits_kernel, dim3(1), dim3(256), 0, stream, draft, target, a_star_tab,
+                     step_counter, n_tab_steps, saved_idx, saved_val, accept_len, accept_total, rng_step,
+                     batch, k, vocab);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 int dflash_harness_plant(const int32_t* draft, int32_t* target, const int32_t* a_star_tab,
                          const int32_t* fill_tab, int32_t* step_counter, int n_tab_steps,
                          const int32_t* accept_len, long long* accept_total, int batch, int k,

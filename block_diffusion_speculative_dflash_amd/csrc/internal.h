@@ -22,6 +22,7 @@ enum Epi : int {
   EPI_RESID = 3,   // residual add into h, next RMSNorm input h*g (packed) + per-tile sum of h^2
   EPI_SWIGLU = 4,  // silu(gate) * up with the RMSNorm factor applied to both (packed)
   EPI_ARGMAX = 5,  // logits = factor * acc, split-vocab argmax, optional logits out
+  EPI_SAMPLE = 6,  // logits out, Gumbel-max draw over logits / T, per-tile log-sum-exp partials
 };
 
 constexpr int kBN = 64;           // output columns per workgroup tile (4 MFMA column blocks)
@@ -70,6 +71,13 @@ struct GemmArgs {
   int32_t* draft;            // [M]
   float* logits;             // [M, N] or nullptr
   uint32_t* dev_error;
+  // EPI_SAMPLE: s = logits / T; draft = argmax(s + Gumbel noise of row m);
+  // lse_part[m * n_parts + t] = (max, sum exp(s - max)) over column tile t
+  float inv_temp;
+  unsigned long long seed, step;
+  const unsigned long long* step_dev;  // when set, the step is read from here at run time
+  float2* lse_part;
+  int n_parts;
 };
 
 struct GemmPlan {
@@ -149,6 +157,33 @@ struct VerifyArgs {
   int batch, block_k, vocab;
 };
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+
+// Log-sum-exp of each row from its per-tile (max, sum) partials.
+hipError_t launch_lse_merge(const float2* part, int n_parts, int rows, float* lse, hipStream_t stream);
+
+// Sampled verification: per-row log-sum-exp of the target logits and the
+// acceptance scan (first kernel), then the residual / bonus draw and the commit.
+struct VerifySampledArgs {
+  const int32_t* draft;         // [B, k]
+  const float* draft_logits;    // [B, k, V]
+  const float* draft_lse;       // [B, k]  log-sum-exp of draft_logits / T
+  const float* target_logits;   // [B, k+1, V]
+  int32_t* ctx_len;
+  int32_t* anchor;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  uint32_t* dev_error;
+  float2* part;                 // [B, k+1, n_chunks] target row partials
+  unsigned* counters;           // [2 B] zero-initialised arrival counters
+  float4* decision;             // [B] (accepted length, target lse, draft lse, -)
+  unsigned long long* keys;     // [2 B * kKeyStride] zero-initialised argmax keys
+  int batch, block_k, vocab, n_chunks;
+  float inv_temp;
+  unsigned long long seed, step;
+  const unsigned long long* step_dev;  // when set, the step is read from here at run time
+};
+constexpr int kVerifyChunk = 8192;  // vocabulary entries per verify workgroup
+hipError_t launch_verify_sampled(const VerifySampledArgs& a, hipStream_t stream);
 
 hipError_t launch_commit_rows(int32_t* ctx_len, const int32_t* n_rows, int batch, int n_max,
                               uint32_t* dev_error, hipStream_t stream);

@@ -1,0 +1,264 @@
+// Sampled (temperature > 0) verification and the drafter's per-row log-sum-exp.
+//
+// Rejection sampling as the aufer article's data-flow section names the target's
+// check (the zhihu answer's §2 gives the draft / verify / accept loop, §6 the
+// guarantee that the target's distribution is kept).  With q_i = softmax(z_i / T)
+// the drafter's distribution at block row i, p_i = softmax(t_i / T) the target's:
+// draft x_i is accepted while u_i q_i(x_i) <= p_i(x_i); at the first rejection a
+// the emitted token is a draw from max(0, p_a - q_a) (from p_a if rounding left no
+// positive entry); after k acceptances it is a draw from p_k.  Draws are Gumbel-max
+// over Philox4x64-10 noise (philox.h).
+//
+// Two kernels, both reading the caller's fp32 logits once in 8192-entry chunks:
+//  1. (chunk, row i <= k, sequence b): log-sum-exp partial of t_i / T; the last
+//     workgroup of a sequence to arrive merges its k + 1 rows and runs the k
+//     acceptance tests in one wavefront (lane i, ballot, first zero = a);
+//  2. (chunk, sequence b): the residual (or bonus) row a, scores + noise, split-vocab
+//     argmax through keys; the last arriving workgroup commits: accepted length,
+//     emitted tokens, anchor, committed length.
+#include "common.h"
+#include "internal.h"
+#include "philox.h"
+
+namespace dflash {
+
+// log-sum-exp of one row from its per-tile partials: one workgroup per row
+__global__ __launch_bounds__(kThreads) void lse_merge_kernel(const float2* part, int n_parts, float* lse) {
+  __shared__ float red_m[kThreads / kWave], red_s[kThreads / kWave];
+  const int tid = threadIdx.x, row = blockIdx.x;
+  const float2* p = part + static_cast<size_t>(row) * n_parts;
+  float m = -INFINITY, s = 0.f;
+  for (int t0 = tid; t0 < n_parts; t0 += 4 * kThreads) {
+    float2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * kThreads;
+      v[u] = t < n_parts ? p[t] : make_float2(-INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) lse_merge(m, s, v[u].x, v[u].y);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, kWave), os = __shfl_xor(s, o, kWave);
+    lse_merge(m, s, om, os);
+  }
+  if ((tid & 63) == 0) {
+    red_m[tid >> 6] = m;
+    red_s[tid >> 6] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kThreads / kWave; ++w) lse_merge(m, s, red_m[w], red_s[w]);
+    lse[row] = m + ln_f32(s);
+  }
+}
+
+hipError_t launch_lse_merge(const float2* part, int n_parts, int rows, float* lse, hipStream_t stream) {
+  if (rows <= 0 || n_parts <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(rows), dim3(kThreads), 0, stream, part, n_parts, lse);
+  return hipGetLastError();
+}
+
+// Loads the n <= 8 logits row[v0 .. v0 + n) (v0 a multiple of 8); float4 pairs when
+// rows are 16-byte aligned (vocab % 4 == 0), scalar loads otherwise.
+__device__ __forceinline__ void load8(const float* row, int v0, int n, bool vec, float out[8]) {
+  if (vec && n == 8) {
+    const float4 a = *reinterpret_cast<const float4*>(row + v0);
+    const float4 c = *reinterpret_cast<const float4*>(row + v0 + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = c.x; out[5] = c.y; out[6] = c.z; out[7] = c.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = e < n ? row[v0 + e] : -INFINITY;
+  }
+}
+
+constexpr int kGroups = kVerifyChunk / (8 * kThreads);  // 8-entry groups per thread
+
+__global__ __launch_bounds__(kThreads) void verify_lse_kernel(VerifySampledArgs a) {
+  __shared__ float red_m[kThreads / kWave], red_s[kThreads / kWave];
+  __shared__ float lp_s[kWave + 1];
+  __shared__ int last_s;
+  const int chunk = blockIdx.x, i = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int k = a.block_k, V = a.vocab;
+  const bool vec = (V & 3) == 0;
+  const float* trow_b = a.target_logits + static_cast<size_t>(b) * (k + 1) * V;
+  const float* row = trow_b + static_cast<size_t>(i) * V;
+  const int v0 = chunk * kVerifyChunk, v1 = min(V, v0 + kVerifyChunk);
+
+  float vals[kGroups][8];
+#pragma unroll
+  for (int j = 0; j < kGroups; ++j) {
+    const int vb = v0 + 8 * (tid + kThreads * j);
+    load8(row, vb, max(0, min(8, v1 - vb)), vec, vals[j]);
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kGroups; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      vals[j][e] *= a.inv_temp;
+      m = fmaxf(m, vals[j][e]);
+    }
+  float s = 0.f;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f((vals[j][e] - m) * kLog2e);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, kWave), os = __shfl_xor(s, o, kWave);
+    lse_merge(m, s, om, os);
+  }
+  if ((tid & 63) == 0) {
+    red_m[tid >> 6] = m;
+    red_s[tid >> 6] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kThreads / kWave; ++w) lse_merge(m, s, red_m[w], red_s[w]);
+    float* dst = reinterpret_cast<float*>(a.part + (static_cast<size_t>(b) * (k + 1) + i) * a.n_chunks + chunk);
+    coherent_store(dst, m);
+    coherent_store(dst + 1, s);
+  }
+  if (!arrive_last(&a.counters[b], static_cast<unsigned>((k + 1) * a.n_chunks), &last_s)) return;
+
+  // last workgroup of sequence b: row log-sum-exps, then the acceptance tests
+  for (int r = tid; r <= k; r += kThreads) {
+    const float* pr = reinterpret_cast<const float*>(a.part + (static_cast<size_t>(b) * (k + 1) + r) * a.n_chunks);
+    float mm = -INFINITY, ss = 0.f;
+    for (int c = 0; c < a.n_chunks; ++c) {
+      const float2 v = coherent_load2(pr + 2 * c);
+      lse_merge(mm, ss, v.x, v.y);
+    }
+    lp_s[r] = mm + ln_f32(ss);
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const int lane = tid;
+    bool ok = false, bad = false;
+    if (lane < k) {
+      int x = a.draft[static_cast<size_t>(b) * k + lane];
+      if (x < 0 || x >= V) { bad = true; x = min(max(x, 0), V - 1); }
+      const float lp = trow_b[static_cast<size_t>(lane) * V + x] * a.inv_temp - lp_s[lane];
+      const float lq = a.draft_logits[(static_cast<size_t>(b) * k + lane) * V + x] * a.inv_temp -
+                       a.draft_lse[static_cast<size_t>(b) * k + lane];
+      uint32_t h[8];
+      const unsigned long long step = a.step_dev != nullptr ? *a.step_dev : a.step;
+      philox_u32x8(static_cast<unsigned>(lane), static_cast<unsigned>(b), step, 0ull, a.seed, kStreamAccept, h);
+      ok = lp - lq - ln_uniform(h[0]) >= 0.f;  // u q(x) <= p(x)
+    }
+    const unsigned long long ones = __ballot(ok);
+    const int acc = __ffsll(static_cast<long long>(~ones)) - 1;  // lanes >= k never accept: acc <= k
+    if (__ballot(bad) != 0ull && lane == 0) atomicOr(a.dev_error, 1u);
+    if (lane == 0) {
+      const float lq_a = acc < k ? a.draft_lse[static_cast<size_t>(b) * k + acc] : 0.f;
+      a.decision[b] = make_float4(static_cast<float>(acc), lp_s[acc], lq_a, 0.f);
+      reset_counter(&a.counters[b]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void verify_emit_kernel(VerifySampledArgs a) {
+  __shared__ unsigned long long red[2][kThreads / kWave];
+  __shared__ int last_s, tok_s;
+  const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int k = a.block_k, V = a.vocab;
+  const bool vec = (V & 3) == 0;
+  const float4 dec = a.decision[b];
+  const int acc = min(max(static_cast<int>(dec.x), 0), k);
+  const bool resid = acc < k;
+  const float lse_p = dec.y, lse_q = dec.z;
+  const float* trow = a.target_logits + (static_cast<size_t>(b) * (k + 1) + acc) * V;
+  const float* zrow = a.draft_logits + (static_cast<size_t>(b) * k + min(acc, k - 1)) * V;
+  const int v0 = chunk * kVerifyChunk, v1 = min(V, v0 + kVerifyChunk);
+
+  const unsigned long long step = a.step_dev != nullptr ? *a.step_dev : a.step;
+  unsigned long long kr = 0ull, kp = 0ull;  // residual draw, draw from p itself
+#pragma unroll
+  for (int j = 0; j < kGroups; ++j) {
+    const int vb = v0 + 8 * (tid + kThreads * j);
+    const int n = max(0, min(8, v1 - vb));
+    if (n == 0) continue;
+    float tv[8], zv[8];
+    load8(trow, vb, n, vec, tv);
+    if (resid) load8(zrow, vb, n, vec, zv);
+    uint32_t h[8];
+    philox_u32x8(static_cast<unsigned>(vb >> 3), static_cast<unsigned>(b), step, 0ull, a.seed, kStreamEmit, h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e >= n) continue;
+      const int v = vb + e;
+      const float g = gumbel_f32(h[e]);
+      const float lp = tv[e] * a.inv_temp - lse_p;
+      const unsigned long long kpe = argmax_key(lp + g, v);
+      kp = kpe > kp ? kpe : kp;
+      if (resid) {
+        const float lq = zv[e] * a.inv_temp - lse_q;
+        if (lp > lq) {  // log(p - q) = log p + log(1 - q / p)
+          const float lr = lp + ln_f32(-expm1f(lq - lp));
+          const unsigned long long kre = argmax_key(lr + g, v);
+          kr = kre > kr ? kre : kr;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long orr = __shfl_xor(kr, o, kWave), op = __shfl_xor(kp, o, kWave);
+    kr = orr > kr ? orr : kr;
+    kp = op > kp ? op : kp;
+  }
+  if (lane == 0) {
+    red[0][tid >> 6] = kr;
+    red[1][tid >> 6] = kp;
+  }
+  __syncthreads();
+  unsigned long long* keys = a.keys + static_cast<size_t>(b) * 2 * kKeyStride;
+  if (tid == 0) {
+    for (int w = 1; w < kThreads / kWave; ++w) {
+      kr = red[0][w] > kr ? red[0][w] : kr;
+      kp = red[1][w] > kp ? red[1][w] : kp;
+    }
+    if (kr != 0ull) atomicMax(&keys[0], kr);
+    if (kp != 0ull) atomicMax(&keys[kKeyStride], kp);
+  }
+  if (!arrive_last(&a.counters[a.batch + b], static_cast<unsigned>(a.n_chunks), &last_s)) return;
+
+  if (tid == 0) {
+    const unsigned long long fr = __hip_atomic_exchange(&keys[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long fp =
+        __hip_atomic_exchange(&keys[kKeyStride], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tok_s = argmax_key_index(resid && fr != 0ull ? fr : fp);
+  }
+  __syncthreads();
+  const int y = tok_s;
+  for (int t = tid; t <= k; t += kThreads) {
+    int tok = -1;
+    if (t < acc) tok = min(max(a.draft[static_cast<size_t>(b) * k + t], 0), V - 1);
+    else if (t == acc) tok = y;
+    a.out_tokens[static_cast<size_t>(b) * (k + 1) + t] = tok;
+  }
+  if (tid == 0) {
+    const int P = a.ctx_len[b];
+    if (P < 0) atomicOr(a.dev_error, 4u);
+    a.accept_len[b] = acc;
+    a.anchor[b] = y;
+    a.ctx_len[b] = max(P, 0) + acc + 1;
+    reset_counter(&a.counters[a.batch + b]);
+  }
+}
+
+hipError_t launch_verify_sampled(const VerifySampledArgs& a, hipStream_t stream) {
+  if (a.batch <= 0 || a.block_k <= 0 || a.block_k >= kWave || a.n_chunks <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(verify_lse_kernel, dim3(a.n_chunks, a.block_k + 1, a.batch), dim3(kThreads), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_emit_kernel, dim3(a.n_chunks, a.batch), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -26,6 +26,8 @@ def lib() -> ctypes.CDLL:
         P, I = ctypes.c_void_p, ctypes.c_int
         L.dflash_harness_plant.argtypes = [P, P, P, P, P, I, P, P, I, I, I, P]
         L.dflash_harness_plant.restype = ctypes.c_int
+        L.dflash_harness_plant_logits.argtypes = [P, P, P, P, I, P, P, P, P, P, I, I, I, P]
+        L.dflash_harness_plant_logits.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -43,3 +45,20 @@ def plant(draft: torch.Tensor, target: torch.Tensor, a_star_tab: torch.Tensor,
                                     accept_len.data_ptr(), accept_total.data_ptr(), B, k, vocab, s)
     if st != 0:
         raise RuntimeError(f"dflash_harness_plant failed ({st})")
+
+
+def plant_logits(draft: torch.Tensor, target: torch.Tensor, a_star_tab: torch.Tensor,
+                 step_counter: torch.Tensor, saved_idx: torch.Tensor, saved_val: torch.Tensor,
+                 accept_len: torch.Tensor, accept_total: torch.Tensor, rng_step=None, stream=None) -> None:
+    """Sampled-verification stand-in: restore last step's planted logits, plant
+    +1e4 / -1e4 on the drafted tokens so that a* drafts are accepted, advance
+    rng_step (if given), accept_total += sum(accept_len), step_counter += 1."""
+    B, k = draft.shape
+    V = target.shape[-1]
+    s = (torch.cuda.current_stream() if stream is None else stream).cuda_stream
+    st = lib().dflash_harness_plant_logits(draft.data_ptr(), target.data_ptr(), a_star_tab.data_ptr(),
+                                           step_counter.data_ptr(), a_star_tab.shape[0], saved_idx.data_ptr(),
+                                           saved_val.data_ptr(), accept_len.data_ptr(), accept_total.data_ptr(),
+                                           None if rng_step is None else rng_step.data_ptr(), B, k, V, s)
+    if st != 0:
+        raise RuntimeError(f"dflash_harness_plant_logits failed ({st})")

@@ -3,7 +3,10 @@
 Counted: every weight matrix once per call that uses it (so the K/V rows of w_qkv
 count in both the injection and the draft), the committed K/V window each layer
 reads, the new K/V rows, the taps, the embedding row of each anchor, and tokens.
-Not counted: activations between kernels (fusible) and logits (never written).
+Not counted: activations between kernels (fusible) and, for greedy steps, logits
+(never written).  A sampled step adds the drafter's logits (written once by the LM
+head, its log-sum-exp partials), the target's logits (read once by the verify) and
+the residual row of each sequence (target and draft rows re-read).
 """
 from __future__ import annotations
 
@@ -28,7 +31,7 @@ class StepCost:
     head_flops: float
 
 
-def step_cost(d: Dims, mean_ctx: float) -> StepCost:
+def step_cost(d: Dims, mean_ctx: float, sampled: bool = False) -> StepCost:
     e = 2 if d.dtype == BF16 else 4
     B, k, L, D = d.batch, d.block_k, d.n_layers, d.hidden
     Hq, Hkv, dh, F, V = d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn, d.vocab
@@ -47,7 +50,12 @@ def step_cost(d: Dims, mean_ctx: float) -> StepCost:
     flops = (2 * rows_d * (L * p_layer + p_head) + 4 * rows_d * L * Hq * dh * (n_ctx + k)
              + 2 * rows_i * (p_fuse + p_inject))
     head_bytes = p_head * e + rows_d * D * e + rows_d * 4 * ((D + 63) // 64) + rows_d * 4
-    return StepCost(weights + kv_read + kv_write + taps + tokens, flops, weights, kv_read,
+    extra = 0
+    if sampled:
+        logits_out = rows_d * V * 4 + rows_d * ((V + 63) // 64) * 8
+        head_bytes += logits_out
+        extra = logits_out + rows_d * ((V + 63) // 64) * 8 + rows_d * 4 + B * (k + 1) * V * 4 + 2 * B * V * 4
+    return StepCost(weights + kv_read + kv_write + taps + tokens + extra, flops, weights, kv_read,
                     kv_write, taps, head_bytes, 2.0 * rows_d * p_head)
 
 

@@ -12,7 +12,9 @@ Recipe (seed 0 unless a caller says otherwise):
   * taps (hidden states of the 5 target layers): N(0, 1), same rounding;
   * anchors and filler target tokens: uniform integers;
   * planted accepted length a*: min(G, k) with P(G >= j) = q^j (truncated
-    geometric), or uniform on 0..k.
+    geometric), or uniform on 0..k;
+  * logits standing in for the target's (sampled verification): N(0, s^2) fp32
+    filler, with planted rows (see plant_target_logits).
 Every tensor has its own generator seeded from (seed, tensor id, ...), so any
 tensor can be regenerated alone.  Tensors are drawn with torch on the device that
 will hold them; the oracle receives host copies of exactly those values.
@@ -32,7 +34,7 @@ _GAINS = ("fuse_norm", "attn_norm", "mlp_norm", "final_norm")
 WEIGHT_STD = 0.02
 
 # tensor ids of the non-weight streams
-_TAPS, _ANCHOR, _CTX, _ACCEPT, _FILL = 100, 101, 102, 103, 104
+_TAPS, _ANCHOR, _CTX, _ACCEPT, _FILL, _LOGITS = 100, 101, 102, 103, 104, 105
 
 
 def stream_seed(seed: int, *ids: int) -> int:
@@ -150,3 +152,31 @@ def plant_targets(draft: np.ndarray, a_star: np.ndarray, fill: np.ndarray,
         if a < k:
             T[b, a] = (draft[b, a] + 1 + int(fill[b, a]) % (vocab - 1)) % vocab
     return T.astype(np.int32)
+
+
+def make_logits(shape, seed: int = 0, stream: int = 0, scale: float = 2.0, device="cpu") -> torch.Tensor:
+    """N(0, scale^2) fp32 logits of the given shape."""
+    return _normal(tuple(shape), seed, (_LOGITS, stream), scale, torch.float32, device)
+
+
+def plant_target_logits(draft_logits: torch.Tensor, draft: np.ndarray, a_star: np.ndarray,
+                        fill: torch.Tensor, soft: float = 0.0, seed: int = 0) -> torch.Tensor:
+    """Target-logit stand-in for sampled verification, [B, k+1, V] fp32.
+
+    Rows i < a*: the draft's own logits (so p_i = q_i and the draft is accepted),
+    plus N(0, soft^2) noise when soft > 0 (then acceptance is likely, not certain);
+    row a* < k: filler with the drafted token's logit at -1e4 (p(x) = 0: rejected);
+    every other row, and the bonus row k: filler."""
+    z = draft_logits.float()
+    B, k, V = z.shape
+    t = fill.float().clone()
+    dr = np.asarray(draft, dtype=np.int64)
+    for b in range(B):
+        a = int(a_star[b])
+        if a > 0:
+            t[b, :a] = z[b, :a]
+            if soft > 0:
+                t[b, :a] += _normal((a, V), seed, (_LOGITS, 10_000 + b), soft, torch.float32, z.device)
+        if a < k:
+            t[b, a, int(dr[b, a])] = -1.0e4
+    return t

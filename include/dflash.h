@@ -200,6 +200,72 @@ int dflash_verify_commit(const dflash_dims *dims, const int32_t *draft,
                          const int32_t *target, const dflash_cache *cache,
                          int32_t *accept_len, int32_t *out_tokens, hipStream_t stream);
 
+/* (host) Parameters of sampled drafting and verification.
+ *   temperature  T > 0 and finite: the drafter's and the target's distributions are
+ *                softmax(logits / T) (one temperature for both)
+ *   reserved     must be 0
+ *   seed, step   key word and counter word of the random draws; give every decode
+ *                round a new step (draws of different rounds are then independent)
+ *   step_dev     optional device pointer: when non-NULL the kernels read the step
+ *                from *step_dev when they run and `step` is ignored, so a captured
+ *                HIP graph draws new numbers on every replay once the caller
+ *                advances that word between rounds
+ * Every draw comes from Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011), key (seed, stream), its four output
+ * words read as eight 32-bit values h (low half of word 0 first); a uniform is
+ * (h + 1/2) 2^-32 and a Gumbel variate -ln(-ln u); a sample of softmax(s) is
+ * argmax_v (s_v + Gumbel_v), smallest v on ties.  Streams and counters:
+ *   1  draft noise of block row m = b*k + i, token v: counter
+ *      (16 (v >> 5) + (v & 15), m >> 2, step, 0), value 2 (m & 3) + ((v >> 4) & 1)
+ *   2  acceptance uniform of row i of sequence b: counter (i, b, step, 0), value 0
+ *   3  noise of the emitted token of sequence b, token v: counter (v >> 3, b, step, 0),
+ *      value v & 7 */
+typedef struct {
+  float temperature;
+  uint32_t reserved;
+  uint64_t seed, step;
+  const uint64_t *step_dev;
+} dflash_sampling;
+
+/* Sampled drafting: the forward of dflash_draft_step, with draft[b, i] a sample of
+ * q_i = softmax(z[b, i] / T) instead of its argmax (stream 1 above).
+ *   sampling    (host) temperature, seed, step
+ *   draft       [B, k] int32 output
+ *   logits_out  [B, k, V] float output, required: the raw logits z (the verify
+ *               reads the draft's residual row from here)
+ *   lse_out     [B, k] float output, required: natural log-sum-exp of z[b, i] / T
+ * Reads the cache, writes only draft, logits_out, lse_out and the workspace. */
+int dflash_draft_step_sampled(const dflash_dims *dims, const dflash_weights *w,
+                              const dflash_cache *cache, const dflash_sampling *sampling,
+                              int32_t *draft, float *logits_out, float *lse_out,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Sampled verification by rejection sampling, commit / rollback, in place (the
+ * aufer article's data-flow section names the target's check rejection sampling;
+ * zhihu answer §2 gives the accept loop, §6 the guarantee that the output follows
+ * the target's distribution).  With p_i = softmax(target_logits[b, i] / T) and
+ * q_i = softmax(draft_logits[b, i] / T): draft[b, i] is accepted while
+ * u_i q_i(x_i) <= p_i(x_i) (u_i from stream 2); at the first rejection a_b the
+ * emitted token is a sample of max(0, p_a - q_a) (of p_a if rounding left no
+ * positive entry); after k acceptances, a sample of p_k (stream 3).
+ *   sampling       (host) the same temperature, seed and step as the draft call
+ *   draft          [B, k] int32 drafts of dflash_draft_step_sampled
+ *   draft_logits   [B, k, V] float (its logits_out), 16-byte aligned
+ *   draft_lse      [B, k] float (its lse_out)
+ *   target_logits  [B, k+1, V] float, 16-byte aligned: row i is the target's logits
+ *                  for position P_b+i+1 given the anchor and draft[b, 0..i-1]
+ *   accept_len     [B] int32 output a_b in [0, k]
+ *   out_tokens     [B, k+1] int32 output: draft[b, 0..a_b-1], the emitted token, -1
+ * Updates ctx_len[b] += a_b + 1 and anchor[b] = emitted token, with the same
+ * commit / rollback of K/V rows as dflash_verify_commit.  Uses the workspace of the
+ * other calls (they must not overlap on it). */
+int dflash_verify_sampled(const dflash_dims *dims, const dflash_sampling *sampling,
+                          const int32_t *draft, const float *draft_logits,
+                          const float *draft_lse, const float *target_logits,
+                          const dflash_cache *cache, int32_t *accept_len,
+                          int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
 /* Same as dflash_draft_step, and records head_begin / head_end on `stream` right
  * before and after the fused final-norm + LM-head + argmax kernel, so a caller can
  * time that kernel alone with hipEventElapsedTime.  Either event may be NULL. */
@@ -208,6 +274,15 @@ int dflash_draft_step_timed(const dflash_dims *dims, const dflash_weights *w,
                             float *logits_out, void *workspace, size_t workspace_bytes,
                             hipStream_t stream, hipEvent_t head_begin,
                             hipEvent_t head_end);
+
+/* Same as dflash_draft_step_sampled, with the LM-head events of
+ * dflash_draft_step_timed around the fused LM-head + sampling kernel. */
+int dflash_draft_step_sampled_timed(const dflash_dims *dims, const dflash_weights *w,
+                                    const dflash_cache *cache, const dflash_sampling *sampling,
+                                    int32_t *draft, float *logits_out, float *lse_out,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream, hipEvent_t head_begin,
+                                    hipEvent_t head_end);
 
 #ifdef __cplusplus
 }

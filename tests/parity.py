@@ -74,6 +74,29 @@ class StepReport:
         return self.logits_ok and self.draft_mismatch == 0 and self.state_mismatch == 0 and self.kv_ok
 
 
+@dataclass
+class SampledReport:
+    logit_err: float
+    logit_ref_max: float
+    logits_ok: bool
+    lse_err: float
+    lse_ok: bool
+    drafts_checked: int
+    drafts_total: int
+    draft_mismatch: int
+    seqs_checked: int
+    seqs_excluded: int
+    state_mismatch: int
+    kv_err: float
+    kv_ok: bool
+    accept: List[int] = field(default_factory=list)
+
+    @property
+    def ok(self) -> bool:
+        return (self.logits_ok and self.lse_ok and self.draft_mismatch == 0 and self.state_mismatch == 0
+                and self.kv_ok)
+
+
 class ParityRun:
     def __init__(self, dims: Dims, W, ctx_start: Sequence[int], anchors: Sequence[int],
                  prefill_rows: Sequence[int], sample: Optional[Sequence[int]] = None, seed: int = 0,
@@ -123,6 +146,116 @@ class ParityRun:
 
     def dev_error(self) -> int:
         return int(self.cache["dev_error"].item())
+
+    def _kv_error(self):
+        """Largest |K/V| error over the committed window rows of the sampled sequences."""
+        d, s = self.d, self.sample
+        kv_err, kv_max = 0.0, 0.0
+        if self.check_kv:
+            kc = self.cache["k"][:, s].float().cpu().numpy()
+            vc = self.cache["v"][:, s].float().cpu().numpy()
+            for j in range(len(s)):
+                P = int(self.st.ctx_len[j])
+                slots = np.array([orc.slot_of(d, int(p)) for p in orc.window_positions(d, P)], dtype=np.int64)
+                for ring, cache_np in ((self.st.k_ring, kc), (self.st.v_ring, vc)):
+                    ref = ring[:, j][:, :, slots]
+                    got = cache_np[:, j][:, :, slots]
+                    kv_err = max(kv_err, float(np.max(np.abs(got - ref))) if ref.size else 0.0)
+                    kv_max = max(kv_max, float(np.max(np.abs(ref))) if ref.size else 0.0)
+        return kv_err, kv_max
+
+    def _inject_block(self):
+        """Tentative K/V rows of the k+1 positions the target just processed (both sides)."""
+        d, k, s = self.d, self.d.block_k, self.sample
+        taps = synth.make_taps(d, k + 1, seed=self.seed, stream=1 + self.step_idx, device="cuda")
+        n_rows = torch.full((d.batch,), k + 1, dtype=torch.int32, device="cuda")
+        bd.dflash_fuse_inject(d, self.W, taps, n_rows, k + 1, False, self.cache, self.ws)
+        orc.fuse_inject(d, self.Wn, self.st, taps[s].float().cpu().numpy(), np.full(len(s), k + 1), commit=False)
+
+    def step_sampled(self, a_star: Sequence[int], temperature: float, seed: int = 1234,
+                     soft: float = 0.0) -> "SampledReport":
+        """One sampled round: dflash_draft_step_sampled, tentative injection,
+        dflash_verify_sampled, against the oracle's draft forward, Gumbel-max drafts
+        and rejection-sampling verification with the same seed and step.
+
+        The logits and log-sum-exps are checked against the logit tolerance; each
+        decision is then compared where its distance from the threshold exceeds what
+        the measured errors can move it: err_s = max |z_gpu - z_ref| / T, err_l = max
+        |lse_gpu - lse_ref|; drafts where the perturbed top-2 gap >= 2 err_s + 1e-3;
+        a sequence's verification where every acceptance score |log p - log q - log u|
+        >= err_s + err_l + 1e-3 (the target logits are the same values on both sides)
+        and the emitted draw's gap >= 2 (err_s + err_l) slack + 1e-3."""
+        from oracle import sampling as sp
+        d, W, s = self.d, self.W, self.sample
+        B, k, V = d.batch, d.block_k, d.vocab
+        T = float(temperature)
+        step = self.step_idx
+        smp = bd.sampling_struct(T, seed, step)
+        say(f"[parity] sampled step {step}: draft_step_sampled B={B} k={k} V={V} T={T}")
+        draft = torch.empty((B, k), dtype=torch.int32, device="cuda")
+        logits = torch.empty((B, k, V), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, k), dtype=torch.float32, device="cuda")
+        bd.dflash_draft_step_sampled(d, W, self.cache, smp, draft, logits, lse, self.ws)
+        torch.cuda.synchronize()
+        o = orc.draft_step(d, self.Wn, self.st)
+        zr = o["logits"]
+        sd = sp.sample_drafts(zr, T, seed, step, seq_ids=s)
+        xr, gap, lse_r = sd["draft"], sd["gap"], sd["lse"]
+        zg = logits[s].cpu().numpy().astype(np.float64)
+        dg = draft[s].cpu().numpy().astype(np.int64)
+        err = float(np.max(np.abs(zg - zr)))
+        ref_max = float(np.max(np.abs(zr)))
+        lse_err = float(np.max(np.abs(lse[s].cpu().numpy() - lse_r)))
+        tol_z = self.tol.logit_abs if self.tol.logit_abs is not None else self.tol.logit_rel * ref_max
+        err_s = err / T
+        thr = 2 * err_s + 1e-3
+        gate = gap >= thr
+        mism = int(np.sum((dg != xr) & gate))
+
+        # target stand-in: planted from the oracle's drafts and logits where sampled
+        x_all = draft.cpu().numpy().astype(np.int64)
+        x_all[s] = xr
+        z_all = logits.clone()
+        z_all[s] = torch.as_tensor(zr, dtype=torch.float32, device="cuda")
+        fill = synth.make_logits((B, k + 1, V), seed=self.seed, stream=7919 * (step + 1), device="cuda")
+        tgt = synth.plant_target_logits(z_all, x_all, np.asarray(a_star), fill, soft=soft, seed=step).contiguous()
+        say(f"[parity] sampled step {step}: fuse_inject + verify_sampled")
+        self._inject_block()
+        acc = torch.empty(B, dtype=torch.int32, device="cuda")
+        out = torch.empty((B, k + 1), dtype=torch.int32, device="cuda")
+        bd.dflash_verify_sampled(d, smp, draft, logits, lse, tgt, self.cache, acc, out, self.ws)
+        torch.cuda.synchronize()
+        r = sp.verify_sampled(xr, zr, tgt[s].cpu().numpy().astype(np.float64), T, seed, step, seq_ids=s)
+        sp.commit_sampled(d, self.st, r)
+
+        acc_g, out_g = acc[s].cpu().numpy(), out[s].cpu().numpy()
+        ctx_g, anc_g = self.cache["ctx_len"][s].cpu().numpy(), self.cache["anchor"][s].cpu().numpy()
+        checked = excluded = state_mism = 0
+        for j, b in enumerate(s):
+            a_ref = int(r["accept_len"][j])
+            dq = err_s + lse_err
+            ok = (all(gap[j, i] >= thr for i in range(0, min(a_ref, k - 1) + 1))
+                  and r["accept_margin"][j] >= dq + 1e-3
+                  and r["emit_gap"][j] >= 2 * dq * r["emit_slack"][j] + 1e-3)
+            if ok:
+                checked += 1
+                same = (acc_g[j] == a_ref and np.array_equal(out_g[j], r["out_tokens"][j])
+                        and ctx_g[j] == self.st.ctx_len[j] and anc_g[j] == self.st.anchor[j])
+                state_mism += int(not same)
+            else:
+                excluded += 1
+                self.cache["ctx_len"][b] = int(self.st.ctx_len[j])
+                self.cache["anchor"][b] = int(self.st.anchor[j])
+        kv_err, kv_max = self._kv_error()
+        self.step_idx += 1
+        # log-sum-exp is 1-Lipschitz in the max norm: |d lse| <= max |dz| / T
+        rep = SampledReport(err, ref_max, self.tol.logit_ok(err, ref_max), lse_err, lse_err <= tol_z / T + 1e-5,
+                            int(gate.sum()), gate.size, mism, checked, excluded, state_mism, kv_err,
+                            self.tol.logit_ok(kv_err, max(kv_max, 1e-30)), list(map(int, acc_g)))
+        say(f"[parity] sampled step {step}: logit_err={err:.3g} lse_err={lse_err:.3g} drafts "
+            f"{rep.drafts_checked}/{rep.drafts_total} gated, mismatches {mism}; seqs checked {checked}, "
+            f"excluded {excluded}, state mismatches {state_mism}; kv_err={kv_err:.3g} accept={rep.accept[:8]}")
+        return rep
 
     def step(self, a_star: Sequence[int]) -> StepReport:
         d, W, s = self.d, self.W, self.sample
@@ -176,18 +309,7 @@ class ParityRun:
                 self.cache["ctx_len"][b] = int(self.st.ctx_len[j])
                 self.cache["anchor"][b] = int(self.st.anchor[j])
 
-        kv_err, kv_max = 0.0, 0.0
-        if self.check_kv:
-            kc = self.cache["k"][:, s].float().cpu().numpy()
-            vc = self.cache["v"][:, s].float().cpu().numpy()
-            for j in range(len(s)):
-                P = int(self.st.ctx_len[j])
-                slots = np.array([orc.slot_of(d, int(p)) for p in orc.window_positions(d, P)], dtype=np.int64)
-                for ring, cache_np in ((self.st.k_ring, kc), (self.st.v_ring, vc)):
-                    ref = ring[:, j][:, :, slots]
-                    got = cache_np[:, j][:, :, slots]
-                    kv_err = max(kv_err, float(np.max(np.abs(got - ref))) if ref.size else 0.0)
-                    kv_max = max(kv_max, float(np.max(np.abs(ref))) if ref.size else 0.0)
+        kv_err, kv_max = self._kv_error()
         self.step_idx += 1
         rep = StepReport(err, ref_max, self.tol.logit_ok(err, ref_max), int(gate.sum()), gate.size,
                          mism, checked, excluded, state_mism, kv_err, kv_max,

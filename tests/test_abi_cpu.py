@@ -117,3 +117,51 @@ def test_invalid_arguments_are_rejected_on_the_host():
     # block size beyond one wavefront
     bad = bd.dims_struct(replace(configs.C2.dims, block_k=64, max_inject_rows=80))
     assert L.dflash_verify_commit(by(bad), FAKE, FAKE, by(c), FAKE, FAKE, None) == bd.DFLASH_E_INVALID
+
+
+@needs_lib
+def test_sampled_calls_reject_bad_arguments_on_the_host():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation probe runs on CPU-only hosts")
+    L = bd.lib()
+    d = bd.dims_struct(configs.C2.dims)
+    w, c = _weights(), _cache()
+    ws = bd.dflash_workspace_bytes(configs.C2.dims)
+    by = ctypes.byref
+    good = bd.sampling_struct(0.8, 1, 2)
+    bad_samplings = [bd.sampling_struct(t, 1, 2) for t in (0.0, -1.0, float("nan"), float("inf"))]
+    r = bd.sampling_struct(0.8, 1, 2)
+    r.reserved = 1
+    bad_samplings.append(r)
+    for sm in bad_samplings:
+        assert L.dflash_draft_step_sampled(by(d), by(w), by(c), by(sm), FAKE, FAKE, FAKE, FAKE, ws,
+                                           None) == bd.DFLASH_E_INVALID
+        assert L.dflash_verify_sampled(by(d), by(sm), FAKE, FAKE, FAKE, FAKE, by(c), FAKE, FAKE, FAKE, ws,
+                                       None) == bd.DFLASH_E_INVALID
+    assert L.dflash_draft_step_sampled(by(d), by(w), by(c), None, FAKE, FAKE, FAKE, FAKE, ws,
+                                       None) == bd.DFLASH_E_INVALID
+    # logits and lse outputs are required; lse must be 4-byte aligned
+    assert L.dflash_draft_step_sampled(by(d), by(w), by(c), by(good), FAKE, None, FAKE, FAKE, ws,
+                                       None) == bd.DFLASH_E_INVALID
+    assert L.dflash_draft_step_sampled(by(d), by(w), by(c), by(good), FAKE, FAKE, None, FAKE, ws,
+                                       None) == bd.DFLASH_E_INVALID
+    assert L.dflash_draft_step_sampled(by(d), by(w), by(c), by(good), FAKE, FAKE, FAKE + 2, FAKE, ws,
+                                       None) == bd.DFLASH_E_INVALID
+    assert L.dflash_draft_step_sampled(by(d), by(w), by(c), by(good), FAKE, FAKE, FAKE, FAKE, ws - 1,
+                                       None) == bd.DFLASH_E_WORKSPACE
+    # verify: NULL inputs / outputs, logits rows not 16-byte aligned, small workspace
+    args = [FAKE] * 4
+    for j in range(4):
+        a = list(args)
+        a[j] = None
+        assert L.dflash_verify_sampled(by(d), by(good), *a, by(c), FAKE, FAKE, FAKE, ws,
+                                       None) == bd.DFLASH_E_INVALID
+    assert L.dflash_verify_sampled(by(d), by(good), FAKE, FAKE + 4, FAKE, FAKE, by(c), FAKE, FAKE, FAKE, ws,
+                                   None) == bd.DFLASH_E_INVALID
+    assert L.dflash_verify_sampled(by(d), by(good), FAKE, FAKE, FAKE, FAKE + 8, by(c), FAKE, FAKE, FAKE, ws,
+                                   None) == bd.DFLASH_E_INVALID
+    assert L.dflash_verify_sampled(by(d), by(good), FAKE, FAKE, FAKE, FAKE, by(c), None, FAKE, FAKE, ws,
+                                   None) == bd.DFLASH_E_INVALID
+    assert L.dflash_verify_sampled(by(d), by(good), FAKE, FAKE, FAKE, FAKE, by(c), FAKE, FAKE, FAKE, ws - 1,
+                                   None) == bd.DFLASH_E_WORKSPACE

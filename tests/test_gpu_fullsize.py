@@ -62,3 +62,26 @@ def test_fullsize_swa_with_attention_sink():
         assert r.state_mismatch == 0
         assert r.kv_ok, f"step {s}: kv error {r.kv_err}"
     assert run.dev_error() == 0
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,sample", [(configs.C2.name, [0]), (configs.C5.name, [0, 100, 255])])
+def test_fullsize_sampled_round(name, sample):
+    """One sampled round (temperature 1) at full size: Gumbel-max drafts from the
+    fused LM head, rejection-sampling verification over the full vocabulary."""
+    w = configs.WORKLOADS[name]
+    d = w.dims
+    say(f"[fullsize] sampled {name}: B={d.batch} k={d.block_k} V={d.vocab} sample={sample}")
+    W = synth.make_weights(d, seed=0, device="cuda")
+    ctx = synth.make_context_lengths(w, seed=0)
+    pre = np.minimum(ctx, w.prefill)
+    kind, q = w.accept
+    a_tab = synth.planted_accept(kind, q, d.block_k, 1, d.batch, seed=0)
+    run = ParityRun(d, W, ctx, synth.make_anchors(d), pre, sample=sample, seed=0)
+    r = run.step_sampled(a_tab[0], 1.0, seed=5)
+    assert r.logits_ok, f"max |dz| {r.logit_err} > 0.05"
+    assert r.lse_ok, f"lse error {r.lse_err}"
+    assert r.draft_mismatch == 0
+    assert r.state_mismatch == 0
+    assert r.kv_ok, f"kv error {r.kv_err}"
+    assert run.dev_error() == 0
