@@ -221,8 +221,10 @@ def verify_sampled(draft, draft_logits, target_logits, temperature: float, seed:
     Returns accept_len [n], emitted [n] (the residual or bonus token), out_tokens
     [n, k+1] (the accepted drafts, the emitted token, then -1), accept_margin [n]
     (the smallest |accept_score| over the acceptance tests made: how far each
-    decision was from its threshold) and emit_gap [n] (top-2 gap of the emitted
-    draw's perturbed scores)."""
+    decision was from its threshold), emit_gap [n] (top-2 gap of the emitted
+    draw's perturbed scores) and emit_slack [n] (for a residual draw, the largest
+    q / (p - q) of those two tokens: how strongly an error in log q moves their
+    scores; 0 for a draw from p)."""
     x = np.asarray(draft, dtype=np.int64)
     lq = log_softmax(draft_logits, temperature)      # [n, k, V]
     lp = log_softmax(target_logits, temperature)     # [n, k+1, V]
@@ -233,6 +235,7 @@ def verify_sampled(draft, draft_logits, target_logits, temperature: float, seed:
     out = np.full((n, k + 1), -1, np.int64)
     margin = np.full(n, np.inf)
     egap = np.zeros(n)
+    slack = np.zeros(n)
     for j in range(n):
         b = int(ids[j])
         a = 0
@@ -243,12 +246,20 @@ def verify_sampled(draft, draft_logits, target_logits, temperature: float, seed:
                 break
             a += 1
         s = residual_scores(lp[j, a], lq[j, a]) if a < k else lp[j, k]
-        y, egap[j] = gumbel_max(s, emit_noise(seed, step, b, V))
+        noise = emit_noise(seed, step, b, V)
+        y, egap[j] = gumbel_max(s, noise)
+        if a < k and np.any(np.exp(lp[j, a]) > np.exp(lq[j, a])):
+            pert = s + noise
+            pert[y] = -np.inf
+            for v in (y, int(np.argmax(pert))):
+                pv, qv = np.exp(lp[j, a, v]), np.exp(lq[j, a, v])
+                if pv > qv:
+                    slack[j] = max(slack[j], qv / (pv - qv))
         acc[j], emitted[j] = a, y
         out[j, :a] = x[j, :a]
         out[j, a] = y
     return {"accept_len": acc, "emitted": emitted, "out_tokens": out,
-            "accept_margin": margin, "emit_gap": egap}
+            "accept_margin": margin, "emit_gap": egap, "emit_slack": slack}
 
 
 def commit_sampled(dims, st, result) -> None:
