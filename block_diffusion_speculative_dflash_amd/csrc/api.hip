@@ -115,7 +115,7 @@ size_t partial_bytes(const dflash_dims& d);
 
 struct Layout {
   size_t h, xa, ssq, q, kb, vb, o, act, cu, ssq_c, partials, counters, keys, attn_cnt, attn_o,
-      attn_ml, lse_part, v_part, v_cnt, v_dec, v_keys, total;
+      attn_ml, lse_part, v_part, v_cnt, v_rowlse, v_dec, v_keys, total;
   int v_chunks;
   int np_d, S_d, S_o, S_f;
   AttnPlan ap;
@@ -153,9 +153,10 @@ Layout layout(const dflash_dims& d) {
   L.attn_ml = take(groups * L.ap.max_splits * 64 * 2 * 4);
   // sampled drafting / verification
   L.lse_part = take(Mb * size_t(cdiv(d.vocab, kBN)) * 8);
-  L.v_chunks = cdiv(d.vocab, kVerifyChunk);
+  L.v_chunks = verify_chunks(static_cast<long long>(d.batch) * (d.block_k + 1), d.vocab);
   L.v_part = take(size_t(d.batch) * (d.block_k + 1) * L.v_chunks * 8);
-  L.v_cnt = take(size_t(d.batch) * 2 * 4);
+  L.v_cnt = take(size_t(d.batch) * (d.block_k + 3) * 4);
+  L.v_rowlse = take(size_t(d.batch) * (d.block_k + 1) * 4);
   L.v_dec = take(size_t(d.batch) * 16);
   L.v_keys = take(size_t(d.batch) * 2 * kKeyStride * 8);
   L.total = off;
@@ -707,12 +708,14 @@ int dflash_verify_sampled(const dflash_dims* dims, const dflash_sampling* sampli
   v.dev_error = cache->dev_error;
   v.part = reinterpret_cast<float2*>(ws + L.v_part);
   v.counters = reinterpret_cast<unsigned*>(ws + L.v_cnt);
+  v.row_lse = reinterpret_cast<float*>(ws + L.v_rowlse);
   v.decision = reinterpret_cast<float4*>(ws + L.v_dec);
   v.keys = reinterpret_cast<unsigned long long*>(ws + L.v_keys);
   v.batch = d.batch;
   v.block_k = d.block_k;
   v.vocab = d.vocab;
   v.n_chunks = L.v_chunks;
+  v.n_chunks_emit = verify_chunks(d.batch, d.vocab);
   v.inv_temp = 1.f / sampling->temperature;
   v.seed = sampling->seed;
   v.step = sampling->step;

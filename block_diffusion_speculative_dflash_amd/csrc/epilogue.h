@@ -14,7 +14,7 @@
 #pragma once
 
 #include "common.h"
-#include "internal.h"
+#include "gemm.h"
 
 namespace dflash {
 

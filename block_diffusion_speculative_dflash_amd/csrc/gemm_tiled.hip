@@ -30,7 +30,7 @@
 
 #include "common.h"
 #include "epilogue.h"
-#include "internal.h"
+#include "gemm.h"
 #include "philox.h"
 
 namespace dflash {

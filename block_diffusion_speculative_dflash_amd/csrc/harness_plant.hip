@@ -11,7 +11,22 @@
 
 extern "C" {
 
-__global__ void plant_kernel(const int32_t* draft, int32_t* target, const int32_t* a_star_tab,
+constexpr int kPlantThreads = 1024;
+
+// sum of accept_len[0 .. batch) over the workgroup (kPlantThreads threads)
+__device__ long long block_sum(const int32_t* accept_len, int batch) {
+  __shared__ long long part[kPlantThreads / 64];
+  long long v = 0;
+  for (int b = threadIdx.x; b < batch; b += blockDim.x) v += accept_len[b];
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  long long t = 0;
+  for (int w = 0; w < kPlantThreads / 64; ++w) t += part[w];
+  return t;
+}
+
+__global__ __launch_bounds__(kPlantThreads) void plant_kernel(const int32_t* draft, int32_t* target, const int32_t* a_star_tab,
                              const int32_t* fill_tab, int32_t* step_counter, int n_tab_steps,
                              const int32_t* accept_len, long long* accept_total, int batch, int k,
                              int vocab) {
@@ -29,9 +44,8 @@ __global__ void plant_kernel(const int32_t* draft, int32_t* target, const int32_
     else t = f % vocab;
     target[idx] = t;
   }
+  const long long add = block_sum(accept_len, batch);
   if (threadIdx.x == 0) {
-    long long add = 0;
-    for (int b = 0; b < batch; ++b) add += accept_len[b];
     accept_total[0] += add;
     step_counter[0] = step_s + 1;
   }
@@ -44,7 +58,7 @@ __global__ void plant_kernel(const int32_t* draft, int32_t* target, const int32_
 // drafts are accepted at any temperature up to 100.  Advances *rng_step (the device
 // step word the sampled calls read) and accumulates accepted lengths like
 // plant_kernel.
-__global__ void plant_logits_kernel(const int32_t* draft, float* target, const int32_t* a_star_tab,
+__global__ __launch_bounds__(kPlantThreads) void plant_logits_kernel(const int32_t* draft, float* target, const int32_t* a_star_tab,
                                     int32_t* step_counter, int n_tab_steps, int32_t* saved_idx,
                                     float* saved_val, const int32_t* accept_len, long long* accept_total,
                                     unsigned long long* rng_step, int batch, int k, int vocab) {
@@ -66,9 +80,8 @@ __global__ void plant_logits_kernel(const int32_t* draft, float* target, const i
     }
     saved_idx[idx] = x;
   }
+  const long long add = block_sum(accept_len, batch);
   if (threadIdx.x == 0) {
-    long long add = 0;
-    for (int b = 0; b < batch; ++b) add += accept_len[b];
     accept_total[0] += add;
     step_counter[0] = step_s + 1;
     if (rng_step != nullptr) rng_step[0] += 1ull;
@@ -81,7 +94,7 @@ int dflash_harness_plant_logits(const int32_t* draft, float* target, const int32
                                 unsigned long long* rng_step, int batch, int k, int vocab,
                                 hipStream_t stream) {
   if (batch < 1 || k < 1 || vocab < 2 || n_tab_steps < 1) return -1;
-  hipLaunchKernelGGL(plant_logits_kernel, dim3(1), dim3(256), 0, stream, draft, target, a_star_tab,
+  hipLaunchKernelGGL(plant_logits_kernel, dim3(1), dim3(kPlantThreads), 0, stream, draft, target, a_star_tab,
                      step_counter, n_tab_steps, saved_idx, saved_val, accept_len, accept_total, rng_step,
                      batch, k, vocab);
   return hipGetLastError() == hipSuccess ? 0 : -4;
@@ -92,7 +105,7 @@ int dflash_harness_plant(const int32_t* draft, int32_t* target, const int32_t* a
                          const int32_t* accept_len, long long* accept_total, int batch, int k,
                          int vocab, hipStream_t stream) {
   if (batch < 1 || k < 1 || vocab < 2 || n_tab_steps < 1) return -1;
-  hipLaunchKernelGGL(plant_kernel, dim3(1), dim3(256), 0, stream, draft, target, a_star_tab,
+  hipLaunchKernelGGL(plant_kernel, dim3(1), dim3(kPlantThreads), 0, stream, draft, target, a_star_tab,
                      fill_tab, step_counter, n_tab_steps, accept_len, accept_total, batch, k, vocab);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

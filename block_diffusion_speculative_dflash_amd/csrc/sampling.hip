@@ -9,10 +9,14 @@
 // positive entry); after k acceptances it is a draw from p_k.  Draws are Gumbel-max
 // over Philox4x64-10 noise (philox.h).
 //
-// Two kernels, both reading the caller's fp32 logits once in 8192-entry chunks:
+// Two kernels, both reading the caller's fp32 logits once in chunks of 2048 G
+// entries (G = 4, 2 or 1 groups of 8 per thread, each kernel taking the largest
+// that still gives it >= 256 workgroups):
 //  1. (chunk, row i <= k, sequence b): log-sum-exp partial of t_i / T; the last
-//     workgroup of a sequence to arrive merges its k + 1 rows and runs the k
-//     acceptance tests in one wavefront (lane i, ballot, first zero = a);
+//     workgroup of a row to arrive merges that row's partials, and the last row of
+//     a sequence to finish runs the k acceptance tests in one wavefront (lane i,
+//     ballot, first zero = a) -- two arrival levels, so no counter sees more than
+//     max(n_chunks, k + 1) atomics;
 //  2. (chunk, sequence b): the residual (or bonus) row a, scores + noise, split-vocab
 //     argmax through keys; the last arriving workgroup commits: accepted length,
 //     emitted tokens, anchor, committed length.
@@ -74,18 +78,40 @@ __device__ __forceinline__ void load8(const float* row, int v0, int n, bool vec,
   }
 }
 
-constexpr int kGroups = kVerifyChunk / (8 * kThreads);  // 8-entry groups per thread
+// log-sum-exp of the partials pr[0 .. n) (device-coherent loads, four in flight per
+// lane), reduced over one wavefront; every lane returns the result
+__device__ __forceinline__ float wave_lse_of_partials(const float* pr, int n) {
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY, s = 0.f;
+  for (int c0 = lane; c0 < n; c0 += 4 * kWave) {
+    float2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * kWave;
+      v[u] = c < n ? coherent_load2(pr + 2 * c) : make_float2(-INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) lse_merge(m, s, v[u].x, v[u].y);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, kWave), os = __shfl_xor(s, o, kWave);
+    lse_merge(m, s, om, os);
+  }
+  return m + ln_f32(s);
+}
 
+template <int G>
 __global__ __launch_bounds__(kThreads) void verify_lse_kernel(VerifySampledArgs a) {
+  constexpr int kGroups = G, kChunk = 8 * kThreads * G;
   __shared__ float red_m[kThreads / kWave], red_s[kThreads / kWave];
-  __shared__ float lp_s[kWave + 1];
   __shared__ int last_s;
   const int chunk = blockIdx.x, i = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int k = a.block_k, V = a.vocab;
   const bool vec = (V & 3) == 0;
   const float* trow_b = a.target_logits + static_cast<size_t>(b) * (k + 1) * V;
   const float* row = trow_b + static_cast<size_t>(i) * V;
-  const int v0 = chunk * kVerifyChunk, v1 = min(V, v0 + kVerifyChunk);
+  const int v0 = chunk * kChunk, v1 = min(V, v0 + kChunk);
 
   float vals[kGroups][8];
 #pragma unroll
@@ -124,26 +150,29 @@ __global__ __launch_bounds__(kThreads) void verify_lse_kernel(VerifySampledArgs 
     coherent_store(dst, m);
     coherent_store(dst + 1, s);
   }
-  if (!arrive_last(&a.counters[b], static_cast<unsigned>((k + 1) * a.n_chunks), &last_s)) return;
+  unsigned* row_cnt = &a.counters[2 * a.batch + static_cast<size_t>(b) * (k + 1) + i];
+  if (!arrive_last(row_cnt, static_cast<unsigned>(a.n_chunks), &last_s)) return;
 
-  // last workgroup of sequence b: row log-sum-exps, then the acceptance tests
-  for (int r = tid; r <= k; r += kThreads) {
-    const float* pr = reinterpret_cast<const float*>(a.part + (static_cast<size_t>(b) * (k + 1) + r) * a.n_chunks);
-    float mm = -INFINITY, ss = 0.f;
-    for (int c = 0; c < a.n_chunks; ++c) {
-      const float2 v = coherent_load2(pr + 2 * c);
-      lse_merge(mm, ss, v.x, v.y);
+  // last workgroup of row (b, i): the row's log-sum-exp
+  if (tid < kWave) {
+    const float* pr = reinterpret_cast<const float*>(a.part + (static_cast<size_t>(b) * (k + 1) + i) * a.n_chunks);
+    const float l = wave_lse_of_partials(pr, a.n_chunks);
+    if (tid == 0) {
+      coherent_store(&a.row_lse[static_cast<size_t>(b) * (k + 1) + i], l);
+      reset_counter(row_cnt);
     }
-    lp_s[r] = mm + ln_f32(ss);
   }
-  __syncthreads();
+  if (!arrive_last(&a.counters[b], static_cast<unsigned>(k + 1), &last_s)) return;
+
+  // last row of sequence b: the acceptance tests
   if (tid < kWave) {
     const int lane = tid;
+    const float lse_t = lane <= k ? coherent_load(&a.row_lse[static_cast<size_t>(b) * (k + 1) + lane]) : 0.f;
     bool ok = false, bad = false;
     if (lane < k) {
       int x = a.draft[static_cast<size_t>(b) * k + lane];
       if (x < 0 || x >= V) { bad = true; x = min(max(x, 0), V - 1); }
-      const float lp = trow_b[static_cast<size_t>(lane) * V + x] * a.inv_temp - lp_s[lane];
+      const float lp = trow_b[static_cast<size_t>(lane) * V + x] * a.inv_temp - lse_t;
       const float lq = a.draft_logits[(static_cast<size_t>(b) * k + lane) * V + x] * a.inv_temp -
                        a.draft_lse[static_cast<size_t>(b) * k + lane];
       uint32_t h[8];
@@ -153,16 +182,19 @@ __global__ __launch_bounds__(kThreads) void verify_lse_kernel(VerifySampledArgs 
     }
     const unsigned long long ones = __ballot(ok);
     const int acc = __ffsll(static_cast<long long>(~ones)) - 1;  // lanes >= k never accept: acc <= k
+    const float lse_a = __shfl(lse_t, acc, kWave);
     if (__ballot(bad) != 0ull && lane == 0) atomicOr(a.dev_error, 1u);
     if (lane == 0) {
       const float lq_a = acc < k ? a.draft_lse[static_cast<size_t>(b) * k + acc] : 0.f;
-      a.decision[b] = make_float4(static_cast<float>(acc), lp_s[acc], lq_a, 0.f);
+      a.decision[b] = make_float4(static_cast<float>(acc), lse_a, lq_a, 0.f);
       reset_counter(&a.counters[b]);
     }
   }
 }
 
+template <int G>
 __global__ __launch_bounds__(kThreads) void verify_emit_kernel(VerifySampledArgs a) {
+  constexpr int kGroups = G, kChunk = 8 * kThreads * G;
   __shared__ unsigned long long red[2][kThreads / kWave];
   __shared__ int last_s, tok_s;
   const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
@@ -174,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void verify_emit_kernel(VerifySampledArgs
   const float lse_p = dec.y, lse_q = dec.z;
   const float* trow = a.target_logits + (static_cast<size_t>(b) * (k + 1) + acc) * V;
   const float* zrow = a.draft_logits + (static_cast<size_t>(b) * k + min(acc, k - 1)) * V;
-  const int v0 = chunk * kVerifyChunk, v1 = min(V, v0 + kVerifyChunk);
+  const int v0 = chunk * kChunk, v1 = min(V, v0 + kChunk);
 
   const unsigned long long step = a.step_dev != nullptr ? *a.step_dev : a.step;
   unsigned long long kr = 0ull, kp = 0ull;  // residual draw, draw from p itself
@@ -226,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void verify_emit_kernel(VerifySampledArgs
     if (kr != 0ull) atomicMax(&keys[0], kr);
     if (kp != 0ull) atomicMax(&keys[kKeyStride], kp);
   }
-  if (!arrive_last(&a.counters[a.batch + b], static_cast<unsigned>(a.n_chunks), &last_s)) return;
+  if (!arrive_last(&a.counters[a.batch + b], static_cast<unsigned>(a.n_chunks_emit), &last_s)) return;
 
   if (tid == 0) {
     const unsigned long long fr = __hip_atomic_exchange(&keys[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -253,11 +285,24 @@ __global__ __launch_bounds__(kThreads) void verify_emit_kernel(VerifySampledArgs
 }
 
 hipError_t launch_verify_sampled(const VerifySampledArgs& a, hipStream_t stream) {
-  if (a.batch <= 0 || a.block_k <= 0 || a.block_k >= kWave || a.n_chunks <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(verify_lse_kernel, dim3(a.n_chunks, a.block_k + 1, a.batch), dim3(kThreads), 0, stream, a);
+  if (a.batch <= 0 || a.block_k <= 0 || a.block_k >= kWave) return hipErrorInvalidValue;
+  const long long rows_lse = static_cast<long long>(a.batch) * (a.block_k + 1);
+  const int g1 = verify_groups(rows_lse, a.vocab), g2 = verify_groups(a.batch, a.vocab);
+  if (a.n_chunks != verify_chunks(rows_lse, a.vocab) || a.n_chunks_emit != verify_chunks(a.batch, a.vocab))
+    return hipErrorInvalidValue;
+  const dim3 grid1(a.n_chunks, a.block_k + 1, a.batch), grid2(a.n_chunks_emit, a.batch);
+  switch (g1) {
+    case 1: hipLaunchKernelGGL(verify_lse_kernel<1>, grid1, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(verify_lse_kernel<2>, grid1, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL(verify_lse_kernel<4>, grid1, dim3(kThreads), 0, stream, a); break;
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_emit_kernel, dim3(a.n_chunks, a.batch), dim3(kThreads), 0, stream, a);
+  switch (g2) {
+    case 1: hipLaunchKernelGGL(verify_emit_kernel<1>, grid2, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(verify_emit_kernel<2>, grid2, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL(verify_emit_kernel<4>, grid2, dim3(kThreads), 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -76,7 +76,8 @@ def _verify_rounds(V, B, k, T, soft, seed=0, rounds=2, planted=None):
 @pytest.mark.parametrize("V,B,k,T,soft", [
     (1000, 6, 5, 1.0, 0.5),     # one chunk, ragged
     (1001, 3, 7, 0.7, 0.3),     # vocabulary not a multiple of 4: scalar loads
-    (20000, 4, 4, 1.5, 0.0),    # three chunks, ragged tail
+    (20000, 4, 4, 1.5, 0.0),    # ten 2048-entry chunks, ragged tail
+    (20000, 4, 16, 1.2, 0.3),   # 4096-entry chunks in the log-sum-exp kernel
     (8192, 2, 1, 0.3, 1.0),     # exactly one chunk, block of one
     (3000, 2, 16, 2.0, 0.5),    # long block
 ])
@@ -162,8 +163,9 @@ def test_sampled_draws_are_reproducible_and_step_dependent():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("V,B,k", [(151936, 8, 16), (128256, 8, 10)])
+@pytest.mark.parametrize("V,B,k", [(151936, 8, 16), (128256, 8, 10), (151936, 3, 12), (151936, 1, 16)])
 def test_verify_sampled_full_vocabulary(V, B, k):
-    """The verify kernels at full vocabulary (19 and 16 chunks per row) on identical
-    inputs, so every decision is compared at the 1e-3 gate."""
+    """The verify kernels at full vocabulary on identical inputs, so every decision is
+    compared at the 1e-3 gate; the shapes take 8192-, 4096- and 2048-entry chunks
+    (the last is the batch-1, block-16 launch of the Qwen3-8B-shaped workload)."""
     _verify_rounds(V, B, k, 1.0, 0.3, seed=11, rounds=1)
