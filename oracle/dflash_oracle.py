@@ -216,50 +216,79 @@ def window_positions(dims, P: int) -> np.ndarray:
 # block draft
 # ----------------------------------------------------------------------------
 
-def draft_step(dims, W, st: State, want_logits: bool = True) -> Dict[str, np.ndarray]:
-    """One forward of the draft transformer over the block of every sequence.
+def block_lengths(dims, batch: int, block_len=None) -> np.ndarray:
+    """Per-sequence block length k_b in [0, k] (None: every sequence drafts k rows).
+    k_b = 0 means speculation is off for that sequence this round (hotdry blog,
+    acceptance-rate section: the dynamic fallback may shrink the block or turn
+    speculative decoding off)."""
+    k = dims.block_k
+    kb = np.full(batch, k, np.int64) if block_len is None else np.asarray(block_len, dtype=np.int64)
+    if kb.shape != (batch,) or np.any(kb < 0) or np.any(kb > k):
+        raise ValueError("block_len must hold one length in [0, k] per sequence")
+    return kb
 
-    Returns draft [B, k] (argmax, smallest id on ties), logits [B, k, V] and
-    margin [B, k] (top-1 minus top-2 logit).
-    """
-    B, k = st.ctx_len.shape[0], dims.block_k
+
+def block_logits(dims, W, st: State, b: int, kb: int) -> np.ndarray:
+    """Logits [kb, V] of sequence b's block of kb rows: the anchor at position P,
+    then kb - 1 mask positions; every row sees the committed window and all kb
+    block keys (bidirectional inside the block)."""
     Hq, Hkv, dh, D, F = dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.hidden, dims.ffn
     eps, theta = dims.rms_eps, dims.rope_theta
+    P = int(st.ctx_len[b])
 
-    # block construction: anchor at P, mask embedding at P+1 .. P+k-1
-    h = np.empty((B, k, D), dtype=np.float64)
-    h[:, 0] = f64(np.asarray(W["embed"])[st.anchor])
-    h[:, 1:] = f64(W["mask_embed"])
-    pos = st.ctx_len[:, None] + np.arange(k)[None, :]           # [B, k]
+    # block construction: anchor at P, mask embedding at P+1 .. P+kb-1
+    h = np.empty((kb, D), dtype=np.float64)
+    h[0] = f64(np.asarray(W["embed"])[st.anchor[b]])
+    h[1:] = f64(W["mask_embed"])
+    pos = P + np.arange(kb)
+    slots = np.array([slot_of(dims, int(p)) for p in window_positions(dims, P)], dtype=np.int64)
 
     for l in range(dims.n_layers):
         x = rms_norm(h, W["attn_norm"][l], eps)
         qkv = linear(x, W["w_qkv"][l])
-        q = qkv[..., :Hq * dh].reshape(B, k, Hq, dh)
-        kb = qkv[..., Hq * dh:(Hq + Hkv) * dh].reshape(B, k, Hkv, dh)
-        vb = qkv[..., (Hq + Hkv) * dh:].reshape(B, k, Hkv, dh)
-        q = rope(q, pos[:, :, None], theta)
-        kb = rope(kb, pos[:, :, None], theta)
+        q = qkv[:, :Hq * dh].reshape(kb, Hq, dh)
+        kk = qkv[:, Hq * dh:(Hq + Hkv) * dh].reshape(kb, Hkv, dh)
+        vv = qkv[:, (Hq + Hkv) * dh:].reshape(kb, Hkv, dh)
+        q = rope(q, pos[:, None], theta)
+        kk = rope(kk, pos[:, None], theta)
 
-        o = np.empty((B, k, Hq, dh), dtype=np.float64)
-        for b in range(B):
-            slots = np.array([slot_of(dims, int(p)) for p in window_positions(dims, int(st.ctx_len[b]))],
-                             dtype=np.int64)
-            for hq in range(Hq):
-                g = kv_head_of(hq, Hq, Hkv)
-                keys = np.concatenate([st.k_ring[l, b, g, slots], kb[b, :, g]], axis=0)
-                vals = np.concatenate([st.v_ring[l, b, g, slots], vb[b, :, g]], axis=0)
-                o[b, :, hq] = attend(q[b, :, hq], keys, vals)   # no mask inside the block
-        h = h + linear(o.reshape(B, k, Hq * dh), W["w_o"][l])
+        o = np.empty((kb, Hq, dh), dtype=np.float64)
+        for hq in range(Hq):
+            g = kv_head_of(hq, Hq, Hkv)
+            keys = np.concatenate([st.k_ring[l, b, g, slots], kk[:, g]], axis=0)
+            vals = np.concatenate([st.v_ring[l, b, g, slots], vv[:, g]], axis=0)
+            o[:, hq] = attend(q[:, hq], keys, vals)           # no mask inside the block
+        h = h + linear(o.reshape(kb, Hq * dh), W["w_o"][l])
 
         y = rms_norm(h, W["mlp_norm"][l], eps)
         gu = linear(y, W["w_gate_up"][l])
-        h = h + linear(silu(gu[..., :F]) * gu[..., F:], W["w_down"][l])
+        h = h + linear(silu(gu[:, :F]) * gu[:, F:], W["w_down"][l])
 
-    z = linear(rms_norm(h, W["final_norm"], eps), W["lm_head"])   # [B, k, V]
-    draft = np.argmax(z, axis=-1)                                   # first max = smallest id
-    top2 = np.sort(z, axis=-1)[..., -2:]
-    out = {"draft": draft.astype(np.int64), "margin": top2[..., 1] - top2[..., 0]}
+    return linear(rms_norm(h, W["final_norm"], eps), W["lm_head"])   # [kb, V]
+
+
+def draft_step(dims, W, st: State, want_logits: bool = True, block_len=None) -> Dict[str, np.ndarray]:
+    """One forward of the draft transformer over the block of every sequence.
+
+    block_len: per-sequence block length k_b (default k for all).  Returns draft
+    [B, k] (argmax, smallest id on ties; -1 past k_b), logits [B, k, V] (NaN past
+    k_b) and margin [B, k] (top-1 minus top-2 logit; inf past k_b).
+    """
+    B, k, V = st.ctx_len.shape[0], dims.block_k, dims.vocab
+    kb = block_lengths(dims, B, block_len)
+    z = np.full((B, k, V), np.nan)
+    draft = np.full((B, k), -1, np.int64)
+    margin = np.full((B, k), np.inf)
+    for b in range(B):
+        n = int(kb[b])
+        if n == 0:
+            continue
+        zb = block_logits(dims, W, st, b, n)
+        z[b, :n] = zb
+        draft[b, :n] = np.argmax(zb, axis=-1)                       # first max = smallest id
+        top2 = np.sort(zb, axis=-1)[:, -2:]
+        margin[b, :n] = top2[:, 1] - top2[:, 0]
+    out = {"draft": draft, "margin": margin}
     if want_logits:
         out["logits"] = z
     return out
@@ -277,26 +306,29 @@ def accepted_length(draft_row: Sequence[int], target_row: Sequence[int], k: int)
     return a
 
 
-def verify_commit(dims, st: State, draft, target) -> Dict[str, np.ndarray]:
+def verify_commit(dims, st: State, draft, target, block_len=None) -> Dict[str, np.ndarray]:
     """Greedy longest-prefix verify, bonus token, commit or roll back (in place).
 
     target[b] holds k+1 tokens: the target's greedy token for positions P+1..P+k+1
-    given the anchor and the drafts before it.  Emits target[b, 0..a]; the new
-    committed length is P + a + 1 and the new anchor is the bonus target[b, a].
-    Rows written for positions past the new committed length are rolled back
-    (poisoned with NaN here, since their content is never to be read again).
+    given the anchor and the drafts before it.  With a block of k_b rows only
+    draft[b, :k_b] is tested and target[b, k_b] is the bonus after a full accept.
+    Emits target[b, 0..a]; the new committed length is P + a + 1 and the new anchor
+    is target[b, a].  Rows written for positions past the new committed length are
+    rolled back (poisoned with NaN here, since their content is never read again).
     """
     B, k = st.ctx_len.shape[0], dims.block_k
+    kb = block_lengths(dims, B, block_len)
     draft = np.asarray(draft, dtype=np.int64)
     target = np.asarray(target, dtype=np.int64)
     acc = np.zeros(B, np.int64)
     out = np.full((B, k + 1), -1, np.int64)
     for b in range(B):
-        a = accepted_length(draft[b], target[b], k)
+        n = int(kb[b])
+        a = accepted_length(draft[b], target[b], n)
         acc[b] = a
         out[b, :a + 1] = target[b, :a + 1]
         P = int(st.ctx_len[b])
-        dead = np.array([slot_of(dims, p) for p in range(P + a + 1, P + k + 1)], dtype=np.int64)
+        dead = np.array([slot_of(dims, p) for p in range(P + a + 1, P + n + 1)], dtype=np.int64)
         st.k_ring[:, b][:, :, dead, :] = np.nan
         st.v_ring[:, b][:, :, dead, :] = np.nan
         st.ctx_len[b] = P + a + 1

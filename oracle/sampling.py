@@ -177,24 +177,35 @@ def _ids(n: int, seq_ids: Optional[Sequence[int]]) -> np.ndarray:
     return np.arange(n) if seq_ids is None else np.asarray(seq_ids, dtype=np.int64)
 
 
+def _lengths(n: int, k: int, block_len) -> np.ndarray:
+    kb = np.full(n, k, np.int64) if block_len is None else np.asarray(block_len, dtype=np.int64)
+    if kb.shape != (n,) or np.any(kb < 0) or np.any(kb > k):
+        raise ValueError("block_len must hold one length in [0, k] per sequence")
+    return kb
+
+
 def sample_drafts(draft_logits, temperature: float, seed: int, step: int,
-                  seq_ids: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+                  seq_ids: Optional[Sequence[int]] = None, block_len=None) -> Dict[str, np.ndarray]:
     """Drafts x[b, i] ~ softmax(z[b, i] / T) by Gumbel-max with stream 1.
 
     seq_ids: the batch index of each given sequence (the noise of row m = b*k + i
-    depends on it).  Returns draft [n, k], gap [n, k] (top-2 gap of the perturbed
-    scores, i.e. how far the draw is from a tie) and lse [n, k] = log-sum-exp of
-    z / T."""
+    depends on it); block_len: rows drafted per sequence (default k).  Returns
+    draft [n, k] (-1 past the block), gap [n, k] (top-2 gap of the perturbed scores,
+    i.e. how far the draw is from a tie; inf past the block) and lse [n, k] =
+    log-sum-exp of z / T (NaN past the block)."""
     z = np.asarray(draft_logits, dtype=np.float64)
     n, k, V = z.shape
     ids = _ids(n, seq_ids)
-    x = np.zeros((n, k), np.int64)
-    gap = np.zeros((n, k))
+    kb = _lengths(n, k, block_len)
+    x = np.full((n, k), -1, np.int64)
+    gap = np.full((n, k), np.inf)
+    lse = np.full((n, k), np.nan)
     for j in range(n):
-        for i in range(k):
+        for i in range(int(kb[j])):
             x[j, i], gap[j, i] = gumbel_max(z[j, i] / temperature,
                                             draft_noise(seed, step, int(ids[j]) * k + i, V))
-    return {"draft": x, "gap": gap, "lse": logsumexp(z, temperature)}
+            lse[j, i] = logsumexp(z[j, i], temperature)
+    return {"draft": x, "gap": gap, "lse": lse}
 
 
 def accept_score(lp_x: float, lq_x: float, u: float) -> float:
@@ -215,8 +226,9 @@ def residual_scores(lp_row, lq_row) -> np.ndarray:
 
 
 def verify_sampled(draft, draft_logits, target_logits, temperature: float, seed: int, step: int,
-                   seq_ids: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
-    """Rejection-sampling verification of each sequence's block.
+                   seq_ids: Optional[Sequence[int]] = None, block_len=None) -> Dict[str, np.ndarray]:
+    """Rejection-sampling verification of each sequence's block (of block_len[b]
+    rows, default k: rows past it are not tested and the bonus row is k_b).
 
     Returns accept_len [n], emitted [n] (the residual or bonus token), out_tokens
     [n, k+1] (the accepted drafts, the emitted token, then -1), accept_margin [n]
@@ -226,10 +238,12 @@ def verify_sampled(draft, draft_logits, target_logits, temperature: float, seed:
     q / (p - q) of those two tokens: how strongly an error in log q moves their
     scores; 0 for a draw from p)."""
     x = np.asarray(draft, dtype=np.int64)
-    lq = log_softmax(draft_logits, temperature)      # [n, k, V]
-    lp = log_softmax(target_logits, temperature)     # [n, k+1, V]
+    with np.errstate(invalid="ignore"):               # rows past a block may be NaN
+        lq = log_softmax(draft_logits, temperature)   # [n, k, V]
+        lp = log_softmax(target_logits, temperature)  # [n, k+1, V]
     n, k, V = lq.shape
     ids = _ids(n, seq_ids)
+    kb = _lengths(n, k, block_len)
     acc = np.zeros(n, np.int64)
     emitted = np.zeros(n, np.int64)
     out = np.full((n, k + 1), -1, np.int64)
@@ -238,17 +252,18 @@ def verify_sampled(draft, draft_logits, target_logits, temperature: float, seed:
     slack = np.zeros(n)
     for j in range(n):
         b = int(ids[j])
+        nb = int(kb[j])
         a = 0
-        while a < k:
+        while a < nb:
             d = accept_score(lp[j, a, x[j, a]], lq[j, a, x[j, a]], accept_uniform(seed, step, b, a))
             margin[j] = min(margin[j], abs(d))
             if d < 0:
                 break
             a += 1
-        s = residual_scores(lp[j, a], lq[j, a]) if a < k else lp[j, k]
+        s = residual_scores(lp[j, a], lq[j, a]) if a < nb else lp[j, nb]
         noise = emit_noise(seed, step, b, V)
         y, egap[j] = gumbel_max(s, noise)
-        if a < k and np.any(np.exp(lp[j, a]) > np.exp(lq[j, a])):
+        if a < nb and np.any(np.exp(lp[j, a]) > np.exp(lq[j, a])):
             pert = s + noise
             pert[y] = -np.inf
             for v in (y, int(np.argmax(pert))):
@@ -262,15 +277,16 @@ def verify_sampled(draft, draft_logits, target_logits, temperature: float, seed:
             "accept_margin": margin, "emit_gap": egap, "emit_slack": slack}
 
 
-def commit_sampled(dims, st, result) -> None:
+def commit_sampled(dims, st, result, block_len=None) -> None:
     """Advance the decode state exactly as greedy verification does: P += a + 1,
-    anchor = emitted token; rows past the new length are rolled back (NaN here)."""
+    anchor = emitted token; rows past the new length (up to P + k_b) are rolled
+    back (NaN here)."""
     from oracle import dflash_oracle as orc
-    k = dims.block_k
+    kb = _lengths(st.ctx_len.shape[0], dims.block_k, block_len)
     for j in range(st.ctx_len.shape[0]):
         a = int(result["accept_len"][j])
         P = int(st.ctx_len[j])
-        dead = np.array([orc.slot_of(dims, p) for p in range(P + a + 1, P + k + 1)], dtype=np.int64)
+        dead = np.array([orc.slot_of(dims, p) for p in range(P + a + 1, P + int(kb[j]) + 1)], dtype=np.int64)
         st.k_ring[:, j][:, :, dead, :] = np.nan
         st.v_ring[:, j][:, :, dead, :] = np.nan
         st.ctx_len[j] = P + a + 1
