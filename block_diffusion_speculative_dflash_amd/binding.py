@@ -39,7 +39,12 @@ class DflashWeights(ctypes.Structure):
 
 class DflashCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("ctx_len", ctypes.c_void_p),
-                ("anchor", ctypes.c_void_p), ("dev_error", ctypes.c_void_p)]
+                ("anchor", ctypes.c_void_p), ("dev_error", ctypes.c_void_p), ("block_len", ctypes.c_void_p)]
+
+
+class DflashAdaptParams(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_float), ("theta_down", ctypes.c_float), ("theta_off", ctypes.c_float),
+                ("theta_up", ctypes.c_float), ("cooldown", ctypes.c_int32)]
 
 
 class DflashSampling(ctypes.Structure):
@@ -58,7 +63,7 @@ _lib: Optional[ctypes.CDLL] = None
 EXPORTED = ("dflash_workspace_bytes", "dflash_status_string", "dflash_packed_bytes",
             "dflash_pack_weights", "dflash_fuse_inject", "dflash_draft_step",
             "dflash_verify_commit", "dflash_draft_step_timed", "dflash_draft_step_sampled",
-            "dflash_draft_step_sampled_timed", "dflash_verify_sampled")
+            "dflash_draft_step_sampled_timed", "dflash_verify_sampled", "dflash_adapt_block_len")
 
 
 def lib() -> ctypes.CDLL:
@@ -100,6 +105,9 @@ def lib() -> ctypes.CDLL:
     L.dflash_verify_sampled.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashSampling),
                                         P, P, P, P, ctypes.POINTER(DflashCache), P, P, P, S, P]
     L.dflash_verify_sampled.restype = ctypes.c_int
+    L.dflash_adapt_block_len.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashAdaptParams), P,
+                                         ctypes.POINTER(DflashCache), P, P, P]
+    L.dflash_adapt_block_len.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -129,7 +137,8 @@ def weights_struct(W: Dict[str, torch.Tensor]) -> DflashWeights:
 
 def cache_struct(cache: Dict[str, torch.Tensor]) -> DflashCache:
     return DflashCache(k=_ptr(cache["k"]), v=_ptr(cache["v"]), ctx_len=_ptr(cache["ctx_len"]),
-                       anchor=_ptr(cache["anchor"]), dev_error=_ptr(cache["dev_error"]))
+                       anchor=_ptr(cache["anchor"]), dev_error=_ptr(cache["dev_error"]),
+                       block_len=_ptr(cache.get("block_len")))
 
 
 def _stream(stream) -> int:
@@ -256,6 +265,20 @@ def dflash_verify_sampled(dims: Dims, sampling: DflashSampling, draft: torch.Ten
                                      _ptr(out_tokens), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream))
     _check("dflash_verify_sampled", st)
+
+
+def adapt_params(alpha: float = 0.25, theta_down: float = 4.0, theta_off: float = 2.0,
+                 theta_up: float = 6.0, cooldown: int = 16) -> DflashAdaptParams:
+    return DflashAdaptParams(alpha=alpha, theta_down=theta_down, theta_off=theta_off, theta_up=theta_up,
+                             cooldown=cooldown)
+
+
+def dflash_adapt_block_len(dims: Dims, params: DflashAdaptParams, accept_len: torch.Tensor, cache,
+                           ema: torch.Tensor, off_left: torch.Tensor, stream=None) -> None:
+    ds, cs = dims_struct(dims), cache_struct(cache)
+    st = lib().dflash_adapt_block_len(ctypes.byref(ds), ctypes.byref(params), _ptr(accept_len), ctypes.byref(cs),
+                                      _ptr(ema), _ptr(off_left), _stream(stream))
+    _check("dflash_adapt_block_len", st)
 
 
 # ----------------------------------------------------------------------------- buffers

@@ -332,6 +332,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     if (p == nullptr || !aligned16(p)) return DFLASH_E_INVALID;
   if (!cache->k || !cache->v || !aligned16(cache->k) || !aligned16(cache->v)) return DFLASH_E_INVALID;
   if (!cache->ctx_len || !cache->anchor || !cache->dev_error || !aligned4(draft)) return DFLASH_E_INVALID;
+  if (!aligned4(cache->block_len)) return DFLASH_E_INVALID;
   if (logits_out != nullptr && !aligned4(logits_out)) return DFLASH_E_INVALID;
   PackLayout P;
   if (!pack_layout(d, P)) return DFLASH_E_UNSUPPORTED;
@@ -404,6 +405,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     at.window = d.window;
     at.sink = d.sink;
     at.keys_per_split = L.ap.kps;
+    at.block_len = cache->block_len;
     at.max_splits = L.ap.max_splits;
     at.n_rb = L.ap.n_rb;
     at.rows_per_block = L.ap.rows;
@@ -473,6 +475,8 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   a.keys = c.at<unsigned long long>(L.keys);
   a.draft = draft;
   a.logits = logits_out;
+  a.block_len = cache->block_len;
+  a.rows_per_seq = d.block_k;
   const int epi = smp != nullptr ? EPI_SAMPLE : EPI_ARGMAX;
   if (smp != nullptr) {
     const GemmPlan hp = gemm_plan(d, EPI_SAMPLE, a.M, a.n_tiles, a.S, false, partial_bytes(d));
@@ -674,9 +678,11 @@ int dflash_verify_commit(const dflash_dims* dims, const int32_t* draft, const in
   v.accept_len = accept_len;
   v.out_tokens = out_tokens;
   v.dev_error = cache->dev_error;
+  v.block_len = cache->block_len;
   v.batch = dims->batch;
   v.block_k = dims->block_k;
   v.vocab = dims->vocab;
+  if (!aligned4(cache->block_len)) return DFLASH_E_INVALID;
   DF_CHECK(launch_verify(v, stream));
   return DFLASH_OK;
 }
@@ -690,7 +696,7 @@ int dflash_verify_sampled(const dflash_dims* dims, const dflash_sampling* sampli
       !cache->ctx_len || !cache->anchor || !cache->dev_error)
     return DFLASH_E_INVALID;
   if (!aligned4(draft) || !aligned16(draft_logits) || !aligned4(draft_lse) || !aligned16(target_logits) ||
-      !aligned4(accept_len) || !aligned4(out_tokens))
+      !aligned4(accept_len) || !aligned4(out_tokens) || !aligned4(cache->block_len))
     return DFLASH_E_INVALID;
   const dflash_dims& d = *dims;
   const Layout L = layout(d);
@@ -701,6 +707,7 @@ int dflash_verify_sampled(const dflash_dims* dims, const dflash_sampling* sampli
   v.draft_logits = draft_logits;
   v.draft_lse = draft_lse;
   v.target_logits = target_logits;
+  v.block_len = cache->block_len;
   v.ctx_len = cache->ctx_len;
   v.anchor = cache->anchor;
   v.accept_len = accept_len;
@@ -721,6 +728,33 @@ int dflash_verify_sampled(const dflash_dims* dims, const dflash_sampling* sampli
   v.step = sampling->step;
   v.step_dev = reinterpret_cast<const unsigned long long*>(sampling->step_dev);
   DF_CHECK(launch_verify_sampled(v, stream));
+  return DFLASH_OK;
+}
+
+int dflash_adapt_block_len(const dflash_dims* dims, const dflash_adapt_params* params, const int32_t* accept_len,
+                           const dflash_cache* cache, float* ema, int32_t* off_left, hipStream_t stream) {
+  if (!dims_ok(dims) || params == nullptr || cache == nullptr) return DFLASH_E_INVALID;
+  if (!accept_len || !cache->block_len || !cache->dev_error || !ema || !off_left) return DFLASH_E_INVALID;
+  if (!aligned4(accept_len) || !aligned4(cache->block_len) || !aligned4(ema) || !aligned4(off_left))
+    return DFLASH_E_INVALID;
+  const dflash_adapt_params& p = *params;
+  if (!(p.alpha > 0.f && p.alpha <= 1.f) || p.cooldown < 1 || !std::isfinite(p.theta_down) ||
+      !std::isfinite(p.theta_off) || !std::isfinite(p.theta_up))
+    return DFLASH_E_INVALID;
+  AdaptArgs a{};
+  a.accept_len = accept_len;
+  a.block_len = cache->block_len;
+  a.ema = ema;
+  a.off_left = off_left;
+  a.dev_error = cache->dev_error;
+  a.batch = dims->batch;
+  a.block_k = dims->block_k;
+  a.cooldown = p.cooldown;
+  a.alpha = p.alpha;
+  a.theta_down = p.theta_down;
+  a.theta_off = p.theta_off;
+  a.theta_up = p.theta_up;
+  DF_CHECK(launch_adapt(a, stream));
   return DFLASH_OK;
 }
 

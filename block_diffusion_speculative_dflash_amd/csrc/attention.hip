@@ -67,12 +67,14 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnArgs a) {
   item /= a.n_rb;
   const int g = item % a.n_kv_heads, b = item / a.n_kv_heads;
   const int k = a.block_k, G = a.n_q_heads / a.n_kv_heads;
-  // key list: the sink positions 0..n_sink-1, the window positions ws..P-1, the block
+  // key list: the sink positions 0..n_sink-1, the window positions ws..P-1, the
+  // sequence's kb block rows
   const int P = max(a.ctx_len[b], 0);
   const int n_sink = min(a.sink, P);
   const int ws = max(n_sink, P - a.window);
   const int n_ctx = n_sink + (P - ws);
-  const int n_keys = n_ctx + k;
+  const int kb = a.block_len != nullptr ? min(max(a.block_len[b], 0), k) : k;
+  const int n_keys = n_ctx + kb;
   const int n_split_b = (n_keys + a.keys_per_split - 1) / a.keys_per_split;
   if (split >= n_split_b) return;  // uniform per workgroup
   const int j0 = split * a.keys_per_split;
@@ -278,9 +280,10 @@ __global__ __launch_bounds__(kThreads) void attention_merge_kernel(AttnArgs a) {
   const int k = a.block_k, G = a.n_q_heads / a.n_kv_heads;
   const int P = max(a.ctx_len[b], 0);
   const int n_sink = min(a.sink, P);
-  const int n_keys = n_sink + (P - max(n_sink, P - a.window)) + k;
+  const int kb = a.block_len != nullptr ? min(max(a.block_len[b], 0), k) : k;
+  const int n_keys = n_sink + (P - max(n_sink, P - a.window)) + kb;
   const int n_split_b = (n_keys + a.keys_per_split - 1) / a.keys_per_split;
-  if (n_split_b == 1) return;  // uniform per workgroup
+  if (n_split_b <= 1) return;  // uniform per workgroup (0: no keys, the rows lie outside any block)
   const int t = threadIdx.x, dq = t % TPR, sub = (t / TPR) % NSUB, rw = t / (TPR * NSUB);
   const int r0 = rb * rows;
   const int rr = (blockIdx.x % wg_per_grp) * RPW + rw;

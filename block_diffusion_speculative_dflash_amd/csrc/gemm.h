@@ -70,6 +70,7 @@ struct GemmArgs {
   void* cache_v;
   unsigned long long* keys;  // [M * kKeyStride] zero-initialised argmax keys (ARGMAX)
   int32_t* draft;            // [M]
+  const int32_t* block_len;  // ARGMAX / SAMPLE: [B] or nullptr; rows i >= block_len[b] draft -1
   float* logits;             // [M, N] or nullptr
   uint32_t* dev_error;
   // EPI_SAMPLE: s = logits / T; draft = argmax(s + Gumbel noise of row m);

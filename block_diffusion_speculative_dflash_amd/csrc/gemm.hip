@@ -303,7 +303,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       const unsigned long long key =
           __hip_atomic_exchange(&g.keys[static_cast<size_t>(m) * kKeyStride], 0ull, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
-      g.draft[m] = argmax_key_index(key);
+      const bool in_block = g.block_len == nullptr || m % g.rows_per_seq < g.block_len[m / g.rows_per_seq];
+      g.draft[m] = in_block ? argmax_key_index(key) : -1;
     }
     if (tid == 0) reset_counter(&g.counters[tile_m]);
   }

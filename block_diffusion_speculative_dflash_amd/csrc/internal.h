@@ -57,6 +57,7 @@ struct AttnArgs {
   unsigned* counters;  // [B, Hkv, n_rb]
   int batch, block_k, n_q_heads, n_kv_heads, head_dim, cache_slots, window, sink;
   int keys_per_split, max_splits, n_rb, rows_per_block;  // rows_per_block: 16, 32, 48 or 64
+  const int32_t* block_len;  // [B] or nullptr: block keys of sequence b are rows 0 .. block_len[b]-1
 };
 hipError_t launch_attention(bool f32, const AttnArgs& a, hipStream_t stream);
 
@@ -68,9 +69,22 @@ struct VerifyArgs {
   int32_t* accept_len;
   int32_t* out_tokens;
   uint32_t* dev_error;
+  const int32_t* block_len;  // [B] or nullptr (k drafts each)
   int batch, block_k, vocab;
 };
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+
+// Runtime block-size controller (one thread per sequence).
+struct AdaptArgs {
+  const int32_t* accept_len;
+  int32_t* block_len;
+  float* ema;
+  int32_t* off_left;
+  uint32_t* dev_error;
+  int batch, block_k, cooldown;
+  float alpha, theta_down, theta_off, theta_up;
+};
+hipError_t launch_adapt(const AdaptArgs& a, hipStream_t stream);
 
 // Log-sum-exp of each row from its per-tile (max, sum) partials.
 hipError_t launch_lse_merge(const float2* part, int n_parts, int rows, float* lse, hipStream_t stream);
@@ -82,6 +96,7 @@ struct VerifySampledArgs {
   const float* draft_logits;    // [B, k, V]
   const float* draft_lse;       // [B, k]  log-sum-exp of draft_logits / T
   const float* target_logits;   // [B, k+1, V]
+  const int32_t* block_len;     // [B] or nullptr (k drafts each)
   int32_t* ctx_len;
   int32_t* anchor;
   int32_t* accept_len;

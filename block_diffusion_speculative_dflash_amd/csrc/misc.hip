@@ -69,6 +69,12 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
   const int k = a.block_k;
   const int32_t* dr = a.draft + static_cast<size_t>(b) * k;
   const int32_t* tg = a.target + static_cast<size_t>(b) * (k + 1);
+  int kb = k;  // drafts of this sequence's block
+  if (a.block_len != nullptr) {
+    kb = a.block_len[b];
+    if ((kb < 0 || kb > k) && lane == 0) atomicOr(a.dev_error, 16u);
+    kb = min(max(kb, 0), k);
+  }
   bool bad = false;
   int t = 0;
   if (lane <= k) {
@@ -76,13 +82,13 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
     if (t < 0 || t >= a.vocab) { bad = true; t = min(max(t, 0), a.vocab - 1); }
   }
   bool match = false;
-  if (lane < k) {
+  if (lane < kb) {
     int dv = dr[lane];
     if (dv < 0 || dv >= a.vocab) { bad = true; dv = min(max(dv, 0), a.vocab - 1); }
     match = (dv == t);
   }
   const unsigned long long ones = __ballot(match);
-  // lanes >= k never match, so the first zero bit is at most k
+  // lanes >= kb never match, so the first zero bit is at most kb
   const int acc = __ffsll(static_cast<long long>(~ones)) - 1;
   const int bonus = __shfl(t, acc, kWave);
   if (lane <= k) a.out_tokens[static_cast<size_t>(b) * (k + 1) + lane] = lane <= acc ? t : -1;
@@ -99,6 +105,64 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
   const dim3 grid((a.batch + 3) / 4);
   hipLaunchKernelGGL(verify_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Runtime block-size controller, one thread per sequence (the hotdry blog's dynamic
+// fallback; rungs full k, half k/2, off).  The moving average is float32 with every
+// operation rounded separately (no contraction into fused multiply-adds), so the
+// rung decisions taken from it are reproducible operation by operation.
+__global__ void adapt_kernel(AdaptArgs a) {
+#pragma clang fp contract(off)
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= a.batch) return;
+  const int full = a.block_k, h = a.block_k / 2;
+  const int half = (h > 0 && h < full) ? h : 0;  // 0: no middle rung
+  int kb = a.block_len[b];
+  if (kb < 0 || kb > full) {
+    atomicOr(a.dev_error, 16u);
+    kb = min(max(kb, 0), full);
+  }
+  float m = a.ema[b];
+  int off = a.off_left[b];
+  if (kb == 0) {
+    off -= 1;
+    if (off <= 0) {
+      kb = half > 0 ? half : full;
+      m = a.theta_down;
+      off = 0;
+    }
+  } else {
+    const int acc = min(max(a.accept_len[b], 0), kb);
+    // correctly rounded division (hipcc's default), then products and sums kept
+    // apart by the contract(off) pragma of this function
+    const float scale = static_cast<float>(full) / static_cast<float>(kb);
+    const float tau = 1.f + static_cast<float>(acc) * scale;
+    const float step = a.alpha * (tau - m);
+    m = m + step;
+    if (kb == full) {
+      if (m < a.theta_down) {
+        if (half > 0) {
+          kb = half;
+        } else {
+          kb = 0;
+          off = a.cooldown;
+        }
+      }
+    } else if (m < a.theta_off) {
+      kb = 0;
+      off = a.cooldown;
+    } else if (m >= a.theta_up) {
+      kb = full;
+    }
+  }
+  a.block_len[b] = kb;
+  a.ema[b] = m;
+  a.off_left[b] = off;
+}
+
+hipError_t launch_adapt(const AdaptArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(adapt_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

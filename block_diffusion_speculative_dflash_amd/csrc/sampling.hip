@@ -108,6 +108,8 @@ __global__ __launch_bounds__(kThreads) void verify_lse_kernel(VerifySampledArgs 
   __shared__ int last_s;
   const int chunk = blockIdx.x, i = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int k = a.block_k, V = a.vocab;
+  const int kb = a.block_len != nullptr ? min(max(a.block_len[b], 0), k) : k;
+  if (i > kb) return;  // target rows past the bonus row of this sequence's block: unused
   const bool vec = (V & 3) == 0;
   const float* trow_b = a.target_logits + static_cast<size_t>(b) * (k + 1) * V;
   const float* row = trow_b + static_cast<size_t>(i) * V;
@@ -162,14 +164,14 @@ __global__ __launch_bounds__(kThreads) void verify_lse_kernel(VerifySampledArgs 
       reset_counter(row_cnt);
     }
   }
-  if (!arrive_last(&a.counters[b], static_cast<unsigned>(k + 1), &last_s)) return;
+  if (!arrive_last(&a.counters[b], static_cast<unsigned>(kb + 1), &last_s)) return;
 
   // last row of sequence b: the acceptance tests
   if (tid < kWave) {
     const int lane = tid;
-    const float lse_t = lane <= k ? coherent_load(&a.row_lse[static_cast<size_t>(b) * (k + 1) + lane]) : 0.f;
+    const float lse_t = lane <= kb ? coherent_load(&a.row_lse[static_cast<size_t>(b) * (k + 1) + lane]) : 0.f;
     bool ok = false, bad = false;
-    if (lane < k) {
+    if (lane < kb) {
       int x = a.draft[static_cast<size_t>(b) * k + lane];
       if (x < 0 || x >= V) { bad = true; x = min(max(x, 0), V - 1); }
       const float lp = trow_b[static_cast<size_t>(lane) * V + x] * a.inv_temp - lse_t;
@@ -181,11 +183,12 @@ __global__ __launch_bounds__(kThreads) void verify_lse_kernel(VerifySampledArgs 
       ok = lp - lq - ln_uniform(h[0]) >= 0.f;  // u q(x) <= p(x)
     }
     const unsigned long long ones = __ballot(ok);
-    const int acc = __ffsll(static_cast<long long>(~ones)) - 1;  // lanes >= k never accept: acc <= k
+    const int acc = __ffsll(static_cast<long long>(~ones)) - 1;  // lanes >= kb never accept: acc <= kb
     const float lse_a = __shfl(lse_t, acc, kWave);
     if (__ballot(bad) != 0ull && lane == 0) atomicOr(a.dev_error, 1u);
     if (lane == 0) {
-      const float lq_a = acc < k ? a.draft_lse[static_cast<size_t>(b) * k + acc] : 0.f;
+      if (a.block_len != nullptr && (a.block_len[b] < 0 || a.block_len[b] > k)) atomicOr(a.dev_error, 16u);
+      const float lq_a = acc < kb ? a.draft_lse[static_cast<size_t>(b) * k + acc] : 0.f;
       a.decision[b] = make_float4(static_cast<float>(acc), lse_a, lq_a, 0.f);
       reset_counter(&a.counters[b]);
     }
@@ -201,8 +204,9 @@ __global__ __launch_bounds__(kThreads) void verify_emit_kernel(VerifySampledArgs
   const int k = a.block_k, V = a.vocab;
   const bool vec = (V & 3) == 0;
   const float4 dec = a.decision[b];
-  const int acc = min(max(static_cast<int>(dec.x), 0), k);
-  const bool resid = acc < k;
+  const int kb = a.block_len != nullptr ? min(max(a.block_len[b], 0), k) : k;
+  const int acc = min(max(static_cast<int>(dec.x), 0), kb);
+  const bool resid = acc < kb;  // otherwise the bonus draw from target row kb
   const float lse_p = dec.y, lse_q = dec.z;
   const float* trow = a.target_logits + (static_cast<size_t>(b) * (k + 1) + acc) * V;
   const float* zrow = a.draft_logits + (static_cast<size_t>(b) * k + min(acc, k - 1)) * V;

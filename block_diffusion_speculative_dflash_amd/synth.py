@@ -177,6 +177,6 @@ def plant_target_logits(draft_logits: torch.Tensor, draft: np.ndarray, a_star: n
             t[b, :a] = z[b, :a]
             if soft > 0:
                 t[b, :a] += _normal((a, V), seed, (_LOGITS, 10_000 + b), soft, torch.float32, z.device)
-        if a < k:
+        if a < k and dr[b, a] >= 0:  # a draft past a shorter block (-1) has nothing to reject
             t[b, a, int(dr[b, a])] = -1.0e4
     return t

@@ -72,6 +72,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 #define DFLASH_DEVERR_ROWS 2u    /* n_rows[b] outside [0, n_max]: clamped */
 #define DFLASH_DEVERR_CTXLEN 4u  /* ctx_len[b] negative: treated as 0 */
 #define DFLASH_DEVERR_RANGE 8u   /* a bf16 weight beyond the fp16 range: saturated when packed */
+#define DFLASH_DEVERR_BLOCK 16u  /* block_len[b] outside [0, k]: clamped */
 
 /* (host) Static shapes of one drafter; read during a call only.
  *   batch B, block_k k (1..63), n_layers L, hidden d, n_q_heads Hq, n_kv_heads Hkv
@@ -123,11 +124,20 @@ typedef struct {
  *              k rows carry RoPE at position p
  *   ctx_len    [B] int32 committed length P_b (a logical position, may exceed C)
  *   anchor     [B] int32 token at position P_b (the visible first row of the block)
- *   dev_error  [1] uint32 sticky DFLASH_DEVERR_* bits */
+ *   dev_error  [1] uint32 sticky DFLASH_DEVERR_* bits
+ *   block_len  [B] int32 or NULL: the number of draft rows k_b in [0, k] of sequence b
+ *              this round (NULL: k for every sequence).  A block of k_b rows is the
+ *              anchor plus k_b - 1 mask rows and its keys; rows past k_b are not part
+ *              of it (their drafts read -1, their logits are unspecified); k_b = 0
+ *              turns speculation off for the sequence (the round commits the target's
+ *              own next token).  The verify calls test k_b drafts and take the bonus
+ *              from target row k_b; the fuse_inject of the round writes k_b + 1 rows
+ *              (n_rows[b] = k_b + 1).  dflash_adapt_block_len updates it. */
 typedef struct {
   void *k, *v;
   int32_t *ctx_len, *anchor;
   uint32_t *dev_error;
+  int32_t *block_len;
 } dflash_cache;
 
 /* Bytes of device workspace the three calls need for these dims.  The workspace
@@ -265,6 +275,34 @@ int dflash_verify_sampled(const dflash_dims *dims, const dflash_sampling *sampli
                           const dflash_cache *cache, int32_t *accept_len,
                           int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/* (host) Parameters of the runtime block-size controller (the hotdry blog's dynamic
+ * fallback: while measured acceptance stays below the scenario's threshold the
+ * block is shrunk step by step, 8 -> 4, or speculation is turned off for a while;
+ * its reference thresholds on the mean accepted length at block 8 are code >= 6.0,
+ * math >= 5.0, agent >= 4.0, open chat < 4.0).  Rungs: full k, half k/2 (absent when
+ * 0), off.  Per sequence a float32 moving average m of the accepted length at the
+ * full block: after a round of k_b > 0 drafts with a accepted,
+ * tau = 1 + a * (k / k_b), m = m + alpha * (tau - m) (each operation rounded).
+ *   full: m < theta_down -> one rung down;  half: m < theta_off -> off,
+ *   m >= theta_up -> full;  off: `cooldown` rounds, then half (full if there is no
+ *   half rung) with m = theta_down.
+ * Suggested: alpha 0.25, theta_down 4.0, theta_off 2.0, theta_up 6.0, cooldown 16. */
+typedef struct {
+  float alpha, theta_down, theta_off, theta_up;
+  int32_t cooldown;
+} dflash_adapt_params;
+
+/* One controller round after a verify call, in place:
+ *   params      (host) the controller parameters (0 < alpha <= 1, cooldown >= 1)
+ *   accept_len  [B] int32 accepted lengths of the round just verified
+ *   cache       its block_len (required here) is read and updated
+ *   ema         [B] float moving averages m (initialise to theta_up)
+ *   off_left    [B] int32 rounds left with speculation off (initialise to 0)
+ * Sequences whose block_len is 0 count their cool-down down and ignore accept_len. */
+int dflash_adapt_block_len(const dflash_dims *dims, const dflash_adapt_params *params,
+                           const int32_t *accept_len, const dflash_cache *cache, float *ema,
+                           int32_t *off_left, hipStream_t stream);
 
 /* Same as dflash_draft_step, and records head_begin / head_end on `stream` right
  * before and after the fused final-norm + LM-head + argmax kernel, so a caller can

@@ -164,16 +164,28 @@ class ParityRun:
                     kv_max = max(kv_max, float(np.max(np.abs(ref))) if ref.size else 0.0)
         return kv_err, kv_max
 
-    def _inject_block(self):
-        """Tentative K/V rows of the k+1 positions the target just processed (both sides)."""
+    def _set_block_len(self, block_len):
+        """Per-sequence block lengths of this round (None: k for all); returns the host
+        array of every sequence's k_b."""
+        d = self.d
+        if block_len is None:
+            self.cache.pop("block_len", None)
+            return np.full(d.batch, d.block_k, np.int64)
+        kb = np.asarray(block_len, dtype=np.int64)
+        self.cache["block_len"] = torch.as_tensor(kb, dtype=torch.int32, device="cuda")
+        return kb
+
+    def _inject_block(self, kb=None):
+        """Tentative K/V rows of the k_b+1 positions the target just processed (both sides)."""
         d, k, s = self.d, self.d.block_k, self.sample
+        kb = np.full(d.batch, k, np.int64) if kb is None else np.asarray(kb, np.int64)
         taps = synth.make_taps(d, k + 1, seed=self.seed, stream=1 + self.step_idx, device="cuda")
-        n_rows = torch.full((d.batch,), k + 1, dtype=torch.int32, device="cuda")
+        n_rows = torch.as_tensor(kb + 1, dtype=torch.int32, device="cuda")
         bd.dflash_fuse_inject(d, self.W, taps, n_rows, k + 1, False, self.cache, self.ws)
-        orc.fuse_inject(d, self.Wn, self.st, taps[s].float().cpu().numpy(), np.full(len(s), k + 1), commit=False)
+        orc.fuse_inject(d, self.Wn, self.st, taps[s].float().cpu().numpy(), kb[s] + 1, commit=False)
 
     def step_sampled(self, a_star: Sequence[int], temperature: float, seed: int = 1234,
-                     soft: float = 0.0) -> "SampledReport":
+                     soft: float = 0.0, block_len=None) -> "SampledReport":
         """One sampled round: dflash_draft_step_sampled, tentative injection,
         dflash_verify_sampled, against the oracle's draft forward, Gumbel-max drafts
         and rejection-sampling verification with the same seed and step.
@@ -191,21 +203,25 @@ class ParityRun:
         T = float(temperature)
         step = self.step_idx
         smp = bd.sampling_struct(T, seed, step)
-        say(f"[parity] sampled step {step}: draft_step_sampled B={B} k={k} V={V} T={T}")
+        kb = self._set_block_len(block_len)
+        a_star = np.minimum(np.asarray(a_star, np.int64), kb)
+        say(f"[parity] sampled step {step}: draft_step_sampled B={B} k={k} V={V} T={T} kb={list(kb[:8])}")
         draft = torch.empty((B, k), dtype=torch.int32, device="cuda")
         logits = torch.empty((B, k, V), dtype=torch.float32, device="cuda")
         lse = torch.empty((B, k), dtype=torch.float32, device="cuda")
         bd.dflash_draft_step_sampled(d, W, self.cache, smp, draft, logits, lse, self.ws)
         torch.cuda.synchronize()
-        o = orc.draft_step(d, self.Wn, self.st)
+        o = orc.draft_step(d, self.Wn, self.st, block_len=kb[s])
         zr = o["logits"]
-        sd = sp.sample_drafts(zr, T, seed, step, seq_ids=s)
+        sd = sp.sample_drafts(zr, T, seed, step, seq_ids=s, block_len=kb[s])
         xr, gap, lse_r = sd["draft"], sd["gap"], sd["lse"]
+        live = np.arange(k)[None, :] < kb[s][:, None]               # rows inside each block
         zg = logits[s].cpu().numpy().astype(np.float64)
         dg = draft[s].cpu().numpy().astype(np.int64)
-        err = float(np.max(np.abs(zg - zr)))
-        ref_max = float(np.max(np.abs(zr)))
-        lse_err = float(np.max(np.abs(lse[s].cpu().numpy() - lse_r)))
+        err = float(np.max(np.abs(zg - zr)[live])) if live.any() else 0.0
+        ref_max = float(np.max(np.abs(zr[live]))) if live.any() else 1.0
+        lse_err = float(np.max(np.abs(lse[s].cpu().numpy() - lse_r)[live])) if live.any() else 0.0
+        assert np.all(dg[~live] == -1), "drafts past a block must read -1"
         tol_z = self.tol.logit_abs if self.tol.logit_abs is not None else self.tol.logit_rel * ref_max
         err_s = err / T
         thr = 2 * err_s + 1e-3
@@ -216,17 +232,18 @@ class ParityRun:
         x_all = draft.cpu().numpy().astype(np.int64)
         x_all[s] = xr
         z_all = logits.clone()
-        z_all[s] = torch.as_tensor(zr, dtype=torch.float32, device="cuda")
+        z_all[s] = torch.as_tensor(np.nan_to_num(zr), dtype=torch.float32, device="cuda")
         fill = synth.make_logits((B, k + 1, V), seed=self.seed, stream=7919 * (step + 1), device="cuda")
         tgt = synth.plant_target_logits(z_all, x_all, np.asarray(a_star), fill, soft=soft, seed=step).contiguous()
         say(f"[parity] sampled step {step}: fuse_inject + verify_sampled")
-        self._inject_block()
+        self._inject_block(kb)
         acc = torch.empty(B, dtype=torch.int32, device="cuda")
         out = torch.empty((B, k + 1), dtype=torch.int32, device="cuda")
         bd.dflash_verify_sampled(d, smp, draft, logits, lse, tgt, self.cache, acc, out, self.ws)
         torch.cuda.synchronize()
-        r = sp.verify_sampled(xr, zr, tgt[s].cpu().numpy().astype(np.float64), T, seed, step, seq_ids=s)
-        sp.commit_sampled(d, self.st, r)
+        r = sp.verify_sampled(xr, zr, tgt[s].cpu().numpy().astype(np.float64), T, seed, step, seq_ids=s,
+                              block_len=kb[s])
+        sp.commit_sampled(d, self.st, r, block_len=kb[s])
 
         acc_g, out_g = acc[s].cpu().numpy(), out[s].cpu().numpy()
         ctx_g, anc_g = self.cache["ctx_len"][s].cpu().numpy(), self.cache["anchor"][s].cpu().numpy()
@@ -234,7 +251,7 @@ class ParityRun:
         for j, b in enumerate(s):
             a_ref = int(r["accept_len"][j])
             dq = err_s + lse_err
-            ok = (all(gap[j, i] >= thr for i in range(0, min(a_ref, k - 1) + 1))
+            ok = (all(gap[j, i] >= thr for i in range(0, min(a_ref, int(kb[b]) - 1) + 1))
                   and r["accept_margin"][j] >= dq + 1e-3
                   and r["emit_gap"][j] >= 2 * dq * r["emit_slack"][j] + 1e-3)
             if ok:
@@ -257,30 +274,33 @@ class ParityRun:
             f"excluded {excluded}, state mismatches {state_mism}; kv_err={kv_err:.3g} accept={rep.accept[:8]}")
         return rep
 
-    def step(self, a_star: Sequence[int]) -> StepReport:
+    def step(self, a_star: Sequence[int], block_len=None) -> StepReport:
         d, W, s = self.d, self.W, self.sample
         B, k, V = d.batch, d.block_k, d.vocab
-        say(f"[parity] step {self.step_idx}: draft_step B={B} k={k} V={V}")
+        kb = self._set_block_len(block_len)
+        a_star = np.minimum(np.asarray(a_star, np.int64), kb)
+        say(f"[parity] step {self.step_idx}: draft_step B={B} k={k} V={V} kb={list(kb[:8])}")
         draft = torch.empty((B, k), dtype=torch.int32, device="cuda")
         logits = torch.empty((B, k, V), dtype=torch.float32, device="cuda")
         bd.dflash_draft_step(d, W, self.cache, draft, logits, self.ws)
         torch.cuda.synchronize()
-        o = orc.draft_step(d, self.Wn, self.st)
+        o = orc.draft_step(d, self.Wn, self.st, block_len=kb[s])
         zg = logits[s].cpu().numpy().astype(np.float64)
         dg = draft[s].cpu().numpy().astype(np.int64)
         zr, dr, mr = o["logits"], o["draft"], o["margin"]
-        err = float(np.max(np.abs(zg - zr)))
-        ref_max = float(np.max(np.abs(zr)))
-        gate = mr >= self.tol.margin
-        mism = int(np.sum((dg != dr) & gate))
+        live = np.arange(k)[None, :] < kb[s][:, None]               # rows inside each block
+        err = float(np.max(np.abs(zg - zr)[live])) if live.any() else 0.0
+        ref_max = float(np.max(np.abs(zr[live]))) if live.any() else 1.0
+        gate = (mr >= self.tol.margin) & live
+        mism = int(np.sum((dg != dr) & gate)) + int(np.sum(dg[~live] != -1))
 
         # target stand-in: planted from the oracle's drafts for sampled sequences
         fill = synth.target_fill(k, 1, B, seed=self.seed + 7919 * (self.step_idx + 1))[0]
         a_star = np.asarray(a_star, np.int64)
-        T = synth.plant_targets(draft.cpu().numpy(), a_star, fill, V)
-        T[s] = synth.plant_targets(dr, a_star[s], fill[s], V)
+        T = synth.plant_targets(np.maximum(draft.cpu().numpy(), 0), a_star, fill, V)
+        T[s] = synth.plant_targets(np.maximum(dr, 0), a_star[s], fill[s], V)
         taps = synth.make_taps(d, k + 1, seed=self.seed, stream=1 + self.step_idx, device="cuda")
-        n_rows = torch.full((B,), k + 1, dtype=torch.int32, device="cuda")
+        n_rows = torch.as_tensor(kb + 1, dtype=torch.int32, device="cuda")
         say(f"[parity] step {self.step_idx}: fuse_inject + verify_commit")
         bd.dflash_fuse_inject(d, W, taps, n_rows, k + 1, False, self.cache, self.ws)
         acc = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -288,8 +308,8 @@ class ParityRun:
         Tt = torch.as_tensor(T, dtype=torch.int32).cuda()
         bd.dflash_verify_commit(d, draft, Tt, self.cache, acc, out)
         torch.cuda.synchronize()
-        orc.fuse_inject(d, self.Wn, self.st, taps[s].float().cpu().numpy(), np.full(len(s), k + 1), commit=False)
-        r = orc.verify_commit(d, self.st, dr, T[s])
+        orc.fuse_inject(d, self.Wn, self.st, taps[s].float().cpu().numpy(), kb[s] + 1, commit=False)
+        r = orc.verify_commit(d, self.st, np.maximum(dr, 0), T[s], block_len=kb[s])
 
         acc_g = acc[s].cpu().numpy()
         out_g = out[s].cpu().numpy()
@@ -298,7 +318,7 @@ class ParityRun:
         checked = excluded = state_mism = 0
         for j, b in enumerate(s):
             a_ref = int(r["accept_len"][j])
-            deciding = range(0, min(a_ref, k - 1) + 1)
+            deciding = range(0, min(a_ref, int(kb[b]) - 1) + 1)
             if all(mr[j, i] >= self.tol.margin for i in deciding):
                 checked += 1
                 same = (acc_g[j] == a_ref and np.array_equal(out_g[j], r["out_tokens"][j])
