@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--temperature", type=float, default=0.0,
                    help="0: greedy drafting and verification; > 0: sampled drafting and "
                         "rejection-sampling verification at this temperature")
+    p.add_argument("--adaptive", action="store_true",
+                   help="per-sequence block lengths chosen every step by the block-size controller "
+                        "(dflash_adapt_block_len, default thresholds) from the accepted lengths")
     p.add_argument("--sink", type=int, default=0,
                    help="attention sink: positions 0..S-1 stay visible beside the window "
                         "(adds S cache slots; the sink rows are injected before the prefill)")
@@ -162,6 +165,16 @@ def main() -> int:
     pool = [synth.make_taps(d, k + 1, seed=args.seed, stream=1 + i, device=dev) for i in range(4)]
     saved_ctx = cache["ctx_len"].clone()
     sampled = args.temperature > 0
+    adaptive = args.adaptive
+    if adaptive:
+        # controller state: every sequence starts at the full block with the average at theta_up
+        aparams = bd.adapt_params()
+        cache["block_len"] = torch.full((B,), k, dtype=torch.int32, device=dev)
+        ema = torch.full((B,), aparams.theta_up, dtype=torch.float32, device=dev)
+        off_left = torch.zeros(B, dtype=torch.int32, device=dev)
+        kb_total = torch.zeros(1, dtype=torch.int64, device=dev)  # block rows drafted (harness)
+    blk = cache.get("block_len")
+    n_rows_in = torch.full((B,), k + 1, dtype=torch.int32, device=dev)
     if sampled:
         # sampled target stand-in: resident filler logits, planted per step from the drafts
         tgt_logits = synth.make_logits((B, k + 1, V), seed=args.seed, stream=31_337, device=dev)
@@ -173,17 +186,22 @@ def main() -> int:
         smp = bd.sampling_struct(args.temperature, args.seed + 1, 0, step_dev=rng_step)
 
     def step(taps):
+        n_rows = n_rows_in if adaptive else n_rows_step
         if sampled:
             bd.dflash_draft_step_sampled(d, W, cache, smp, draft, logits, lse, ws)
             harness.plant_logits(draft, tgt_logits, a_tab_d, step_ctr, saved_idx, saved_val, accept,
-                                 acc_total, rng_step)
-            bd.dflash_fuse_inject(d, W, taps, n_rows_step, k + 1, False, cache, ws)
+                                 acc_total, rng_step, block_len=blk, n_rows=n_rows_in if adaptive else None,
+                                 kb_total=kb_total if adaptive else None)
+            bd.dflash_fuse_inject(d, W, taps, n_rows, k + 1, False, cache, ws)
             bd.dflash_verify_sampled(d, smp, draft, logits, lse, tgt_logits, cache, accept, out_tok, ws)
-            return
-        bd.dflash_draft_step(d, W, cache, draft, None, ws)
-        harness.plant(draft, target, a_tab_d, fill_d, step_ctr, accept, acc_total, V)
-        bd.dflash_fuse_inject(d, W, taps, n_rows_step, k + 1, False, cache, ws)
-        bd.dflash_verify_commit(d, draft, target, cache, accept, out_tok)
+        else:
+            bd.dflash_draft_step(d, W, cache, draft, None, ws)
+            harness.plant(draft, target, a_tab_d, fill_d, step_ctr, accept, acc_total, V, block_len=blk,
+                          n_rows=n_rows_in if adaptive else None, kb_total=kb_total if adaptive else None)
+            bd.dflash_fuse_inject(d, W, taps, n_rows, k + 1, False, cache, ws)
+            bd.dflash_verify_commit(d, draft, target, cache, accept, out_tok)
+        if adaptive:
+            bd.dflash_adapt_block_len(d, aparams, accept, cache, ema, off_left)
 
     # eager warm-up of every code path, then capture one graph per taps slot
     stream = torch.cuda.Stream()
@@ -203,6 +221,11 @@ def main() -> int:
     step_ctr.zero_()
     acc_total.zero_()
     accept.zero_()
+    if adaptive:
+        blk.fill_(k)
+        ema.fill_(aparams.theta_up)
+        off_left.zero_()
+        kb_total.zero_()
     torch.cuda.synchronize()
 
     def run(n, s0):
@@ -214,6 +237,7 @@ def main() -> int:
     run(args.warmup, 0)
     torch.cuda.synchronize()
     tot0, acc0 = int(acc_total.item()), accept.clone()
+    kb0 = int(kb_total.item()) if adaptive else 0
     t0 = time.perf_counter()
     run(args.steps, args.warmup)
     torch.cuda.synchronize()
@@ -222,6 +246,14 @@ def main() -> int:
     accepted = tot1 - tot0 - int(acc0.sum().item()) + int(accept.sum().item())
     elapsed = t1 - t0
     planted = int(a_tab[args.warmup:args.warmup + args.steps].sum())
+    adapt_info = None
+    if adaptive:
+        final = cache["block_len"].cpu().numpy()
+        adapt_info = {"mean_block_len": round((int(kb_total.item()) - kb0) / (args.steps * B), 4),
+                      "final_block_len_hist": {str(v): int((final == v).sum()) for v in sorted(set(final.tolist()))},
+                      "params": {"alpha": aparams.alpha, "theta_down": aparams.theta_down,
+                                 "theta_off": aparams.theta_off, "theta_up": aparams.theta_up,
+                                 "cooldown": aparams.cooldown}}
     err = int(cache["dev_error"].item())
     steps_per_s = args.steps / elapsed
     committed = accepted + args.steps * B
@@ -293,11 +325,13 @@ def main() -> int:
                 + (", N(0,4) target logits with planted acceptance)" if sampled else ")"),
         "config": {"workload": wl.name, "batch": B, "block_k": k, "context": int(ctx.max()),
                    "window": d.window, "sink": d.sink, "layers": d.n_layers, "hidden": d.hidden,
-                   "ffn": d.ffn, "vocab": V, "accept": [kind, q], "temperature": args.temperature},
+                   "ffn": d.ffn, "vocab": V, "accept": [kind, q], "temperature": args.temperature,
+                   "adaptive": adaptive},
         "accepted_tok_s": round(accepted / elapsed, 1),
         "committed_tok_s": round(committed / elapsed, 1),
         "mean_accept": round(accepted / (args.steps * B), 4),
-        "planted_accept_matches": accepted == planted,
+        "planted_accept_matches": (accepted == planted) if not adaptive else None,
+        "adaptive": adapt_info,
         "step_roofline": step_roof,
         "roofline": head_roof,
         "cpu_baseline": cpu,

@@ -165,3 +165,32 @@ def test_sampled_calls_reject_bad_arguments_on_the_host():
                                    None) == bd.DFLASH_E_INVALID
     assert L.dflash_verify_sampled(by(d), by(good), FAKE, FAKE, FAKE, FAKE, by(c), FAKE, FAKE, FAKE, ws - 1,
                                    None) == bd.DFLASH_E_WORKSPACE
+
+
+@needs_lib
+def test_block_length_calls_reject_bad_arguments_on_the_host():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation probe runs on CPU-only hosts")
+    L = bd.lib()
+    d = bd.dims_struct(configs.C2.dims)
+    by = ctypes.byref
+    c = _cache()
+    c.block_len = FAKE
+    good = bd.adapt_params()
+    bad = [bd.adapt_params(alpha=0.0), bd.adapt_params(alpha=1.5), bd.adapt_params(cooldown=0),
+           bd.adapt_params(theta_down=float("nan")), bd.adapt_params(theta_up=float("inf"))]
+    for p in bad:
+        assert L.dflash_adapt_block_len(by(d), by(p), FAKE, by(c), FAKE, FAKE, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_adapt_block_len(by(d), None, FAKE, by(c), FAKE, FAKE, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_adapt_block_len(by(d), by(good), None, by(c), FAKE, FAKE, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_adapt_block_len(by(d), by(good), FAKE, by(c), None, FAKE, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_adapt_block_len(by(d), by(good), FAKE, by(c), FAKE, FAKE + 2, None) == bd.DFLASH_E_INVALID
+    c0 = _cache()                                   # the controller needs block_len
+    assert L.dflash_adapt_block_len(by(d), by(good), FAKE, by(c0), FAKE, FAKE, None) == bd.DFLASH_E_INVALID
+    # a misaligned block_len is rejected by every call that reads it
+    c2 = _cache()
+    c2.block_len = FAKE + 1
+    ws = bd.dflash_workspace_bytes(configs.C2.dims)
+    assert L.dflash_draft_step(by(d), by(_weights()), by(c2), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
+    assert L.dflash_verify_commit(by(d), FAKE, FAKE, by(c2), FAKE, FAKE, None) == bd.DFLASH_E_INVALID
