@@ -65,8 +65,8 @@ def step_cost(d: Dims, mean_ctx: float, sampled: bool = False) -> StepCost:
 # the kernel sources it was taken with; `measured_head_traffic` returns None otherwise.
 HEAD_TRAFFIC = {
     "qwen3_8b_b1_k16_ctx4096": {
-        "source_sha256": "820b6f7f994ab6777710a3e6b12e8ae1dd37ebd154ba4bf8538c86b7529affde",
-        "bytes": 1256618707,
+        "source_sha256": "857923487aa596824cf85fe2dd53cb64f72bfd123efee158e8ce744c6c5bb261",
+        "bytes": 1256430472,
     },
 }
 # every source of the weight-streaming GEMM's translation unit (besides HIP's own)
