@@ -180,3 +180,30 @@ def test_draft_is_deterministic_and_logits_optional():
     assert torch.equal(outs[0][1], outs[1][1])          # bitwise reproducible
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][0], outs[2][0])
     assert cache["ctx_len"].cpu().tolist() == [40, 33]
+
+
+def _large_vocab_dims(batch, block_k):
+    """bf16, hidden 1024 (32 K steps) and a 65 600-token vocabulary (1025 column tiles,
+    the last ragged): the 16-row weight-streaming LM head over many more tiles than
+    the GPU has workgroup slots."""
+    return replace(configs.C1.dims, batch=batch, block_k=block_k, hidden=1024, n_q_heads=8, n_kv_heads=2,
+                   head_dim=128, ffn=2048, vocab=65600, tap_dim=512, window=32, cache_slots=32 + block_k,
+                   dtype=BF16, max_inject_rows=max(16, block_k + 1))
+
+
+def test_large_vocab_lm_head_bf16():
+    d = _large_vocab_dims(1, 16)
+    say(f"[test] large-vocabulary LM head {d}")
+    _assert_ok(_run(d, [40], [32], [[16], [5], [0], [9]]))
+
+
+def test_large_vocab_lm_head_partial_rows_and_block_lengths():
+    """9 of 16 rows, per-sequence block lengths (drafts past a block read -1)."""
+    d = _large_vocab_dims(3, 3)
+    say(f"[test] large-vocabulary LM head, 9 rows {d}")
+    W = synth.make_weights(d, seed=2, device="cuda")
+    run = ParityRun(d, W, [20, 33, 7], synth.make_anchors(d, seed=2), [20, 32, 7], seed=2)
+    reps = [run.step([3, 1, 0], block_len=[3, 2, 0]), run.step([2, 3, 1], block_len=[1, 3, 3]),
+            run.step([0, 2, 3])]
+    assert run.dev_error() == 0
+    _assert_ok(reps)

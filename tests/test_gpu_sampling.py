@@ -169,3 +169,12 @@ def test_verify_sampled_full_vocabulary(V, B, k):
     compared at the 1e-3 gate; the shapes take 8192-, 4096- and 2048-entry chunks
     (the last is the batch-1, block-16 launch of the Qwen3-8B-shaped workload)."""
     _verify_rounds(V, B, k, 1.0, 0.3, seed=11, rounds=1)
+
+
+def test_sampled_rounds_large_vocab_lm_head():
+    """The 16-row LM head over 1025 column tiles (bf16, hidden 1024) with the sampled
+    epilogue: draws, logits and log-sum-exps across many tiles and a ragged tail."""
+    d = replace(configs.C1.dims, batch=1, block_k=16, hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                ffn=2048, vocab=65600, tap_dim=512, window=32, cache_slots=48, dtype=BF16, max_inject_rows=17)
+    say(f"[test] sampled large-vocabulary head {d}")
+    _sampled_run(d, [40], [32], [[16], [4], [9]], [1.0, 0.8, 1.5], soft=0.2)
