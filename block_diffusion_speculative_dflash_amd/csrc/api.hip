@@ -100,13 +100,18 @@ AttnPlan attn_plan(const dflash_dims& d) {
   const int nw = std::min(4, row_tiles);
   p.n_rb = cdiv(row_tiles, nw);
   p.rows = 16 * nw;
-  // Split keys only while the workgroups alone leave CUs idle (about four per CU),
-  // keeping >= 128 keys per split; splits need a merge.
+  // Split keys only for long key lists over few workgroups: a split costs a merge
+  // kernel (a fixed few microseconds) plus writing and reading fp32 partials, which
+  // measured slower than one workgroup walking up to ~1000 keys, or than leaving the
+  // keys whole once there are >= 256 workgroups.  When splitting, fill about 256
+  // workgroups with >= 256 keys each.
   const int max_keys = d.sink + d.window + d.block_k;
   const long long base = static_cast<long long>(d.batch) * d.n_kv_heads * p.n_rb;
-  const int want = static_cast<int>(std::max(1ll, (1024 + base - 1) / base));
-  const int kps = std::max(128, round_up(cdiv(max_keys, want), 32));
-  p.kps = std::min(kps, round_up(max_keys, 32));
+  p.kps = round_up(max_keys, 32);
+  if (max_keys > 1024 && base < 256) {
+    const int want = static_cast<int>((256 + base - 1) / base);
+    p.kps = std::min(p.kps, std::max(256, round_up(cdiv(max_keys, want), 32)));
+  }
   p.max_splits = cdiv(max_keys, p.kps);
   return p;
 }

@@ -109,6 +109,33 @@ def test_attention_sink_gqa_bf16():
     _assert_ok(_run(d, [40, 17, 2], [40, 17, 2], [[4, 0, 2], [1, 4, 3], [2, 2, 4], [0, 1, 1], [3, 3, 0]]))
 
 
+def test_key_splits_fp32_sink_ragged():
+    """Key lists past 1024 over few workgroups are split (>= 256 keys per split) and
+    the fp32 partials merged: a ring wrapped behind a 4-position sink (6 splits), a
+    shorter context (3 splits) and one that fits a single split, in one launch."""
+    d = replace(configs.C1.dims, batch=3, sink=4, window=1500, cache_slots=4 + 1500 + 8 + 5,
+                max_inject_rows=256)
+    say(f"[test] key splits fp32 {d}")
+    ctx = [1700, 700, 90]
+    _assert_ok(_run(d, ctx, ctx, [[8, 3, 0], [2, 8, 5], [5, 0, 8]]))
+
+
+def test_key_splits_gqa_bf16_head_dim_128_block_lengths():
+    """64 query rows per kv head (GQA 4/1, block 16, head size 128: the batch-1
+    Qwen3-8B attention shape) over 2016 keys in 256-key splits, with per-sequence
+    block lengths masking block keys inside the last split."""
+    d = replace(configs.C1.dims, batch=2, block_k=16, n_q_heads=4, n_kv_heads=1, head_dim=128, hidden=512,
+                tap_dim=128, ffn=1000, vocab=2000, window=2000, cache_slots=2000 + 16 + 8, dtype=BF16,
+                max_inject_rows=512)
+    say(f"[test] key splits gqa bf16 {d}")
+    ctx = [2100, 1100]
+    W = synth.make_weights(d, seed=2, device="cuda")
+    run = ParityRun(d, W, ctx, synth.make_anchors(d, seed=2), [min(c, d.window) for c in ctx], seed=2)
+    reps = [run.step([16, 4]), run.step([3, 5], block_len=[16, 7]), run.step([0, 2], block_len=[5, 16])]
+    assert run.dev_error() == 0
+    _assert_ok(reps)
+
+
 def test_block_of_one_and_empty_context():
     d = replace(configs.C1.dims, batch=2, block_k=1, window=32, cache_slots=33, max_inject_rows=8)
     say(f"[test] k=1, empty context {d}")
