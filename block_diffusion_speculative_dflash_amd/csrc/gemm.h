@@ -42,8 +42,12 @@ struct GemmArgs {
   const void* W;
   int N, n_tiles, m_tiles;
   int layer_tiles, inj_tile0, inj_tiles;  // INJECT: K/V head tiles inside per-layer QKV regions
-  // split-K
+  // split-K: split z of a tile covers steps [z * steps_per_split, ..).  Balanced
+  // pieces (streaming GEMM, piece_base > 0): grid x enumerates (tile, piece) pairs,
+  // tiles 0 .. piece_extra-1 having piece_base + 1 pieces and the rest piece_base;
+  // piece p of P covers steps [p*S/P, (p+1)*S/P), and splits is the largest P.
   int splits, steps_per_split;
+  int piece_base, piece_extra;
   float* partials;     // [splits, M, n_tiles * kBN] fp32
   unsigned* counters;  // zero-initialised; one per (m tile, n tile), or per m tile (ARGMAX)
   // RMSNorm of the A rows, folded into the epilogue as a per-row factor
@@ -86,6 +90,7 @@ struct GemmPlan {
   int tiled;    // 0: weight-streaming GEMM, 1: tiled MFMA GEMM
   int mt;       // streaming: 16-row MFMA blocks per workgroup (1, 2 or 4); tiled: kTile128 / kTile256
   int m_tiles, n_tiles, splits, steps_per_split, depth;
+  int piece_base, piece_extra;  // streaming: balanced K pieces (0: uniform splits)
 };
 
 constexpr int kTile128 = 128;  // tiled GEMM: 128 x 128 tiles, 4 wavefronts, two workgroups per CU

@@ -103,8 +103,31 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
-  const int tile_n = blockIdx.x, tile_m = blockIdx.y, split = blockIdx.z;
+  const int tile_m = blockIdx.y;
   const int m0 = tile_m * BM;
+  // this workgroup's output tile, its piece of the tile's K steps, and the tile's
+  // piece count (all uniform per workgroup)
+  int tile_n, split, n_split, s_lo, s_hi;
+  if (g.piece_base > 0) {
+    const int w = blockIdx.x, wide = g.piece_base + 1, n_wide = g.piece_extra * wide;
+    if (w < n_wide) {
+      tile_n = w / wide;
+      split = w % wide;
+      n_split = wide;
+    } else {
+      tile_n = g.piece_extra + (w - n_wide) / g.piece_base;
+      split = (w - n_wide) % g.piece_base;
+      n_split = g.piece_base;
+    }
+    s_lo = split * g.S / n_split;
+    s_hi = (split + 1) * g.S / n_split;
+  } else {
+    tile_n = blockIdx.x;
+    split = blockIdx.z;
+    n_split = g.splits;
+    s_lo = split * g.steps_per_split;
+    s_hi = min(g.S, s_lo + g.steps_per_split);
+  }
 
   size_t wtile = tile_n;
   if constexpr (EPI == EPI_INJECT) {
@@ -112,8 +135,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     wtile = static_cast<size_t>(l) * g.layer_tiles + g.inj_tile0 + tile_n % g.inj_tiles;
   }
   const E* Wt = static_cast<const E*>(g.W) + wtile * g.S * kTileStepElems + lane * 8;
-  const int s_lo = split * g.steps_per_split;
-  const int s_hi = min(g.S, s_lo + g.steps_per_split);
   const int n_w = (s_hi - s_lo + 3) >> 2;  // steps per wavefront, rounded up
   const int NI = (n_w + D - 1) / D * D;
 
@@ -232,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  if (g.splits > 1) {
+  if (n_split > 1) {
     const size_t np = static_cast<size_t>(g.n_tiles) * kBN;
     for (int idx = tid; idx < BM * kBN; idx += kThreads) {
       const int r = idx / kBN, c = idx % kBN, m = m0 + r;
@@ -240,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         coherent_store(&g.partials[(static_cast<size_t>(split) * g.M + m) * np + tile_n * kBN + c], tile[r][c]);
     }
     unsigned* counter = &g.counters[tile_m * g.n_tiles + tile_n];
-    if (!arrive_last(counter, g.splits, &last_s)) return;
+    if (!arrive_last(counter, n_split, &last_s)) return;
     // every partial of this thread's elements is requested before any is summed
     constexpr int PER = BM * kBN / kThreads;  // elements per thread
     constexpr int kMaxSplits = 16 / MT;  // the plan never splits further
@@ -250,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       const int idx = tid + e * kThreads, r = idx / kBN, c = idx % kBN, m = min(m0 + r, g.M - 1);
 #pragma unroll
       for (int sp = 0; sp < kMaxSplits; ++sp)
-        if (sp < g.splits)
+        if (sp < n_split)
           pv[e][sp] = coherent_load(&g.partials[(static_cast<size_t>(sp) * g.M + m) * np + tile_n * kBN + c]);
     }
 #pragma unroll
@@ -259,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       float s = 0.f;
 #pragma unroll
       for (int sp = 0; sp < kMaxSplits; ++sp)
-        if (sp < g.splits) s += pv[e][sp];
+        if (sp < n_split) s += pv[e][sp];
       tile[r][c] = s;
     }
     if (tid == 0) reset_counter(counter);
@@ -312,9 +333,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
 template <typename TIN, int MT, int EPI>
 static hipError_t launch_t(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
-  const dim3 grid(p.n_tiles, p.m_tiles, p.splits);
+  const dim3 grid = p.piece_base > 0 ? dim3(p.n_tiles * p.piece_base + p.piece_extra, p.m_tiles, 1)
+                                     : dim3(p.n_tiles, p.m_tiles, p.splits);
   constexpr int D = MT == 4 ? 2 : (MT == 1 ? 8 : 4);
   if (p.depth != D) return hipErrorInvalidValue;
+  if (p.piece_base > 0 && (p.piece_extra >= p.n_tiles || p.splits != p.piece_base + (p.piece_extra > 0) ||
+                           p.splits > 16 / MT || a.piece_base != p.piece_base || a.piece_extra != p.piece_extra))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_kernel<TIN, MT, EPI, D>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -65,8 +65,8 @@ def step_cost(d: Dims, mean_ctx: float, sampled: bool = False) -> StepCost:
 # the kernel sources it was taken with; `measured_head_traffic` returns None otherwise.
 HEAD_TRAFFIC = {
     "qwen3_8b_b1_k16_ctx4096": {
-        "source_sha256": "857923487aa596824cf85fe2dd53cb64f72bfd123efee158e8ce744c6c5bb261",
-        "bytes": 1256430472,
+        "source_sha256": "98061cc8f0100db7e03779b20ce619347e01f8eef1362d06779e21b0dd7d92cb",
+        "bytes": 1256480020,
     },
 }
 # every source of the weight-streaming GEMM's translation unit (besides HIP's own)

@@ -136,6 +136,17 @@ def test_key_splits_gqa_bf16_head_dim_128_block_lengths():
     _assert_ok(reps)
 
 
+def test_balanced_k_pieces_qkv_bf16():
+    """Hidden 4096 with 16/4 heads: the QKV projection (48 column tiles, 128 K steps)
+    would split 8 ways into 384 workgroups, so it takes balanced pieces instead,
+    10 or 11 per tile (512 workgroups, pieces of 11 and 12 K steps)."""
+    d = replace(configs.C1.dims, batch=1, block_k=16, n_layers=1, hidden=4096, n_q_heads=16, n_kv_heads=4,
+                head_dim=128, ffn=1024, vocab=3000, tap_dim=512, window=64, cache_slots=64 + 16 + 8, dtype=BF16,
+                max_inject_rows=17)
+    say(f"[test] balanced K pieces {d}")
+    _assert_ok(_run(d, [70], [64], [[16], [5], [0]], seed=4))
+
+
 def test_block_of_one_and_empty_context():
     d = replace(configs.C1.dims, batch=2, block_k=1, window=32, cache_slots=33, max_inject_rows=8)
     say(f"[test] k=1, empty context {d}")
