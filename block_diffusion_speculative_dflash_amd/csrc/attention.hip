@@ -7,11 +7,11 @@
 //
 // Workgroup = (sequence b, kv head g, row block, key split).  The rows of kv head g
 // are its G = Hq/Hkv query heads times the k block rows; a row block is up to four
-// tiles of 16 of them, one per wavefront.  The workgroup streams its keys in chunks
-// of 32: every chunk's K and V rows are loaded from HBM once, cooperatively, into
-// registers and from there into a double-buffered LDS stage (up to three later chunks'
-// loads are in flight while one is used), and every wavefront reads its operands from
-// there.
+// tiles of 16 of them.  The workgroup's wavefronts are row tile x key group: it
+// streams its keys in rounds of two 32-key chunks, every chunk's K and V rows loaded
+// from HBM once, cooperatively, into LDS (the next round's loads in flight in
+// registers meanwhile); key group g computes on chunk g of each round, and the two
+// groups' (max, sum, O) states of a row tile merge in LDS at the end.
 //
 // Everything is computed transposed so that one query row lives in one lane:
 //   S^T = K Q^T     A = 16 keys x 32 head dims (straight from the key rows),
@@ -40,13 +40,6 @@ constexpr int kKC = 32;    // keys per chunk (one MFMA reduction step of P V)
 template <typename T> struct VPad;
 template <> struct VPad<f16> { static constexpr int value = 16; };   // 288-byte rows: 8 rows on disjoint banks
 template <> struct VPad<float> { static constexpr int value = 4; };  // 16-byte rows
-
-// lgkmcnt(0) only (gfx9 s_waitcnt encoding, vmcnt and expcnt left at their maxima):
-// this wavefront's LDS writes are complete before its other lanes read them.
-__device__ __forceinline__ void lds_written() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_wave_barrier();
-}
 
 // Reductions over the four lanes l, l^16, l^32, l^48 that hold one query row, with
 // the gfx950 lane-swap instructions (VALU, no LDS round trip).  Called with the same
