@@ -151,7 +151,7 @@ Layout layout(const dflash_dims& d) {
   L.ssq_c = take(Mi * L.np_d * 4);
   L.partials = take(partial_bytes(d));
   L.counters = take(size_t(kGemmCounters) * 4);
-  L.keys = take(Mb * 8 * kKeyStride);
+  L.keys = take(Mb * size_t(cdiv(d.vocab, kBN)) * 8);  // LM head: best key per row and column tile
   const size_t groups = size_t(d.batch) * d.n_kv_heads * L.ap.n_rb;
   L.attn_cnt = take(groups * 4);
   L.attn_o = take(groups * L.ap.max_splits * 64 * d.head_dim * 4);
@@ -503,19 +503,29 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   a.block_len = cache->block_len;
   a.rows_per_seq = d.block_k;
   const int epi = smp != nullptr ? EPI_SAMPLE : EPI_ARGMAX;
+  // one key (and with sampling one (max, sum) pair) per row and column tile
+  const GemmPlan hp = gemm_plan(d, epi, a.M, a.n_tiles, a.S, false, partial_bytes(d));
+  a.n_parts = hp.tiled ? cdiv(a.n_tiles, hp.mt / kBN) : a.n_tiles;
   if (smp != nullptr) {
-    const GemmPlan hp = gemm_plan(d, EPI_SAMPLE, a.M, a.n_tiles, a.S, false, partial_bytes(d));
     a.inv_temp = 1.f / smp->temperature;
     a.seed = smp->seed;
     a.step = smp->step;
     a.step_dev = reinterpret_cast<const unsigned long long*>(smp->step_dev);
     a.lse_part = c.at<float2>(L.lse_part);
-    a.n_parts = hp.tiled ? cdiv(a.n_tiles, hp.mt / kBN) : a.n_tiles;
   }
   if (ev0) DF_CHECK(hipEventRecord(ev0, stream));
   if (int st = run_gemm(epi, c, a, false, stream)) return st;
   if (ev1) DF_CHECK(hipEventRecord(ev1, stream));
-  if (smp != nullptr) DF_CHECK(launch_lse_merge(a.lse_part, a.n_parts, a.M, lse_out, stream));
+  HeadFinalizeArgs f;
+  f.keys = a.keys;
+  f.part = smp != nullptr ? a.lse_part : nullptr;
+  f.n_parts = a.n_parts;
+  f.rows = a.M;
+  f.rows_per_seq = d.block_k;
+  f.draft = draft;
+  f.lse = smp != nullptr ? lse_out : nullptr;
+  f.block_len = cache->block_len;
+  DF_CHECK(launch_head_finalize(f, stream));
   return DFLASH_OK;
 }
 

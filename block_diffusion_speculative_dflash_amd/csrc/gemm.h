@@ -72,7 +72,7 @@ struct GemmArgs {
   float theta;
   void* cache_k;  // [L, B, Hkv, C, dh]
   void* cache_v;
-  unsigned long long* keys;  // [M * kKeyStride] zero-initialised argmax keys (ARGMAX)
+  unsigned long long* keys;  // ARGMAX / SAMPLE: [M, n_parts] best key of each column tile
   int32_t* draft;            // [M]
   const int32_t* block_len;  // ARGMAX / SAMPLE: [B] or nullptr; rows i >= block_len[b] draft -1
   float* logits;             // [M, N] or nullptr

@@ -83,7 +83,7 @@ __device__ __forceinline__ void sample_tile(const GemmArgs& g, const float (*til
       for (int rr = 0; rr < 4; ++rr) {
         const int m = m0 + 4 * rg + rr;
         if (m < g.M) {
-          if (key[rr] != 0ull) atomicMax(&g.keys[static_cast<size_t>(m) * kKeyStride], key[rr]);
+          g.keys[static_cast<size_t>(m) * g.n_parts + tile_n] = key[rr];
           g.lse_part[static_cast<size_t>(m) * g.n_parts + tile_n] = make_float2(mx[rr], sm[rr]);
         }
       }
@@ -315,19 +315,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         if (g.logits != nullptr) g.logits[static_cast<size_t>(m) * g.N + n] = v;
       }
       wave_argmax(v, idx);
-      if (lane == 0) atomicMax(&g.keys[static_cast<size_t>(m) * kKeyStride], argmax_key(v, idx));
+      if (lane == 0) g.keys[static_cast<size_t>(m) * g.n_parts + tile_n] = argmax_key(v, idx);
     }
-    if (!arrive_last(&g.counters[tile_m], g.n_tiles, &last_s)) return;
-    for (int r = tid; r < BM; r += kThreads) {
-      const int m = m0 + r;
-      if (m >= g.M) continue;
-      const unsigned long long key =
-          __hip_atomic_exchange(&g.keys[static_cast<size_t>(m) * kKeyStride], 0ull, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-      const bool in_block = g.block_len == nullptr || m % g.rows_per_seq < g.block_len[m / g.rows_per_seq];
-      g.draft[m] = in_block ? argmax_key_index(key) : -1;
-    }
-    if (tid == 0) reset_counter(&g.counters[tile_m]);
+    // the row's draft is the largest tile key: launch_head_finalize, after this kernel
   }
 }
 

@@ -386,7 +386,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) {
     __syncthreads();
     for (int r = tid; r < BM; r += NT)
-      if (m0 + r < g.M) atomicMax(&g.keys[static_cast<size_t>(m0 + r) * kKeyStride], best_s[r]);
+      if (m0 + r < g.M) g.keys[static_cast<size_t>(m0 + r) * g.n_parts + tn] = best_s[r];
     if constexpr (EPI == EPI_SAMPLE) {
       const float2* lse_s = reinterpret_cast<const float2*>(smem);
       for (int r = tid; r < BM; r += NT) {
@@ -397,18 +397,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
         g.lse_part[static_cast<size_t>(m0 + r) * g.n_parts + tn] = make_float2(mx, sm);
       }
     }
-    unsigned* counter = &g.counters[tm];
-    if (!arrive_last(counter, n_big, &last_s)) return;
-    for (int r = tid; r < BM; r += NT) {
-      const int m = m0 + r;
-      if (m >= g.M) continue;
-      const unsigned long long key =
-          __hip_atomic_exchange(&g.keys[static_cast<size_t>(m) * kKeyStride], 0ull, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-      const bool in_block = g.block_len == nullptr || m % g.rows_per_seq < g.block_len[m / g.rows_per_seq];
-      g.draft[m] = in_block ? argmax_key_index(key) : -1;
-    }
-    if (tid == 0) reset_counter(counter);
+    // the row's draft is the largest tile key: launch_head_finalize, after this kernel
   }
 }
 

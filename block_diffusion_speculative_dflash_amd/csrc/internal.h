@@ -86,8 +86,18 @@ struct AdaptArgs {
 };
 hipError_t launch_adapt(const AdaptArgs& a, hipStream_t stream);
 
-// Log-sum-exp of each row from its per-tile (max, sum) partials.
-hipError_t launch_lse_merge(const float2* part, int n_parts, int rows, float* lse, hipStream_t stream);
+// LM-head finalisation: per row the largest of the column tiles' argmax keys -> draft
+// (-1 past the block length), and with part != nullptr the log-sum-exp of the tiles'
+// (max, sum) partials -> lse.
+struct HeadFinalizeArgs {
+  const unsigned long long* keys;  // [rows, n_parts]
+  const float2* part;              // [rows, n_parts] or nullptr
+  int n_parts, rows, rows_per_seq;
+  int32_t* draft;                  // [rows]
+  float* lse;                      // [rows], with part
+  const int32_t* block_len;        // [rows / rows_per_seq] or nullptr
+};
+hipError_t launch_head_finalize(const HeadFinalizeArgs& a, hipStream_t stream);
 
 // Sampled verification: per-row log-sum-exp of the target logits and the
 // acceptance scan (first kernel), then the residual / bonus draw and the commit.

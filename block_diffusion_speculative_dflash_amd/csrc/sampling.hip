@@ -26,41 +26,70 @@
 
 namespace dflash {
 
-// log-sum-exp of one row from its per-tile partials: one workgroup per row
-__global__ __launch_bounds__(kThreads) void lse_merge_kernel(const float2* part, int n_parts, float* lse) {
+// LM-head finalisation, one workgroup per draft row: the draft is the largest of the
+// column tiles' best keys (order-preserving value bits over the inverted index, so a
+// tie goes to the lower index; -1 past the sequence's block length), and, when the
+// tiles left (max, sum) pairs (sampling), the row's log-sum-exp merged in a fixed
+// order.  The tiles store their keys with plain stores: no same-address atomics and no
+// arrival counter in the LM head itself.
+__global__ __launch_bounds__(kThreads) void head_finalize_kernel(HeadFinalizeArgs a) {
   __shared__ float red_m[kThreads / kWave], red_s[kThreads / kWave];
+  __shared__ unsigned long long red_k[kThreads / kWave];
   const int tid = threadIdx.x, row = blockIdx.x;
-  const float2* p = part + static_cast<size_t>(row) * n_parts;
-  float m = -INFINITY, s = 0.f;
+  const int n_parts = a.n_parts;
+  const unsigned long long* kp = a.keys + static_cast<size_t>(row) * n_parts;
+  unsigned long long best = 0ull;
   for (int t0 = tid; t0 < n_parts; t0 += 4 * kThreads) {
-    float2 v[4];
+    unsigned long long v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = t0 + u * kThreads;
-      v[u] = t < n_parts ? p[t] : make_float2(-INFINITY, 0.f);
+      v[u] = t < n_parts ? kp[t] : 0ull;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) lse_merge(m, s, v[u].x, v[u].y);
+    for (int u = 0; u < 4; ++u) best = v[u] > best ? v[u] : best;
+  }
+  float m = -INFINITY, s = 0.f;
+  if (a.part != nullptr) {
+    const float2* p = a.part + static_cast<size_t>(row) * n_parts;
+    for (int t0 = tid; t0 < n_parts; t0 += 4 * kThreads) {
+      float2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + u * kThreads;
+        v[u] = t < n_parts ? p[t] : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lse_merge(m, s, v[u].x, v[u].y);
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long ok = __shfl_xor(best, o, kWave);
+    best = ok > best ? ok : best;
     const float om = __shfl_xor(m, o, kWave), os = __shfl_xor(s, o, kWave);
     lse_merge(m, s, om, os);
   }
   if ((tid & 63) == 0) {
+    red_k[tid >> 6] = best;
     red_m[tid >> 6] = m;
     red_s[tid >> 6] = s;
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < kThreads / kWave; ++w) lse_merge(m, s, red_m[w], red_s[w]);
-    lse[row] = m + ln_f32(s);
+    for (int w = 1; w < kThreads / kWave; ++w) {
+      best = red_k[w] > best ? red_k[w] : best;
+      lse_merge(m, s, red_m[w], red_s[w]);
+    }
+    const bool in_block = a.block_len == nullptr || row % a.rows_per_seq < a.block_len[row / a.rows_per_seq];
+    a.draft[row] = in_block ? argmax_key_index(best) : -1;
+    if (a.part != nullptr) a.lse[row] = m + ln_f32(s);
   }
 }
 
-hipError_t launch_lse_merge(const float2* part, int n_parts, int rows, float* lse, hipStream_t stream) {
-  if (rows <= 0 || n_parts <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(rows), dim3(kThreads), 0, stream, part, n_parts, lse);
+hipError_t launch_head_finalize(const HeadFinalizeArgs& a, hipStream_t stream) {
+  if (a.rows <= 0 || a.n_parts <= 0 || (a.part != nullptr) != (a.lse != nullptr)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(head_finalize_kernel, dim3(a.rows), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
