@@ -49,12 +49,18 @@ def step_cost(d: Dims, mean_ctx: float, sampled: bool = False) -> StepCost:
     rows_d, rows_i = B * k, B * (k + 1)
     flops = (2 * rows_d * (L * p_layer + p_head) + 4 * rows_d * L * Hq * dh * (n_ctx + k)
              + 2 * rows_i * (p_fuse + p_inject))
-    head_bytes = p_head * e + rows_d * D * e + rows_d * 4 * ((D + 63) // 64) + rows_d * 4
-    extra = 0
+    # LM head: weights, normalised rows, sum-of-squares partials, and one 8-byte argmax
+    # key per row and 64-column tile (the streaming head's tiling; the tiled head at
+    # >= 128 rows writes 4x or 2x fewer); the finalisation kernel reads the keys back
+    # (the drafts it writes are counted with the tokens)
+    n_col = (V + 63) // 64
+    keys = rows_d * n_col * 8
+    head_bytes = p_head * e + rows_d * D * e + rows_d * 4 * ((D + 63) // 64) + keys
+    extra = keys
     if sampled:
-        logits_out = rows_d * V * 4 + rows_d * ((V + 63) // 64) * 8
+        logits_out = rows_d * V * 4 + rows_d * n_col * 8
         head_bytes += logits_out
-        extra = logits_out + rows_d * ((V + 63) // 64) * 8 + rows_d * 4 + B * (k + 1) * V * 4 + 2 * B * V * 4
+        extra += logits_out + rows_d * n_col * 8 + rows_d * 4 + B * (k + 1) * V * 4 + 2 * B * V * 4
     return StepCost(weights + kv_read + kv_write + taps + tokens + extra, flops, weights, kv_read,
                     kv_write, taps, head_bytes, 2.0 * rows_d * p_head)
 
@@ -65,8 +71,8 @@ def step_cost(d: Dims, mean_ctx: float, sampled: bool = False) -> StepCost:
 # the kernel sources it was taken with; `measured_head_traffic` returns None otherwise.
 HEAD_TRAFFIC = {
     "qwen3_8b_b1_k16_ctx4096": {
-        "source_sha256": "98061cc8f0100db7e03779b20ce619347e01f8eef1362d06779e21b0dd7d92cb",
-        "bytes": 1256480020,
+        "source_sha256": "90c1450c815f5b1beffc351bcfd2882fecdb7b06e2c122b65826e97d73591613",
+        "bytes": 1256493909,
     },
 }
 # every source of the weight-streaming GEMM's translation unit (besides HIP's own)
