@@ -237,39 +237,27 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
   // Cross-wavefront reduction in fixed order 0, 1, 2, 3.  MFMA output layout:
   // lane l, register r holds row 4*(l/16) + r, column l%16 of each 16x16 block.
-  if constexpr (MT <= 2) {
-    // every wavefront stores its partial tile, then all threads sum them in order:
-    // one barrier between, instead of one per wavefront
-    __shared__ float part[4][BM][kBN + 4];
+  {
+    // every wavefront stores its partial tile (wavefront 0's into the output tile
+    // itself), then all threads sum them in order: one barrier between, instead of
+    // one per wavefront
+    __shared__ float xpart[3][BM][kBN + 4];
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part[wave][mi * 16 + 4 * (lane >> 4) + r][ni * 16 + (lane & 15)] = acc[mi][ni][r];
+        for (int r = 0; r < 4; ++r) {
+          const int row = mi * 16 + 4 * (lane >> 4) + r, col = ni * 16 + (lane & 15);
+          (wave == 0 ? tile[row] : xpart[wave - 1][row])[col] = acc[mi][ni][r];
+        }
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < BM * kBN / kThreads; ++e) {
       const int idx = tid + e * kThreads, row = idx / kBN, col = idx % kBN;
-      tile[row][col] = (((0.f + part[0][row][col]) + part[1][row][col]) + part[2][row][col]) + part[3][row][col];
+      tile[row][col] = (((0.f + tile[row][col]) + xpart[0][row][col]) + xpart[1][row][col]) + xpart[2][row][col];
     }
     __syncthreads();
-  } else {
-    for (int w = 0; w < 4; ++w) {
-      if (wave == w) {
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int row = mi * 16 + 4 * (lane >> 4) + r;
-              const int col = ni * 16 + (lane & 15);
-              tile[row][col] = (w == 0 ? 0.f : tile[row][col]) + acc[mi][ni][r];
-            }
-      }
-      __syncthreads();
-    }
   }
 
   if (n_split > 1) {
