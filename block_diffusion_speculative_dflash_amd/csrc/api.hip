@@ -218,16 +218,19 @@ GemmPlan stream_plan(int M, int n_tiles, int S, bool allow_split, size_t partial
 }
 
 // Tile plan of one tiled GEMM: 256 x 256 tiles (one workgroup per CU) or 128 x 128
-// (two per CU), K split 1..8 ways.  Cost model: the grid runs in rounds of one
-// workgroup per CU slot; a round takes the time of one workgroup's multiply at the
-// per-CU MFMA rate, doubled when two workgroups share a CU; split K adds the fp32
-// partial-tile traffic.  partial_cap = 0 disables splitting.
+// (two per CU), K split 1..8 ways.  Cost model with per-CU rates measured on MI355X
+// (batch-64 and batch-256 drafter shapes, every tile shape and split count timed):
+// a 256 x 256 workgroup multiplies at ~4.3 TFLOP/s; 128 x 128 workgroups reach
+// ~3.5 TFLOP/s per CU two at a time but only ~2.0 alone (one wavefront per SIMD).
+// The dispatcher fills CUs as workgroups finish, so the grid runs in rounds of one
+// workgroup per CU slot; a last round of at most one 128 x 128 workgroup per CU
+// runs at the single-workgroup rate.  Split K costs its fp32 partial-tile traffic
+// plus ~20 us for the last arriver's reduction.  partial_cap = 0 disables splitting.
 GemmPlan tiled_plan(int M, int n_tiles, int S, bool allow_split, size_t partial_cap) {
-  const double cu_flops = 1.0e15 / kCUs, hbm = 5.0e12;
+  constexpr double r256 = 4.3e12, r128_pair = 3.5e12, r128_alone = 2.0e12, hbm = 5.0e12, split_fixed = 20e-6;
   GemmPlan best{};
   double best_t = 1e30;
   for (int cfg : {kTile256, kTile128}) {
-    const int slots = cfg == kTile256 ? kCUs : 2 * kCUs;
     const int m_tiles = cdiv(M, cfg), n_big = cdiv(n_tiles, cfg / kBN);
     for (int want = 1; want <= (allow_split ? 8 : 1); ++want) {
       const int sps = cdiv(S, want);
@@ -238,9 +241,18 @@ GemmPlan tiled_plan(int M, int n_tiles, int S, bool allow_split, size_t partial_
         if (double(splits) * M * n_tiles * kBN * 4 > double(partial_cap)) continue;
         if (size_t(m_tiles) * n_big > size_t(kGemmCounters)) continue;
       }
-      const double rounds = cdiv(m_tiles * n_big * splits, slots);
-      const double round_t = 2.0 * cfg * cfg * kKStep * sps / cu_flops * (slots / kCUs);
-      const double t = rounds * round_t + (splits > 1 ? 2.0 * splits * M * n_tiles * kBN * 4 / hbm : 0.0);
+      const long long n = static_cast<long long>(m_tiles) * n_big * splits;
+      const double work = 2.0 * cfg * cfg * kKStep * sps;  // flops of one workgroup
+      double t;
+      if (cfg == kTile256) {
+        t = static_cast<double>((n + kCUs - 1) / kCUs) * work / r256;
+      } else {
+        const long long full = n / (2 * kCUs), rem = n - full * 2 * kCUs;
+        t = static_cast<double>(full) * work / (r128_pair / 2);
+        if (rem > kCUs) t += work / (r128_pair / 2);
+        else if (rem > 0) t += work / r128_alone;
+      }
+      if (splits > 1) t += 2.0 * splits * M * n_tiles * kBN * 4 / hbm + split_fixed;
       if (t < best_t * 0.999) {
         best_t = t;
         best.tiled = 1;
@@ -272,9 +284,13 @@ size_t partial_bytes(const dflash_dims& d) {
   const int qkv_tiles = (d.n_q_heads + 2 * d.n_kv_heads) * tph;
   const int D = d.hidden, Sd = ksteps(D);
   struct G { int M, n_tiles, S; };
+  // injection row counts: the verify round's k + 1 per sequence and the largest call
   const int Mb = d.batch * d.block_k, Mi = d.batch * d.max_inject_rows;
+  const int Mv = d.batch * std::min(d.block_k + 1, d.max_inject_rows);
   const G gs[] = {{Mi, cdiv(D, kBN), ksteps(d.n_taps * d.tap_dim)},
                   {Mi, d.n_layers * 2 * d.n_kv_heads * tph, Sd},
+                  {Mv, cdiv(D, kBN), ksteps(d.n_taps * d.tap_dim)},
+                  {Mv, d.n_layers * 2 * d.n_kv_heads * tph, Sd},
                   {Mb, qkv_tiles, Sd},
                   {Mb, cdiv(D, kBN), ksteps(d.n_q_heads * d.head_dim)},
                   {Mb, cdiv(d.ffn, kBN / 2), Sd},
