@@ -75,6 +75,28 @@ constexpr float kLazy = 8.f;  // largest allowed growth of a row maximum before 
 // key group kg computes on chunk kg, so KG independent online-softmax streams share
 // every SIMD.  At the end the KG partial states (max, sum, O) of each row tile merge
 // in LDS, pairwise in a fixed tree order.
+// Ragged contexts: the workgroups of one kv head are dispatched to one XCD in slot order
+// and spread over its CUs breadth first, so a CU holds slots c and c + B/2.  Slot i of
+// the first half takes the sequence of rank i by context length (longest first, ties by
+// index), slot i of the second half rank 3B/2 - 1 - i: each CU pairs a long context with
+// a short one.  A permutation of the sequences, so results do not depend on it.
+__device__ int balanced_sequence(const AttnArgs& a, int slot) {
+  __shared__ int seq_s;
+  const int B = a.batch, half = (B + 1) / 2;
+  const int want = slot < half ? slot : (B - 1) - (slot - half);
+  for (int t = threadIdx.x; t < B; t += blockDim.x) {
+    const int lt = a.ctx_len[t];
+    int rank = 0;
+    for (int s = 0; s < B; ++s) {
+      const int ls = a.ctx_len[s];
+      rank += (ls > lt || (ls == lt && s < t)) ? 1 : 0;
+    }
+    if (rank == want) seq_s = t;
+  }
+  __syncthreads();
+  return seq_s;
+}
+
 template <typename T, int DH, int NW, int KG>
 __global__ __launch_bounds__(64 * NW * KG) void attention_kernel(AttnArgs a) {
   constexpr int KS = DH / 32;  // MFMA reduction steps over the head dimension (S^T)
@@ -99,7 +121,8 @@ __global__ __launch_bounds__(64 * NW * KG) void attention_kernel(AttnArgs a) {
   item /= a.max_splits;
   const int rb = item % a.n_rb;
   item /= a.n_rb;
-  const int g = item % a.n_kv_heads, b = item / a.n_kv_heads;
+  const int g = item % a.n_kv_heads;
+  const int b = a.balance ? balanced_sequence(a, item / a.n_kv_heads) : item / a.n_kv_heads;
   const int k = a.block_k, G = a.n_q_heads / a.n_kv_heads;
   const int rr0 = rt * 16;                   // this wavefront's rows within the row block
   const int r0 = rb * a.rows_per_block;      // first row of the row block

@@ -80,6 +80,34 @@ def test_head_dim_128_bf16():
     _assert_ok(_run(d, [70, 64], [64, 64], [[8, 1], [2, 7], [4, 4]]))
 
 
+def test_two_row_tiles_streaming():
+    """Just over one 64-row streaming tile: 8 x 9 injected rows (fusion and injection
+    over two row tiles, the second nearly empty) with 64 block rows, then 80 block rows
+    (every draft projection and the LM head over two row tiles) with 90 injected rows;
+    bf16 GQA and fp32."""
+    for B, dtype in ((8, BF16), (10, BF16), (9, F32)):
+        d = replace(configs.C1.dims, batch=B, block_k=8, n_layers=2, n_q_heads=4, n_kv_heads=2,
+                    window=32, cache_slots=40, dtype=dtype)
+        say(f"[test] two row tiles, streaming {d}")
+        ctx = [40 + (5 * b) % 19 for b in range(B)]
+        pre = [min(c, d.window) for c in ctx]
+        steps = [[(2 * b + s) % 9 for b in range(B)] for s in range(2)]
+        _assert_ok(_run(d, ctx, pre, steps))
+
+
+def test_ragged_long_windows_balanced_attention():
+    """64 sequences with ragged full-attention contexts of 200..1100 keys over a window
+    above 1024, keys unsplit: the attention places sequences by context-length rank
+    (a permutation), fp32 and bf16."""
+    for dtype in (F32, BF16):
+        d = replace(configs.C1.dims, batch=64, block_k=4, n_layers=1, window=1100, cache_slots=1104,
+                    dtype=dtype)
+        say(f"[test] balanced attention {d}")
+        ctx = [200 + (37 * b) % 901 for b in range(d.batch)]
+        steps = [[(b + s) % 5 for b in range(d.batch)] for s in range(2)]
+        _assert_ok(_run(d, ctx, ctx, steps))
+
+
 def test_tiled_gemm_path_bf16():
     """Batch x block >= 128 rows takes the tiled MFMA GEMM for every projection: row
     tails (160 draft rows, 180 and 320 injected rows), ragged SwiGLU width and

@@ -122,9 +122,9 @@ def test_sampled_rounds_tiny_fp32():
 
 
 def test_sampled_rounds_bf16_streaming_row_blocks():
-    """bf16 with 8, 24 and 40 block rows: the LM head streams with 16-, 32- and
-    64-row blocks."""
-    for B in (1, 3, 5):
+    """bf16 with 8, 24, 40 and 80 block rows: the LM head streams with 16-, 32- and
+    64-row blocks (80 rows: two 64-row tiles)."""
+    for B in (1, 3, 5, 10):
         d = replace(configs.C1.dims, batch=B, dtype=BF16, window=32, cache_slots=40)
         say(f"[test] sampled bf16 streaming B={B}")
         ctx = [60 + 11 * b for b in range(B)]
