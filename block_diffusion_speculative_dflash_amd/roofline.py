@@ -71,8 +71,8 @@ def step_cost(d: Dims, mean_ctx: float, sampled: bool = False) -> StepCost:
 # the kernel sources it was taken with; `measured_head_traffic` returns None otherwise.
 HEAD_TRAFFIC = {
     "qwen3_8b_b1_k16_ctx4096": {
-        "source_sha256": "90c1450c815f5b1beffc351bcfd2882fecdb7b06e2c122b65826e97d73591613",
-        "bytes": 1256493909,
+        "source_sha256": "fa926957bee60069be18fe225739fffbff67f1c08bf5f45538ecee180799a7d6",
+        "bytes": 1256440233,
     },
 }
 # every source of the weight-streaming GEMM's translation unit (besides HIP's own)
