@@ -108,6 +108,64 @@ def test_ragged_long_windows_balanced_attention():
         _assert_ok(_run(d, ctx, ctx, steps))
 
 
+def test_round_touches_only_tentative_ring_slots():
+    """Cache traffic of one round, bitwise: the draft step writes no K/V byte; the
+    injection of n rows at committed length P writes exactly the ring slots of
+    positions P .. P+n-1 (sink slots fixed, ring wrap) in every layer and kv head and
+    leaves every other byte alone; the verify moves ctx_len by a+1 and the anchor to
+    the bonus token without touching K/V (rollback = the committed pointer)."""
+    for dtype, sink in ((BF16, 0), (F32, 2)):
+        d = replace(configs.C1.dims, batch=5, block_k=6, n_layers=2, n_q_heads=4, n_kv_heads=2,
+                    window=24, cache_slots=24 + 6 + sink, sink=sink, dtype=dtype)
+        say(f"[test] ring slots of one round {d}")
+        W = bd.pack_weights(d, synth.make_weights(d, seed=3, device="cuda"))
+        B, k, C = d.batch, d.block_k, d.cache_slots
+        ctx = np.array([0, 5, 23, 40, 77], dtype=np.int32)  # empty, short, full window, wrapped
+        cache = bd.alloc_cache(d, device="cuda", ctx_len=ctx, anchor=synth.make_anchors(d, seed=3))
+        g = torch.Generator(device="cuda").manual_seed(11)
+        cache["k"].copy_(torch.randn(cache["k"].shape, generator=g, device="cuda").to(cache["k"].dtype))
+        cache["v"].copy_(torch.randn(cache["v"].shape, generator=g, device="cuda").to(cache["v"].dtype))
+        ws = bd.alloc_workspace(d, device="cuda")
+        k0, v0 = cache["k"].clone(), cache["v"].clone()
+
+        draft = torch.zeros((B, k), dtype=torch.int32, device="cuda")
+        bd.dflash_draft_step(d, W, cache, draft, None, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(cache["k"], k0) and torch.equal(cache["v"], v0)
+
+        n = np.array([k + 1, 1, k + 1, 3, k + 1], dtype=np.int32)  # rows injected per sequence
+        taps = synth.make_taps(d, k + 1, seed=3, stream=7, device="cuda")
+        bd.dflash_fuse_inject(d, W, taps, torch.as_tensor(n, device="cuda"), k + 1, False, cache, ws)
+        torch.cuda.synchronize()
+        written = np.zeros((B, C), dtype=bool)
+        for b in range(B):
+            for p in range(int(ctx[b]), int(ctx[b]) + int(n[b])):
+                written[b, orc.slot_of(d, p)] = True
+        changed_k = (cache["k"] != k0).any(dim=-1).cpu().numpy()  # [L, B, Hkv, C]
+        changed_v = (cache["v"] != v0).any(dim=-1).cpu().numpy()
+        for ch in (changed_k, changed_v):
+            assert np.array_equal(ch, np.broadcast_to(written[None, :, None, :], ch.shape))
+        np.testing.assert_array_equal(cache["ctx_len"].cpu().numpy(), ctx)  # commit = 0
+
+        target = torch.as_tensor(np.concatenate([draft.cpu().numpy(), np.zeros((B, 1), np.int32)], 1) + 0,
+                                 device="cuda")
+        a_plant = [0, 2, k, 4, 1]
+        for b, a in enumerate(a_plant):
+            if a < k:
+                target[b, a] = (draft[b, a] + 1) % d.vocab
+        k1, v1 = cache["k"].clone(), cache["v"].clone()
+        acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+        out = torch.zeros((B, k + 1), dtype=torch.int32, device="cuda")
+        bd.dflash_verify_commit(d, draft, target, cache, acc, out)
+        torch.cuda.synchronize()
+        assert torch.equal(cache["k"], k1) and torch.equal(cache["v"], v1)
+        np.testing.assert_array_equal(acc.cpu().numpy(), a_plant)
+        np.testing.assert_array_equal(cache["ctx_len"].cpu().numpy(), ctx + np.array(a_plant) + 1)
+        tg = target.cpu().numpy()
+        np.testing.assert_array_equal(cache["anchor"].cpu().numpy(), [tg[b, a] for b, a in enumerate(a_plant)])
+        assert int(cache["dev_error"].item()) == 0
+
+
 def test_tiled_gemm_path_bf16():
     """Batch x block >= 128 rows takes the tiled MFMA GEMM for every projection: row
     tails (160 draft rows, 180 and 320 injected rows), ragged SwiGLU width and
