@@ -74,6 +74,10 @@ HEAD_TRAFFIC = {
         "source_sha256": "fa926957bee60069be18fe225739fffbff67f1c08bf5f45538ecee180799a7d6",
         "bytes": 1256440233,
     },
+    "mimo_swa_b8_k8_w128_ctx65536": {
+        "source_sha256": "fa926957bee60069be18fe225739fffbff67f1c08bf5f45538ecee180799a7d6",
+        "bytes": 1292458118,
+    },
 }
 # every source of the weight-streaming GEMM's translation unit (besides HIP's own)
 _KERNEL_SOURCES = ("gemm.hip", "gemm.h", "common.h", "epilogue.h", "philox.h")
