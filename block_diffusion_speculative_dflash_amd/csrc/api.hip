@@ -451,7 +451,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     at.n_rb = L.ap.n_rb;
     at.rows_per_block = L.ap.rows;
     // long full-attention windows over many sequences: contexts may be ragged
-    at.balance = L.ap.max_splits == 1 && B >= 16 && d.window > 1024;
+    at.balance = L.ap.max_splits == 1 && B >= 16 && B <= kMaxBalanceBatch && d.window > 1024;
     DF_CHECK(launch_attention(f32, at, stream));
 
     // output projection + residual; produces the MLP's RMSNorm input

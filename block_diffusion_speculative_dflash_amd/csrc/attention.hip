@@ -80,15 +80,19 @@ constexpr float kLazy = 8.f;  // largest allowed growth of a row maximum before 
 // the first half takes the sequence of rank i by context length (longest first, ties by
 // index), slot i of the second half rank 3B/2 - 1 - i: each CU pairs a long context with
 // a short one.  A permutation of the sequences, so results do not depend on it.
+// The context lengths go through LDS once; the host enables this for B <= kMaxBalanceBatch.
 __device__ int balanced_sequence(const AttnArgs& a, int slot) {
   __shared__ int seq_s;
+  __shared__ int len_s[kMaxBalanceBatch];
   const int B = a.batch, half = (B + 1) / 2;
   const int want = slot < half ? slot : (B - 1) - (slot - half);
+  for (int t = threadIdx.x; t < B; t += blockDim.x) len_s[t] = a.ctx_len[t];
+  __syncthreads();
   for (int t = threadIdx.x; t < B; t += blockDim.x) {
-    const int lt = a.ctx_len[t];
+    const int lt = len_s[t];
     int rank = 0;
     for (int s = 0; s < B; ++s) {
-      const int ls = a.ctx_len[s];
+      const int ls = len_s[s];
       rank += (ls > lt || (ls == lt && s < t)) ? 1 : 0;
     }
     if (rank == want) seq_s = t;

@@ -58,8 +58,9 @@ struct AttnArgs {
   int batch, block_k, n_q_heads, n_kv_heads, head_dim, cache_slots, window, sink;
   int keys_per_split, max_splits, n_rb, rows_per_block;  // rows_per_block: 16, 32, 48 or 64
   const int32_t* block_len;  // [B] or nullptr: block keys of sequence b are rows 0 .. block_len[b]-1
-  int balance;  // 1: pair long and short contexts on a CU (see balanced_sequence)
+  int balance;  // 1: pair long and short contexts on a CU (see balanced_sequence); batch <= kMaxBalanceBatch
 };
+constexpr int kMaxBalanceBatch = 256;
 hipError_t launch_attention(bool f32, const AttnArgs& a, hipStream_t stream);
 
 struct VerifyArgs {
