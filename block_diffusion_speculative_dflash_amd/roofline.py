@@ -68,27 +68,46 @@ def step_cost(d: Dims, mean_ctx: float, sampled: bool = False) -> StepCost:
 # HBM traffic of the LM-head kernel measured with hardware counters (FETCH_SIZE and
 # WRITE_SIZE per dispatch, each scaled by what the counter reads for a device copy of
 # 1 GiB: fetch x2.000, write x1.000), keyed by workload name.  A figure holds only for
-# the kernel sources it was taken with; `measured_head_traffic` returns None otherwise.
+# the kernel sources it was taken with ("stream": the weight-streaming GEMM of batches
+# up to 127 rows, "tiled": the tiled MFMA GEMM); `measured_head_traffic` returns None
+# otherwise.  The tiled heads read the weights once per 256-row tile of the batch, less
+# what the L2s and the MALL catch: 3 row tiles at batch 64 -> 1.30x, 8 at batch 256 -> 3.18x
+# the weights-once figure.
 HEAD_TRAFFIC = {
     "qwen3_8b_b1_k16_ctx4096": {
+        "sources": "stream",
         "source_sha256": "fa926957bee60069be18fe225739fffbff67f1c08bf5f45538ecee180799a7d6",
         "bytes": 1256440233,
     },
     "mimo_swa_b8_k8_w128_ctx65536": {
+        "sources": "stream",
         "source_sha256": "fa926957bee60069be18fe225739fffbff67f1c08bf5f45538ecee180799a7d6",
         "bytes": 1292458118,
     },
+    "llama31_8b_b64_k10_ragged2048": {
+        "sources": "tiled",
+        "source_sha256": "1fc7e562a659696c1f06e127f40c0eded31856bc32b4f3f82c60f4129ecdaadc",
+        "bytes": 1381126642,
+    },
+    "longctx_swa_b256_k8_w128_ctx262144": {
+        "sources": "tiled",
+        "source_sha256": "1fc7e562a659696c1f06e127f40c0eded31856bc32b4f3f82c60f4129ecdaadc",
+        "bytes": 4136986883,
+    },
 }
-# every source of the weight-streaming GEMM's translation unit (besides HIP's own)
-_KERNEL_SOURCES = ("gemm.hip", "gemm.h", "common.h", "epilogue.h", "philox.h")
+# every source of each GEMM's translation unit (besides HIP's own)
+_KERNEL_SOURCES = {
+    "stream": ("gemm.hip", "gemm.h", "common.h", "epilogue.h", "philox.h"),
+    "tiled": ("gemm_tiled.hip", "gemm.h", "common.h", "epilogue.h", "philox.h"),
+}
 
 
-def kernel_source_sha256() -> str:
+def kernel_source_sha256(kind: str = "stream") -> str:
     import hashlib
     import os
     h = hashlib.sha256()
     base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-    for f in _KERNEL_SOURCES:
+    for f in _KERNEL_SOURCES[kind]:
         with open(os.path.join(base, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -96,6 +115,6 @@ def kernel_source_sha256() -> str:
 
 def measured_head_traffic(workload: str):
     rec = HEAD_TRAFFIC.get(workload)
-    if rec is None or rec["source_sha256"] != kernel_source_sha256():
+    if rec is None or rec["source_sha256"] != kernel_source_sha256(rec["sources"]):
         return None
     return rec["bytes"]
