@@ -28,16 +28,26 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
   TA* xa = static_cast<TA*>(a.xa);
   float* h = a.h + static_cast<size_t>(m) * d;
   const int steps = (d + kKStep - 1) / kKStep;
+  // 8 consecutive features per thread and pass: one 16- (bf16) or 32-byte (fp32) load
+  // of the row and of the gain, two 16-byte stores of h, and one store of the packed
+  // operand (8 consecutive k of one row are contiguous in the fragment layout)
+  typedef T T8 __attribute__((ext_vector_type(8)));
+  typedef TA TA8 __attribute__((ext_vector_type(8)));
   float ss = 0.f;
   for (int n0 = threadIdx.x * 8; n0 < d; n0 += kThreads * 8) {  // d is a multiple of 64
-    TA* dst = xa + pa_index(m, n0, steps);
+    const T8 sv = *reinterpret_cast<const T8*>(src + n0);
+    const T8 gv = *reinterpret_cast<const T8*>(gain + n0);
+    float v[8];
+    TA8 out;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float v = to_f32(src[n0 + j]);
-      h[n0 + j] = v;
-      dst[j] = from_f32<TA>(v * to_f32(gain[n0 + j]));
-      ss += v * v;
+      v[j] = to_f32(static_cast<T>(sv[j]));
+      out[j] = from_f32<TA>(v[j] * to_f32(static_cast<T>(gv[j])));
+      ss += v[j] * v[j];
     }
+    reinterpret_cast<float4*>(h + n0)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(h + n0)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    *reinterpret_cast<TA8*>(xa + pa_index(m, n0, steps)) = out;
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
