@@ -272,7 +272,11 @@ bool use_tiled(const dflash_dims& d, int M) { return !is_f32(d) && M >= kTiledMi
 
 GemmPlan gemm_plan(const dflash_dims& d, int epi, int M, int n_tiles, int S, bool allow_split,
                    size_t partial_cap) {
-  if (use_tiled(d, M)) return tiled_plan(M, n_tiles, S, allow_split && epi != EPI_ARGMAX, partial_cap);
+  // The fusion GEMM (K = 5 taps x tap width) goes tiled from 65 rows: one 128-row tile
+  // streams fuse_w once where two 64-row streaming tiles read it twice, and its long K
+  // amortises the tiled kernel's fixed costs (batch 8's 72 rows: 61 against 66-72 us).
+  if (use_tiled(d, M) || (epi == EPI_FUSE && !is_f32(d) && M > 64))
+    return tiled_plan(M, n_tiles, S, allow_split && epi != EPI_ARGMAX, partial_cap);
   return stream_plan(M, n_tiles, S, allow_split, partial_cap);
 }
 
