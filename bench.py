@@ -6,13 +6,16 @@ dflash_fuse_inject(commit = 0) -> dflash_verify_commit over the whole batch, wit
 synthetic seeded inputs already resident in HBM.  With --temperature T > 0 the step
 samples instead: dflash_draft_step_sampled (Gumbel-max drafts, logits and
 log-sum-exps out) -> target stand-in (planted target logits) -> dflash_fuse_inject
--> dflash_verify_sampled (rejection sampling over the full vocabulary).  Steps are captured as HIP
-graphs and replayed.  Prints one JSON line:
-  value      block steps/s (all B sequences per step)
-  roofline   the dominant kernel (fused final-norm + LM-head + argmax), timed with
-             HIP events on its own stream, against the 8 TB/s HBM peak
+-> dflash_verify_sampled (rejection sampling over the full vocabulary).  Steps are
+captured as HIP graphs and replayed.  Prints one JSON line:
+  value         block steps/s of the headline workload (all B sequences per step)
+  roofline      its dominant kernel (fused final-norm + LM head + argmax), timed with
+                HIP events on the stream it runs on, against the MFMA peak (batches of
+                >= 128 block rows) or the 8 TB/s HBM peak (smaller batches)
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample
-Default workload: the Qwen3-8B-shaped drafter (batch 1, block 16, context 4096).
+  also          the other bf16 workloads, measured the same way in the same run
+Default headline workload: batch 256, block 8, SWA window 128 at logical position
+262144 (the long-context throughput configuration); --only skips the others.
 """
 from __future__ import annotations
 
@@ -38,9 +41,11 @@ def parse():
     from block_diffusion_speculative_dflash_amd import configs
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default=configs.C2.name, choices=sorted(configs.WORKLOADS))
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=configs.C5.name, choices=sorted(configs.WORKLOADS))
+    p.add_argument("--only", action="store_true",
+                   help="measure the chosen workload alone (default: also the other bf16 workloads)")
     p.add_argument("--accept-q", type=float, default=None,
                    help="override the planted geometric q (sub-runs of the SWA workload)")
     p.add_argument("--head-launches", type=int, default=50)
@@ -92,23 +97,49 @@ class HipEvents:
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs the DFlash step on one GPU only; "
-                          "run with --gpus 1", "n_gpus": args.gpus}), flush=True)
+        print(json.dumps({"error": "this build runs the DFlash step on one GPU only (the data-parallel "
+                          "shard of one GPU is the whole measurement); run with --gpus 1",
+                          "n_gpus": args.gpus}), flush=True)
         return 2
+    import torch
+    from block_diffusion_speculative_dflash_amd import configs
+
+    torch.cuda.init()
+    wl = configs.WORKLOADS[args.workload]
+    res = measure(args, wl, headline=True)
+    if res is None:  # --pmc-probe
+        return 0
+    if not args.only:
+        also = {}
+        for other in configs.ALL:
+            if other.name == wl.name or other.dims.dtype != configs.BF16:
+                continue
+            torch.cuda.empty_cache()
+            r = measure(args, other, headline=False)
+            also[other.name] = {key: r[key] for key in ("value", "unit", "ms_per_step", "committed_tok_s",
+                                                        "accepted_tok_s", "mean_accept",
+                                                        "planted_accept_matches", "step_roofline",
+                                                        "roofline", "dev_error")}
+        res["also"] = also
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def measure(args, wl, headline: bool):
+    """Prefill, capture and time one workload; returns its result record (None for
+    a hardware-counter probe run)."""
     import torch
     from block_diffusion_speculative_dflash_amd import binding as bd
     from block_diffusion_speculative_dflash_amd import configs, harness, synth
     from block_diffusion_speculative_dflash_amd.roofline import (HBM_PEAK_GBS, MFMA_BF16_PEAK_TFLOPS,
                                                                   measured_head_traffic, step_cost)
 
-    wl = configs.WORKLOADS[args.workload]
     d = wl.dims
     if args.sink:
         from dataclasses import replace
         d = replace(d, sink=args.sink, cache_slots=d.cache_slots + args.sink)
     B, k, V = d.batch, d.block_k, d.vocab
     dev = "cuda"
-    torch.cuda.init()
     log(f"[bench] workload {wl.name}: {wl.description}")
     W = bd.pack_weights(d, synth.make_weights(d, seed=args.seed, device=dev))
     ctx = synth.make_context_lengths(wl, seed=args.seed)
@@ -144,7 +175,7 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log("[bench] pmc probe done: 5 draft steps, 5 copies of 1073741824 bytes")
-        return 0
+        return None
 
     # planted acceptance and the target stand-in tables
     kind, q = wl.accept
@@ -153,80 +184,35 @@ def main() -> int:
     n_tab = args.warmup + args.steps + 8
     a_tab = synth.planted_accept(kind, q, k, n_tab, B, seed=args.seed)
     fill = synth.target_fill(k, n_tab, B, seed=args.seed)
-    a_tab_d = torch.as_tensor(a_tab, dtype=torch.int32, device=dev)
-    fill_d = torch.as_tensor(fill, dtype=torch.int32, device=dev)
-    step_ctr = torch.zeros(1, dtype=torch.int32, device=dev)
-    acc_total = torch.zeros(1, dtype=torch.int64, device=dev)
-    draft = torch.zeros((B, k), dtype=torch.int32, device=dev)
-    target = torch.zeros((B, k + 1), dtype=torch.int32, device=dev)
-    accept = torch.zeros(B, dtype=torch.int32, device=dev)
-    out_tok = torch.zeros((B, k + 1), dtype=torch.int32, device=dev)
-    n_rows_step = torch.full((B,), k + 1, dtype=torch.int32, device=dev)
     pool = [synth.make_taps(d, k + 1, seed=args.seed, stream=1 + i, device=dev) for i in range(4)]
     saved_ctx = cache["ctx_len"].clone()
     sampled = args.temperature > 0
     adaptive = args.adaptive
-    if adaptive:
-        # controller state: every sequence starts at the full block with the average at theta_up
-        aparams = bd.adapt_params()
-        cache["block_len"] = torch.full((B,), k, dtype=torch.int32, device=dev)
-        ema = torch.full((B,), aparams.theta_up, dtype=torch.float32, device=dev)
-        off_left = torch.zeros(B, dtype=torch.int32, device=dev)
-        kb_total = torch.zeros(1, dtype=torch.int64, device=dev)  # block rows drafted (harness)
-    blk = cache.get("block_len")
-    n_rows_in = torch.full((B,), k + 1, dtype=torch.int32, device=dev)
-    if sampled:
-        # sampled target stand-in: resident filler logits, planted per step from the drafts
-        tgt_logits = synth.make_logits((B, k + 1, V), seed=args.seed, stream=31_337, device=dev)
-        saved_idx = torch.full((B, k + 1), -1, dtype=torch.int32, device=dev)
-        saved_val = torch.zeros((B, k + 1), dtype=torch.float32, device=dev)
-        logits = torch.empty((B, k, V), dtype=torch.float32, device=dev)
-        lse = torch.empty((B, k), dtype=torch.float32, device=dev)
-        rng_step = torch.zeros(1, dtype=torch.int64, device=dev)
-        smp = bd.sampling_struct(args.temperature, args.seed + 1, 0, step_dev=rng_step)
-
-    def step(taps):
-        n_rows = n_rows_in if adaptive else n_rows_step
-        if sampled:
-            bd.dflash_draft_step_sampled(d, W, cache, smp, draft, logits, lse, ws)
-            harness.plant_logits(draft, tgt_logits, a_tab_d, step_ctr, saved_idx, saved_val, accept,
-                                 acc_total, rng_step, block_len=blk, n_rows=n_rows_in if adaptive else None,
-                                 kb_total=kb_total if adaptive else None)
-            bd.dflash_fuse_inject(d, W, taps, n_rows, k + 1, False, cache, ws)
-            bd.dflash_verify_sampled(d, smp, draft, logits, lse, tgt_logits, cache, accept, out_tok, ws)
-        else:
-            bd.dflash_draft_step(d, W, cache, draft, None, ws)
-            harness.plant(draft, target, a_tab_d, fill_d, step_ctr, accept, acc_total, V, block_len=blk,
-                          n_rows=n_rows_in if adaptive else None, kb_total=kb_total if adaptive else None)
-            bd.dflash_fuse_inject(d, W, taps, n_rows, k + 1, False, cache, ws)
-            bd.dflash_verify_commit(d, draft, target, cache, accept, out_tok)
-        if adaptive:
-            bd.dflash_adapt_block_len(d, aparams, accept, cache, ema, off_left)
+    loop = harness.RoundLoop(d, W, cache, ws, a_tab, fill, seed=args.seed, temperature=args.temperature,
+                             adaptive=adaptive, device=dev)
 
     # eager warm-up of every code path, then capture one graph per taps slot
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
-        step(pool[0])
+        loop.round(pool[0])
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
     graphs = []
     for taps in pool:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(taps)
+            loop.round(taps)
         graphs.append(g)
     # the eager warm-up and the captures consumed table entries; restart the tables
-    cache["ctx_len"].copy_(saved_ctx)
-    step_ctr.zero_()
-    acc_total.zero_()
-    accept.zero_()
-    if adaptive:
-        blk.fill_(k)
-        ema.fill_(aparams.theta_up)
-        off_left.zero_()
-        kb_total.zero_()
+    loop.restart(saved_ctx)
     torch.cuda.synchronize()
+    acc_total, accept = loop.acc_total, loop.accept
+    if adaptive:
+        kb_total, aparams = loop.kb_total, loop.aparams
+    if sampled:
+        smp, logits, lse = loop.smp, loop.logits, loop.lse
+    draft = loop.draft
 
     def run(n, s0):
         for s in range(s0, s0 + n):
@@ -306,7 +292,7 @@ def main() -> int:
                      "avg_us": round(head_ms * 1e3, 2), "bytes_per_launch": cost.head_bytes}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if headline and not args.no_cpu_baseline:
         cpu = cpu_baseline(args, d, W, ctx, pre, anchors, a_tab)
 
     res = {
@@ -320,13 +306,16 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if d.dtype == configs.BF16 else "f32",
+        # a bf16 drafter's matrix-core operands, q/k/v and K/V cache are fp16 (its
+        # weights and taps arrive as bf16, accumulation and residual are fp32)
+        "dtype": "fp16" if d.dtype == configs.BF16 else "f32",
+        "precision": ("bf16 weights and taps; fp16 MFMA operands, q/k/v and K/V cache; fp32 accumulation, "
+                      "residual and softmax" if d.dtype == configs.BF16 else "fp32 throughout"),
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps, planted targets"
                 + (", N(0,4) target logits with planted acceptance)" if sampled else ")"),
-        "config": {"workload": wl.name, "batch": B, "block_k": k, "context": int(ctx.max()),
-                   "window": d.window, "sink": d.sink, "layers": d.n_layers, "hidden": d.hidden,
-                   "ffn": d.ffn, "vocab": V, "accept": [kind, q], "temperature": args.temperature,
-                   "adaptive": adaptive},
+        "config": {"workload": wl.name},
+        "options": {"accept": [kind, q], "temperature": args.temperature, "adaptive": adaptive,
+                    "sink": d.sink, "context": [int(ctx.min()), int(ctx.max())]},
         "accepted_tok_s": round(accepted / elapsed, 1),
         "committed_tok_s": round(committed / elapsed, 1),
         "mean_accept": round(accepted / (args.steps * B), 4),
@@ -337,8 +326,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "dev_error": err,
     }
-    print(json.dumps(res), flush=True)
-    return 0
+    return res
 
 
 def prefill_taps(d, n_pre: int, r0: int, seed: int):

@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdflash.so")
 
 DFLASH_OK, DFLASH_E_INVALID, DFLASH_E_UNSUPPORTED, DFLASH_E_WORKSPACE, DFLASH_E_HIP = 0, -1, -2, -3, -4
-DEVERR_TOKEN, DEVERR_ROWS, DEVERR_CTXLEN = 1, 2, 4
+DEVERR_TOKEN, DEVERR_ROWS, DEVERR_CTXLEN, DEVERR_RANGE, DEVERR_BLOCK, DEVERR_OVERFLOW = 1, 2, 4, 8, 16, 32
 
 _INT_FIELDS = ("batch", "block_k", "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim",
                "ffn", "vocab", "n_taps", "tap_dim", "window", "cache_slots", "dtype",
@@ -63,7 +63,9 @@ _lib: Optional[ctypes.CDLL] = None
 EXPORTED = ("dflash_workspace_bytes", "dflash_status_string", "dflash_packed_bytes",
             "dflash_pack_weights", "dflash_fuse_inject", "dflash_draft_step",
             "dflash_verify_commit", "dflash_draft_step_timed", "dflash_draft_step_sampled",
-            "dflash_draft_step_sampled_timed", "dflash_verify_sampled", "dflash_adapt_block_len")
+            "dflash_draft_step_sampled_timed", "dflash_verify_sampled", "dflash_adapt_block_len",
+            "dflash_debug_poison")
+POISON_RING, POISON_WORKSPACE = 1, 2
 
 
 def lib() -> ctypes.CDLL:
@@ -108,6 +110,8 @@ def lib() -> ctypes.CDLL:
     L.dflash_adapt_block_len.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashAdaptParams), P,
                                          ctypes.POINTER(DflashCache), P, P, P]
     L.dflash_adapt_block_len.restype = ctypes.c_int
+    L.dflash_debug_poison.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashCache), P, S, I, P]
+    L.dflash_debug_poison.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -178,7 +182,7 @@ def dflash_pack_weights(dims: Dims, weights, packed: torch.Tensor, dev_error: to
 def pack_weights(dims: Dims, weights: Dict[str, torch.Tensor], device="cuda") -> Dict[str, torch.Tensor]:
     """Add the packed GEMM copy (dflash_pack_weights) to a weight dict, in place."""
     packed = torch.empty(dflash_packed_bytes(dims), dtype=torch.uint8, device=device)
-    err = torch.zeros(1, dtype=torch.int32, device=device)
+    err = torch.zeros(1, dtype=torch.uint32, device=device)
     dflash_pack_weights(dims, weights, packed, err)
     torch.cuda.synchronize()
     if int(err.item()) != 0:
@@ -281,6 +285,16 @@ def dflash_adapt_block_len(dims: Dims, params: DflashAdaptParams, accept_len: to
     _check("dflash_adapt_block_len", st)
 
 
+def dflash_debug_poison(dims: Dims, cache, workspace: Optional[torch.Tensor], what: int, stream=None) -> None:
+    ds = dims_struct(dims)
+    cs = cache_struct(cache) if cache is not None else None
+    st = lib().dflash_debug_poison(ctypes.byref(ds), ctypes.byref(cs) if cs is not None else None,
+                                   _ptr(workspace),
+                                   0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                   int(what), _stream(stream))
+    _check("dflash_debug_poison", st)
+
+
 # ----------------------------------------------------------------------------- buffers
 def alloc_cache(dims: Dims, device="cuda", ctx_len=None, anchor=None) -> Dict[str, torch.Tensor]:
     """Caller-owned decode state: K/V rings (fp16 for bf16 drafters, fp32 for fp32
@@ -297,7 +311,7 @@ def alloc_cache(dims: Dims, device="cuda", ctx_len=None, anchor=None) -> Dict[st
     return {"k": torch.zeros(shape, dtype=dt, device=device),
             "v": torch.zeros(shape, dtype=dt, device=device),
             "ctx_len": ints(ctx_len), "anchor": ints(anchor),
-            "dev_error": torch.zeros(1, dtype=torch.int32, device=device)}
+            "dev_error": torch.zeros(1, dtype=torch.uint32, device=device)}
 
 
 def cache_dtype(dims: Dims) -> torch.dtype:

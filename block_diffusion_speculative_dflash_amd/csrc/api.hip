@@ -313,6 +313,7 @@ struct Ctx {
   const PackLayout& P;
   char* ws;
   const char* packed;
+  uint32_t* dev_error;
   template <typename X> X* at(size_t off) const { return reinterpret_cast<X*>(ws + off); }
   const void* reg(const Region& r) const { return packed + r.off; }
 };
@@ -333,6 +334,7 @@ GemmArgs base_args(const Ctx& c) {
   a.sink = c.d.sink;
   a.ffn = c.d.ffn;
   a.theta = c.d.rope_theta;
+  a.dev_error = c.dev_error;
   return a;
 }
 
@@ -384,7 +386,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   const Layout L = layout(d);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < L.total) return DFLASH_E_WORKSPACE;
 
-  const Ctx c{d, L, P, static_cast<char*>(workspace), static_cast<const char*>(w->packed)};
+  const Ctx c{d, L, P, static_cast<char*>(workspace), static_cast<const char*>(w->packed), cache->dev_error};
   const bool f32 = is_f32(d);
   const size_t e = elem(d);
   const int D = d.hidden, k = d.block_k, B = d.batch, F = d.ffn;
@@ -637,7 +639,7 @@ int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const v
   const Layout L = layout(d);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < L.total) return DFLASH_E_WORKSPACE;
 
-  const Ctx c{d, L, P, static_cast<char*>(workspace), static_cast<const char*>(w->packed)};
+  const Ctx c{d, L, P, static_cast<char*>(workspace), static_cast<const char*>(w->packed), cache->dev_error};
   const int D = d.hidden;
   const int Mi = d.batch * n_max;
   const int K = d.n_taps * d.tap_dim;
@@ -678,7 +680,6 @@ int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const v
   a.n_rows = n_rows;
   a.cache_k = cache->k;
   a.cache_v = cache->v;
-  a.dev_error = cache->dev_error;
   if (int st = run_gemm(EPI_INJECT, c, a, true, stream)) return st;
 
   if (commit) DF_CHECK(launch_commit_rows(cache->ctx_len, n_rows, d.batch, n_max, cache->dev_error, stream));
@@ -812,6 +813,48 @@ int dflash_adapt_block_len(const dflash_dims* dims, const dflash_adapt_params* p
   a.theta_off = p.theta_off;
   a.theta_up = p.theta_up;
   DF_CHECK(launch_adapt(a, stream));
+  return DFLASH_OK;
+}
+
+int dflash_debug_poison(const dflash_dims* dims, const dflash_cache* cache, void* workspace,
+                        size_t workspace_bytes, int32_t what, hipStream_t stream) {
+  if (!dims_ok(dims) || (what & ~(DFLASH_POISON_RING | DFLASH_POISON_WORKSPACE)) != 0) return DFLASH_E_INVALID;
+  const dflash_dims& d = *dims;
+  if (what & DFLASH_POISON_RING) {
+    if (cache == nullptr || !cache->k || !cache->v || !cache->ctx_len || !aligned16(cache->k) ||
+        !aligned16(cache->v) || !aligned4(cache->ctx_len))
+      return DFLASH_E_INVALID;
+    PoisonRingArgs a{};
+    a.cache_k = cache->k;
+    a.cache_v = cache->v;
+    a.ctx_len = cache->ctx_len;
+    a.n_layers = d.n_layers;
+    a.batch = d.batch;
+    a.n_kv_heads = d.n_kv_heads;
+    a.cache_slots = d.cache_slots;
+    a.sink = d.sink;
+    a.n_dead = d.cache_slots - d.sink - d.window;
+    a.row_bytes = static_cast<int>(d.head_dim * elem(d));
+    DF_CHECK(launch_poison_ring(a, stream));
+  }
+  if (what & DFLASH_POISON_WORKSPACE) {
+    const Layout L = layout(d);
+    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < L.total) return DFLASH_E_WORKSPACE;
+    // every region in workspace order; the arrival counters and the zero-initialised
+    // keys of the sampled verification carry state between calls (zero) and are kept
+    struct R { size_t off; bool keep; };
+    const R regions[] = {{L.h, false}, {L.xa, false}, {L.ssq, false}, {L.q, false}, {L.kb, false},
+                         {L.vb, false}, {L.o, false}, {L.act, false}, {L.cu, false}, {L.ssq_c, false},
+                         {L.partials, false}, {L.counters, true}, {L.keys, false}, {L.attn_cnt, true},
+                         {L.attn_o, false}, {L.attn_ml, false}, {L.lse_part, false}, {L.v_part, false},
+                         {L.v_cnt, true}, {L.v_rowlse, false}, {L.v_dec, false}, {L.v_keys, true},
+                         {L.total, true}};
+    char* ws = static_cast<char*>(workspace);
+    for (size_t i = 0; i + 1 < sizeof(regions) / sizeof(regions[0]); ++i) {
+      if (regions[i].keep) continue;
+      DF_CHECK(launch_fill_ones(ws + regions[i].off, (regions[i + 1].off - regions[i].off) / 16 * 16, stream));
+    }
+  }
   return DFLASH_OK;
 }
 

@@ -26,6 +26,27 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
 template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return static_cast<f16>(x); }
 
+// Device-detected error bits (the DFLASH_DEVERR_* values of the C header).
+constexpr uint32_t kErrToken = 1u, kErrRows = 2u, kErrCtxLen = 4u, kErrRange = 8u, kErrBlock = 16u,
+                   kErrOverflow = 32u;
+
+// Conversion of an activation, q/k/v or K/V value to the compute type.  For fp16 a
+// finite value beyond the largest finite fp16 (65504) saturates to +-65504 instead
+// of becoming an infinity, and a value that is not finite passes through; both set
+// `bad`, which the caller reports as kErrOverflow.  fp32 values pass unchanged.
+template <typename T> __device__ __forceinline__ T to_act(float x, bool& bad);
+template <> __device__ __forceinline__ float to_act<float>(float x, bool&) { return x; }
+template <> __device__ __forceinline__ f16 to_act<f16>(float x, bool& bad) {
+  if (!(fabsf(x) <= 65504.f)) {
+    bad = true;
+    if (fabsf(x) > 65504.f) x = copysignf(65504.f, x);  // NaN stays NaN
+  }
+  return static_cast<f16>(x);
+}
+__device__ __forceinline__ void report_overflow(bool bad, uint32_t* dev_error) {
+  if (bad && dev_error != nullptr) atomicOr(dev_error, kErrOverflow);
+}
+
 // Activation / compute type of a drafter whose weights arrive as T: bf16 drafters
 // compute in fp16, fp32 drafters in fp32.
 template <typename T> struct ActOf;

@@ -11,6 +11,8 @@
 //   INJECT  RoPE on K, scatter of K and V rows into their cache slots (positions
 //           below the sink keep slot = position, the rest ring over C - sink)
 // The split-vocab argmax differs between the two GEMMs and lives with each.
+// Values stored in fp16 (bf16 drafters) saturate at the fp16 range and set the
+// overflow bit of g.dev_error (see to_act); the fp32 residual stream is unaffected.
 #pragma once
 
 #include "common.h"
@@ -25,6 +27,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
                                               int tile_n, int m0, const float (*hres)[8]) {
   typedef typename ActOf<TIN>::type TA;
   const int tid = threadIdx.x;
+  bool bad = false;
   if constexpr (EPI == EPI_FUSE || EPI == EPI_RESID) {
     // 8 threads per row, 8 consecutive columns each: one packed 8-element store
     constexpr int RPP = NT / 8;  // rows per pass
@@ -57,7 +60,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
           x[j] = tile[r][c8 * 8 + j] * rs[r];
           if constexpr (EPI == EPI_RESID) x[j] += hv[j];
           ss += x[j] * x[j];
-          dst[j] = from_f32<TA>(x[j] * to_f32(gain[n0 + j]));
+          dst[j] = to_act<TA>(x[j] * to_f32(gain[n0 + j]), bad);
         }
         if constexpr (EPI == EPI_RESID) {
           float4* hp = reinterpret_cast<float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
@@ -75,10 +78,16 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
     for (int idx = tid; idx < BM * 32; idx += NT) {
       const int r = idx >> 5, p = idx & 31, m = m0 + r;
       const int j = tile_n * 32 + p;
-      if (m >= g.M || j >= g.ffn) continue;
-      const float gv = tile[r][p] * rs[r];
-      const float uv = tile[r][p + 32] * rs[r];
-      act[pa_index(m, j, g.out_steps)] = from_f32<TA>(gv / (1.f + expf(-gv)) * uv);
+      if (m >= g.M) continue;
+      // columns past ffn are the down projection's K padding: written as zeros, so
+      // the product never depends on what the workspace held before
+      float y = 0.f;
+      if (j < g.ffn) {
+        const float gv = tile[r][p] * rs[r];
+        const float uv = tile[r][p + 32] * rs[r];
+        y = gv / (1.f + expf(-gv)) * uv;
+      }
+      act[pa_index(m, j, g.out_steps)] = to_act<TA>(y, bad);
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     const int dh = g.head_dim, half = dh / 2;
@@ -105,11 +114,16 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
       int n_valid = g.rows_per_seq;
       if constexpr (EPI == EPI_INJECT) {
         const int nr = g.n_rows[b];
-        if ((nr < 0 || nr > g.rows_per_seq) && i == 0 && p == 0) atomicOr(g.dev_error, 2u);
+        if ((nr < 0 || nr > g.rows_per_seq) && i == 0 && p == 0) atomicOr(g.dev_error, kErrRows);
         n_valid = min(max(nr, 0), g.rows_per_seq);
       }
       if (i >= n_valid) continue;
       const int pos = max(g.ctx_len[b], 0) + i;
+      // A call with more than C - s ring rows for one sequence: rows i and
+      // i + (C - s) share a slot, and writes in position order leave the later one,
+      // so the earlier row is not written at all (no two writers race on a slot).
+      if constexpr (EPI == EPI_INJECT)
+        if (pos >= g.sink && i + (g.cache_slots - g.sink) < n_valid) continue;
       const float x1 = tile[r][p] * rs[r], x2 = tile[r][p + 32] * rs[r];
       float y1 = x1, y2 = x2;
       if (kind != 2) {
@@ -127,10 +141,11 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
         dst = static_cast<TA*>(kind == 1 ? g.cache_k : g.cache_v) +
               (((static_cast<size_t>(layer) * g.batch + b) * g.n_kv_heads + head) * g.cache_slots + slot) * dh;
       }
-      dst[d1] = from_f32<TA>(y1);
-      dst[d1 + half] = from_f32<TA>(y2);
+      dst[d1] = to_act<TA>(y1, bad);
+      dst[d1 + half] = to_act<TA>(y2, bad);
     }
   }
+  report_overflow(bad, g.dev_error);
 }
 
 // RMSNorm factor of A row m from the producer's per-tile partial sums of squares.

@@ -147,4 +147,16 @@ hipError_t launch_verify_sampled(const VerifySampledArgs& a, hipStream_t stream)
 hipError_t launch_commit_rows(int32_t* ctx_len, const int32_t* n_rows, int batch, int n_max,
                               uint32_t* dev_error, hipStream_t stream);
 
+// Debug poisoning: all-ones bytes (NaN in fp16 and fp32) into memory no later call
+// may depend on.
+struct PoisonRingArgs {
+  void* cache_k;  // [L, B, Hkv, C, dh]
+  void* cache_v;
+  const int32_t* ctx_len;
+  int n_layers, batch, n_kv_heads, cache_slots, sink, n_dead;  // positions ctx_len .. ctx_len + n_dead - 1
+  int row_bytes;                                               // dh * element size (a multiple of 16)
+};
+hipError_t launch_poison_ring(const PoisonRingArgs& a, hipStream_t stream);
+hipError_t launch_fill_ones(void* p, size_t bytes, hipStream_t stream);  // p, bytes: multiples of 16
+
 }  // namespace dflash

@@ -1,5 +1,7 @@
 // Small kernels of the step: block construction, greedy verify + commit, and the
 // committed-length update of a prefill injection.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -18,10 +20,10 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
   const int d = a.hidden;
   int tok = a.anchor[b];
   if (tok < 0 || tok >= a.vocab) {
-    if (threadIdx.x == 0 && i == 0) atomicOr(a.dev_error, 1u);
+    if (threadIdx.x == 0 && i == 0) atomicOr(a.dev_error, kErrToken);
     tok = min(max(tok, 0), a.vocab - 1);
   }
-  if (threadIdx.x == 0 && i == 0 && a.ctx_len[b] < 0) atomicOr(a.dev_error, 4u);
+  if (threadIdx.x == 0 && i == 0 && a.ctx_len[b] < 0) atomicOr(a.dev_error, kErrCtxLen);
   const T* src = i == 0 ? static_cast<const T*>(a.embed) + static_cast<size_t>(tok) * d
                         : static_cast<const T*>(a.mask_embed);
   const T* gain = static_cast<const T*>(a.gain);
@@ -34,6 +36,7 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
   typedef T T8 __attribute__((ext_vector_type(8)));
   typedef TA TA8 __attribute__((ext_vector_type(8)));
   float ss = 0.f;
+  bool bad = false;
   for (int n0 = threadIdx.x * 8; n0 < d; n0 += kThreads * 8) {  // d is a multiple of 64
     const T8 sv = *reinterpret_cast<const T8*>(src + n0);
     const T8 gv = *reinterpret_cast<const T8*>(gain + n0);
@@ -42,13 +45,14 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       v[j] = to_f32(static_cast<T>(sv[j]));
-      out[j] = from_f32<TA>(v[j] * to_f32(static_cast<T>(gv[j])));
+      out[j] = to_act<TA>(v[j] * to_f32(static_cast<T>(gv[j])), bad);
       ss += v[j] * v[j];
     }
     reinterpret_cast<float4*>(h + n0)[0] = make_float4(v[0], v[1], v[2], v[3]);
     reinterpret_cast<float4*>(h + n0)[1] = make_float4(v[4], v[5], v[6], v[7]);
     *reinterpret_cast<TA8*>(xa + pa_index(m, n0, steps)) = out;
   }
+  report_overflow(bad, a.dev_error);
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
   int kb = k;  // drafts of this sequence's block
   if (a.block_len != nullptr) {
     kb = a.block_len[b];
-    if ((kb < 0 || kb > k) && lane == 0) atomicOr(a.dev_error, 16u);
+    if ((kb < 0 || kb > k) && lane == 0) atomicOr(a.dev_error, kErrBlock);
     kb = min(max(kb, 0), k);
   }
   bool bad = false;
@@ -102,10 +106,10 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
   const int acc = __ffsll(static_cast<long long>(~ones)) - 1;
   const int bonus = __shfl(t, acc, kWave);
   if (lane <= k) a.out_tokens[static_cast<size_t>(b) * (k + 1) + lane] = lane <= acc ? t : -1;
-  if (__ballot(bad) != 0ull && lane == 0) atomicOr(a.dev_error, 1u);
+  if (__ballot(bad) != 0ull && lane == 0) atomicOr(a.dev_error, kErrToken);
   if (lane == 0) {
     const int P = a.ctx_len[b];
-    if (P < 0) atomicOr(a.dev_error, 4u);
+    if (P < 0) atomicOr(a.dev_error, kErrCtxLen);
     a.accept_len[b] = acc;
     a.anchor[b] = bonus;
     a.ctx_len[b] = max(P, 0) + acc + 1;
@@ -130,7 +134,7 @@ __global__ void adapt_kernel(AdaptArgs a) {
   const int half = (h > 0 && h < full) ? h : 0;  // 0: no middle rung
   int kb = a.block_len[b];
   if (kb < 0 || kb > full) {
-    atomicOr(a.dev_error, 16u);
+    atomicOr(a.dev_error, kErrBlock);
     kb = min(max(kb, 0), full);
   }
   float m = a.ema[b];
@@ -181,9 +185,9 @@ __global__ void commit_rows_kernel(int32_t* ctx_len, const int32_t* n_rows, int 
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= batch) return;
   int n = n_rows[b];
-  if (n < 0 || n > n_max) { atomicOr(dev_error, 2u); n = min(max(n, 0), n_max); }
+  if (n < 0 || n > n_max) { atomicOr(dev_error, kErrRows); n = min(max(n, 0), n_max); }
   const int P = ctx_len[b];
-  if (P < 0) atomicOr(dev_error, 4u);
+  if (P < 0) atomicOr(dev_error, kErrCtxLen);
   ctx_len[b] = max(P, 0) + n;
 }
 
@@ -191,6 +195,47 @@ hipError_t launch_commit_rows(int32_t* ctx_len, const int32_t* n_rows, int batch
                               uint32_t* dev_error, hipStream_t stream) {
   hipLaunchKernelGGL(commit_rows_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, ctx_len,
                      n_rows, batch, n_max, dev_error);
+  return hipGetLastError();
+}
+
+// Debug poisoning of the ring slots no window reaches: one workgroup per (layer,
+// sequence, kv head) fills the rows of positions ctx_len .. ctx_len + n_dead - 1.
+__global__ __launch_bounds__(kThreads) void poison_ring_kernel(PoisonRingArgs a) {
+  const int item = blockIdx.x;  // (layer * B + b) * Hkv + head
+  const int b = (item / a.n_kv_heads) % a.batch;
+  const int P = max(a.ctx_len[b], 0);
+  const int per_row = a.row_bytes / 16;
+  const size_t base = static_cast<size_t>(item) * a.cache_slots * a.row_bytes;
+  const uint4 ones = make_uint4(~0u, ~0u, ~0u, ~0u);
+  for (int t = threadIdx.x; t < a.n_dead * per_row; t += blockDim.x) {
+    const int p = P + t / per_row;
+    const int slot = p < a.sink ? p : a.sink + (p - a.sink) % (a.cache_slots - a.sink);
+    const size_t off = base + static_cast<size_t>(slot) * a.row_bytes + (t % per_row) * 16;
+    *reinterpret_cast<uint4*>(static_cast<char*>(a.cache_k) + off) = ones;
+    *reinterpret_cast<uint4*>(static_cast<char*>(a.cache_v) + off) = ones;
+  }
+}
+
+hipError_t launch_poison_ring(const PoisonRingArgs& a, hipStream_t stream) {
+  const long long items = static_cast<long long>(a.n_layers) * a.batch * a.n_kv_heads;
+  if (a.n_dead <= 0 || items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(poison_ring_kernel, dim3(static_cast<unsigned>(items)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kThreads) void fill_ones_kernel(uint4* p, size_t n) {
+  const uint4 ones = make_uint4(~0u, ~0u, ~0u, ~0u);
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = ones;
+}
+
+hipError_t launch_fill_ones(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n = bytes / 16;
+  if (n == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n + kThreads - 1) / kThreads, 4096);
+  hipLaunchKernelGGL(fill_ones_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                     static_cast<uint4*>(p), n);
   return hipGetLastError();
 }
 

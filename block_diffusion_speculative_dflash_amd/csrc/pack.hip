@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
       dst[idx * 8 + j] = from_f32<TD>(v);
     }
   }
-  if (range_err) atomicOr(a.dev_error, 8u);
+  if (range_err) atomicOr(a.dev_error, kErrRange);
 }
 
 hipError_t launch_pack(bool f32, const PackArgs& a, hipStream_t stream) {

@@ -214,9 +214,9 @@ __global__ __launch_bounds__(kThreads) void verify_lse_kernel(VerifySampledArgs 
     const unsigned long long ones = __ballot(ok);
     const int acc = __ffsll(static_cast<long long>(~ones)) - 1;  // lanes >= kb never accept: acc <= kb
     const float lse_a = __shfl(lse_t, acc, kWave);
-    if (__ballot(bad) != 0ull && lane == 0) atomicOr(a.dev_error, 1u);
+    if (__ballot(bad) != 0ull && lane == 0) atomicOr(a.dev_error, kErrToken);
     if (lane == 0) {
-      if (a.block_len != nullptr && (a.block_len[b] < 0 || a.block_len[b] > k)) atomicOr(a.dev_error, 16u);
+      if (a.block_len != nullptr && (a.block_len[b] < 0 || a.block_len[b] > k)) atomicOr(a.dev_error, kErrBlock);
       const float lq_a = acc < kb ? a.draft_lse[static_cast<size_t>(b) * k + acc] : 0.f;
       a.decision[b] = make_float4(static_cast<float>(acc), lse_a, lq_a, 0.f);
       reset_counter(&a.counters[b]);
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void verify_emit_kernel(VerifySampledArgs
   }
   if (tid == 0) {
     const int P = a.ctx_len[b];
-    if (P < 0) atomicOr(a.dev_error, 4u);
+    if (P < 0) atomicOr(a.dev_error, kErrCtxLen);
     a.accept_len[b] = acc;
     a.anchor[b] = y;
     a.ctx_len[b] = max(P, 0) + acc + 1;

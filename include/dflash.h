@@ -35,8 +35,12 @@
  *     fp16 with fp32 accumulation: its K/V cache, q/k/v and the activations that
  *     feed the matrix cores are fp16 (bf16 weights convert to fp16 exactly inside
  *     fp16's normal range, and fp16 rounds 8x finer than bf16 at the same bytes);
- *     the residual stream is fp32.  An fp32 drafter is fp32 throughout.  Token ids
- *     are int32.
+ *     the residual stream is fp32.  A value headed for fp16 storage that lies beyond
+ *     fp16's finite range is stored as +-65504 and sets DFLASH_DEVERR_OVERFLOW (so
+ *     weights or inputs far outside the trained range are reported, not silently
+ *     turned into infinities); the attention output, a convex combination of fp16
+ *     values, and the softmax weights (at most 2^8 before normalisation) cannot
+ *     exceed the range.  An fp32 drafter is fp32 throughout.  Token ids are int32.
  *   - The GEMM weights are read from a packed copy (dflash_pack_weights), laid out
  *     so every wavefront load is 1 KB of contiguous memory.
  *   - Order of one decode round: dflash_draft_step -> (target model verifies) ->
@@ -73,6 +77,8 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 #define DFLASH_DEVERR_CTXLEN 4u  /* ctx_len[b] negative: treated as 0 */
 #define DFLASH_DEVERR_RANGE 8u   /* a bf16 weight beyond the fp16 range: saturated when packed */
 #define DFLASH_DEVERR_BLOCK 16u  /* block_len[b] outside [0, k]: clamped */
+#define DFLASH_DEVERR_OVERFLOW 32u /* bf16 drafter: an fp16 activation, q/k/v or K/V value beyond
+                                      +-65504 (saturated there) or not finite */
 
 /* (host) Static shapes of one drafter; read during a call only.
  *   batch B, block_k k (1..63), n_layers L, hidden d, n_q_heads Hq, n_kv_heads Hkv
@@ -169,6 +175,9 @@ int dflash_pack_weights(const dflash_dims *dims, const dflash_weights *w, void *
  *   n_max    (host) 1 .. dims->max_inject_rows
  *   commit   (host) 0: rows are tentative (the per-round path, n_rows = k+1);
  *            1: also advance ctx_len[b] by n_rows[b] (prefill)
+ * A call may carry more rows for a sequence than its ring holds (C - s slots after
+ * the sink): the cache then ends as if the rows were written in position order,
+ * every ring slot holding the last of the rows that map to it.
  * For every row and layer l: c = RMSNorm(fuse_w . concat(taps)) * fuse_norm, then
  * K = RoPE(W_k^l c, position) and V = W_v^l c are written to the position's slot
  * (see dflash_cache). */
@@ -321,6 +330,24 @@ int dflash_draft_step_sampled_timed(const dflash_dims *dims, const dflash_weight
                                     void *workspace, size_t workspace_bytes,
                                     hipStream_t stream, hipEvent_t head_begin,
                                     hipEvent_t head_end);
+
+/* Debug aid: fill memory whose content no later call may depend on with all-ones
+ * bytes (NaN as fp16 and fp32), so that a kernel reading it would show up as
+ * non-finite or changed results.  `what` is an OR of
+ *   DFLASH_POISON_RING       the ring slots of positions ctx_len[b] ..
+ *                            ctx_len[b] + (C - s - W) - 1 of every layer, sequence and
+ *                            kv head: after dflash_verify_commit they hold the
+ *                            rolled-back rows, and no block's window reaches them before
+ *                            the next dflash_fuse_inject rewrites them
+ *   DFLASH_POISON_WORKSPACE  every workspace byte except the arrival counters and
+ *                            zero-initialised keys, which each call leaves at zero
+ * Enqueued on `stream`; the other calls' results must not change (the tests check
+ * this bitwise).  workspace may be NULL without DFLASH_POISON_WORKSPACE, cache may be
+ * NULL without DFLASH_POISON_RING. */
+#define DFLASH_POISON_RING 1
+#define DFLASH_POISON_WORKSPACE 2
+int dflash_debug_poison(const dflash_dims *dims, const dflash_cache *cache, void *workspace,
+                        size_t workspace_bytes, int32_t what, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -36,6 +36,13 @@ one reading and says so at the point of use:
   - ties in argmax go to the smallest token id.
 Every function here is pinned by the CPU tests (brute force on tiny inputs,
 library special cases, invariants); none is "parity unpinned".
+
+Precision study only: fuse_inject and draft_step take an optional `act_round`
+function, applied to the values an implementation stores between its matrix
+products (the normalised matrix inputs, q/k/v, the injected K/V rows, the attention
+output, the SwiGLU product).  With the default None nothing is rounded and the
+computation is the exact float64 one above; a test passes bf16 or fp16 rounding to
+measure what storing those values in 16 bits costs in logit error.
 """
 from __future__ import annotations
 
@@ -171,13 +178,19 @@ def inject_kv(dims, W, layer: int, c, pos):
     return K, V
 
 
-def fuse_inject(dims, W, st: State, taps, n_rows, commit: bool) -> None:
+def _exact(a):
+    return a
+
+
+def fuse_inject(dims, W, st: State, taps, n_rows, commit: bool, act_round=None) -> None:
     """Fuse the taps of n_rows[b] new positions starting at ctx_len[b] and write
-    their K/V rows into every layer's ring; with commit, advance ctx_len."""
+    their K/V rows into every layer's ring; with commit, advance ctx_len.
+    act_round: precision study only (see the module notes); None = exact."""
+    R = act_round or _exact
     taps = f64(taps)
     B = st.ctx_len.shape[0]
     n_rows = np.asarray(n_rows, dtype=np.int64)
-    c = fuse(dims, W, taps)                                  # [B, n_max, d]
+    c = R(fuse(dims, W, taps))                               # [B, n_max, d]
     for b in range(B):
         n = int(n_rows[b])
         if n == 0:
@@ -185,6 +198,7 @@ def fuse_inject(dims, W, st: State, taps, n_rows, commit: bool) -> None:
         pos = st.ctx_len[b] + np.arange(n)
         for l in range(dims.n_layers):
             K, V = inject_kv(dims, W, l, c[b, :n], pos)     # [n, Hkv, dh]
+            K, V = R(K), R(V)
             for r in range(n):                               # in position order
                 slot = slot_of(dims, int(pos[r]))
                 st.k_ring[l, b, :, slot, :] = K[r]
@@ -228,10 +242,11 @@ def block_lengths(dims, batch: int, block_len=None) -> np.ndarray:
     return kb
 
 
-def block_logits(dims, W, st: State, b: int, kb: int) -> np.ndarray:
+def block_logits(dims, W, st: State, b: int, kb: int, act_round=None) -> np.ndarray:
     """Logits [kb, V] of sequence b's block of kb rows: the anchor at position P,
     then kb - 1 mask positions; every row sees the committed window and all kb
-    block keys (bidirectional inside the block)."""
+    block keys (bidirectional inside the block).  act_round: precision study only."""
+    R = act_round or _exact
     Hq, Hkv, dh, D, F = dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.hidden, dims.ffn
     eps, theta = dims.rms_eps, dims.rope_theta
     P = int(st.ctx_len[b])
@@ -244,13 +259,13 @@ def block_logits(dims, W, st: State, b: int, kb: int) -> np.ndarray:
     slots = np.array([slot_of(dims, int(p)) for p in window_positions(dims, P)], dtype=np.int64)
 
     for l in range(dims.n_layers):
-        x = rms_norm(h, W["attn_norm"][l], eps)
+        x = R(rms_norm(h, W["attn_norm"][l], eps))
         qkv = linear(x, W["w_qkv"][l])
         q = qkv[:, :Hq * dh].reshape(kb, Hq, dh)
         kk = qkv[:, Hq * dh:(Hq + Hkv) * dh].reshape(kb, Hkv, dh)
-        vv = qkv[:, (Hq + Hkv) * dh:].reshape(kb, Hkv, dh)
-        q = rope(q, pos[:, None], theta)
-        kk = rope(kk, pos[:, None], theta)
+        vv = R(qkv[:, (Hq + Hkv) * dh:].reshape(kb, Hkv, dh))
+        q = R(rope(q, pos[:, None], theta))
+        kk = R(rope(kk, pos[:, None], theta))
 
         o = np.empty((kb, Hq, dh), dtype=np.float64)
         for hq in range(Hq):
@@ -258,21 +273,23 @@ def block_logits(dims, W, st: State, b: int, kb: int) -> np.ndarray:
             keys = np.concatenate([st.k_ring[l, b, g, slots], kk[:, g]], axis=0)
             vals = np.concatenate([st.v_ring[l, b, g, slots], vv[:, g]], axis=0)
             o[:, hq] = attend(q[:, hq], keys, vals)           # no mask inside the block
-        h = h + linear(o.reshape(kb, Hq * dh), W["w_o"][l])
+        h = h + linear(R(o.reshape(kb, Hq * dh)), W["w_o"][l])
 
-        y = rms_norm(h, W["mlp_norm"][l], eps)
+        y = R(rms_norm(h, W["mlp_norm"][l], eps))
         gu = linear(y, W["w_gate_up"][l])
-        h = h + linear(silu(gu[:, :F]) * gu[:, F:], W["w_down"][l])
+        h = h + linear(R(silu(gu[:, :F]) * gu[:, F:]), W["w_down"][l])
 
-    return linear(rms_norm(h, W["final_norm"], eps), W["lm_head"])   # [kb, V]
+    return linear(R(rms_norm(h, W["final_norm"], eps)), W["lm_head"])   # [kb, V]
 
 
-def draft_step(dims, W, st: State, want_logits: bool = True, block_len=None) -> Dict[str, np.ndarray]:
+def draft_step(dims, W, st: State, want_logits: bool = True, block_len=None,
+               act_round=None) -> Dict[str, np.ndarray]:
     """One forward of the draft transformer over the block of every sequence.
 
     block_len: per-sequence block length k_b (default k for all).  Returns draft
     [B, k] (argmax, smallest id on ties; -1 past k_b), logits [B, k, V] (NaN past
     k_b) and margin [B, k] (top-1 minus top-2 logit; inf past k_b).
+    act_round: precision study only (see the module notes); None = exact.
     """
     B, k, V = st.ctx_len.shape[0], dims.block_k, dims.vocab
     kb = block_lengths(dims, B, block_len)
@@ -283,7 +300,7 @@ def draft_step(dims, W, st: State, want_logits: bool = True, block_len=None) -> 
         n = int(kb[b])
         if n == 0:
             continue
-        zb = block_logits(dims, W, st, b, n)
+        zb = block_logits(dims, W, st, b, n, act_round=act_round)
         z[b, :n] = zb
         draft[b, :n] = np.argmax(zb, axis=-1)                       # first max = smallest id
         top2 = np.sort(zb, axis=-1)[:, -2:]

@@ -5,9 +5,14 @@ the same seeded inputs, step by step, with the parity rules:
   bit-exact wherever the oracle's top-1/top-2 margin is >= 1e-3;
 * bf16 drafters: max |z_gpu - z_ref| <= 0.05; drafts bit-exact wherever the
   oracle's margin is >= 0.1;
-* accepted lengths, emitted tokens, committed lengths and anchors bit-exact for
-  every sequence whose deciding positions (0 .. min(a, k-1)) all pass the margin
-  gate; K/V rows of the committed window within the logit tolerance.
+* greedy verification is integer work, so for every sampled sequence the accepted
+  length, emitted tokens, committed length and anchor the GPU produced from its
+  own drafts and the planted target tokens must equal what the oracle's
+  verify_commit makes of those same drafts and tokens, with no margin gate;
+* accepted lengths, emitted tokens, committed lengths and anchors also bit-exact
+  against the oracle's own trajectory for every sequence whose deciding positions
+  (0 .. min(a, k-1)) all pass the margin gate; K/V rows of the committed window
+  within the logit tolerance.
 The oracle plants the target tokens from its own drafts; a sequence whose GPU
 accepted length differs at a low-margin position is re-synchronised to the
 oracle's committed length and anchor (counted as excluded).
@@ -68,10 +73,21 @@ class StepReport:
     kv_ref_max: float
     kv_ok: bool
     accept: List[int] = field(default_factory=list)
+    seqs_verified: int = 0       # sequences whose verify/commit was compared with no gate
+    verify_mismatch: int = 0     # ... and disagreed with the oracle's verify_commit
 
     @property
     def ok(self) -> bool:
-        return self.logits_ok and self.draft_mismatch == 0 and self.state_mismatch == 0 and self.kv_ok
+        return (self.logits_ok and self.draft_mismatch == 0 and self.state_mismatch == 0 and self.kv_ok
+                and self.verify_mismatch == 0)
+
+
+def integer_state(ctx_len, anchor, dims) -> "orc.State":
+    """Oracle state carrying only the integer part (committed lengths, anchors):
+    the K/V rings are empty arrays, which verify_commit's rollback indexes freely."""
+    n = len(ctx_len)
+    ring = np.empty((1, n, 1, dims.cache_slots, 0))
+    return orc.State(ring, ring.copy(), np.array(ctx_len, np.int64), np.array(anchor, np.int64))
 
 
 @dataclass
@@ -100,8 +116,12 @@ class SampledReport:
 class ParityRun:
     def __init__(self, dims: Dims, W, ctx_start: Sequence[int], anchors: Sequence[int],
                  prefill_rows: Sequence[int], sample: Optional[Sequence[int]] = None, seed: int = 0,
-                 check_kv: bool = True):
-        self.d, self.W, self.seed, self.check_kv = dims, W, seed, check_kv
+                 check_kv: bool = True, poison: bool = False):
+        """poison: before every library call fill the workspace's scratch with NaN, and
+        after every verification the ring slots no window reaches (dflash_debug_poison),
+        so any read of stale memory shows in the results."""
+        self.d, self.W, self.seed, self.check_kv, self.poison = dims, W, seed, check_kv, poison
+        self.last = {}
         self.Wn = oracle_weights(W)
         if "packed" not in W:
             bd.pack_weights(dims, W)
@@ -124,6 +144,7 @@ class ParityRun:
             say(f"[parity] sink rows 0..{dims.sink - 1} (B={B})")
             self.cache["ctx_len"].zero_()
             sr = torch.full((B,), dims.sink, dtype=torch.int32, device="cuda")
+            self._poison()
             bd.dflash_fuse_inject(dims, W, sink_taps, sr, dims.sink, True, self.cache, self.ws)
             self.cache["ctx_len"].copy_(torch.as_tensor(p0, dtype=torch.int32))
             torch.cuda.synchronize()
@@ -138,6 +159,7 @@ class ParityRun:
             for r0 in range(0, n_pre, n_max):
                 chunk = taps[:, r0:r0 + n_max].contiguous()
                 n_rows = torch.as_tensor(np.clip(pre - r0, 0, chunk.shape[1]), dtype=torch.int32).cuda()
+                self._poison()
                 bd.dflash_fuse_inject(dims, W, chunk, n_rows, chunk.shape[1], True, self.cache, self.ws)
             torch.cuda.synchronize()
         if n_pre > 0:
@@ -146,6 +168,11 @@ class ParityRun:
 
     def dev_error(self) -> int:
         return int(self.cache["dev_error"].item())
+
+    def _poison(self, ring: bool = False) -> None:
+        if self.poison:
+            bd.dflash_debug_poison(self.d, self.cache, self.ws,
+                                   bd.POISON_WORKSPACE | (bd.POISON_RING if ring else 0))
 
     def _kv_error(self):
         """Largest |K/V| error over the committed window rows of the sampled sequences."""
@@ -181,6 +208,7 @@ class ParityRun:
         kb = np.full(d.batch, k, np.int64) if kb is None else np.asarray(kb, np.int64)
         taps = synth.make_taps(d, k + 1, seed=self.seed, stream=1 + self.step_idx, device="cuda")
         n_rows = torch.as_tensor(kb + 1, dtype=torch.int32, device="cuda")
+        self._poison()
         bd.dflash_fuse_inject(d, self.W, taps, n_rows, k + 1, False, self.cache, self.ws)
         orc.fuse_inject(d, self.Wn, self.st, taps[s].float().cpu().numpy(), kb[s] + 1, commit=False)
 
@@ -209,8 +237,10 @@ class ParityRun:
         draft = torch.empty((B, k), dtype=torch.int32, device="cuda")
         logits = torch.empty((B, k, V), dtype=torch.float32, device="cuda")
         lse = torch.empty((B, k), dtype=torch.float32, device="cuda")
+        self._poison()
         bd.dflash_draft_step_sampled(d, W, self.cache, smp, draft, logits, lse, self.ws)
         torch.cuda.synchronize()
+        self.last = {"draft": draft.clone(), "logits": logits.clone(), "lse": lse.clone()}
         o = orc.draft_step(d, self.Wn, self.st, block_len=kb[s])
         zr = o["logits"]
         sd = sp.sample_drafts(zr, T, seed, step, seq_ids=s, block_len=kb[s])
@@ -239,8 +269,10 @@ class ParityRun:
         self._inject_block(kb)
         acc = torch.empty(B, dtype=torch.int32, device="cuda")
         out = torch.empty((B, k + 1), dtype=torch.int32, device="cuda")
+        self._poison()
         bd.dflash_verify_sampled(d, smp, draft, logits, lse, tgt, self.cache, acc, out, self.ws)
         torch.cuda.synchronize()
+        self.last.update(accept=acc.clone(), out=out.clone())
         r = sp.verify_sampled(xr, zr, tgt[s].cpu().numpy().astype(np.float64), T, seed, step, seq_ids=s,
                               block_len=kb[s])
         sp.commit_sampled(d, self.st, r, block_len=kb[s])
@@ -263,6 +295,8 @@ class ParityRun:
                 excluded += 1
                 self.cache["ctx_len"][b] = int(self.st.ctx_len[j])
                 self.cache["anchor"][b] = int(self.st.anchor[j])
+        # rolled-back rows (after any re-synchronisation of the committed lengths)
+        self._poison(ring=True)
         kv_err, kv_max = self._kv_error()
         self.step_idx += 1
         # log-sum-exp is 1-Lipschitz in the max norm: |d lse| <= max |dz| / T
@@ -280,10 +314,14 @@ class ParityRun:
         kb = self._set_block_len(block_len)
         a_star = np.minimum(np.asarray(a_star, np.int64), kb)
         say(f"[parity] step {self.step_idx}: draft_step B={B} k={k} V={V} kb={list(kb[:8])}")
+        ctx_before = self.cache["ctx_len"][s].cpu().numpy()
+        anc_before = self.cache["anchor"][s].cpu().numpy()
         draft = torch.empty((B, k), dtype=torch.int32, device="cuda")
         logits = torch.empty((B, k, V), dtype=torch.float32, device="cuda")
+        self._poison()
         bd.dflash_draft_step(d, W, self.cache, draft, logits, self.ws)
         torch.cuda.synchronize()
+        self.last = {"draft": draft.clone(), "logits": logits.clone()}
         o = orc.draft_step(d, self.Wn, self.st, block_len=kb[s])
         zg = logits[s].cpu().numpy().astype(np.float64)
         dg = draft[s].cpu().numpy().astype(np.int64)
@@ -302,12 +340,14 @@ class ParityRun:
         taps = synth.make_taps(d, k + 1, seed=self.seed, stream=1 + self.step_idx, device="cuda")
         n_rows = torch.as_tensor(kb + 1, dtype=torch.int32, device="cuda")
         say(f"[parity] step {self.step_idx}: fuse_inject + verify_commit")
+        self._poison()
         bd.dflash_fuse_inject(d, W, taps, n_rows, k + 1, False, self.cache, self.ws)
         acc = torch.empty(B, dtype=torch.int32, device="cuda")
         out = torch.empty((B, k + 1), dtype=torch.int32, device="cuda")
         Tt = torch.as_tensor(T, dtype=torch.int32).cuda()
         bd.dflash_verify_commit(d, draft, Tt, self.cache, acc, out)
         torch.cuda.synchronize()
+        self.last.update(accept=acc.clone(), out=out.clone())
         orc.fuse_inject(d, self.Wn, self.st, taps[s].float().cpu().numpy(), kb[s] + 1, commit=False)
         r = orc.verify_commit(d, self.st, np.maximum(dr, 0), T[s], block_len=kb[s])
 
@@ -315,6 +355,15 @@ class ParityRun:
         out_g = out[s].cpu().numpy()
         ctx_g = self.cache["ctx_len"][s].cpu().numpy()
         anc_g = self.cache["anchor"][s].cpu().numpy()
+        # verify/commit of the GPU's own drafts against the same targets, every
+        # sampled sequence, no margin gate (integer work: must be bit-exact)
+        ist = integer_state(ctx_before, anc_before, d)
+        ri = orc.verify_commit(d, ist, dg, T[s], block_len=kb[s])
+        verify_mism = 0
+        for j in range(len(s)):
+            same = (acc_g[j] == ri["accept_len"][j] and np.array_equal(out_g[j], ri["out_tokens"][j])
+                    and ctx_g[j] == ist.ctx_len[j] and anc_g[j] == ist.anchor[j])
+            verify_mism += int(not same)
         checked = excluded = state_mism = 0
         for j, b in enumerate(s):
             a_ref = int(r["accept_len"][j])
@@ -329,13 +378,17 @@ class ParityRun:
                 self.cache["ctx_len"][b] = int(self.st.ctx_len[j])
                 self.cache["anchor"][b] = int(self.st.anchor[j])
 
+        # rolled-back rows (after any re-synchronisation of the committed lengths)
+        self._poison(ring=True)
         kv_err, kv_max = self._kv_error()
         self.step_idx += 1
         rep = StepReport(err, ref_max, self.tol.logit_ok(err, ref_max), int(gate.sum()), gate.size,
                          mism, checked, excluded, state_mism, kv_err, kv_max,
-                         self.tol.logit_ok(kv_err, max(kv_max, 1e-30)), list(map(int, acc_g)))
+                         self.tol.logit_ok(kv_err, max(kv_max, 1e-30)), list(map(int, acc_g)),
+                         len(s), verify_mism)
         say(f"[parity] step {self.step_idx - 1}: logit_err={err:.3g} (ref max {ref_max:.3g}) "
             f"drafts {rep.drafts_checked}/{rep.drafts_total} gated, mismatches {mism}; "
+            f"verify on own drafts {len(s) - verify_mism}/{len(s)} exact; "
             f"seqs checked {checked}, excluded {excluded}, state mismatches {state_mism}; "
             f"kv_err={kv_err:.3g} accept={rep.accept[:8]}")
         return rep

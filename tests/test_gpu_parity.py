@@ -35,6 +35,7 @@ def _assert_ok(reps):
         assert r.logits_ok, f"step {i}: logit error {r.logit_err} (ref max {r.logit_ref_max})"
         assert r.draft_mismatch == 0, f"step {i}: {r.draft_mismatch} gated draft mismatches"
         assert r.state_mismatch == 0, f"step {i}: {r.state_mismatch} state mismatches"
+        assert r.verify_mismatch == 0, f"step {i}: verify/commit of the GPU drafts differs for {r.verify_mismatch}"
         assert r.kv_ok, f"step {i}: kv error {r.kv_err}"
 
 
@@ -331,3 +332,42 @@ def test_large_vocab_lm_head_partial_rows_and_block_lengths():
             run.step([0, 2, 3])]
     assert run.dev_error() == 0
     _assert_ok(reps)
+
+
+def test_prefill_chunk_longer_than_ring():
+    """One fuse_inject call carrying more rows per sequence than the ring holds: the
+    cache must end as if the rows were written in position order (each ring slot
+    keeps the last of its rows), for a plain ring (bf16 GQA) and with an attention
+    sink whose positions arrive in the same call (fp32)."""
+    d = replace(configs.C1.dims, batch=3, block_k=4, n_layers=2, n_q_heads=4, n_kv_heads=2, window=16,
+                cache_slots=20, dtype=BF16, max_inject_rows=64)
+    say(f"[test] prefill chunk > ring {d}")
+    _assert_ok(_run(d, [50, 61, 21], [50, 61, 21], [[4, 0, 2], [1, 3, 4]]))
+    d = replace(configs.C1.dims, batch=2, block_k=4, n_layers=1, window=12, sink=2, cache_slots=2 + 12 + 4,
+                max_inject_rows=64)
+    say(f"[test] prefill chunk > ring, sink in the same call {d}")
+    _assert_ok(_run(d, [45, 33], [45, 33], [[2, 4], [4, 1]]))
+
+
+def test_fp16_overflow_saturates_and_sets_the_error_word():
+    """bf16 drafter whose SwiGLU products exceed the fp16 range (gate/up weights
+    scaled up): the kernels finish, the stored values saturate (finite logits) and
+    dev_error carries the overflow bit; the same drafter at the normal scale leaves
+    the word clear."""
+    d = replace(configs.C1.dims, dtype=BF16)
+    for scale, expect in ((1.0, 0), (2000.0, bd.DEVERR_OVERFLOW)):
+        W = synth.make_weights(d, seed=0, device="cuda")
+        W["w_gate_up"] = (W["w_gate_up"].float() * scale).to(torch.bfloat16)
+        bd.pack_weights(d, W)
+        cache = bd.alloc_cache(d, ctx_len=[0], anchor=[3])
+        ws = bd.alloc_workspace(d)
+        taps = synth.make_taps(d, 32, seed=0, device="cuda")
+        bd.dflash_fuse_inject(d, W, taps, torch.tensor([32], dtype=torch.int32, device="cuda"), 32, True, cache, ws)
+        draft = torch.empty((1, d.block_k), dtype=torch.int32, device="cuda")
+        logits = torch.empty((1, d.block_k, d.vocab), dtype=torch.float32, device="cuda")
+        bd.dflash_draft_step(d, W, cache, draft, logits, ws)
+        torch.cuda.synchronize()
+        err = int(cache["dev_error"].item())
+        say(f"[test] gate/up x{scale}: dev_error {err}, max |logit| {float(logits.abs().max()):.3g}")
+        assert err == expect
+        assert bool(torch.isfinite(logits).all())
