@@ -18,6 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdflash.so")
 
 DFLASH_OK, DFLASH_E_INVALID, DFLASH_E_UNSUPPORTED, DFLASH_E_WORKSPACE, DFLASH_E_HIP = 0, -1, -2, -3, -4
+DFLASH_E_TOO_LARGE = -5
+NOALLOC_SCRATCH_BYTES = 96 << 20
 DEVERR_TOKEN, DEVERR_ROWS, DEVERR_CTXLEN, DEVERR_RANGE, DEVERR_BLOCK, DEVERR_OVERFLOW = 1, 2, 4, 8, 16, 32
 
 _INT_FIELDS = ("batch", "block_k", "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim",
@@ -64,7 +66,7 @@ EXPORTED = ("dflash_workspace_bytes", "dflash_status_string", "dflash_packed_byt
             "dflash_pack_weights", "dflash_fuse_inject", "dflash_draft_step",
             "dflash_verify_commit", "dflash_draft_step_timed", "dflash_draft_step_sampled",
             "dflash_draft_step_sampled_timed", "dflash_verify_sampled", "dflash_adapt_block_len",
-            "dflash_debug_poison")
+            "dflash_debug_poison", "dflash_draft_step_noalloc")
 POISON_RING, POISON_WORKSPACE = 1, 2
 
 
@@ -112,6 +114,9 @@ def lib() -> ctypes.CDLL:
     L.dflash_adapt_block_len.restype = ctypes.c_int
     L.dflash_debug_poison.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashCache), P, S, I, P]
     L.dflash_debug_poison.restype = ctypes.c_int
+    L.dflash_draft_step_noalloc.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashWeights),
+                                            ctypes.POINTER(DflashCache), P, P, P]
+    L.dflash_draft_step_noalloc.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -207,6 +212,14 @@ def dflash_draft_step(dims: Dims, weights, cache, draft: torch.Tensor,
                                  _ptr(logits_out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     _check("dflash_draft_step", st)
+
+
+def dflash_draft_step_noalloc(dims: Dims, weights, cache, draft: torch.Tensor,
+                              logits_out: Optional[torch.Tensor], stream=None) -> None:
+    ds, ws, cs = dims_struct(dims), weights_struct(weights), cache_struct(cache)
+    st = lib().dflash_draft_step_noalloc(ctypes.byref(ds), ctypes.byref(ws), ctypes.byref(cs), _ptr(draft),
+                                         _ptr(logits_out), _stream(stream))
+    _check("dflash_draft_step_noalloc", st)
 
 
 def dflash_draft_step_timed(dims: Dims, weights, cache, draft: torch.Tensor,

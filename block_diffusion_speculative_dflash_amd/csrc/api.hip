@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dflash.h"
 #include "internal.h"
@@ -366,10 +367,13 @@ bool sampling_ok(const dflash_sampling* smp) {
 
 // smp == nullptr: greedy drafts (argmax); otherwise Gumbel-max draws at temperature
 // smp->temperature, raw logits to logits_out and row log-sum-exps of logits / T to lse_out.
+// zero_counters: clear the workspace's arrival counters before the first kernel (the
+// shared scratch of the no-allocation entry point, whose previous contents are not
+// the caller's to vouch for).
 int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_cache* cache,
                const dflash_sampling* smp, int32_t* draft, float* logits_out, float* lse_out,
                void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t ev0,
-               hipEvent_t ev1) {
+               hipEvent_t ev1, bool zero_counters = false) {
   if (!dims_ok(dims) || w == nullptr || cache == nullptr || draft == nullptr) return DFLASH_E_INVALID;
   if (smp != nullptr && (!sampling_ok(smp) || logits_out == nullptr || lse_out == nullptr || !aligned4(lse_out)))
     return DFLASH_E_INVALID;
@@ -394,6 +398,11 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   const int hq_dh = d.n_q_heads * d.head_dim;
   const size_t layer_cache = size_t(B) * d.n_kv_heads * d.cache_slots * d.head_dim * e;
   auto gain = [&](const void* base, int l) { return static_cast<const char*>(base) + size_t(l) * D * e; };
+
+  if (zero_counters) {
+    DF_CHECK(launch_fill_zero(c.at<void>(L.counters), L.keys - L.counters, stream));
+    DF_CHECK(launch_fill_zero(c.at<void>(L.attn_cnt), L.attn_o - L.attn_cnt, stream));
+  }
 
   EmbedArgs em{};
   em.anchor = cache->anchor;
@@ -553,6 +562,43 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   return DFLASH_OK;
 }
 
+// ---------------------------------------------------------------------------
+// No-allocation draft step: the workspace is a static device array of the library
+// (one per GPU, held until the process ends) instead of a caller's buffer.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = DFLASH_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per device
+// (each device holds its own copy of the array).  The host-side name of the array is
+// only a stand-in and never reaches a kernel.
+void* scratch_ptr(int* status) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = DFLASH_E_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      *status = DFLASH_E_HIP;
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  *status = DFLASH_OK;
+  return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -575,6 +621,7 @@ const char* dflash_status_string(int status) {
     case DFLASH_E_UNSUPPORTED: return "unsupported configuration";
     case DFLASH_E_WORKSPACE: return "workspace missing or too small";
     case DFLASH_E_HIP: return "HIP runtime error";
+    case DFLASH_E_TOO_LARGE: return "workspace of these dims exceeds the no-allocation scratch";
     default: return "unknown status";
   }
 }
@@ -699,6 +746,17 @@ int dflash_draft_step_sampled(const dflash_dims* dims, const dflash_weights* w, 
   if (sampling == nullptr) return DFLASH_E_INVALID;
   return draft_impl(dims, w, cache, sampling, draft, logits_out, lse_out, workspace, workspace_bytes, stream,
                     nullptr, nullptr);
+}
+
+int dflash_draft_step_noalloc(const dflash_dims* dims, const dflash_weights* w, const dflash_cache* cache,
+                              int32_t* draft, float* logits_out, hipStream_t stream) {
+  if (!dims_ok(dims)) return DFLASH_E_INVALID;
+  if (layout(*dims).total > kScratchBytes) return DFLASH_E_TOO_LARGE;
+  int st = DFLASH_OK;
+  void* ws = scratch_ptr(&st);
+  if (st != DFLASH_OK) return st;
+  return draft_impl(dims, w, cache, nullptr, draft, logits_out, nullptr, ws, kScratchBytes, stream, nullptr,
+                    nullptr, true);
 }
 
 int dflash_draft_step_timed(const dflash_dims* dims, const dflash_weights* w,

@@ -158,5 +158,6 @@ struct PoisonRingArgs {
 };
 hipError_t launch_poison_ring(const PoisonRingArgs& a, hipStream_t stream);
 hipError_t launch_fill_ones(void* p, size_t bytes, hipStream_t stream);  // p, bytes: multiples of 16
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);  // p, bytes: multiples of 16
 
 }  // namespace dflash

@@ -223,20 +223,25 @@ hipError_t launch_poison_ring(const PoisonRingArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(kThreads) void fill_ones_kernel(uint4* p, size_t n) {
-  const uint4 ones = make_uint4(~0u, ~0u, ~0u, ~0u);
+// Fill of 16-byte words with one value (a kernel, not hipMemsetAsync, so callers may
+// capture it into a graph).
+__global__ __launch_bounds__(kThreads) void fill_kernel(uint4* p, size_t n, unsigned v) {
+  const uint4 w = make_uint4(v, v, v, v);
   for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += static_cast<size_t>(gridDim.x) * blockDim.x)
-    p[i] = ones;
+    p[i] = w;
 }
 
-hipError_t launch_fill_ones(void* p, size_t bytes, hipStream_t stream) {
+static hipError_t launch_fill(void* p, size_t bytes, unsigned v, hipStream_t stream) {
   const size_t n = bytes / 16;
   if (n == 0) return hipSuccess;
   const size_t blocks = std::min<size_t>((n + kThreads - 1) / kThreads, 4096);
-  hipLaunchKernelGGL(fill_ones_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                     static_cast<uint4*>(p), n);
+  hipLaunchKernelGGL(fill_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                     static_cast<uint4*>(p), n, v);
   return hipGetLastError();
 }
+
+hipError_t launch_fill_ones(void* p, size_t bytes, hipStream_t stream) { return launch_fill(p, bytes, ~0u, stream); }
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) { return launch_fill(p, bytes, 0u, stream); }
 
 }  // namespace dflash

@@ -66,7 +66,8 @@ typedef enum {
   DFLASH_E_INVALID = -1,     /* bad dims, NULL or misaligned pointer, bad argument */
   DFLASH_E_UNSUPPORTED = -2, /* valid but not handled by this build (e.g. head_dim) */
   DFLASH_E_WORKSPACE = -3,   /* workspace NULL or smaller than dflash_workspace_bytes */
-  DFLASH_E_HIP = -4          /* a HIP runtime call or kernel launch failed */
+  DFLASH_E_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  DFLASH_E_TOO_LARGE = -5    /* dflash_draft_step_noalloc: the dims need more than its scratch */
 } dflash_status;
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
@@ -312,6 +313,21 @@ typedef struct {
 int dflash_adapt_block_len(const dflash_dims *dims, const dflash_adapt_params *params,
                            const int32_t *accept_len, const dflash_cache *cache, float *ema,
                            int32_t *off_left, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): dflash_draft_step without
+ * a workspace argument.  Its workspace is a static device array of the library,
+ * DFLASH_NOALLOC_SCRATCH_BYTES bytes on every GPU the library runs on, held until
+ * the process ends; the call allocates nothing.  Dims whose workspace
+ * (dflash_workspace_bytes) exceeds that size return DFLASH_E_TOO_LARGE with nothing
+ * enqueued (96 MiB covers the batch-1 and batch-8 drafters of hidden 4096).  Every
+ * call on one GPU uses the same array and clears its counters first: calls that
+ * overlap on one GPU (two streams, two threads) race and must be serialised by the
+ * caller.  Results are those of dflash_draft_step. */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int dflash_draft_step_noalloc(const dflash_dims *dims, const dflash_weights *w,
+                              const dflash_cache *cache, int32_t *draft, float *logits_out,
+                              hipStream_t stream);
 
 /* Same as dflash_draft_step, and records head_begin / head_end on `stream` right
  * before and after the fused final-norm + LM-head + argmax kernel, so a caller can
