@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--adaptive", action="store_true",
                    help="per-sequence block lengths chosen every step by the block-size controller "
                         "(dflash_adapt_block_len, default thresholds) from the accepted lengths")
+    p.add_argument("--persistent", action="store_true",
+                   help="greedy draft step as one persistent kernel per layer (dflash_draft_step_persistent; "
+                        "bf16 drafters with <= 64 block rows)")
     p.add_argument("--sink", type=int, default=0,
                    help="attention sink: positions 0..S-1 stay visible beside the window "
                         "(adds S cache slots; the sink rows are injected before the prefill)")
@@ -189,7 +192,7 @@ def measure(args, wl, headline: bool):
     sampled = args.temperature > 0
     adaptive = args.adaptive
     loop = harness.RoundLoop(d, W, cache, ws, a_tab, fill, seed=args.seed, temperature=args.temperature,
-                             adaptive=adaptive, device=dev)
+                             adaptive=adaptive, persistent=args.persistent, device=dev)
 
     # eager warm-up of every code path, then capture one graph per taps slot
     stream = torch.cuda.Stream()
@@ -315,6 +318,7 @@ def measure(args, wl, headline: bool):
                 + (", N(0,4) target logits with planted acceptance)" if sampled else ")"),
         "config": {"workload": wl.name},
         "options": {"accept": [kind, q], "temperature": args.temperature, "adaptive": adaptive,
+                    "persistent": bool(args.persistent),
                     "sink": d.sink, "context": [int(ctx.min()), int(ctx.max())]},
         "accepted_tok_s": round(accepted / elapsed, 1),
         "committed_tok_s": round(committed / elapsed, 1),

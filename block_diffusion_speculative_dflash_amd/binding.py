@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(PKG, "libdflash.so")
 DFLASH_OK, DFLASH_E_INVALID, DFLASH_E_UNSUPPORTED, DFLASH_E_WORKSPACE, DFLASH_E_HIP = 0, -1, -2, -3, -4
 DFLASH_E_TOO_LARGE = -5
 NOALLOC_SCRATCH_BYTES = 96 << 20
-DEVERR_TOKEN, DEVERR_ROWS, DEVERR_CTXLEN, DEVERR_RANGE, DEVERR_BLOCK, DEVERR_OVERFLOW = 1, 2, 4, 8, 16, 32
+DEVERR_TOKEN, DEVERR_ROWS, DEVERR_CTXLEN, DEVERR_RANGE, DEVERR_BLOCK, DEVERR_OVERFLOW, DEVERR_TIMEOUT = \
+    1, 2, 4, 8, 16, 32, 64
 
 _INT_FIELDS = ("batch", "block_k", "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim",
                "ffn", "vocab", "n_taps", "tap_dim", "window", "cache_slots", "dtype",
@@ -66,7 +67,7 @@ EXPORTED = ("dflash_workspace_bytes", "dflash_status_string", "dflash_packed_byt
             "dflash_pack_weights", "dflash_fuse_inject", "dflash_draft_step",
             "dflash_verify_commit", "dflash_draft_step_timed", "dflash_draft_step_sampled",
             "dflash_draft_step_sampled_timed", "dflash_verify_sampled", "dflash_adapt_block_len",
-            "dflash_debug_poison", "dflash_draft_step_noalloc")
+            "dflash_debug_poison", "dflash_draft_step_noalloc", "dflash_draft_step_persistent")
 POISON_RING, POISON_WORKSPACE = 1, 2
 
 
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.dflash_draft_step.argtypes = [ctypes.POINTER(DflashDims), ctypes.POINTER(DflashWeights),
                                     ctypes.POINTER(DflashCache), P, P, P, S, P]
     L.dflash_draft_step.restype = ctypes.c_int
+    L.dflash_draft_step_persistent.argtypes = L.dflash_draft_step.argtypes
+    L.dflash_draft_step_persistent.restype = ctypes.c_int
     L.dflash_draft_step_timed.argtypes = L.dflash_draft_step.argtypes + [P, P]
     L.dflash_draft_step_timed.restype = ctypes.c_int
     L.dflash_verify_commit.argtypes = [ctypes.POINTER(DflashDims), P, P, ctypes.POINTER(DflashCache),
@@ -212,6 +215,15 @@ def dflash_draft_step(dims: Dims, weights, cache, draft: torch.Tensor,
                                  _ptr(logits_out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     _check("dflash_draft_step", st)
+
+
+def dflash_draft_step_persistent(dims: Dims, weights, cache, draft: torch.Tensor,
+                                 logits_out: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
+    ds, ws, cs = dims_struct(dims), weights_struct(weights), cache_struct(cache)
+    st = lib().dflash_draft_step_persistent(ctypes.byref(ds), ctypes.byref(ws), ctypes.byref(cs), _ptr(draft),
+                                            _ptr(logits_out), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dflash_draft_step_persistent", st)
 
 
 def dflash_draft_step_noalloc(dims: Dims, weights, cache, draft: torch.Tensor,

@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
 HARNESS_LIB = os.path.join(PKG, "libdflash_harness.so")
 
-LIB_SOURCES = ["api.hip", "gemm.hip", "gemm_tiled.hip", "attention.hip", "misc.hip", "pack.hip", "sampling.hip"]
+LIB_SOURCES = ["api.hip", "gemm.hip", "gemm_tiled.hip", "attention.hip", "misc.hip", "pack.hip", "sampling.hip",
+               "persist.hip"]
 HARNESS_SOURCES = ["harness_plant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -33,7 +34,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
 
 # Per-source flags.  attention.hip: MFMA accumulators in VGPRs, so the online-softmax
 # rescale of the output accumulators needs no moves between AGPRs and VGPRs.
-SOURCE_FLAGS = {"attention.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+                "persist.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

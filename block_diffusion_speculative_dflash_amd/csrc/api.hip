@@ -19,6 +19,7 @@ constexpr int kGemmCounters = 1 << 16;
 constexpr int kSplitBelow = 256;                   // streaming GEMM: split K only below this many tiles (one per CU)
 constexpr int kCUs = 256;
 constexpr int kTiledMinRows = 128;                 // bf16 GEMMs with at least this many rows go tiled
+constexpr int kBarriersPerLayer = 6 * 64;          // persistent layer kernel: words of its 6 grid barriers
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -121,7 +122,7 @@ size_t partial_bytes(const dflash_dims& d);
 
 struct Layout {
   size_t h, xa, ssq, q, kb, vb, o, act, cu, ssq_c, partials, counters, keys, attn_cnt, attn_o,
-      attn_ml, lse_part, v_part, v_cnt, v_rowlse, v_dec, v_keys, total;
+      attn_ml, lse_part, v_part, v_cnt, v_rowlse, v_dec, v_keys, barriers, total;
   int v_chunks;
   int np_d, S_d, S_o, S_f;
   AttnPlan ap;
@@ -153,7 +154,11 @@ Layout layout(const dflash_dims& d) {
   L.partials = take(partial_bytes(d));
   L.counters = take(size_t(kGemmCounters) * 4);
   L.keys = take(Mb * size_t(cdiv(d.vocab, kBN)) * 8);  // LM head: best key per row and column tile
-  const size_t groups = size_t(d.batch) * d.n_kv_heads * L.ap.n_rb;
+  // attention split partials per (sequence, kv head, row block): row blocks of the
+  // separate kernel (up to 4 row tiles) or of the persistent layer kernel (up to 2)
+  const int row_tiles = cdiv(d.n_q_heads / d.n_kv_heads * d.block_k, 16);
+  const int n_rb_alloc = std::max(L.ap.n_rb, cdiv(row_tiles, std::min(2, row_tiles)));
+  const size_t groups = size_t(d.batch) * d.n_kv_heads * n_rb_alloc;
   L.attn_cnt = take(groups * 4);
   L.attn_o = take(groups * L.ap.max_splits * 64 * d.head_dim * 4);
   L.attn_ml = take(groups * L.ap.max_splits * 64 * 2 * 4);
@@ -165,6 +170,7 @@ Layout layout(const dflash_dims& d) {
   L.v_rowlse = take(size_t(d.batch) * (d.block_k + 1) * 4);
   L.v_dec = take(size_t(d.batch) * 16);
   L.v_keys = take(size_t(d.batch) * 2 * kKeyStride * 8);
+  L.barriers = take(size_t(d.n_layers) * kBarriersPerLayer * 4);  // persistent layer kernel
   L.total = off;
   return L;
 }
@@ -344,7 +350,8 @@ GemmArgs base_args(const Ctx& c) {
     if ((call) != hipSuccess) return DFLASH_E_HIP; \
   } while (0)
 
-int run_gemm(int epi, const Ctx& c, GemmArgs a, bool allow_split, hipStream_t s) {
+// The plan of one GEMM, with its split fields copied into the arguments.
+GemmPlan plan_gemm(int epi, const Ctx& c, GemmArgs& a, bool allow_split) {
   const size_t cap = partial_bytes(c.d);
   // the tiled fusion GEMM gathers whole 16-byte pieces of tap rows
   const bool fuse_ok = epi != EPI_FUSE || (a.K == a.S * kKStep && a.lda % 8 == 0);
@@ -355,8 +362,35 @@ int run_gemm(int epi, const Ctx& c, GemmArgs a, bool allow_split, hipStream_t s)
   a.piece_base = p.tiled ? 0 : p.piece_base;
   a.piece_extra = p.tiled ? 0 : p.piece_extra;
   a.m_tiles = p.m_tiles;
+  return p;
+}
+
+int run_gemm(int epi, const Ctx& c, GemmArgs a, bool allow_split, hipStream_t s) {
+  const GemmPlan p = plan_gemm(epi, c, a, allow_split);
   if (p.tiled) DF_CHECK(launch_gemm_tiled(epi, p, a, s));
   else DF_CHECK(launch_gemm(epi, is_f32(c.d), p, a, s));
+  return DFLASH_OK;
+}
+
+// The separate streaming kernel's grid, as the persistent kernel's work items.
+PhaseGrid stream_grid(const GemmPlan& p) {
+  if (p.piece_base > 0) return PhaseGrid{p.n_tiles * p.piece_base + p.piece_extra, p.m_tiles, 1};
+  return PhaseGrid{p.n_tiles, p.m_tiles, p.splits};
+}
+
+// Compute units of the current device, looked up once per device.
+int device_cus(int* cus) {
+  static std::mutex mu;
+  static int n[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DFLASH_E_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (n[dev] == 0 && (hipDeviceGetAttribute(&n[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+                      n[dev] <= 0)) {
+    n[dev] = 0;
+    return DFLASH_E_HIP;
+  }
+  *cus = n[dev];
   return DFLASH_OK;
 }
 
@@ -370,10 +404,12 @@ bool sampling_ok(const dflash_sampling* smp) {
 // zero_counters: clear the workspace's arrival counters before the first kernel (the
 // shared scratch of the no-allocation entry point, whose previous contents are not
 // the caller's to vouch for).
+// persistent: every draft layer as one launch of the persistent layer kernel
+// (DFLASH_E_UNSUPPORTED, before anything is enqueued, for drafters it does not cover).
 int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_cache* cache,
                const dflash_sampling* smp, int32_t* draft, float* logits_out, float* lse_out,
                void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t ev0,
-               hipEvent_t ev1, bool zero_counters = false) {
+               hipEvent_t ev1, bool zero_counters = false, bool persistent = false) {
   if (!dims_ok(dims) || w == nullptr || cache == nullptr || draft == nullptr) return DFLASH_E_INVALID;
   if (smp != nullptr && (!sampling_ok(smp) || logits_out == nullptr || lse_out == nullptr || !aligned4(lse_out)))
     return DFLASH_E_INVALID;
@@ -395,6 +431,22 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   const size_t e = elem(d);
   const int D = d.hidden, k = d.block_k, B = d.batch, F = d.ffn;
   const int Mb = B * k;
+
+  // Persistent layer kernel: bf16 drafters whose block rows stay on the streaming GEMM,
+  // head_dim 128; attention with at most two 16-row tiles per workgroup (the same
+  // per-row arithmetic as the separate kernel, so the same results bitwise)
+  const int G = d.n_q_heads / d.n_kv_heads;
+  const int p_nw = std::min(2, cdiv(G * k, 16));
+  const int p_mt = Mb <= 16 ? 1 : (Mb <= 32 ? 2 : 4);
+  int p_capacity = 0;
+  if (persistent) {
+    if (f32 || use_tiled(d, Mb) || Mb > 64 || d.head_dim != 128) return DFLASH_E_UNSUPPORTED;
+    int cus = 0;
+    if (int st = device_cus(&cus)) return st;
+    p_capacity = persistent_capacity(p_mt, p_nw, cus);
+    if (p_capacity <= 0) return DFLASH_E_UNSUPPORTED;
+    DF_CHECK(launch_fill_zero(c.at<void>(L.barriers), size_t(d.n_layers) * kBarriersPerLayer * 4, stream));
+  }
   const int hq_dh = d.n_q_heads * d.head_dim;
   const size_t layer_cache = size_t(B) * d.n_kv_heads * d.cache_slots * d.head_dim * e;
   auto gain = [&](const void* base, int l) { return static_cast<const char*>(base) + size_t(l) * D * e; };
@@ -421,6 +473,17 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   DF_CHECK(launch_embed(f32, em, stream));
 
   for (int l = 0; l < d.n_layers; ++l) {
+    // persistent mode: the layer's four GEMMs and its attention are collected into one
+    // launch of the layer kernel; otherwise each runs as its own kernel
+    LayerArgs la{};
+    auto stage_gemm = [&](int slot, int epi, GemmArgs ga) -> int {
+      if (!persistent) return run_gemm(epi, c, ga, true, stream);
+      const GemmPlan gp = plan_gemm(epi, c, ga, true);
+      if (gp.tiled || gp.mt != p_mt) return DFLASH_E_UNSUPPORTED;
+      la.gemm[slot] = ga;
+      la.grid[slot] = stream_grid(gp);
+      return DFLASH_OK;
+    };
     // RMSNorm + fused QKV projection + RoPE
     GemmArgs a = base_args(c);
     a.A = c.at<void>(L.xa);
@@ -437,7 +500,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     a.out3 = c.at<void>(L.vb);
     a.rows_per_seq = k;
     a.ctx_len = cache->ctx_len;
-    if (int st = run_gemm(EPI_QKV, c, a, true, stream)) return st;
+    if (int st = stage_gemm(0, EPI_QKV, a)) return st;
 
     // block attention over window + block
     AttnArgs at{};
@@ -467,7 +530,17 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     at.rows_per_block = L.ap.rows;
     // long full-attention windows over many sequences: contexts may be ragged
     at.balance = L.ap.max_splits == 1 && B >= 16 && B <= kMaxBalanceBatch && d.window > 1024;
-    DF_CHECK(launch_attention(f32, at, stream));
+    if (!persistent) {
+      DF_CHECK(launch_attention(f32, at, stream));
+    } else {
+      // rows of at most two 16-row tiles per workgroup (256 threads, two key groups)
+      const int row_tiles = cdiv(G * k, 16);
+      at.rows_per_block = 16 * p_nw;
+      at.n_rb = cdiv(row_tiles, p_nw);
+      la.attn = at;
+      la.attn_items = B * d.n_kv_heads * at.n_rb * at.max_splits;
+      la.merge_items = at.max_splits > 1 ? B * d.n_kv_heads * at.n_rb * at.rows_per_block : 0;  // one row each
+    }
 
     // output projection + residual; produces the MLP's RMSNorm input
     a = base_args(c);
@@ -484,7 +557,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     a.gain = gain(w->mlp_norm, l);
     a.ssq_out = c.at<float>(L.ssq);
     a.np_out = L.np_d;
-    if (int st = run_gemm(EPI_RESID, c, a, true, stream)) return st;
+    if (int st = stage_gemm(1, EPI_RESID, a)) return st;
 
     // RMSNorm + gate/up projection + SwiGLU
     a = base_args(c);
@@ -499,7 +572,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     a.np_in = L.np_d;
     a.out = c.at<void>(L.act);
     a.out_steps = L.S_f;
-    if (int st = run_gemm(EPI_SWIGLU, c, a, true, stream)) return st;
+    if (int st = stage_gemm(2, EPI_SWIGLU, a)) return st;
 
     // down projection + residual; produces the next RMSNorm input
     a = base_args(c);
@@ -516,7 +589,15 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     a.gain = l + 1 < d.n_layers ? gain(w->attn_norm, l + 1) : w->final_norm;
     a.ssq_out = c.at<float>(L.ssq);
     a.np_out = L.np_d;
-    if (int st = run_gemm(EPI_RESID, c, a, true, stream)) return st;
+    if (int st = stage_gemm(3, EPI_RESID, a)) return st;
+
+    if (persistent) {
+      la.barrier = c.at<unsigned>(L.barriers) + size_t(l) * kBarriersPerLayer;
+      la.dev_error = cache->dev_error;
+      int items = std::max(la.attn_items, la.merge_items);
+      for (const PhaseGrid& pg : la.grid) items = std::max(items, pg.x * pg.y * pg.z);
+      DF_CHECK(launch_layer_persistent(la, p_mt, p_nw, std::min(items, p_capacity), stream));
+    }
   }
 
   // final RMSNorm + LM head + split-vocab argmax
@@ -757,6 +838,13 @@ int dflash_draft_step_noalloc(const dflash_dims* dims, const dflash_weights* w, 
   if (st != DFLASH_OK) return st;
   return draft_impl(dims, w, cache, nullptr, draft, logits_out, nullptr, ws, kScratchBytes, stream, nullptr,
                     nullptr, true);
+}
+
+int dflash_draft_step_persistent(const dflash_dims* dims, const dflash_weights* w, const dflash_cache* cache,
+                                 int32_t* draft, float* logits_out, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  return draft_impl(dims, w, cache, nullptr, draft, logits_out, nullptr, workspace, workspace_bytes, stream, nullptr,
+                    nullptr, false, true);
 }
 
 int dflash_draft_step_timed(const dflash_dims* dims, const dflash_weights* w,

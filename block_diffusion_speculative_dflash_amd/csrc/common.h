@@ -28,7 +28,12 @@ template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return stati
 
 // Device-detected error bits (the DFLASH_DEVERR_* values of the C header).
 constexpr uint32_t kErrToken = 1u, kErrRows = 2u, kErrCtxLen = 4u, kErrRange = 8u, kErrBlock = 16u,
-                   kErrOverflow = 32u;
+                   kErrOverflow = 32u, kErrTimeout = 64u;
+
+// Bound of every spin-wait on other workgroups (polls with a ~100-cycle sleep, about
+// a quarter of a second in all): a wait that runs out sets kErrTimeout and the kernel
+// exits rather than hang.
+constexpr long long kSpinLimit = 1ll << 22;
 
 // Conversion of an activation, q/k/v or K/V value to the compute type.  For fp16 a
 // finite value beyond the largest finite fp16 (65504) saturates to +-65504 instead
@@ -180,6 +185,60 @@ __device__ __forceinline__ float2 coherent_load2(const float* p) {
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return make_float2(__uint_as_float(static_cast<uint32_t>(u)), __uint_as_float(static_cast<uint32_t>(u >> 32)));
 }
+// 16 bytes as two device-coherent 8-byte loads / stores (the destination type V is
+// any 16-byte vector), and a device-coherent 2-byte store.
+template <typename V>
+__device__ __forceinline__ V coherent_load16(const void* p) {
+  static_assert(sizeof(V) == 16, "16-byte value");
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<void*>(p));
+  union {
+    unsigned long long u[2];
+    V v;
+  } x;
+  x.u[0] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  x.u[1] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return x.v;
+}
+template <typename V>
+__device__ __forceinline__ void coherent_store16(void* p, const V& v) {
+  static_assert(sizeof(V) == 16, "16-byte value");
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+  union {
+    unsigned long long u[2];
+    V v;
+  } x;
+  x.v = v;
+  __hip_atomic_store(q, x.u[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, x.u[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store(f16* p, f16 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned short*>(p), __builtin_bit_cast(unsigned short, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Stores and loads of data that another workgroup reads (or wrote) inside the same
+// kernel launch: device-coherent when COH, plain otherwise.
+template <bool COH, typename T>
+__device__ __forceinline__ void put(T* p, T v) {
+  if constexpr (COH) coherent_store(p, v);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ float get(const float* p) {
+  if constexpr (COH) return coherent_load(p);
+  else return *p;
+}
+template <bool COH, typename V>
+__device__ __forceinline__ V get16(const void* p) {
+  if constexpr (COH) return coherent_load16<V>(p);
+  else return *reinterpret_cast<const V*>(p);
+}
+template <bool COH, typename V>
+__device__ __forceinline__ void put16(void* p, const V& v) {
+  if constexpr (COH) coherent_store16(p, v);
+  else *reinterpret_cast<V*>(p) = v;
+}
+
 // All of this thread's memory operations have completed.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 // Arrival counter: returns true in exactly one thread block, the last of `expected`.

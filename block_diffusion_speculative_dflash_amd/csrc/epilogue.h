@@ -21,8 +21,9 @@
 namespace dflash {
 
 // hres: RESID only, the residual tile prefetched by the caller (row pass `it` of
-// this thread, 8 columns), or nullptr to read it here.
-template <typename TIN, int EPI, int BM, int NT>
+// this thread, 8 columns), or nullptr to read it here.  COH: the outputs (and the
+// residual read here) are device-coherent, for a consumer inside the same launch.
+template <typename TIN, int EPI, int BM, int NT, bool COH = false>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*tile)[kBN + 4], const float* rs,
                                               int tile_n, int m0, const float (*hres)[8]) {
   typedef typename ActOf<TIN>::type TA;
@@ -50,28 +51,32 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
             for (int j = 0; j < 8; ++j) hv[j] = hres[it][j];
           } else {
             const float4* hp = reinterpret_cast<const float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
-            const float4 h0 = hp[0], h1 = hp[1];
+            const float4 h0 = get16<COH, float4>(hp), h1 = get16<COH, float4>(hp + 1);
             hv[0] = h0.x; hv[1] = h0.y; hv[2] = h0.z; hv[3] = h0.w;
             hv[4] = h1.x; hv[5] = h1.y; hv[6] = h1.z; hv[7] = h1.w;
           }
         }
+        typedef TA TA8 __attribute__((ext_vector_type(8)));
+        TA8 y;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           x[j] = tile[r][c8 * 8 + j] * rs[r];
           if constexpr (EPI == EPI_RESID) x[j] += hv[j];
           ss += x[j] * x[j];
-          dst[j] = to_act<TA>(x[j] * to_f32(gain[n0 + j]), bad);
+          y[j] = to_act<TA>(x[j] * to_f32(gain[n0 + j]), bad);
+          if constexpr (!COH) dst[j] = y[j];
         }
+        if constexpr (COH) coherent_store16(dst, y);  // 8 fp16 activations = 16 bytes
         if constexpr (EPI == EPI_RESID) {
           float4* hp = reinterpret_cast<float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
-          hp[0] = make_float4(x[0], x[1], x[2], x[3]);
-          hp[1] = make_float4(x[4], x[5], x[6], x[7]);
+          put16<COH>(hp, make_float4(x[0], x[1], x[2], x[3]));
+          put16<COH>(hp + 1, make_float4(x[4], x[5], x[6], x[7]));
         }
       }
       ss += __shfl_xor(ss, 1, kWave);
       ss += __shfl_xor(ss, 2, kWave);
       ss += __shfl_xor(ss, 4, kWave);
-      if (c8 == 0 && r < BM && m < g.M) g.ssq_out[static_cast<size_t>(m) * g.np_out + tile_n] = ss;
+      if (c8 == 0 && r < BM && m < g.M) put<COH>(&g.ssq_out[static_cast<size_t>(m) * g.np_out + tile_n], ss);
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     TA* act = static_cast<TA*>(g.out);
@@ -87,7 +92,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
         const float uv = tile[r][p + 32] * rs[r];
         y = gv / (1.f + expf(-gv)) * uv;
       }
-      act[pa_index(m, j, g.out_steps)] = to_act<TA>(y, bad);
+      put<COH>(&act[pa_index(m, j, g.out_steps)], to_act<TA>(y, bad));
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     const int dh = g.head_dim, half = dh / 2;
@@ -141,8 +146,8 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
         dst = static_cast<TA*>(kind == 1 ? g.cache_k : g.cache_v) +
               (((static_cast<size_t>(layer) * g.batch + b) * g.n_kv_heads + head) * g.cache_slots + slot) * dh;
       }
-      dst[d1] = to_act<TA>(y1, bad);
-      dst[d1 + half] = to_act<TA>(y2, bad);
+      put<COH>(&dst[d1], to_act<TA>(y1, bad));
+      put<COH>(&dst[d1 + half], to_act<TA>(y2, bad));
     }
   }
   report_overflow(bad, g.dev_error);

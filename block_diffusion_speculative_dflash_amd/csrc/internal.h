@@ -147,6 +147,25 @@ hipError_t launch_verify_sampled(const VerifySampledArgs& a, hipStream_t stream)
 hipError_t launch_commit_rows(int32_t* ctx_len, const int32_t* n_rows, int batch, int n_max,
                               uint32_t* dev_error, hipStream_t stream);
 
+// Persistent layer kernel (persist.hip): one launch per draft layer, phases QKV ->
+// attention -> merge -> O -> gate/up -> down separated by grid barriers.
+struct PhaseGrid {
+  int x, y, z;  // the separate kernel's grid: work item i = (i % x, i / x % y, i / (x y))
+};
+struct LayerArgs {
+  GemmArgs gemm[4];    // QKV, O, gate/up, down (bf16 drafter, streaming plans)
+  PhaseGrid grid[4];
+  AttnArgs attn;       // rows_per_block 16 or 32, two key groups
+  int attn_items;      // B * Hkv * n_rb * max_splits
+  int merge_items;     // 0 when no sequence's keys are split
+  unsigned* barrier;   // [6 barriers][64 words]: arrival counter (word 0), release flag (word 32); zero at launch
+  uint32_t* dev_error;
+};
+// Co-resident workgroups of the layer kernel for streaming row blocks mt (1, 2, 4) and
+// attention row tiles nw (1, 2): 0 when unsupported.
+int persistent_capacity(int mt, int nw, int cus);
+hipError_t launch_layer_persistent(const LayerArgs& a, int mt, int nw, int grid, hipStream_t stream);
+
 // Debug poisoning: all-ones bytes (NaN in fp16 and fp32) into memory no later call
 // may depend on.
 struct PoisonRingArgs {

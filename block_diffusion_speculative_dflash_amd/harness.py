@@ -84,7 +84,7 @@ class RoundLoop:
     numbers."""
 
     def __init__(self, d, W, cache, ws, a_tab, fill, seed: int = 0, temperature: float = 0.0,
-                 adaptive: bool = False, device="cuda"):
+                 adaptive: bool = False, persistent: bool = False, device="cuda"):
         from . import binding as bd
         from . import synth
         self.bd, self.d, self.W, self.cache, self.ws = bd, d, W, cache, ws
@@ -102,6 +102,7 @@ class RoundLoop:
         self.n_rows_in = torch.full((B,), k + 1, dtype=torch.int32, device=device)
         self.sampled = temperature > 0
         self.adaptive = adaptive
+        self.persistent = persistent  # greedy draft step as one persistent kernel per layer
         if adaptive:
             # controller state: every sequence starts at the full block with the average at theta_up
             self.aparams = bd.adapt_params()
@@ -136,7 +137,10 @@ class RoundLoop:
             bd.dflash_verify_sampled(d, self.smp, self.draft, self.logits, self.lse, self.tgt_logits, cache,
                                      self.accept, self.out_tok, ws)
         else:
-            bd.dflash_draft_step(d, W, cache, self.draft, None, ws)
+            if self.persistent:
+                bd.dflash_draft_step_persistent(d, W, cache, self.draft, None, ws)
+            else:
+                bd.dflash_draft_step(d, W, cache, self.draft, None, ws)
             plant(self.draft, self.target, self.a_tab_d, self.fill_d, self.step_ctr, self.accept, self.acc_total,
                   V, block_len=self.blk, n_rows=self.n_rows_in if ad else None,
                   kb_total=self.kb_total if ad else None)

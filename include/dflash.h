@@ -80,6 +80,10 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 #define DFLASH_DEVERR_BLOCK 16u  /* block_len[b] outside [0, k]: clamped */
 #define DFLASH_DEVERR_OVERFLOW 32u /* bf16 drafter: an fp16 activation, q/k/v or K/V value beyond
                                       +-65504 (saturated there) or not finite */
+#define DFLASH_DEVERR_TIMEOUT 64u  /* dflash_draft_step_persistent: a grid barrier's bounded wait
+                                      ran out (the kernel exited; that call's results are
+                                      invalid).  Only if other work on the GPU keeps part of the
+                                      grid from running for about a quarter of a second */
 
 /* (host) Static shapes of one drafter; read during a call only.
  *   batch B, block_k k (1..63), n_layers L, hidden d, n_q_heads Hq, n_kv_heads Hkv
@@ -313,6 +317,22 @@ typedef struct {
 int dflash_adapt_block_len(const dflash_dims *dims, const dflash_adapt_params *params,
                            const int32_t *accept_len, const dflash_cache *cache, float *ema,
                            int32_t *off_left, hipStream_t stream);
+
+/* dflash_draft_step with every draft layer run as ONE launch of a persistent layer
+ * kernel instead of one kernel per operator (the pages' execution-model point: the
+ * hotdry blog's TileRT section and the aufer article's micro-op section locate the
+ * batch-1 cost in the gaps between many small operators).  Inside a launch the
+ * phases QKV -> attention -> key-split merge -> O -> gate/up -> down are separated by
+ * grid barriers (every wait bounded: DFLASH_DEVERR_TIMEOUT, never a hang), each
+ * phase's work items are the separate kernels' workgroups with the same plans, and
+ * the next projection's first weight loads are issued before each barrier wait.
+ * Covers bf16 drafters with batch * block_k <= 64 block rows and head_dim 128;
+ * returns DFLASH_E_UNSUPPORTED (nothing enqueued) otherwise.  Same arguments, same
+ * results as dflash_draft_step (bitwise, when a sequence's keys are split into 1 or
+ * at least 8 pieces; otherwise the split merge sums in another order). */
+int dflash_draft_step_persistent(const dflash_dims *dims, const dflash_weights *w,
+                                 const dflash_cache *cache, int32_t *draft, float *logits_out,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): dflash_draft_step without

@@ -116,11 +116,12 @@ class SampledReport:
 class ParityRun:
     def __init__(self, dims: Dims, W, ctx_start: Sequence[int], anchors: Sequence[int],
                  prefill_rows: Sequence[int], sample: Optional[Sequence[int]] = None, seed: int = 0,
-                 check_kv: bool = True, poison: bool = False):
+                 check_kv: bool = True, poison: bool = False, persistent: bool = False):
         """poison: before every library call fill the workspace's scratch with NaN, and
         after every verification the ring slots no window reaches (dflash_debug_poison),
         so any read of stale memory shows in the results."""
         self.d, self.W, self.seed, self.check_kv, self.poison = dims, W, seed, check_kv, poison
+        self.persistent = persistent  # greedy draft steps through dflash_draft_step_persistent
         self.last = {}
         self.Wn = oracle_weights(W)
         if "packed" not in W:
@@ -319,7 +320,10 @@ class ParityRun:
         draft = torch.empty((B, k), dtype=torch.int32, device="cuda")
         logits = torch.empty((B, k, V), dtype=torch.float32, device="cuda")
         self._poison()
-        bd.dflash_draft_step(d, W, self.cache, draft, logits, self.ws)
+        if self.persistent:
+            bd.dflash_draft_step_persistent(d, W, self.cache, draft, logits, self.ws)
+        else:
+            bd.dflash_draft_step(d, W, self.cache, draft, logits, self.ws)
         torch.cuda.synchronize()
         self.last = {"draft": draft.clone(), "logits": logits.clone()}
         o = orc.draft_step(d, self.Wn, self.st, block_len=kb[s])
