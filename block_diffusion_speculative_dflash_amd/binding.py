@@ -15,7 +15,8 @@ import torch
 from .configs import BF16, Dims
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libdflash.so")
+# DFLASH_LIBRARY: another build of the same library (the host-sanitized test build)
+LIB_PATH = os.environ.get("DFLASH_LIBRARY") or os.path.join(PKG, "libdflash.so")
 
 DFLASH_OK, DFLASH_E_INVALID, DFLASH_E_UNSUPPORTED, DFLASH_E_WORKSPACE, DFLASH_E_HIP = 0, -1, -2, -3, -4
 DFLASH_E_TOO_LARGE = -5

@@ -19,7 +19,6 @@ constexpr int kGemmCounters = 1 << 16;
 constexpr int kSplitBelow = 256;                   // streaming GEMM: split K only below this many tiles (one per CU)
 constexpr int kCUs = 256;
 constexpr int kTiledMinRows = 128;                 // bf16 GEMMs with at least this many rows go tiled
-constexpr int kBarriersPerLayer = 6 * 64;          // persistent layer kernel: words of its 6 grid barriers
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -34,12 +33,19 @@ size_t elem(const dflash_dims& d) { return is_f32(d) ? 4 : 2; }  // weights, act
 
 bool dims_ok(const dflash_dims* d) {
   if (d == nullptr) return false;
-  if (d->batch < 1 || d->block_k < 1 || d->block_k > 63 || d->n_layers < 1) return false;
-  if (d->hidden < 64 || d->hidden % 64 != 0 || d->n_q_heads < 1 || d->n_kv_heads < 1) return false;
-  if (d->n_q_heads % d->n_kv_heads != 0) return false;
+  // field ranges that keep every size and index computed from them far inside int32
+  // (per field) and size_t (products)
+  if (d->batch < 1 || d->batch > (1 << 16) || d->block_k < 1 || d->block_k > 63) return false;
+  if (d->n_layers < 1 || d->n_layers > 64) return false;
+  if (d->hidden < 64 || d->hidden > (1 << 16) || d->hidden % 64 != 0) return false;
+  if (d->n_q_heads < 1 || d->n_q_heads > 1024 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads != 0)
+    return false;
   if (d->head_dim != 64 && d->head_dim != 128) return false;
-  if (d->ffn < 1 || d->vocab < 2 || d->n_taps < 1 || d->tap_dim < 1) return false;
-  if (d->window < 1 || d->sink < 0 || d->cache_slots < d->sink + d->window + d->block_k) return false;
+  if (d->ffn < 1 || d->ffn > (1 << 20) || d->vocab < 2 || d->vocab > (1 << 24)) return false;
+  if (d->n_taps < 1 || d->n_taps > 64 || d->tap_dim < 1 || d->tap_dim > (1 << 16)) return false;
+  if (d->window < 1 || d->window > (1 << 24) || d->sink < 0 || d->sink > (1 << 20)) return false;
+  if (d->cache_slots > (1 << 26) || d->cache_slots < d->sink + d->window + d->block_k) return false;
+  if (d->max_inject_rows > (1 << 16)) return false;
   if (d->dtype != DFLASH_F32 && d->dtype != DFLASH_BF16) return false;
   if (d->max_inject_rows < d->block_k + 1) return false;
   if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.f)) return false;
@@ -122,7 +128,7 @@ size_t partial_bytes(const dflash_dims& d);
 
 struct Layout {
   size_t h, xa, ssq, q, kb, vb, o, act, cu, ssq_c, partials, counters, keys, attn_cnt, attn_o,
-      attn_ml, lse_part, v_part, v_cnt, v_rowlse, v_dec, v_keys, barriers, total;
+      attn_ml, lse_part, v_part, v_cnt, v_rowlse, v_dec, v_keys, xa2, ssq2, sig, row_map, seq_row0, total;
   int v_chunks;
   int np_d, S_d, S_o, S_f;
   AttnPlan ap;
@@ -170,7 +176,15 @@ Layout layout(const dflash_dims& d) {
   L.v_rowlse = take(size_t(d.batch) * (d.block_k + 1) * 4);
   L.v_dec = take(size_t(d.batch) * 16);
   L.v_keys = take(size_t(d.batch) * 2 * kKeyStride * 8);
-  L.barriers = take(size_t(d.n_layers) * kBarriersPerLayer * 4);  // persistent layer kernel
+  // persistent layer kernel: the MLP input and its RMSNorm partials in their own
+  // buffers (the QKV projection may still read xa / ssq while O writes them), and the
+  // signal words of every layer
+  L.xa2 = take(Mb64 * L.S_d * 32 * e);
+  L.ssq2 = take(Mb * L.np_d * 4);
+  L.sig = take(size_t(d.n_layers) * kSigWords * 4);
+  // compacted block rows (runtime block size at large batch)
+  L.row_map = take(Mb * 4);
+  L.seq_row0 = take((size_t(d.batch) + 1) * 4);
   L.total = off;
   return L;
 }
@@ -321,6 +335,8 @@ struct Ctx {
   char* ws;
   const char* packed;
   uint32_t* dev_error;
+  const int32_t* m_live = nullptr;   // compacted block rows (draft step), else nullptr
+  const int32_t* row_map = nullptr;
   template <typename X> X* at(size_t off) const { return reinterpret_cast<X*>(ws + off); }
   const void* reg(const Region& r) const { return packed + r.off; }
 };
@@ -342,6 +358,8 @@ GemmArgs base_args(const Ctx& c) {
   a.ffn = c.d.ffn;
   a.theta = c.d.rope_theta;
   a.dev_error = c.dev_error;
+  a.m_live = c.m_live;
+  a.row_map = c.row_map;
   return a;
 }
 
@@ -426,11 +444,25 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   const Layout L = layout(d);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < L.total) return DFLASH_E_WORKSPACE;
 
-  const Ctx c{d, L, P, static_cast<char*>(workspace), static_cast<const char*>(w->packed), cache->dev_error};
+  Ctx c{d, L, P, static_cast<char*>(workspace), static_cast<const char*>(w->packed), cache->dev_error};
   const bool f32 = is_f32(d);
   const size_t e = elem(d);
   const int D = d.hidden, k = d.block_k, B = d.batch, F = d.ffn;
   const int Mb = B * k;
+  // Runtime block size on the tiled GEMMs (greedy drafts): the rows of shrunken blocks
+  // are compacted away, so the GEMMs multiply only the live rows
+  const bool compact = cache->block_len != nullptr && smp == nullptr && !persistent && use_tiled(d, Mb);
+  if (compact) {
+    CompactArgs ca;
+    ca.block_len = cache->block_len;
+    ca.seq_row0 = c.at<int32_t>(L.seq_row0);
+    ca.row_map = c.at<int32_t>(L.row_map);
+    ca.batch = B;
+    ca.block_k = k;
+    DF_CHECK(launch_compact_rows(ca, stream));
+    c.m_live = ca.seq_row0 + B;
+    c.row_map = ca.row_map;
+  }
 
   // Persistent layer kernel: bf16 drafters whose block rows stay on the streaming GEMM,
   // head_dim 128; attention with at most two 16-row tiles per workgroup (the same
@@ -445,7 +477,11 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     if (int st = device_cus(&cus)) return st;
     p_capacity = persistent_capacity(p_mt, p_nw, cus);
     if (p_capacity <= 0) return DFLASH_E_UNSUPPORTED;
-    DF_CHECK(launch_fill_zero(c.at<void>(L.barriers), size_t(d.n_layers) * kBarriersPerLayer * 4, stream));
+    const int row_tiles = cdiv(G * k, 16);
+    if (d.n_kv_heads > kSigMaxHkv || B * d.n_kv_heads * cdiv(row_tiles, p_nw) > kSigMaxGroups ||
+        cdiv(F, kBN / 2) > kSigMaxGu)
+      return DFLASH_E_UNSUPPORTED;
+    DF_CHECK(launch_fill_zero(c.at<void>(L.sig), size_t(d.n_layers) * kSigWords * 4, stream));
   }
   const int hq_dh = d.n_q_heads * d.head_dim;
   const size_t layer_cache = size_t(B) * d.n_kv_heads * d.cache_slots * d.head_dim * e;
@@ -470,6 +506,8 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   em.hidden = D;
   em.vocab = d.vocab;
   em.dev_error = cache->dev_error;
+  em.row_map = c.row_map;
+  em.m_live = c.m_live;
   DF_CHECK(launch_embed(f32, em, stream));
 
   for (int l = 0; l < d.n_layers; ++l) {
@@ -479,7 +517,15 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     auto stage_gemm = [&](int slot, int epi, GemmArgs ga) -> int {
       if (!persistent) return run_gemm(epi, c, ga, true, stream);
       const GemmPlan gp = plan_gemm(epi, c, ga, true);
-      if (gp.tiled || gp.mt != p_mt) return DFLASH_E_UNSUPPORTED;
+      if (gp.tiled || gp.mt != p_mt || gp.m_tiles != 1) return DFLASH_E_UNSUPPORTED;
+      // the four GEMMs of a layer overlap in time: each gets its own quarter of the
+      // split-K partials and of the arrival counters
+      const size_t quarter = partial_bytes(d) / 4 / 256 * 256;
+      if (size_t(gp.splits) * ga.M * gp.n_tiles * kBN * 4 > quarter ||
+          size_t(gp.m_tiles) * gp.n_tiles > size_t(kGemmCounters / 4))
+        return DFLASH_E_UNSUPPORTED;
+      ga.partials = c.at<float>(L.partials + slot * quarter);
+      ga.counters = c.at<unsigned>(L.counters) + slot * (kGemmCounters / 4);
       la.gemm[slot] = ga;
       la.grid[slot] = stream_grid(gp);
       return DFLASH_OK;
@@ -530,6 +576,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     at.rows_per_block = L.ap.rows;
     // long full-attention windows over many sequences: contexts may be ragged
     at.balance = L.ap.max_splits == 1 && B >= 16 && B <= kMaxBalanceBatch && d.window > 1024;
+    at.seq_row0 = compact ? c.at<int32_t>(L.seq_row0) : nullptr;
     if (!persistent) {
       DF_CHECK(launch_attention(f32, at, stream));
     } else {
@@ -537,6 +584,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
       const int row_tiles = cdiv(G * k, 16);
       at.rows_per_block = 16 * p_nw;
       at.n_rb = cdiv(row_tiles, p_nw);
+      at.balance = 0;  // the dependency signals are per row group in item order
       la.attn = at;
       la.attn_items = B * d.n_kv_heads * at.n_rb * at.max_splits;
       la.merge_items = at.max_splits > 1 ? B * d.n_kv_heads * at.n_rb * at.rows_per_block : 0;  // one row each
@@ -552,23 +600,23 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     a.N = D;
     a.n_tiles = P.o[l].tiles;
     a.h = c.at<float>(L.h);
-    a.out = c.at<void>(L.xa);
+    a.out = c.at<void>(persistent ? L.xa2 : L.xa);
     a.out_steps = L.S_d;
     a.gain = gain(w->mlp_norm, l);
-    a.ssq_out = c.at<float>(L.ssq);
+    a.ssq_out = c.at<float>(persistent ? L.ssq2 : L.ssq);
     a.np_out = L.np_d;
     if (int st = stage_gemm(1, EPI_RESID, a)) return st;
 
     // RMSNorm + gate/up projection + SwiGLU
     a = base_args(c);
-    a.A = c.at<void>(L.xa);
+    a.A = c.at<void>(persistent ? L.xa2 : L.xa);
     a.M = Mb;
     a.K = D;
     a.S = L.S_d;
     a.W = c.reg(P.gu[l]);
     a.N = F;
     a.n_tiles = P.gu[l].tiles;
-    a.ssq_in = c.at<float>(L.ssq);
+    a.ssq_in = c.at<float>(persistent ? L.ssq2 : L.ssq);
     a.np_in = L.np_d;
     a.out = c.at<void>(L.act);
     a.out_steps = L.S_f;
@@ -592,8 +640,12 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     if (int st = stage_gemm(3, EPI_RESID, a)) return st;
 
     if (persistent) {
-      la.barrier = c.at<unsigned>(L.barriers) + size_t(l) * kBarriersPerLayer;
+      la.sig = c.at<unsigned>(L.sig) + size_t(l) * kSigWords;
       la.dev_error = cache->dev_error;
+      la.group = G;
+      la.tiles_per_head = d.head_dim / kBN;
+      la.o_tiles = la.grid[1].x > 0 ? P.o[l].tiles : 0;
+      la.fin_need = la.merge_items > 0 ? B * la.attn.n_rb * la.attn.rows_per_block : B * la.attn.n_rb;
       int items = std::max(la.attn_items, la.merge_items);
       for (const PhaseGrid& pg : la.grid) items = std::max(items, pg.x * pg.y * pg.z);
       DF_CHECK(launch_layer_persistent(la, p_mt, p_nw, std::min(items, p_capacity), stream));
@@ -639,6 +691,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   f.draft = draft;
   f.lse = smp != nullptr ? lse_out : nullptr;
   f.block_len = cache->block_len;
+  f.seq_row0 = compact ? c.at<int32_t>(L.seq_row0) : nullptr;
   DF_CHECK(launch_head_finalize(f, stream));
   return DFLASH_OK;
 }
@@ -994,7 +1047,8 @@ int dflash_debug_poison(const dflash_dims* dims, const dflash_cache* cache, void
                          {L.partials, false}, {L.counters, true}, {L.keys, false}, {L.attn_cnt, true},
                          {L.attn_o, false}, {L.attn_ml, false}, {L.lse_part, false}, {L.v_part, false},
                          {L.v_cnt, true}, {L.v_rowlse, false}, {L.v_dec, false}, {L.v_keys, true},
-                         {L.total, true}};
+                         {L.xa2, false}, {L.ssq2, false}, {L.sig, true}, {L.row_map, false},
+                         {L.seq_row0, false}, {L.total, true}};
     char* ws = static_cast<char*>(workspace);
     for (size_t i = 0; i + 1 < sizeof(regions) / sizeof(regions[0]); ++i) {
       if (regions[i].keep) continue;

@@ -141,6 +141,8 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, int item, Attn
   const int r0 = rb * a.rows_per_block;      // first row of the row block
   const int nr = min(a.rows_per_block, G * k - r0);  // rows of the row block
   const T* qg = static_cast<const T*>(a.q);
+  // first row of sequence b in q, kb, vb and out (compacted blocks: only its live rows)
+  const int rowb = a.seq_row0 != nullptr ? a.seq_row0[b] : b * k;
 
   // Q^T fragments (B operand), resident for the whole key loop: row rr0 + l16.  Their
   // loads do not depend on the context length, so they go out first.
@@ -148,7 +150,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, int item, Attn
   {
     const int rr = rr0 + l16;
     const int r = r0 + (rr < nr ? rr : 0);
-    const T* qrow = qg + ((static_cast<size_t>(b) * k + r % k) * a.n_q_heads + g * G + r / k) * DH;
+    const T* qrow = qg + ((static_cast<size_t>(rowb) + r % k) * a.n_q_heads + g * G + r / k) * DH;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if constexpr (COH) qf[ks].v = coherent_load16<decltype(qf[ks].v)>(qrow + ks * 32 + 8 * q4);
@@ -177,8 +179,8 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, int item, Attn
   const int sk = a.sink, R = a.cache_slots - a.sink;
   const int wrel0 = P > sk ? (ws - sk) % R : 0;  // ring offset of the first window position
   const int blk_stride = a.n_kv_heads * DH;
-  const T* kblk = kbg + (static_cast<size_t>(b) * k * a.n_kv_heads + g) * DH;
-  const T* vblk = vbg + (static_cast<size_t>(b) * k * a.n_kv_heads + g) * DH;
+  const T* kblk = kbg + (static_cast<size_t>(rowb) * a.n_kv_heads + g) * DH;
+  const T* vblk = vbg + (static_cast<size_t>(rowb) * a.n_kv_heads + g) * DH;
   // key j's row: sink slot j, ring slot of window key j, or block row j - n_ctx;
   // selects only (no branch), so the unrolled loads stay in flight together
   auto key_ptr = [&](int j, const T* ring, const T* blk) -> const T* {
@@ -358,11 +360,12 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a, int item, Attn
   const size_t grp = (static_cast<size_t>(b) * a.n_kv_heads + g) * a.n_rb + rb;
   const int r = r0 + rr, hl = r / k, i = r % k;
   if (n_split_b == 1) {
+    if (a.seq_row0 != nullptr && i >= kb) return;  // compacted: the row does not exist
     T* out = static_cast<T*>(a.out);
     const float inv = 1.f / l_run;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      T* dst = out + pa_index(b * k + i, (g * G + hl) * DH + dt * 16 + 4 * q4, a.out_steps);
+      T* dst = out + pa_index(rowb + i, (g * G + hl) * DH + dt * 16 + 4 * q4, a.out_steps);
       put4<COH>(dst, o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
     }
   } else {
@@ -495,7 +498,9 @@ __device__ __forceinline__ void merge_body(const AttnArgs& a, int item, MergeLds
     Lt += red_l[rw][i] * w;
   }
   const int r = r0 + rr, hl = r / k, i = r % k;
-  T* dst = static_cast<T*>(a.out) + pa_index(b * k + i, (g * G + hl) * DH + 4 * dq, a.out_steps);
+  if (a.seq_row0 != nullptr && i >= kb) return;  // compacted: the row does not exist
+  T* dst = static_cast<T*>(a.out) + pa_index((a.seq_row0 != nullptr ? a.seq_row0[b] : b * k) + i,
+                                             (g * G + hl) * DH + 4 * dq, a.out_steps);
   const float inv = 1.f / Lt;
   put4<COH>(dst, o.x * inv, o.y * inv, o.z * inv, o.w * inv);
 }

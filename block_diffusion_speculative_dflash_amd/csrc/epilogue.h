@@ -20,12 +20,13 @@
 
 namespace dflash {
 
+// Rows m >= m_end are skipped (g.M, or the live rows of compacted blocks).
 // hres: RESID only, the residual tile prefetched by the caller (row pass `it` of
 // this thread, 8 columns), or nullptr to read it here.  COH: the outputs (and the
 // residual read here) are device-coherent, for a consumer inside the same launch.
 template <typename TIN, int EPI, int BM, int NT, bool COH = false>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*tile)[kBN + 4], const float* rs,
-                                              int tile_n, int m0, const float (*hres)[8]) {
+                                              int tile_n, int m0, int m_end, const float (*hres)[8]) {
   typedef typename ActOf<TIN>::type TA;
   const int tid = threadIdx.x;
   bool bad = false;
@@ -41,7 +42,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
       const int m = m0 + r;
       const int n0 = tile_n * kBN + c8 * 8;
       float ss = 0.f;
-      if (r < BM && m < g.M && n0 < g.N) {
+      if (r < BM && m < m_end && n0 < g.N) {
         TA* dst = out + pa_index(m, n0, g.out_steps);
         float x[8];
         float hv[8];
@@ -76,14 +77,14 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
       ss += __shfl_xor(ss, 1, kWave);
       ss += __shfl_xor(ss, 2, kWave);
       ss += __shfl_xor(ss, 4, kWave);
-      if (c8 == 0 && r < BM && m < g.M) put<COH>(&g.ssq_out[static_cast<size_t>(m) * g.np_out + tile_n], ss);
+      if (c8 == 0 && r < BM && m < m_end) put<COH>(&g.ssq_out[static_cast<size_t>(m) * g.np_out + tile_n], ss);
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     TA* act = static_cast<TA*>(g.out);
     for (int idx = tid; idx < BM * 32; idx += NT) {
       const int r = idx >> 5, p = idx & 31, m = m0 + r;
       const int j = tile_n * 32 + p;
-      if (m >= g.M) continue;
+      if (m >= m_end) continue;
       // columns past ffn are the down projection's K padding: written as zeros, so
       // the product never depends on what the workspace held before
       float y = 0.f;
@@ -114,8 +115,13 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
     }
     for (int idx = tid; idx < BM * 32; idx += NT) {
       const int r = idx >> 5, m = m0 + r;
-      if (m >= g.M) continue;
-      const int b = m / g.rows_per_seq, i = m % g.rows_per_seq;
+      if (m >= m_end) continue;
+      int b = m / g.rows_per_seq, i = m % g.rows_per_seq;
+      if (g.row_map != nullptr) {
+        const int e = g.row_map[m];
+        b = e >> 6;
+        i = e & 63;
+      }
       int n_valid = g.rows_per_seq;
       if constexpr (EPI == EPI_INJECT) {
         const int nr = g.n_rows[b];
@@ -151,20 +157,6 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
     }
   }
   report_overflow(bad, g.dev_error);
-}
-
-// RMSNorm factor of A row m from the producer's per-tile partial sums of squares.
-__device__ __forceinline__ float rms_factor(const GemmArgs& g, int m) {
-  if (g.ssq_in == nullptr || m >= g.M) return 1.f;
-  const float* src = g.ssq_in + static_cast<size_t>(m) * g.np_in;
-  float v[16];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) v[t] = t < g.np_in ? src[t] : 0.f;
-  float s = 0.f;
-  for (int p = 16; p < g.np_in; ++p) s += src[p];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) s += v[t];
-  return 1.f / sqrtf(s / static_cast<float>(g.norm_dim) + g.eps);
 }
 
 }  // namespace dflash

@@ -84,6 +84,12 @@ struct GemmArgs {
   const unsigned long long* step_dev;  // when set, the step is read from here at run time
   float2* lse_part;
   int n_parts;
+  // compacted block rows (draft step, runtime block size, tiled GEMMs): rows at or
+  // beyond *m_live do not exist (their tiles exit, the epilogues skip them), and
+  // row m is (sequence, position) = (row_map[m] >> 6, row_map[m] & 63); nullptr: all
+  // M rows, row m = (m / rows_per_seq, m % rows_per_seq)
+  const int32_t* m_live;
+  const int32_t* row_map;
 };
 
 struct GemmPlan {

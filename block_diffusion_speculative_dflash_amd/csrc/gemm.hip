@@ -26,7 +26,7 @@ namespace dflash {
 template <typename TIN, int MT, int EPI, int D>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   __shared__ StreamLds<MT> lds;
-  gemm_body<TIN, MT, EPI, D, false>(g, blockIdx.x, blockIdx.y, blockIdx.z, lds, [] {});
+  gemm_body<TIN, MT, EPI, D, false>(g, blockIdx.x, blockIdx.y, blockIdx.z, lds, [](int, int, int) {}, [](int) {});
 }
 
 template <typename TIN, int MT, int EPI>

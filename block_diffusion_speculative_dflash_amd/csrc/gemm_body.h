@@ -86,15 +86,17 @@ struct StreamLds {
 };
 
 // One workgroup's work item (bx, by, bz) of the weight-streaming GEMM (the kernel's
-// blockIdx).  `hook` runs after the weight loads of the first pipeline stages are
-// issued and before anything that depends on the A operand is read: the persistent
-// layer kernel waits there for the previous phase, so the weight stream of this
-// phase is already in flight during the wait.  COH: the A operand, the RMSNorm
+// blockIdx).  `hook(tile_n, s_lo, s_hi)` runs after the weight loads of the first
+// pipeline stages are issued and before anything that depends on the A operand is
+// read: the persistent layer kernel waits there for the producers of the A columns
+// of K steps [s_lo, s_hi), so the weight stream is already in flight during the wait.
+// `done(tile_n)` runs in the workgroup that finished output tile tile_n, after its
+// epilogue (all threads).  COH: the A operand, the RMSNorm
 // partials and the residual are read, and the outputs written, device-coherently
 // (producer and consumer inside one launch).
-template <typename TIN, int MT, int EPI, int D, bool COH, typename Hook>
+template <typename TIN, int MT, int EPI, int D, bool COH, typename Hook, typename Done>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g, int bx, int by, int bz, StreamLds<MT>& lds,
-                                          Hook hook) {
+                                          Hook hook, Done done) {
   typedef typename ActOf<TIN>::type TA;
   typedef typename std::conditional<EPI == EPI_FUSE, TIN, TA>::type E;
   constexpr bool APK = EPI != EPI_FUSE;  // only the fusion GEMM reads a row-major A
@@ -205,7 +207,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int bx, int by, int
   // A operand of those steps and the epilogue's own inputs
 #pragma unroll
   for (int u = 0; u < D; ++u) DFLASH_LOAD_W(u, u);
-  hook();
+  hook(tile_n, s_lo, s_hi);
 #pragma unroll
   for (int u = 0; u < D; ++u) DFLASH_LOAD_A(u, u);
   // Loads the epilogue needs but the product does not (RMSNorm partial sums, the
@@ -326,7 +328,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int bx, int by, int
   __syncthreads();
 
   if constexpr (EPI != EPI_ARGMAX && EPI != EPI_SAMPLE) {
-    epilogue_tile<TIN, EPI, BM, kThreads, COH>(g, tile, rs_s, tile_n, m0, hres);
+    epilogue_tile<TIN, EPI, BM, kThreads, COH>(g, tile, rs_s, tile_n, m0, g.M, hres);
+    done(tile_n);
   } else {  // EPI_ARGMAX, EPI_SAMPLE
     if constexpr (EPI == EPI_SAMPLE) sample_tile<BM>(g, tile, rs_s, tile_n, m0);
     else for (int r = wave; r < BM; r += 4) {

@@ -84,6 +84,12 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   const int tm = L % g.m_tiles, rest = L / g.m_tiles;
   const int tn = rest % n_big, split = rest / n_big;
   const int m0 = tm * BM;
+  // compacted block rows: tiles past the live rows have nothing to do
+  int M = g.M;
+  if (g.m_live != nullptr) {
+    M = min(M, max(*g.m_live, 0));
+    if (m0 >= M) return;  // uniform per workgroup
+  }
   const int s_lo = split * g.steps_per_split;
   const int S = min(g.S, s_lo + g.steps_per_split) - s_lo;  // steps of this split (>= 1)
   const int m_blocks = (g.M + 15) >> 4;
@@ -258,7 +264,11 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
           if (n < g.N) {
             const unsigned long long kj = argmax_key(v, n);
             key = kj > key ? kj : key;
-            if (g.logits != nullptr && m < g.M) g.logits[static_cast<size_t>(m) * g.N + n] = v;
+            if (g.logits != nullptr && m < M) {
+              const int e = g.row_map != nullptr ? g.row_map[m] : 0;
+              const int mo = g.row_map != nullptr ? (e >> 6) * g.rows_per_seq + (e & 63) : m;
+              g.logits[static_cast<size_t>(mo) * g.N + n] = v;
+            }
           }
         }
 #pragma unroll
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
         for (int j = 0; j < WN; ++j) {
           const int n = (tn * BFR + wn * WN + j) * 16 + (lane & 15);
           sv[j] = -INFINITY;
-          if (n < g.N && m < g.M) {
+          if (n < g.N && m < M) {
             const float z = acc[i][j][rr] * f;
             if (g.logits != nullptr) g.logits[static_cast<size_t>(m) * g.N + n] = z;
             sv[j] = z * g.inv_temp;
@@ -361,7 +371,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
         }
       }
       __syncthreads();
-      if (tile_n < g.n_tiles) epilogue_tile<bf16, EPI, BM, NT>(g, tile, rs_s, tile_n, m0, nullptr);
+      if (tile_n < g.n_tiles) epilogue_tile<bf16, EPI, BM, NT>(g, tile, rs_s, tile_n, m0, M, nullptr);
     }
   } else {
 #pragma unroll
@@ -379,18 +389,18 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
             tile[(wm * WM + i) * 16 + 4 * (lane >> 4) + rr][(cb & 3) * 16 + (lane & 15)] = acc[i][j][rr];
       }
       __syncthreads();
-      if (tile_n < g.n_tiles) epilogue_tile<bf16, EPI, BM, NT>(g, tile, rs_s, tile_n, m0, nullptr);
+      if (tile_n < g.n_tiles) epilogue_tile<bf16, EPI, BM, NT>(g, tile, rs_s, tile_n, m0, M, nullptr);
     }
   }
 
   if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) {
     __syncthreads();
     for (int r = tid; r < BM; r += NT)
-      if (m0 + r < g.M) g.keys[static_cast<size_t>(m0 + r) * g.n_parts + tn] = best_s[r];
+      if (m0 + r < M) g.keys[static_cast<size_t>(m0 + r) * g.n_parts + tn] = best_s[r];
     if constexpr (EPI == EPI_SAMPLE) {
       const float2* lse_s = reinterpret_cast<const float2*>(smem);
       for (int r = tid; r < BM; r += NT) {
-        if (m0 + r >= g.M) continue;
+        if (m0 + r >= M) continue;
         float mx = -INFINITY, sm = 0.f;
 #pragma unroll
         for (int w = 0; w < NWN; ++w) lse_merge(mx, sm, lse_s[r * NWN + w].x, lse_s[r * NWN + w].y);

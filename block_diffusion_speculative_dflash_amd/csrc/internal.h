@@ -40,6 +40,9 @@ struct EmbedArgs {
   float* ssq;              // [M, 1]
   int batch, block_k, hidden, vocab;
   uint32_t* dev_error;
+  // compacted block rows (see CompactArgs), or nullptr: row m is (m / k, m % k)
+  const int32_t* row_map;
+  const int32_t* m_live;
 };
 hipError_t launch_embed(bool f32, const EmbedArgs& a, hipStream_t stream);
 
@@ -59,6 +62,9 @@ struct AttnArgs {
   int keys_per_split, max_splits, n_rb, rows_per_block;  // rows_per_block: 16, 32, 48 or 64
   const int32_t* block_len;  // [B] or nullptr: block keys of sequence b are rows 0 .. block_len[b]-1
   int balance;  // 1: pair long and short contexts on a CU (see balanced_sequence); batch <= kMaxBalanceBatch
+  // compacted block rows: sequence b's rows start at seq_row0[b] in q, kb, vb and out,
+  // and rows i >= block_len[b] are neither read as keys nor written; nullptr: b * k
+  const int32_t* seq_row0;
 };
 constexpr int kMaxBalanceBatch = 256;
 hipError_t launch_attention(bool f32, const AttnArgs& a, hipStream_t stream);
@@ -98,6 +104,7 @@ struct HeadFinalizeArgs {
   int32_t* draft;                  // [rows]
   float* lse;                      // [rows], with part
   const int32_t* block_len;        // [rows / rows_per_seq] or nullptr
+  const int32_t* seq_row0;         // compacted rows: the keys of (b, i) are at row seq_row0[b] + i
 };
 hipError_t launch_head_finalize(const HeadFinalizeArgs& a, hipStream_t stream);
 
@@ -147,19 +154,44 @@ hipError_t launch_verify_sampled(const VerifySampledArgs& a, hipStream_t stream)
 hipError_t launch_commit_rows(int32_t* ctx_len, const int32_t* n_rows, int batch, int n_max,
                               uint32_t* dev_error, hipStream_t stream);
 
+// Compaction of the block rows (runtime block size at large batch): sequence b keeps
+// its block_len[b] rows (clamped to [0, k]), numbered consecutively in sequence
+// order.  seq_row0[b] = first row of b, seq_row0[B] = number of live rows;
+// row_map[m] = (b << 6) | i for the live rows m (k <= 63).  One workgroup.
+struct CompactArgs {
+  const int32_t* block_len;  // [B]
+  int32_t* seq_row0;         // [B + 1]
+  int32_t* row_map;          // [B * k]
+  int batch, block_k;
+};
+hipError_t launch_compact_rows(const CompactArgs& a, hipStream_t stream);
+
 // Persistent layer kernel (persist.hip): one launch per draft layer, phases QKV ->
-// attention -> merge -> O -> gate/up -> down separated by grid barriers.
+// attention -> merge -> O -> gate/up -> down with tile-level dependencies.
 struct PhaseGrid {
   int x, y, z;  // the separate kernel's grid: work item i = (i % x, i / x % y, i / (x y))
 };
+// Signal words of one layer (zero at launch), word offsets:
+constexpr int kSigQkv = 0;      // [Hkv] finished QKV tiles of each kv group's heads
+constexpr int kSigFin = 256;    // [Hkv] finished attention output row groups of each kv group
+constexpr int kSigO = 512;      // finished O projection tiles
+constexpr int kSigAtt = 1024;   // [B Hkv n_rb] finished attention items (key splits) per row group
+constexpr int kSigGu = 8192;    // [gate/up tiles] flags: tile done
+constexpr int kSigReady = 16384;  // + w: ready flag of counter word w (set once by the producer that completes it)
+constexpr int kSigWords = 32768;
+constexpr int kSigMaxHkv = 256, kSigMaxGroups = kSigGu - kSigAtt, kSigMaxGu = kSigReady - kSigGu;
 struct LayerArgs {
-  GemmArgs gemm[4];    // QKV, O, gate/up, down (bf16 drafter, streaming plans)
+  GemmArgs gemm[4];    // QKV, O, gate/up, down (bf16 drafter, streaming plans, own partials and counters)
   PhaseGrid grid[4];
-  AttnArgs attn;       // rows_per_block 16 or 32, two key groups
+  AttnArgs attn;       // rows_per_block 16 or 32, two key groups, no balancing
   int attn_items;      // B * Hkv * n_rb * max_splits
   int merge_items;     // 0 when no sequence's keys are split
-  unsigned* barrier;   // [6 barriers][64 words]: arrival counter (word 0), release flag (word 32); zero at launch
+  unsigned* sig;       // kSigWords signal words
   uint32_t* dev_error;
+  int group;           // q heads per kv head
+  int tiles_per_head;  // 64-column tiles per head (head_dim / 64)
+  int o_tiles;         // output tiles of the O projection
+  int fin_need;        // finished row groups of a kv group before its heads' attention output is complete
 };
 // Co-resident workgroups of the layer kernel for streaming row blocks mt (1, 2, 4) and
 // attention row tiles nw (1, 2): 0 when unsupported.

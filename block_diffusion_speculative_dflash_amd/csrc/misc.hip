@@ -16,7 +16,13 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
   typedef typename ActOf<T>::type TA;
   __shared__ float red[kThreads / kWave];
   const int m = blockIdx.x;
-  const int b = m / a.block_k, i = m % a.block_k;
+  int b = m / a.block_k, i = m % a.block_k;
+  if (a.row_map != nullptr) {  // compacted block rows: row m is (b, i) of the map, if live
+    if (m >= *a.m_live) return;
+    const int e = a.row_map[m];
+    b = e >> 6;
+    i = e & 63;
+  }
   const int d = a.hidden;
   int tok = a.anchor[b];
   if (tok < 0 || tok >= a.vocab) {
@@ -61,6 +67,47 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
     for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
     a.ssq[m] = t;
   }
+}
+
+// Compaction of the block rows: an exclusive scan of the clamped block lengths in
+// chunks of kCompactThreads sequences (wavefront scans, then one across the
+// wavefronts), then each sequence's (b, i) entries of the row map.
+constexpr int kCompactThreads = 1024;
+__global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(CompactArgs a) {
+  __shared__ int wave_tot[kCompactThreads / kWave];
+  __shared__ int carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < a.batch; base += kCompactThreads) {
+    const int b = base + tid;
+    const int kb = b < a.batch ? min(max(a.block_len[b], 0), a.block_k) : 0;
+    int incl = kb;  // inclusive scan within the wavefront
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    if (lane == kWave - 1) wave_tot[w] = incl;
+    __syncthreads();
+    int before = carry_s;
+    for (int j = 0; j < w; ++j) before += wave_tot[j];
+    const int row0 = before + incl - kb;
+    if (b < a.batch) {
+      a.seq_row0[b] = row0;
+      for (int i = 0; i < kb; ++i) a.row_map[row0 + i] = (b << 6) | i;
+    }
+    __syncthreads();  // every thread has read carry_s and wave_tot
+    if (tid == kCompactThreads - 1) carry_s = row0 + kb;
+    __syncthreads();
+  }
+  if (tid == 0) a.seq_row0[a.batch] = carry_s;
+}
+
+hipError_t launch_compact_rows(const CompactArgs& a, hipStream_t stream) {
+  if (a.batch <= 0 || a.block_k <= 0 || a.block_k > 63) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(kCompactThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_embed(bool f32, const EmbedArgs& a, hipStream_t stream) {

@@ -9,21 +9,21 @@
 // -> gate/up + SwiGLU -> down projection.  The grid is co-resident (at most the
 // occupancy limit times the CUs); each phase's work items (the same items, with the
 // same split-K plans, as the separate kernels' workgroups, so the results are
-// bitwise those of the separate kernels) go round-robin over the workgroups, and a
-// grid barrier separates dependent phases.
+// bitwise those of the separate kernels) go round-robin over the workgroups, and an
+// item waits only for the items whose results it reads (below), so the phases
+// overlap where the dependencies allow.
 //
 // What the single launch buys: a projection's weights do not depend on the previous
 // phase, so a workgroup issues the weight loads of its next item's first pipeline
-// stages before it waits at the barrier, and the weight stream continues through the
-// phase boundary instead of draining and ramping up again around a kernel launch.
+// stages before it waits, and the weight stream continues through the phase
+// boundary instead of draining and ramping up again around a kernel launch.
 //
 // Coherence: the eight XCD L2 caches are not coherent with each other inside one
 // launch, so everything that crosses a phase boundary (q/k/v, attention partials and
 // output, the residual stream, RMSNorm inputs and partial sums, the SwiGLU
 // activations) is written and read with device-coherent accesses (the COH bodies).
-// A barrier is an arrival counter per phase: a workgroup waits for its own stores to
-// complete, then adds one; waiting workgroups poll with a sleep and give up after a
-// bounded number of polls, setting the time-out error bit instead of hanging.
+// The MLP's normalised input and its RMSNorm partials have buffers of their own, so
+// the O projection never overwrites what a late QKV item may still read.
 #include "attention_body.h"
 #include "common.h"
 #include "epilogue.h"
@@ -46,91 +46,144 @@ struct PersistLds {
   int flag;
 };
 
-// Grid barrier p: an arrival counter and a release flag on separate 128-byte lines
-// (kBarrierWords words per barrier).  A workgroup done with a phase waits for its own
-// stores to complete and adds one to the counter; the one that brings it to n_wg sets
-// the flag.  Waiting workgroups poll only the flag, one thread each, with a sleep
-// between polls, and give up after kSpinLimit polls (time-out error bit, uniform
-// false) instead of hanging.
-constexpr int kBarrierWords = 64;  // 256 bytes: counter at word 0, flag at word 32
+// Dependencies between work items instead of barriers between phases: a workgroup
+// that finishes an output tile (or an attention item) adds one to the signal word of
+// what it produced once its stores have completed; a work item waits, before it
+// reads anything produced in this launch, until the words of exactly the tiles it
+// consumes are complete:
+//   attention of kv group g   all QKV tiles of g's q heads and of its k and v heads
+//   merge of row group r      every key split of r
+//   O piece, K steps s..e     the attention output of the heads covering s..e
+//   gate/up                   every O tile (RMSNorm needs whole rows)
+//   down piece, K steps s..e  the gate/up tiles s..e (tile t produces act step t)
+// Every wait is on items of an earlier phase and every workgroup walks the phases in
+// order, so on a co-resident grid every wait ends; it is bounded anyway (kSpinLimit
+// polls, then the time-out error bit and a uniform false) so nothing can hang.
 
-__device__ __forceinline__ void grid_arrive(unsigned* bar, unsigned n_wg) {
-  wait_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == n_wg - 1) __hip_atomic_store(bar + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// One thread polls until *c >= need (uniform result).
+__device__ __forceinline__ bool poll_ge(const unsigned* c, unsigned need, uint32_t* dev_error) {
+  for (long long it = 0; __hip_atomic_load(const_cast<unsigned*>(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need;
+       ++it) {
+    if (it > kSpinLimit) {
+      atomicOr(dev_error, kErrTimeout);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
   }
+  return true;
 }
 
-__device__ __forceinline__ bool grid_wait(unsigned* bar, uint32_t* dev_error, int* flag_lds) {
+// Thread 0 waits for words c[0], c[stride], .. c[(n-1) stride] >= need; uniform result.
+__device__ __forceinline__ bool wait_words(const unsigned* c, int n, int stride, unsigned need, uint32_t* dev_error,
+                                           int* flag_lds) {
   if (threadIdx.x == 0) {
     int ok = 1;
-    for (long long it = 0; __hip_atomic_load(bar + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u; ++it) {
-      if (it > kSpinLimit) {
-        ok = 0;
-        atomicOr(dev_error, kErrTimeout);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
+    for (int i = 0; i < n && ok; ++i) ok = poll_ge(c + static_cast<size_t>(i) * stride, need, dev_error) ? 1 : 0;
     *flag_lds = ok;
   }
   __syncthreads();
   return *flag_lds != 0;
 }
 
+// This workgroup's stores have completed; then one thread adds one to *c, and the
+// producer whose add completes the count (need) sets c's ready flag, the word waiters
+// poll: polling the counter itself while producers still add to it is much slower.
+__device__ __forceinline__ void signal_add(unsigned* c, unsigned need) {
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0 && __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == need)
+    __hip_atomic_store(c + kSigReady, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 waits for the ready flags of counter words c[0], c[stride], ..; uniform.
+__device__ __forceinline__ bool wait_ready(const unsigned* c, int n, int stride, uint32_t* dev_error, int* flag_lds) {
+  return wait_words(c + kSigReady, n, stride, 1u, dev_error, flag_lds);
+}
+
 template <int MT, int NW>
 __global__ __launch_bounds__(kThreads, 2) void layer_kernel(LayerArgs a) {
-  constexpr int D = MT == 4 ? 2 : (MT == 1 ? 8 : 4);
+  // pipeline depth: as the separate kernels, but 6 at one row block (8 would spill at
+  // the two waves per SIMD the co-resident grid needs)
+  constexpr int D = MT == 4 ? 2 : (MT == 1 ? 6 : 4);
   __shared__ PersistLds<MT, NW> lds;
-  const unsigned n_wg = gridDim.x;
-  bool ok = true;  // uniform: false once a barrier timed out
-  auto bar = [&](int p) { return a.barrier + p * kBarrierWords; };
+  const int n_wg = gridDim.x;
+  bool ok = true;  // uniform: false once a wait timed out
+  unsigned* sig = a.sig;
+  const int Hq = a.gemm[0].n_q_heads, Hkv = a.gemm[0].n_kv_heads, G = a.group, tph = a.tiles_per_head;
 
-  // GEMM phase: items round-robin; the first item's weight loads go out before the
-  // wait for the previous phase (wait_bar < 0: nothing to wait for)
-  auto gemm_phase = [&](auto epi_tag, int i, int wait_bar) {
+  // GEMM phase i: items round-robin; `wait(tile_n, s_lo, s_hi)` runs once the item's
+  // first weight loads are in flight, `done(tile_n)` after the epilogue of a tile
+  auto gemm_phase = [&](auto epi_tag, int i, auto wait, auto done) {
     constexpr int EPI = decltype(epi_tag)::value;
     const GemmArgs& g = a.gemm[i];
     const PhaseGrid pg = a.grid[i];
     const int n = pg.x * pg.y * pg.z;
-    bool waited = wait_bar < 0;
     for (int item = blockIdx.x; item < n && ok; item += n_wg) {
       __syncthreads();  // the previous item is done with LDS
-      gemm_body<bf16, MT, EPI, D, true>(g, item % pg.x, (item / pg.x) % pg.y, item / (pg.x * pg.y), lds.gemm, [&] {
-        if (!waited) {
-          ok = grid_wait(bar(wait_bar), a.dev_error, &lds.flag);
-          waited = true;
-        }
-      });
+      gemm_body<bf16, MT, EPI, D, true>(
+          g, item % pg.x, (item / pg.x) % pg.y, item / (pg.x * pg.y), lds.gemm,
+          [&](int tile_n, int s_lo, int s_hi) {
+            if (ok) ok = wait(tile_n, s_lo, s_hi);
+          },
+          done);
     }
-    if (!waited && ok) ok = grid_wait(bar(wait_bar), a.dev_error, &lds.flag);
   };
+  auto no_wait = [](int, int, int) { return true; };
 
-  gemm_phase(std::integral_constant<int, EPI_QKV>{}, 0, -1);
-  grid_arrive(bar(0), n_wg);
-  if (ok) ok = grid_wait(bar(0), a.dev_error, &lds.flag);
+  // QKV projection: a finished tile counts towards its kv group
+  const unsigned qkv_need = static_cast<unsigned>((G + 2) * tph);
+  gemm_phase(std::integral_constant<int, EPI_QKV>{}, 0, no_wait, [&](int tile_n) {
+    const int hd = tile_n / tph;
+    const int g = hd < Hq ? hd / G : (hd < Hq + Hkv ? hd - Hq : hd - Hq - Hkv);
+    signal_add(&sig[kSigQkv + g], qkv_need);
+  });
+
+  // attention items ((b, g, rb) row group, key split)
+  const AttnArgs& at = a.attn;
+  const unsigned att_need = static_cast<unsigned>(at.max_splits), fin_need = static_cast<unsigned>(a.fin_need);
   for (int item = blockIdx.x; item < a.attn_items && ok; item += n_wg) {
+    const int grp = item / at.max_splits, g = (grp / at.n_rb) % Hkv;
     __syncthreads();
-    attention_body<f16, kPersistDH, NW, kPersistKG, true>(a.attn, item, lds.attn);
+    if (!(ok = wait_ready(&sig[kSigQkv + g], 1, 1, a.dev_error, &lds.flag))) break;
+    attention_body<f16, kPersistDH, NW, kPersistKG, true>(at, item, lds.attn);
+    if (a.merge_items == 0) signal_add(&sig[kSigFin + g], fin_need);
+    else signal_add(&sig[kSigAtt + grp], att_need);
   }
-  grid_arrive(bar(1), n_wg);
-  int last = 1;
-  if (a.merge_items > 0) {
-    if (ok) ok = grid_wait(bar(1), a.dev_error, &lds.flag);
-    for (int item = blockIdx.x; item < a.merge_items && ok; item += n_wg) {
-      __syncthreads();
-      merge_body<f16, kPersistDH, 8, true>(a.attn, item, lds.merge);
-    }
-    grid_arrive(bar(2), n_wg);
-    last = 2;
+  // merge items (one row of a row group each)
+  for (int item = blockIdx.x; item < a.merge_items && ok; item += n_wg) {
+    const int grp = item / at.rows_per_block, g = (grp / at.n_rb) % Hkv;
+    __syncthreads();
+    if (!(ok = wait_ready(&sig[kSigAtt + grp], 1, 1, a.dev_error, &lds.flag))) break;
+    merge_body<f16, kPersistDH, 8, true>(at, item, lds.merge);
+    signal_add(&sig[kSigFin + g], fin_need);
   }
-  gemm_phase(std::integral_constant<int, EPI_RESID>{}, 1, last);  // O projection + residual
-  grid_arrive(bar(3), n_wg);
-  gemm_phase(std::integral_constant<int, EPI_SWIGLU>{}, 2, 3);  // gate/up + SwiGLU
-  grid_arrive(bar(4), n_wg);
-  gemm_phase(std::integral_constant<int, EPI_RESID>{}, 3, 4);  // down + residual
+
+  // O projection + residual: a piece reads the attention output of its K steps' heads
+  const int dh = a.gemm[0].head_dim;
+  gemm_phase(
+      std::integral_constant<int, EPI_RESID>{}, 1,
+      [&](int, int s_lo, int s_hi) {
+        const int g0 = (s_lo * kKStep / dh) / G, g1 = ((s_hi * kKStep - 1) / dh) / G;
+        return wait_ready(&sig[kSigFin + g0], g1 - g0 + 1, 1, a.dev_error, &lds.flag);
+      },
+      [&](int) { signal_add(&sig[kSigO], static_cast<unsigned>(a.o_tiles)); });
+
+  // gate/up + SwiGLU: every O tile (RMSNorm of whole rows)
+  gemm_phase(
+      std::integral_constant<int, EPI_SWIGLU>{}, 2,
+      [&](int, int, int) {
+        return wait_ready(&sig[kSigO], 1, 1, a.dev_error, &lds.flag);
+      },
+      [&](int tile_n) { signal_add(&sig[kSigGu + tile_n], 1u); });
+
+  // down + residual: a piece reads act steps s_lo .. s_hi-1, produced by gate/up tiles
+  // with the same indices
+  gemm_phase(
+      std::integral_constant<int, EPI_RESID>{}, 3,
+      [&](int, int s_lo, int s_hi) {
+        return wait_ready(&sig[kSigGu + s_lo], s_hi - s_lo, 1, a.dev_error, &lds.flag);
+      },
+      [](int) {});
 }
 
 template <int MT, int NW>

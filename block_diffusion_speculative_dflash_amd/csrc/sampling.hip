@@ -37,7 +37,16 @@ __global__ __launch_bounds__(kThreads) void head_finalize_kernel(HeadFinalizeArg
   __shared__ unsigned long long red_k[kThreads / kWave];
   const int tid = threadIdx.x, row = blockIdx.x;
   const int n_parts = a.n_parts;
-  const unsigned long long* kp = a.keys + static_cast<size_t>(row) * n_parts;
+  const bool in_block = a.block_len == nullptr || row % a.rows_per_seq < a.block_len[row / a.rows_per_seq];
+  int krow = row;  // the row of the keys
+  if (a.seq_row0 != nullptr) {  // compacted: only rows inside the block have keys
+    if (!in_block) {
+      if (tid == 0) a.draft[row] = -1;
+      return;  // uniform per workgroup
+    }
+    krow = a.seq_row0[row / a.rows_per_seq] + row % a.rows_per_seq;
+  }
+  const unsigned long long* kp = a.keys + static_cast<size_t>(krow) * n_parts;
   unsigned long long best = 0ull;
   for (int t0 = tid; t0 < n_parts; t0 += 4 * kThreads) {
     unsigned long long v[4];
@@ -51,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void head_finalize_kernel(HeadFinalizeArg
   }
   float m = -INFINITY, s = 0.f;
   if (a.part != nullptr) {
-    const float2* p = a.part + static_cast<size_t>(row) * n_parts;
+    const float2* p = a.part + static_cast<size_t>(krow) * n_parts;
     for (int t0 = tid; t0 < n_parts; t0 += 4 * kThreads) {
       float2 v[4];
 #pragma unroll
@@ -81,7 +90,6 @@ __global__ __launch_bounds__(kThreads) void head_finalize_kernel(HeadFinalizeArg
       best = red_k[w] > best ? red_k[w] : best;
       lse_merge(m, s, red_m[w], red_s[w]);
     }
-    const bool in_block = a.block_len == nullptr || row % a.rows_per_seq < a.block_len[row / a.rows_per_seq];
     a.draft[row] = in_block ? argmax_key_index(best) : -1;
     if (a.part != nullptr) a.lse[row] = m + ln_f32(s);
   }

@@ -80,10 +80,11 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 #define DFLASH_DEVERR_BLOCK 16u  /* block_len[b] outside [0, k]: clamped */
 #define DFLASH_DEVERR_OVERFLOW 32u /* bf16 drafter: an fp16 activation, q/k/v or K/V value beyond
                                       +-65504 (saturated there) or not finite */
-#define DFLASH_DEVERR_TIMEOUT 64u  /* dflash_draft_step_persistent: a grid barrier's bounded wait
-                                      ran out (the kernel exited; that call's results are
-                                      invalid).  Only if other work on the GPU keeps part of the
-                                      grid from running for about a quarter of a second */
+#define DFLASH_DEVERR_TIMEOUT 64u  /* dflash_draft_step_persistent: a bounded wait for another
+                                      workgroup's results ran out (the kernel exited; that call's
+                                      results are invalid).  Only if other work on the GPU keeps
+                                      part of the grid from running for about a quarter of a
+                                      second */
 
 /* (host) Static shapes of one drafter; read during a call only.
  *   batch B, block_k k (1..63), n_layers L, hidden d, n_q_heads Hq, n_kv_heads Hkv
@@ -94,7 +95,13 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
  *   use, >= k + 1; sizes the workspace), rms_eps, rope_theta (RoPE base), sink s
  *   (attention sink: positions 0..s-1 stay visible to every block query after they
  *   leave the window, as the aufer article's micro-op section names it for this
- *   drafter; 0 = plain sliding window). */
+ *   drafter; 0 = plain sliding window).
+ * Accepted ranges (any field outside: DFLASH_E_INVALID, size queries return 0):
+ *   batch <= 65536, n_layers <= 64, hidden a multiple of 64 up to 65536,
+ *   n_q_heads <= 1024, ffn <= 2^20, 2 <= vocab <= 2^24, n_taps <= 64,
+ *   tap_dim <= 65536, window <= 2^24, sink <= 2^20, cache_slots <= 2^26,
+ *   max_inject_rows <= 65536, rms_eps >= 0, rope_theta > 0, and batch * max_inject_rows
+ *   * hidden <= 2e9, batch * block_k * vocab <= 4e9. */
 typedef struct {
   int32_t batch, block_k, n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn,
       vocab, n_taps, tap_dim, window, cache_slots, dtype, max_inject_rows;
@@ -202,7 +209,12 @@ int dflash_fuse_inject(const dflash_dims *dims, const dflash_weights *w,
  * RMSNorm and the LM head give logits; row i's argmax (lowest id on ties) is the
  * draft for position P_b+i+1.
  *   draft       [B, k] int32 output
- *   logits_out  NULL, or [B, k, V] float output of the logits (for tests)
+ *   logits_out  NULL, or [B, k, V] float output of the logits (for tests); with
+ *               cache->block_len, rows i >= block_len[b] are unspecified
+ * With cache->block_len and at least 128 block rows (bf16), the rows of shrunken
+ * blocks are compacted away before the first GEMM: the projections, the attention
+ * and the LM head compute only the sum of the block lengths in rows (the hotdry
+ * blog's fallback section: a shorter block should cost less).
  * Reads the cache, writes only draft, logits_out and the workspace. */
 int dflash_draft_step(const dflash_dims *dims, const dflash_weights *w,
                       const dflash_cache *cache, int32_t *draft, float *logits_out,
@@ -322,10 +334,10 @@ int dflash_adapt_block_len(const dflash_dims *dims, const dflash_adapt_params *p
  * kernel instead of one kernel per operator (the pages' execution-model point: the
  * hotdry blog's TileRT section and the aufer article's micro-op section locate the
  * batch-1 cost in the gaps between many small operators).  Inside a launch the
- * phases QKV -> attention -> key-split merge -> O -> gate/up -> down are separated by
- * grid barriers (every wait bounded: DFLASH_DEVERR_TIMEOUT, never a hang), each
- * phase's work items are the separate kernels' workgroups with the same plans, and
- * the next projection's first weight loads are issued before each barrier wait.
+ * phases QKV -> attention -> key-split merge -> O -> gate/up -> down overlap: each
+ * work item (the separate kernels' workgroups, with the same plans) waits only for
+ * the items that produce what it reads (every wait bounded: DFLASH_DEVERR_TIMEOUT,
+ * never a hang), and a projection's first weight loads are issued before its wait.
  * Covers bf16 drafters with batch * block_k <= 64 block rows and head_dim 128;
  * returns DFLASH_E_UNSUPPORTED (nothing enqueued) otherwise.  Same arguments, same
  * results as dflash_draft_step (bitwise, when a sequence's keys are split into 1 or

@@ -194,3 +194,40 @@ def test_block_length_calls_reject_bad_arguments_on_the_host():
     ws = bd.dflash_workspace_bytes(configs.C2.dims)
     assert L.dflash_draft_step(by(d), by(_weights()), by(c2), FAKE, None, FAKE, ws, None) == bd.DFLASH_E_INVALID
     assert L.dflash_verify_commit(by(d), FAKE, FAKE, by(c2), FAKE, FAKE, None) == bd.DFLASH_E_INVALID
+
+
+EXTREMES = (0, 1, -1, 63, 64, 65, 2 ** 16, 2 ** 24 + 1, 2 ** 30, 2 ** 31 - 1, -2 ** 31)
+
+
+@needs_lib
+@pytest.mark.parametrize("base", ["C2", "C5"])
+def test_size_queries_survive_extreme_dims(base):
+    """Every dims field at the edges of int32 (one at a time, then all at once): the
+    size queries return 0 (rejected) or a 256-byte multiple, and nothing in the host
+    arithmetic overflows (the host-sanitized build aborts on signed overflow)."""
+    L = bd.lib()
+    by = ctypes.byref
+    ref = bd.dims_struct(getattr(configs, base).dims)
+    names = [n for n, _ in bd.DflashDims._fields_ if n not in ("rms_eps", "rope_theta")]
+
+    def check(s):
+        n = L.dflash_workspace_bytes(by(s))
+        p = L.dflash_packed_bytes(by(s))
+        assert n % 256 == 0 and (n == 0) == (p == 0), (n, p)
+
+    for name in names:
+        for v in EXTREMES:
+            s = bd.DflashDims.from_buffer_copy(ref)
+            setattr(s, name, v)
+            check(s)
+    for name in ("rms_eps", "rope_theta"):
+        for v in (float("nan"), float("inf"), -1.0, 0.0, 3.0e38):
+            s = bd.DflashDims.from_buffer_copy(ref)
+            setattr(s, name, v)
+            check(s)
+    for v in (2 ** 31 - 1, 2 ** 24 + 1, 2 ** 16):
+        s = bd.DflashDims.from_buffer_copy(ref)
+        for name in names:
+            if name != "dtype":
+                setattr(s, name, v)
+        check(s)

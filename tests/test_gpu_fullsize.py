@@ -44,10 +44,10 @@ def planted_schedule(w, steps):
     return a_tab
 
 
-def run_steps(name, run, a_tab, min_gated):
+def run_steps(name, run, a_tab, min_gated, block_lens=None):
     checked = excluded = 0
     for s in range(len(a_tab)):
-        r = run.step(a_tab[s])
+        r = run.step(a_tab[s]) if block_lens is None else run.step(a_tab[s], block_len=block_lens[s])
         assert r.logits_ok, f"step {s}: max |dz| {r.logit_err} > 0.05"
         assert r.draft_mismatch == 0
         assert r.seqs_verified == len(run.sample) and r.verify_mismatch == 0, \
@@ -113,3 +113,29 @@ def test_fullsize_sampled_round(name, sample):
     assert r.state_mismatch == 0
     assert r.kv_ok, f"kv error {r.kv_err}"
     assert run.dev_error() == 0
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", [configs.C4.name, configs.C5.name])
+def test_fullsize_compacted_blocks(name):
+    """Per-sequence block lengths (the runtime block size) at the two large batches,
+    where the draft step compacts the live rows of shrunken blocks before the GEMMs:
+    every sequence draws its own k_b in [0, k] each step (about half the rows live),
+    the sampled sequences cover k_b = 0, k and values between."""
+    w = configs.WORKLOADS[name]
+    d = w.dims
+    k, B = d.block_k, d.batch
+    ctx = synth.make_context_lengths(w, seed=0)
+    sample = CASES[name][0](ctx)
+    rng = np.random.default_rng(11)
+    steps = 3
+    lens = rng.integers(0, k + 1, size=(steps, B)).astype(np.int64)
+    for s in range(steps):  # the sampled sequences: 0, k and intermediate lengths
+        lens[s, sample] = [(j * (k + 1) // len(sample) + 3 * s) % (k + 1) for j in range(len(sample))]
+    a_tab = np.minimum(planted_schedule(w, steps), lens)
+    say(f"[fullsize] compacted {name}: B={B} k={k} live rows per step {lens.sum(axis=1).tolist()} of {B * k}; "
+        f"sample={sample} block lengths {[lens[s, sample].tolist() for s in range(steps)]}")
+    W = synth.make_weights(d, seed=0, device="cuda")
+    pre = np.minimum(ctx, w.prefill)
+    run = ParityRun(d, W, ctx, synth.make_anchors(d), pre, sample=sample, seed=0)
+    run_steps(f"compacted {name}", run, a_tab, 2, block_lens=lens)
