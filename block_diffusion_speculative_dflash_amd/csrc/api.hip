@@ -182,8 +182,8 @@ Layout layout(const dflash_dims& d) {
   L.xa2 = take(Mb64 * L.S_d * 32 * e);
   L.ssq2 = take(Mb * L.np_d * 4);
   L.sig = take(size_t(d.n_layers) * kSigWords * 4);
-  // compacted block rows (runtime block size at large batch)
-  L.row_map = take(Mb * 4);
+  // compacted rows: blocks of the runtime block size / injection rows, large batches
+  L.row_map = take(std::max(Mb, Mi) * 4);
   L.seq_row0 = take((size_t(d.batch) + 1) * 4);
   L.total = off;
   return L;
@@ -249,10 +249,12 @@ GemmPlan stream_plan(int M, int n_tiles, int S, bool allow_split, size_t partial
 // plus ~20 us for the last arriver's reduction.  partial_cap = 0 disables splitting.
 GemmPlan tiled_plan(int M, int n_tiles, int S, bool allow_split, size_t partial_cap) {
   constexpr double r256 = 4.3e12, r128_pair = 3.5e12, r128_alone = 2.0e12, hbm = 5.0e12, split_fixed = 20e-6;
+  constexpr double r128x384 = 4.0e12, r256x128 = 3.7e12;
   GemmPlan best{};
   double best_t = 1e30;
-  for (int cfg : {kTile256, kTile128}) {
-    const int m_tiles = cdiv(M, cfg), n_big = cdiv(n_tiles, cfg / kBN);
+  for (int cfg : {kTile256, kTile128, kTile128x384, kTile256x128}) {
+    const int bm = tile_rows(cfg), bn = tile_cols(cfg);
+    const int m_tiles = cdiv(M, bm), n_big = cdiv(n_tiles, bn / kBN);
     for (int want = 1; want <= (allow_split ? 8 : 1); ++want) {
       const int sps = cdiv(S, want);
       const int splits = cdiv(S, sps);
@@ -263,10 +265,11 @@ GemmPlan tiled_plan(int M, int n_tiles, int S, bool allow_split, size_t partial_
         if (size_t(m_tiles) * n_big > size_t(kGemmCounters)) continue;
       }
       const long long n = static_cast<long long>(m_tiles) * n_big * splits;
-      const double work = 2.0 * cfg * cfg * kKStep * sps;  // flops of one workgroup
+      const double work = 2.0 * bm * bn * kKStep * sps;  // flops of one workgroup
       double t;
-      if (cfg == kTile256) {
-        t = static_cast<double>((n + kCUs - 1) / kCUs) * work / r256;
+      if (cfg != kTile128) {  // one workgroup per CU
+        const double rate = cfg == kTile256 ? r256 : (cfg == kTile128x384 ? r128x384 : r256x128);
+        t = static_cast<double>((n + kCUs - 1) / kCUs) * work / rate;
       } else {
         const long long full = n / (2 * kCUs), rem = n - full * 2 * kCUs;
         t = static_cast<double>(full) * work / (r128_pair / 2);
@@ -454,11 +457,13 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   const bool compact = cache->block_len != nullptr && smp == nullptr && !persistent && use_tiled(d, Mb);
   if (compact) {
     CompactArgs ca;
-    ca.block_len = cache->block_len;
+    ca.counts = cache->block_len;
     ca.seq_row0 = c.at<int32_t>(L.seq_row0);
     ca.row_map = c.at<int32_t>(L.row_map);
     ca.batch = B;
-    ca.block_k = k;
+    ca.rows_per_seq = k;
+    ca.dev_error = cache->dev_error;
+    ca.err_bit = DFLASH_DEVERR_BLOCK;
     DF_CHECK(launch_compact_rows(ca, stream));
     c.m_live = ca.seq_row0 + B;
     c.row_map = ca.row_map;
@@ -671,7 +676,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
   const int epi = smp != nullptr ? EPI_SAMPLE : EPI_ARGMAX;
   // one key (and with sampling one (max, sum) pair) per row and column tile
   const GemmPlan hp = gemm_plan(d, epi, a.M, a.n_tiles, a.S, false, partial_bytes(d));
-  a.n_parts = hp.tiled ? cdiv(a.n_tiles, hp.mt / kBN) : a.n_tiles;
+  a.n_parts = hp.tiled ? cdiv(a.n_tiles, tile_cols(hp.mt) / kBN) : a.n_tiles;
   if (smp != nullptr) {
     a.inv_temp = 1.f / smp->temperature;
     a.seed = smp->seed;
@@ -820,11 +825,26 @@ int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const v
   const Layout L = layout(d);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < L.total) return DFLASH_E_WORKSPACE;
 
-  const Ctx c{d, L, P, static_cast<char*>(workspace), static_cast<const char*>(w->packed), cache->dev_error};
+  Ctx c{d, L, P, static_cast<char*>(workspace), static_cast<const char*>(w->packed), cache->dev_error};
   const int D = d.hidden;
   const int Mi = d.batch * n_max;
   const int K = d.n_taps * d.tap_dim;
   const int tph = d.head_dim / kBN;
+  // both GEMMs on the tiled kernel: only the n_rows[b] rows of each sequence are
+  // multiplied (compacted), not n_max
+  if (use_tiled(d, Mi)) {
+    CompactArgs ca;
+    ca.counts = n_rows;
+    ca.seq_row0 = c.at<int32_t>(L.seq_row0);
+    ca.row_map = c.at<int32_t>(L.row_map);
+    ca.batch = d.batch;
+    ca.rows_per_seq = n_max;
+    ca.dev_error = cache->dev_error;
+    ca.err_bit = DFLASH_DEVERR_ROWS;
+    DF_CHECK(launch_compact_rows(ca, stream));
+    c.m_live = ca.seq_row0 + d.batch;
+    c.row_map = ca.row_map;
+  }
 
   GemmArgs a = base_args(c);
   a.A = taps;

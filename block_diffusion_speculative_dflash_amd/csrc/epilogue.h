@@ -119,8 +119,8 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
       int b = m / g.rows_per_seq, i = m % g.rows_per_seq;
       if (g.row_map != nullptr) {
         const int e = g.row_map[m];
-        b = e >> 6;
-        i = e & 63;
+        b = e / g.rows_per_seq;
+        i = e % g.rows_per_seq;
       }
       int n_valid = g.rows_per_seq;
       if constexpr (EPI == EPI_INJECT) {

@@ -84,23 +84,30 @@ struct GemmArgs {
   const unsigned long long* step_dev;  // when set, the step is read from here at run time
   float2* lse_part;
   int n_parts;
-  // compacted block rows (draft step, runtime block size, tiled GEMMs): rows at or
-  // beyond *m_live do not exist (their tiles exit, the epilogues skip them), and
-  // row m is (sequence, position) = (row_map[m] >> 6, row_map[m] & 63); nullptr: all
-  // M rows, row m = (m / rows_per_seq, m % rows_per_seq)
+  // compacted rows (tiled GEMMs of a draft step with per-sequence block lengths or
+  // of an injection with per-sequence row counts): rows at or beyond *m_live do not
+  // exist (their tiles exit, the epilogues skip them), and live row m stands for
+  // uncompacted row row_map[m] (sequence row_map[m] / rows_per_seq, position
+  // row_map[m] % rows_per_seq; the fusion GEMM gathers that tap row); nullptr: all M
+  // rows, uncompacted
   const int32_t* m_live;
   const int32_t* row_map;
 };
 
 struct GemmPlan {
   int tiled;    // 0: weight-streaming GEMM, 1: tiled MFMA GEMM
-  int mt;       // streaming: 16-row MFMA blocks per workgroup (1, 2 or 4); tiled: kTile128 / kTile256
+  int mt;       // streaming: 16-row MFMA blocks per workgroup (1, 2 or 4); tiled: a kTile* shape
   int m_tiles, n_tiles, splits, steps_per_split, depth;
   int piece_base, piece_extra;  // streaming: balanced K pieces (0: uniform splits)
 };
 
-constexpr int kTile128 = 128;  // tiled GEMM: 128 x 128 tiles, 4 wavefronts, two workgroups per CU
-constexpr int kTile256 = 256;  // tiled GEMM: 256 x 256 tiles, 8 wavefronts
+// tiled GEMM tile shapes (GemmPlan::mt)
+constexpr int kTile128 = 128;        // 128 x 128, 4 wavefronts of 64 x 64, two workgroups per CU
+constexpr int kTile256 = 256;        // 256 x 256, 8 wavefronts of 128 x 64
+constexpr int kTile128x384 = 1384;   // 128 x 384, 8 wavefronts of 64 x 96
+constexpr int kTile256x128 = 2128;   // 256 x 128, 8 wavefronts of 64 x 64
+inline int tile_rows(int cfg) { return cfg == kTile128x384 ? 128 : (cfg == kTile256x128 ? 256 : cfg); }
+inline int tile_cols(int cfg) { return cfg == kTile128x384 ? 384 : (cfg == kTile256x128 ? 128 : cfg); }
 
 // f32: true for an fp32 drafter, false for a bf16 drafter (fp16 compute)
 hipError_t launch_gemm(int epi, bool f32, const GemmPlan& plan, const GemmArgs& args,

@@ -47,7 +47,7 @@ struct TileCfg {
   static constexpr int TILE = BM * (kBN + 4) * 4;
   static constexpr int BYTES = MAIN > TILE ? MAIN : TILE;
   static_assert(FR % NW == 0, "chunks split evenly over the wavefronts");
-  static_assert(WN % 4 == 0 || 4 % WN == 0, "wavefront column blocks align with 64-column subtiles");
+  static_assert(WN % 2 == 0, "pairs of 16-column blocks (the sampled noise layout)");
   static_assert(BFR % 4 == 0, "whole 64-column subtiles");
 };
 
@@ -107,7 +107,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
         src[j] = static_cast<const char*>(g.A) + ((static_cast<size_t>(mb) * g.S + s_lo) * 512 + lane * 8) * 2;
         stride[j] = 1024;
       } else {
-        const int row = min(tm * BM + c * 16 + (lane & 15), g.M - 1);
+        int row = min(tm * BM + c * 16 + (lane & 15), M - 1);
+        if (g.row_map != nullptr) row = g.row_map[row];  // compacted rows: gather the tap row
         src[j] = static_cast<const char*>(g.A) +
                  (static_cast<size_t>(row) * g.lda + static_cast<size_t>(s_lo) * kKStep + (lane >> 4) * 8) * 2;
         stride[j] = kKStep * 2;
@@ -264,11 +265,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
           if (n < g.N) {
             const unsigned long long kj = argmax_key(v, n);
             key = kj > key ? kj : key;
-            if (g.logits != nullptr && m < M) {
-              const int e = g.row_map != nullptr ? g.row_map[m] : 0;
-              const int mo = g.row_map != nullptr ? (e >> 6) * g.rows_per_seq + (e & 63) : m;
-              g.logits[static_cast<size_t>(mo) * g.N + n] = v;
-            }
+            if (g.logits != nullptr && m < M)
+              g.logits[static_cast<size_t>(g.row_map != nullptr ? g.row_map[m] : m) * g.N + n] = v;
           }
         }
 #pragma unroll
@@ -426,6 +424,8 @@ static hipError_t launch_tile(const GemmPlan& p, const GemmArgs& a, hipStream_t 
   switch (p.mt) {
     case kTile256: return launch_cfg<EPI, 2, 4, 8, 4>(p, a, s);
     case kTile128: return launch_cfg<EPI, 2, 2, 4, 4>(p, a, s);
+    case kTile128x384: return launch_cfg<EPI, 2, 4, 4, 6>(p, a, s);
+    case kTile256x128: return launch_cfg<EPI, 4, 2, 4, 4>(p, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -154,15 +154,18 @@ hipError_t launch_verify_sampled(const VerifySampledArgs& a, hipStream_t stream)
 hipError_t launch_commit_rows(int32_t* ctx_len, const int32_t* n_rows, int batch, int n_max,
                               uint32_t* dev_error, hipStream_t stream);
 
-// Compaction of the block rows (runtime block size at large batch): sequence b keeps
-// its block_len[b] rows (clamped to [0, k]), numbered consecutively in sequence
-// order.  seq_row0[b] = first row of b, seq_row0[B] = number of live rows;
-// row_map[m] = (b << 6) | i for the live rows m (k <= 63).  One workgroup.
+// Compaction of per-sequence row blocks (the draft step's blocks of block_len[b]
+// rows, an injection's n_rows[b] rows): sequence b keeps counts[b] rows (clamped to
+// [0, rows_per_seq]; out-of-range counts set err_bit), numbered consecutively in
+// sequence order.  seq_row0[b] = first row of b, seq_row0[B] = number of live rows;
+// row_map[m] = b * rows_per_seq + i, the uncompacted row of live row m.  One workgroup.
 struct CompactArgs {
-  const int32_t* block_len;  // [B]
-  int32_t* seq_row0;         // [B + 1]
-  int32_t* row_map;          // [B * k]
-  int batch, block_k;
+  const int32_t* counts;  // [B]
+  int32_t* seq_row0;      // [B + 1]
+  int32_t* row_map;       // [B * rows_per_seq]
+  int batch, rows_per_seq;
+  uint32_t* dev_error;
+  uint32_t err_bit;
 };
 hipError_t launch_compact_rows(const CompactArgs& a, hipStream_t stream);
 

@@ -20,8 +20,8 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(EmbedArgs a) {
   if (a.row_map != nullptr) {  // compacted block rows: row m is (b, i) of the map, if live
     if (m >= *a.m_live) return;
     const int e = a.row_map[m];
-    b = e >> 6;
-    i = e & 63;
+    b = e / a.block_k;
+    i = e % a.block_k;
   }
   const int d = a.hidden;
   int tok = a.anchor[b];
@@ -81,7 +81,9 @@ __global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(CompactAr
   __syncthreads();
   for (int base = 0; base < a.batch; base += kCompactThreads) {
     const int b = base + tid;
-    const int kb = b < a.batch ? min(max(a.block_len[b], 0), a.block_k) : 0;
+    const int raw = b < a.batch ? a.counts[b] : 0;
+    if (raw < 0 || raw > a.rows_per_seq) atomicOr(a.dev_error, a.err_bit);
+    const int kb = min(max(raw, 0), a.rows_per_seq);
     int incl = kb;  // inclusive scan within the wavefront
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(CompactAr
     const int row0 = before + incl - kb;
     if (b < a.batch) {
       a.seq_row0[b] = row0;
-      for (int i = 0; i < kb; ++i) a.row_map[row0 + i] = (b << 6) | i;
+      for (int i = 0; i < kb; ++i) a.row_map[row0 + i] = b * a.rows_per_seq + i;
     }
     __syncthreads();  // every thread has read carry_s and wave_tot
     if (tid == kCompactThreads - 1) carry_s = row0 + kb;
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(CompactAr
 }
 
 hipError_t launch_compact_rows(const CompactArgs& a, hipStream_t stream) {
-  if (a.batch <= 0 || a.block_k <= 0 || a.block_k > 63) return hipErrorInvalidValue;
+  if (a.batch <= 0 || a.rows_per_seq <= 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(kCompactThreads), 0, stream, a);
   return hipGetLastError();
 }
