@@ -9,8 +9,8 @@
 //    by the producing epilogue), so one K step of a 16-row (or 16-column) block is
 //    one contiguous 1 KB chunk, exactly one wavefront MFMA operand.  Chunks go from
 //    HBM/L2 straight into LDS with the gfx950 16-byte LDS-DMA load (64 lanes x 16 B
-//    = 1 KB per instruction, no staging registers), four stages deep: the loads of
-//    step s+3 are in flight while step s is multiplied.  The fusion GEMM's A operand
+//    = 1 KB per instruction, no staging registers), into four stage buffers: the
+//    loads of steps s+2..s+4 are in flight while step s is multiplied.  The fusion GEMM's A operand
 //    is the caller's row-major taps; there each lane supplies its own row address and
 //    the DMA gathers the same fragment layout.
 //  * Wavefront (wm, wn) owns WM x WN blocks of 16 x 16; its fragments for step s+1
@@ -51,7 +51,21 @@ struct TileCfg {
   static_assert(BFR % 4 == 0, "whole 64-column subtiles");
 };
 
+// Larger of a 64-bit key and the key of the lane DPP control CTRL selects (a
+// permutation inside each row of 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max_key(unsigned long long k) {
+  const uint32_t lo =
+      static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(k)), CTRL, 0xF, 0xF, true));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(k >> 32)), CTRL, 0xF, 0xF, true));
+  const unsigned long long o = (static_cast<unsigned long long>(hi) << 32) | lo;
+  return o > k ? o : k;
+}
+
 constexpr int vmcnt_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// vmcnt <= n and every LDS read of this wavefront complete (lgkmcnt 0)
+constexpr int vm_lgkm_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
 
 // 1 KB DMA: lane l's 16 bytes at gp land at LDS byte lds + 16 * l.  m0 (the LDS
 // base of the DMA) is declared clobbered; no other code in these kernels uses m0.
@@ -71,7 +85,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   typedef typename std::conditional<EPI == EPI_FUSE, bf16x8, f16x8>::type E8;
 
   __shared__ __attribute__((aligned(1024))) char smem[C::BYTES];
-  __shared__ float rs_s[BM];
+  __shared__ __attribute__((aligned(16))) float rs_s[BM];
   __shared__ unsigned long long best_s[BM];
   __shared__ int last_s;
 
@@ -141,23 +155,42 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
 #pragma unroll
     for (int i = 0; i < WM; ++i) fa[i] = *reinterpret_cast<const E8*>(st + (wm * WM + i) * 512 + lane * 8);
   };
-  auto mma = [&](const E8* fa, const E8* fb) {
+  // One step's work in LPW chunks: chunk c issues its share of the next step's
+  // fragment reads and of this step's MFMAs (interleaved), then, when `dma`, the c-th
+  // of this wavefront's DMA loads of stage ds into buffer db.  Spreading the DMA
+  // issue over the step keeps it from holding back the MFMA stream after a barrier.
+  auto step_work = [&](int buf_next, const E8* fa, const E8* fb, E8* fan, E8* fbn, bool dma, int ds, int db) {
+    const E* st = reinterpret_cast<const E*>(smem + buf_next * C::STAGE);
+    auto chunk = [&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      constexpr int MM = WM * WN, NR = WM + WN;
+      constexpr int q0 = c * MM / LPW, q1 = (c + 1) * MM / LPW;
+      constexpr int r0 = c * NR / LPW, r1 = (c + 1) * NR / LPW;
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+      for (int r = r0; r < r1; ++r) {
+        if (r < WN) fbn[r] = *reinterpret_cast<const E8*>(st + (AFR + wn * WN + r) * 512 + lane * 8);
+        else fan[r - WN] = *reinterpret_cast<const E8*>(st + (wm * WM + r - WN) * 512 + lane * 8);
+      }
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
+      for (int q = q0; q < q1; ++q) {
+        const int i = q / WN, j = q % WN;
         if constexpr (EPI == EPI_FUSE) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         else acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
-  };
-  auto interleave = [&]() {
-    constexpr int NR = WM + WN, PER = (WM * WN) / NR;
+      constexpr int nm = q1 - q0, nr = r1 - r0, per = nm / (nr + 1);
 #pragma unroll
-    for (int rr = 0; rr < NR; ++rr) {
-      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, WM * WN - PER * NR, 0);
+      for (int k = 0; k < nr; ++k) {
+        if constexpr (per > 0) __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
+      }
+      if constexpr (nm - per * nr > 0) __builtin_amdgcn_sched_group_barrier(0x008, nm - per * nr, 0);
+      if (dma) dma_1k(src[c] + static_cast<size_t>(ds) * stride[c], ldsoff[c] + db * C::STAGE);
+    };
+    static_assert(LPW >= 1 && LPW <= 4, "one to four DMA loads per wavefront and stage");
+    chunk(std::integral_constant<int, 0>{});
+    if constexpr (LPW > 1) chunk(std::integral_constant<int, 1>{});
+    if constexpr (LPW > 2) chunk(std::integral_constant<int, 2>{});
+    if constexpr (LPW > 3) chunk(std::integral_constant<int, 3>{});
   };
 
   // RMSNorm factor of this tile's A rows (thread r < BM: row m0 + r).  The partial
@@ -176,11 +209,13 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
     }
   }
 
-  // prologue: stages 0..2 in flight, wait for 0 and 1
+  // prologue: stages 0..3 in flight, wait for 0 and 1
   issue(0, 0);
   if (1 < S) issue(1, 1);
   if (2 < S) issue(2, 2);
-  if (2 < S) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LPW));
+  if (3 < S) issue(3, 3);
+  if (3 < S) __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * LPW));
+  else if (2 < S) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LPW));
   else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
   if (tid < BM) {
     float f = 1.f;
@@ -200,19 +235,26 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   read(0, fa0, fb0);
+  if (4 < S) {  // stage 4 goes into buffer 0 at step 0: every wavefront has its stage-0 fragments
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(63));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
   // Step t multiplies the fragments read during step t-1 and reads those of step
-  // t+1 (stage t+1 landed at the end of step t-1).  The DMA of step t+3 reuses the
-  // buffer of step t-1, whose last reads completed before the barrier ending t-1.
+  // t+1 (stage t+1 landed at the end of step t-1).  The DMA of stage t+4 goes into
+  // the buffer of stage t: every wavefront's reads of stage t completed (lgkmcnt 0)
+  // before the barrier that ended step t-1, so four stages are in flight and a DMA
+  // has three steps to land.
   for (int s = 0; s < S; s += 4) {
 #define DFLASH_STEP(u, fac, fbc, fan, fbn)                                    \
   if (s + u < S) {                                                            \
-    if (s + u + 3 < S) issue(s + u + 3, (u + 3) & 3);                         \
-    read((u + 1) & 3, fan, fbn);                                              \
-    mma(fac, fbc);                                                            \
-    interleave();                                                             \
+    step_work((u + 1) & 3, fac, fbc, fan, fbn, s + u + 4 < S, s + u + 4, u);  \
     if (s + u + 2 < S) {                                                      \
-      if (s + u + 3 < S) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LPW));         \
-      else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));                         \
+      asm volatile("" ::: "memory");                                          \
+      if (s + u + 4 < S) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * LPW));   \
+      else if (s + u + 3 < S) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(LPW));  \
+      else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));                       \
       __builtin_amdgcn_s_barrier();                                           \
       asm volatile("" ::: "memory");                                          \
     }                                                                         \
@@ -247,35 +289,55 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   }
 
   if constexpr (EPI == EPI_ARGMAX) {
-    // split-vocab argmax straight from the accumulators: per lane, the best of its
-    // WN columns for each of its rows, then across the 16 lanes that share those rows
-    // (xor 1, 2, 4, 8), then across the NWN column wavefronts through an LDS max
+    if (g.logits != nullptr) {  // logits out (uniform branch; tests only)
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = (wm * WM + i) * 16 + 4 * (lane >> 4) + rr, m = m0 + r;
+          if (m >= M) continue;
+          const size_t mo = g.row_map != nullptr ? g.row_map[m] : m;
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            const int n = (tn * BFR + wn * WN + j) * 16 + (lane & 15);
+            if (n < g.N) g.logits[mo * g.N + n] = acc[i][j][rr] * rs_s[r];
+          }
+        }
+    }
+    // split-vocab argmax straight from the accumulators, without branches: per lane
+    // and row the largest 64-bit key of its WN columns (columns past N count as key
+    // 0), then across the 16 lanes that share the row with DPP (xor 1, xor 2, half-row
+    // mirror, row mirror), then across the NWN column wavefronts through an LDS max
+    uint32_t nlo[WN], ok[WN];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int n = (tn * BFR + wn * WN + j) * 16 + (lane & 15);
+      nlo[j] = 0xFFFFFFFFu - static_cast<uint32_t>(n);
+      ok[j] = n < g.N ? 0xFFFFFFFFu : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const float4 f4 = *reinterpret_cast<const float4*>(&rs_s[(wm * WM + i) * 16 + 4 * (lane >> 4)]);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int r = (wm * WM + i) * 16 + 4 * (lane >> 4) + rr;
-        const int m = m0 + r;
-        const float f = rs_s[r];
+        const float f = rr == 0 ? f4.x : (rr == 1 ? f4.y : (rr == 2 ? f4.z : f4.w));
         unsigned long long key = 0ull;
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
-          const int n = (tn * BFR + wn * WN + j) * 16 + (lane & 15);
-          const float v = acc[i][j][rr] * f;
-          if (n < g.N) {
-            const unsigned long long kj = argmax_key(v, n);
-            key = kj > key ? kj : key;
-            if (g.logits != nullptr && m < M)
-              g.logits[static_cast<size_t>(g.row_map != nullptr ? g.row_map[m] : m) * g.N + n] = v;
-          }
+          const uint32_t u = __float_as_uint(acc[i][j][rr] * f);
+          const uint32_t o = u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
+          const unsigned long long kj =
+              (static_cast<unsigned long long>(o & ok[j]) << 32) | static_cast<unsigned long long>(nlo[j] & ok[j]);
+          key = kj > key ? kj : key;
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const unsigned long long other = __shfl_xor(key, o, kWave);
-          key = other > key ? other : key;
-        }
+        key = dpp_max_key<0xB1>(key);   // quad_perm [1,0,3,2]
+        key = dpp_max_key<0x4E>(key);   // quad_perm [2,3,0,1]
+        key = dpp_max_key<0x141>(key);  // row_half_mirror
+        key = dpp_max_key<0x140>(key);  // row_mirror
         if ((lane & 15) == 0 && key != 0ull) atomicMax(&best_s[r], key);
       }
+    }
   } else if constexpr (EPI == EPI_SAMPLE) {
     // sampled drafts straight from the accumulators: for each pair of adjacent 16 x 16
     // column blocks (2p, 2p + 1) one Philox block gives the noise of the lane's 4 rows
