@@ -128,7 +128,7 @@ size_t partial_bytes(const dflash_dims& d);
 
 struct Layout {
   size_t h, xa, ssq, q, kb, vb, o, act, cu, ssq_c, partials, counters, keys, attn_cnt, attn_o,
-      attn_ml, lse_part, v_part, v_cnt, v_rowlse, v_dec, v_keys, xa2, ssq2, sig, row_map, seq_row0, total;
+      attn_ml, lse_part, v_part, v_cnt, v_rowlse, v_dec, v_keys, xa2, ssq2, sig, row_map, seq_row0, rope, total;
   int v_chunks;
   int np_d, S_d, S_o, S_f;
   AttnPlan ap;
@@ -185,6 +185,8 @@ Layout layout(const dflash_dims& d) {
   // compacted rows: blocks of the runtime block size / injection rows, large batches
   L.row_map = take(std::max(Mb, Mi) * 4);
   L.seq_row0 = take((size_t(d.batch) + 1) * 4);
+  // (sin, cos) of the rows' rotation angles for the tiled QKV / injection epilogues
+  L.rope = take(std::max(Mb, Mi) * (d.head_dim / 2) * 8);
   L.total = off;
   return L;
 }
@@ -261,7 +263,8 @@ GemmPlan tiled_plan(int M, int n_tiles, int S, bool allow_split, size_t partial_
       if (splits != want) continue;
       if (splits > 1) {
         if (sps < 16) continue;
-        if (double(splits) * M * n_tiles * kBN * 4 > double(partial_cap)) continue;
+        // partials of whole tiles, padding included
+        if (double(splits) * m_tiles * bm * n_big * bn * 4 > double(partial_cap)) continue;
         if (size_t(m_tiles) * n_big > size_t(kGemmCounters)) continue;
       }
       const long long n = static_cast<long long>(m_tiles) * n_big * splits;
@@ -326,7 +329,9 @@ size_t partial_bytes(const dflash_dims& d) {
   for (const G& g : gs) {
     if (!use_tiled(d, g.M)) continue;
     const GemmPlan p = tiled_plan(g.M, g.n_tiles, g.S, true, kPartialMax);
-    if (p.splits > 1) need = std::max(need, size_t(p.splits) * g.M * g.n_tiles * kBN * 4);
+    if (p.splits > 1)
+      need = std::max(need, size_t(p.splits) * p.m_tiles * tile_rows(p.mt) *
+                                cdiv(g.n_tiles, tile_cols(p.mt) / kBN) * tile_cols(p.mt) * 4);
   }
   return need;
 }
@@ -488,6 +493,14 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
       return DFLASH_E_UNSUPPORTED;
     DF_CHECK(launch_fill_zero(c.at<void>(L.sig), size_t(d.n_layers) * kSigWords * 4, stream));
   }
+  // the tiled QKV epilogue reads the rows' rotation angles from a table built once
+  // per step (every layer rotates the same positions)
+  const float2* rope_tab = nullptr;
+  if (use_tiled(d, Mb) && !persistent) {
+    RopeTabArgs ra{cache->ctx_len, c.at<float2>(L.rope), B, k, d.head_dim, d.rope_theta};
+    DF_CHECK(launch_rope_table(ra, stream));
+    rope_tab = ra.tab;
+  }
   const int hq_dh = d.n_q_heads * d.head_dim;
   const size_t layer_cache = size_t(B) * d.n_kv_heads * d.cache_slots * d.head_dim * e;
   auto gain = [&](const void* base, int l) { return static_cast<const char*>(base) + size_t(l) * D * e; };
@@ -551,6 +564,7 @@ int draft_impl(const dflash_dims* dims, const dflash_weights* w, const dflash_ca
     a.out3 = c.at<void>(L.vb);
     a.rows_per_seq = k;
     a.ctx_len = cache->ctx_len;
+    a.rope_tab = rope_tab;
     if (int st = stage_gemm(0, EPI_QKV, a)) return st;
 
     // block attention over window + block
@@ -831,7 +845,9 @@ int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const v
   const int K = d.n_taps * d.tap_dim;
   const int tph = d.head_dim / kBN;
   // both GEMMs on the tiled kernel: only the n_rows[b] rows of each sequence are
-  // multiplied (compacted), not n_max
+  // multiplied (compacted), not n_max, and the injection epilogue reads the rows'
+  // rotation angles from a table
+  const float2* rope_tab = nullptr;
   if (use_tiled(d, Mi)) {
     CompactArgs ca;
     ca.counts = n_rows;
@@ -844,6 +860,9 @@ int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const v
     DF_CHECK(launch_compact_rows(ca, stream));
     c.m_live = ca.seq_row0 + d.batch;
     c.row_map = ca.row_map;
+    RopeTabArgs ra{cache->ctx_len, c.at<float2>(L.rope), d.batch, n_max, d.head_dim, d.rope_theta};
+    DF_CHECK(launch_rope_table(ra, stream));
+    rope_tab = ra.tab;
   }
 
   GemmArgs a = base_args(c);
@@ -881,6 +900,7 @@ int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const v
   a.n_rows = n_rows;
   a.cache_k = cache->k;
   a.cache_v = cache->v;
+  a.rope_tab = rope_tab;
   if (int st = run_gemm(EPI_INJECT, c, a, true, stream)) return st;
 
   if (commit) DF_CHECK(launch_commit_rows(cache->ctx_len, n_rows, d.batch, n_max, cache->dev_error, stream));

@@ -52,6 +52,17 @@ __device__ __forceinline__ void report_overflow(bool bad, uint32_t* dev_error) {
   if (bad && dev_error != nullptr) atomicOr(dev_error, kErrOverflow);
 }
 
+// Sum over each aligned group of 8 lanes (every lane of the group gets it): DPP
+// quad permutations for the pairs and quads, then the half-row mirror for the other
+// quad of the 8.  The same additions, in the same pairing, as an xor 1, 2, 4
+// butterfly.
+__device__ __forceinline__ float dpp_sum8(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return x;
+}
+
 // Activation / compute type of a drafter whose weights arrive as T: bf16 drafters
 // compute in fp16, fp32 drafters in fp32.
 template <typename T> struct ActOf;

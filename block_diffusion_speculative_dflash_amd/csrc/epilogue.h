@@ -17,6 +17,7 @@
 
 #include "common.h"
 #include "gemm.h"
+#include "philox.h"
 
 namespace dflash {
 
@@ -30,78 +31,100 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
   typedef typename ActOf<TIN>::type TA;
   const int tid = threadIdx.x;
   bool bad = false;
+  typedef TA TA8 __attribute__((ext_vector_type(8)));
   if constexpr (EPI == EPI_FUSE || EPI == EPI_RESID) {
-    // 8 threads per row, 8 consecutive columns each: one packed 8-element store
+    // 8 threads per row, 8 consecutive columns each: one packed 8-element store.
+    // The gains (the same columns in every pass) and the residual rows of all
+    // passes are loaded before anything is computed, so their latencies overlap.
     constexpr int RPP = NT / 8;  // rows per pass
+    constexpr int IT = (BM + RPP - 1) / RPP;
     TA* out = static_cast<TA*>(g.out);
     const TIN* gain = static_cast<const TIN*>(g.gain);
     const int c8 = tid & 7;
+    const int n0 = tile_n * kBN + c8 * 8;
+    const bool col_ok = n0 < g.N;
+    float gn[8];  // several passes: loaded once, up front
+    if constexpr (IT > 1) {
 #pragma unroll
-    for (int it = 0; it < (BM + RPP - 1) / RPP; ++it) {
+      for (int j = 0; j < 8; ++j) gn[j] = col_ok ? to_f32(gain[n0 + j]) : 0.f;
+    }
+    float hv[EPI == EPI_RESID ? IT : 1][8];
+    if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int r = (tid >> 3) + RPP * it, m = m0 + r;
+        if (hres != nullptr) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) hv[it][j] = hres[it][j];
+        } else if (r < BM && m < m_end && col_ok) {
+          const float4* hp = reinterpret_cast<const float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
+          const float4 h0 = get16<COH, float4>(hp), h1 = get16<COH, float4>(hp + 1);
+          hv[it][0] = h0.x; hv[it][1] = h0.y; hv[it][2] = h0.z; hv[it][3] = h0.w;
+          hv[it][4] = h1.x; hv[it][5] = h1.y; hv[it][6] = h1.z; hv[it][7] = h1.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
       const int r = (tid >> 3) + RPP * it;
       const int m = m0 + r;
-      const int n0 = tile_n * kBN + c8 * 8;
       float ss = 0.f;
-      if (r < BM && m < m_end && n0 < g.N) {
-        TA* dst = out + pa_index(m, n0, g.out_steps);
+      if (r < BM && m < m_end && col_ok) {
         float x[8];
-        float hv[8];
-        if constexpr (EPI == EPI_RESID) {
-          if (hres != nullptr) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) hv[j] = hres[it][j];
-          } else {
-            const float4* hp = reinterpret_cast<const float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
-            const float4 h0 = get16<COH, float4>(hp), h1 = get16<COH, float4>(hp + 1);
-            hv[0] = h0.x; hv[1] = h0.y; hv[2] = h0.z; hv[3] = h0.w;
-            hv[4] = h1.x; hv[5] = h1.y; hv[6] = h1.z; hv[7] = h1.w;
-          }
-        }
-        typedef TA TA8 __attribute__((ext_vector_type(8)));
         TA8 y;
+        const float f = rs[r];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          x[j] = tile[r][c8 * 8 + j] * rs[r];
-          if constexpr (EPI == EPI_RESID) x[j] += hv[j];
+          x[j] = tile[r][c8 * 8 + j] * f;
+          if constexpr (EPI == EPI_RESID) x[j] += hv[it][j];
           ss += x[j] * x[j];
-          y[j] = to_act<TA>(x[j] * to_f32(gain[n0 + j]), bad);
-          if constexpr (!COH) dst[j] = y[j];
+          y[j] = to_act<TA>(x[j] * (IT > 1 ? gn[j] : to_f32(gain[n0 + j])), bad);
         }
-        if constexpr (COH) coherent_store16(dst, y);  // 8 fp16 activations = 16 bytes
+        put16<COH>(out + pa_index(m, n0, g.out_steps), y);  // 8 activations, 16 bytes (fp16)
         if constexpr (EPI == EPI_RESID) {
           float4* hp = reinterpret_cast<float4*>(g.h + static_cast<size_t>(m) * g.N + n0);
           put16<COH>(hp, make_float4(x[0], x[1], x[2], x[3]));
           put16<COH>(hp + 1, make_float4(x[4], x[5], x[6], x[7]));
         }
       }
-      ss += __shfl_xor(ss, 1, kWave);
-      ss += __shfl_xor(ss, 2, kWave);
-      ss += __shfl_xor(ss, 4, kWave);
+      ss = dpp_sum8(ss);
       if (c8 == 0 && r < BM && m < m_end) put<COH>(&g.ssq_out[static_cast<size_t>(m) * g.np_out + tile_n], ss);
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
+    // 4 threads per row, 8 consecutive (gate, up) pairs each: one packed 16-byte store
+    constexpr int RPP = NT / 4;
     TA* act = static_cast<TA*>(g.out);
-    for (int idx = tid; idx < BM * 32; idx += NT) {
-      const int r = idx >> 5, p = idx & 31, m = m0 + r;
-      const int j = tile_n * 32 + p;
-      if (m >= m_end) continue;
-      // columns past ffn are the down projection's K padding: written as zeros, so
-      // the product never depends on what the workspace held before
-      float y = 0.f;
-      if (j < g.ffn) {
-        const float gv = tile[r][p] * rs[r];
-        const float uv = tile[r][p + 32] * rs[r];
-        y = gv / (1.f + expf(-gv)) * uv;
+    const int p0 = (tid & 3) * 8;
+    const int j0 = tile_n * 32 + p0;
+#pragma unroll
+    for (int it = 0; it < (BM + RPP - 1) / RPP; ++it) {
+      const int r = (tid >> 2) + RPP * it, m = m0 + r;
+      if (r >= BM || m >= m_end) continue;
+      const float f = rs[r];
+      const float4 ga = *reinterpret_cast<const float4*>(&tile[r][p0]);
+      const float4 gb = *reinterpret_cast<const float4*>(&tile[r][p0 + 4]);
+      const float4 ua = *reinterpret_cast<const float4*>(&tile[r][p0 + 32]);
+      const float4 ub = *reinterpret_cast<const float4*>(&tile[r][p0 + 36]);
+      const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      const float uv[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+      TA8 y;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        // columns past ffn are the down projection's K padding: written as zeros, so
+        // the product never depends on what the workspace held before
+        float v = 0.f;
+        if (j0 + q < g.ffn) {
+          const float gq = gv[q] * f, uq = uv[q] * f;
+          v = gq * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gq * kLog2e)) * uq;
+        }
+        y[q] = to_act<TA>(v, bad);
       }
-      put<COH>(&act[pa_index(m, j, g.out_steps)], to_act<TA>(y, bad));
+      put16<COH>(act + pa_index(m, j0, g.out_steps), y);
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     const int dh = g.head_dim, half = dh / 2;
     const int tph = dh / kBN;
     const int sub = tile_n % tph;
-    const int p = tid & 31;  // constant per thread: NT is a multiple of 32
-    const int d1 = sub * 32 + p;
-    const double inv_freq = rope_inv_freq(d1, dh, g.theta);
     int kind, head, layer = 0;  // kind 0 = q, 1 = k, 2 = v
     if constexpr (EPI == EPI_QKV) {
       const int hd = tile_n / tph;
@@ -113,10 +136,11 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
       kind = hd < g.n_kv_heads ? 1 : 2;
       head = kind == 1 ? hd : hd - g.n_kv_heads;
     }
-    for (int idx = tid; idx < BM * 32; idx += NT) {
-      const int r = idx >> 5, m = m0 + r;
-      if (m >= m_end) continue;
-      int b = m / g.rows_per_seq, i = m % g.rows_per_seq;
+    // Which rows this call writes, and where: row m is (sequence b, block row i) at
+    // position max(ctx_len[b], 0) + i.  Returns false for rows it skips.
+    auto row_target = [&](int m, int lead, int& b, int& i, int& pos) -> bool {
+      b = m / g.rows_per_seq;
+      i = m % g.rows_per_seq;
       if (g.row_map != nullptr) {
         const int e = g.row_map[m];
         b = e / g.rows_per_seq;
@@ -125,35 +149,102 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
       int n_valid = g.rows_per_seq;
       if constexpr (EPI == EPI_INJECT) {
         const int nr = g.n_rows[b];
-        if ((nr < 0 || nr > g.rows_per_seq) && i == 0 && p == 0) atomicOr(g.dev_error, kErrRows);
+        if ((nr < 0 || nr > g.rows_per_seq) && i == 0 && lead) atomicOr(g.dev_error, kErrRows);
         n_valid = min(max(nr, 0), g.rows_per_seq);
       }
-      if (i >= n_valid) continue;
-      const int pos = max(g.ctx_len[b], 0) + i;
+      if (i >= n_valid) return false;
+      pos = max(g.ctx_len[b], 0) + i;
       // A call with more than C - s ring rows for one sequence: rows i and
       // i + (C - s) share a slot, and writes in position order leave the later one,
       // so the earlier row is not written at all (no two writers race on a slot).
       if constexpr (EPI == EPI_INJECT)
-        if (pos >= g.sink && i + (g.cache_slots - g.sink) < n_valid) continue;
-      const float x1 = tile[r][p] * rs[r], x2 = tile[r][p + 32] * rs[r];
-      float y1 = x1, y2 = x2;
-      if (kind != 2) {
-        float sn, cs;
-        rope_sincos(pos, inv_freq, &sn, &cs);
-        y1 = x1 * cs - x2 * sn;
-        y2 = x2 * cs + x1 * sn;
-      }
-      TA* dst;
+        if (pos >= g.sink && i + (g.cache_slots - g.sink) < n_valid) return false;
+      return true;
+    };
+    auto row_dst = [&](int m, int b, int pos) -> TA* {
       if constexpr (EPI == EPI_QKV) {
-        if (kind == 0) dst = static_cast<TA*>(g.out) + (static_cast<size_t>(m) * g.n_q_heads + head) * dh;
-        else dst = static_cast<TA*>(kind == 1 ? g.out2 : g.out3) + (static_cast<size_t>(m) * g.n_kv_heads + head) * dh;
+        if (kind == 0) return static_cast<TA*>(g.out) + (static_cast<size_t>(m) * g.n_q_heads + head) * dh;
+        return static_cast<TA*>(kind == 1 ? g.out2 : g.out3) + (static_cast<size_t>(m) * g.n_kv_heads + head) * dh;
       } else {
         const int slot = pos < g.sink ? pos : g.sink + (pos - g.sink) % (g.cache_slots - g.sink);
-        dst = static_cast<TA*>(kind == 1 ? g.cache_k : g.cache_v) +
-              (((static_cast<size_t>(layer) * g.batch + b) * g.n_kv_heads + head) * g.cache_slots + slot) * dh;
+        return static_cast<TA*>(kind == 1 ? g.cache_k : g.cache_v) +
+               (((static_cast<size_t>(layer) * g.batch + b) * g.n_kv_heads + head) * g.cache_slots + slot) * dh;
       }
-      put<COH>(&dst[d1], to_act<TA>(y1, bad));
-      put<COH>(&dst[d1 + half], to_act<TA>(y2, bad));
+    };
+    if (g.rope_tab != nullptr) {
+      // 4 threads per row, 8 consecutive rotation pairs each, (sin, cos) from the
+      // table: two 16-byte stores per row quarter.  Row targets and angles of every
+      // pass are loaded first, so their latencies overlap.
+      constexpr int RPP = NT / 4;
+      constexpr int IT = (BM + RPP - 1) / RPP;
+      const int p0 = (tid & 3) * 8, d0 = sub * 32 + p0;
+      bool live[IT];
+      int rb[IT], rpos[IT];
+      float4 sc[IT][4];
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int r = (tid >> 2) + RPP * it, m = m0 + r;
+        int b = 0, i = 0, pos = 0;
+        live[it] = r < BM && m < m_end && row_target(m, (tid & 3) == 0, b, i, pos);
+        rb[it] = b;
+        rpos[it] = pos;
+        if (live[it] && kind != 2) {
+          const float4* tp = reinterpret_cast<const float4*>(g.rope_tab + (static_cast<size_t>(b) * g.rows_per_seq + i) * half + d0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sc[it][q] = tp[q];
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        if (!live[it]) continue;
+        const int r = (tid >> 2) + RPP * it, m = m0 + r;
+        const float f = rs[r];
+        float x1[8], x2[8];
+#pragma unroll
+        for (int q = 0; q < 8; q += 4) {
+          const float4 a4 = *reinterpret_cast<const float4*>(&tile[r][p0 + q]);
+          const float4 b4 = *reinterpret_cast<const float4*>(&tile[r][p0 + 32 + q]);
+          x1[q] = a4.x * f; x1[q + 1] = a4.y * f; x1[q + 2] = a4.z * f; x1[q + 3] = a4.w * f;
+          x2[q] = b4.x * f; x2[q + 1] = b4.y * f; x2[q + 2] = b4.z * f; x2[q + 3] = b4.w * f;
+        }
+        TA8 y1, y2;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float v1 = x1[q], v2 = x2[q];
+          if (kind != 2) {
+            const float4 t = sc[it][q >> 1];
+            const float sn = (q & 1) ? t.z : t.x, cs = (q & 1) ? t.w : t.y;
+            v1 = x1[q] * cs - x2[q] * sn;
+            v2 = x2[q] * cs + x1[q] * sn;
+          }
+          y1[q] = to_act<TA>(v1, bad);
+          y2[q] = to_act<TA>(v2, bad);
+        }
+        TA* dst = row_dst(m, rb[it], rpos[it]);
+        put16<COH>(dst + d0, y1);
+        put16<COH>(dst + d0 + half, y2);
+      }
+    } else {
+      const int p = tid & 31;  // constant per thread: NT is a multiple of 32
+      const int d1 = sub * 32 + p;
+      const double inv_freq = rope_inv_freq(d1, dh, g.theta);
+      for (int idx = tid; idx < BM * 32; idx += NT) {
+        const int r = idx >> 5, m = m0 + r;
+        if (m >= m_end) continue;
+        int b, i, pos;
+        if (!row_target(m, p == 0, b, i, pos)) continue;
+        const float x1 = tile[r][p] * rs[r], x2 = tile[r][p + 32] * rs[r];
+        float y1 = x1, y2 = x2;
+        if (kind != 2) {
+          float sn, cs;
+          rope_sincos(pos, inv_freq, &sn, &cs);
+          y1 = x1 * cs - x2 * sn;
+          y2 = x2 * cs + x1 * sn;
+        }
+        TA* dst = row_dst(m, b, pos);
+        put<COH>(&dst[d1], to_act<TA>(y1, bad));
+        put<COH>(&dst[d1 + half], to_act<TA>(y2, bad));
+      }
     }
   }
   report_overflow(bad, g.dev_error);

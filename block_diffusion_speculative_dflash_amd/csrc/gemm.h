@@ -48,7 +48,9 @@ struct GemmArgs {
   // piece p of P covers steps [p*S/P, (p+1)*S/P), and splits is the largest P.
   int splits, steps_per_split;
   int piece_base, piece_extra;
-  float* partials;     // [splits, M, n_tiles * kBN] fp32
+  // split-K partials, fp32: streaming GEMM [splits, M, n_tiles * kBN]; tiled GEMM
+  // [splits, m_tiles * n_big tiles, wavefront, WM, WN, lane] 16-byte accumulator blocks
+  float* partials;
   unsigned* counters;  // zero-initialised; one per (m tile, n tile), or per m tile (ARGMAX)
   // RMSNorm of the A rows, folded into the epilogue as a per-row factor
   const float* ssq_in;  // [M, np_in] partial sums of squares, or nullptr (factor 1)
@@ -70,6 +72,9 @@ struct GemmArgs {
   int n_q_heads, n_kv_heads, head_dim, n_layers, batch, cache_slots, ffn;
   int sink;  // INJECT: positions < sink keep slot = position; the rest ring over cache_slots - sink
   float theta;
+  // QKV / INJECT: when set, the (sin, cos) of row (b, i)'s position for rotation pair
+  // d, at rope_tab[(b * rows_per_seq + i) * head_dim / 2 + d], instead of computing it
+  const float2* rope_tab;
   void* cache_k;  // [L, B, Hkv, C, dh]
   void* cache_v;
   unsigned long long* keys;  // ARGMAX / SAMPLE: [M, n_parts] best key of each column tile

@@ -270,22 +270,48 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   float(*tile)[kBN + 4] = reinterpret_cast<float(*)[kBN + 4]>(smem);
   const size_t np = static_cast<size_t>(g.n_tiles) * kBN;
 
-  if (g.splits > 1) {
-    // partial tile straight from the accumulators (MFMA layout: lane l, register r
-    // holds row 4 * (l / 16) + r, column l % 16 of each 16 x 16 block)
+  if constexpr (EPI != EPI_ARGMAX && EPI != EPI_SAMPLE) {  // the LM head never splits K
+    if (g.splits > 1) {
+      // Split K.  Partials are kept in the accumulators' own layout (one 16-byte
+      // value per lane and 16 x 16 block), so every store and load moves a whole 1 KB
+      // per wavefront.  The last split to arrive reloads all of them, its own
+      // included, and sums them in split order (the same sum whichever split that is),
+      // then carries on with the epilogue as an unsplit tile would.
+      const size_t tiles_all = static_cast<size_t>(g.m_tiles) * n_big;
+      const size_t tile_id = static_cast<size_t>(tm) * n_big + tn;
+      f32x4* part = reinterpret_cast<f32x4*>(g.partials);
+      auto pidx = [&](int sp, int i, int j) -> size_t {
+        return ((((static_cast<size_t>(sp) * tiles_all + tile_id) * NW + wave) * WM + i) * WN + j) * kWave + lane;
+      };
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+      for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int j = 0; j < WN; ++j)
+        for (int j = 0; j < WN; ++j) coherent_store16(&part[pidx(split, i, j)], acc[i][j]);
+      unsigned* counter = &g.counters[tm * n_big + tn];
+      if (!arrive_last(counter, g.splits, &last_s)) return;
+      if (tid == 0) reset_counter(counter);
+      // Half of the wavefront's blocks at a time, split after split: the loads of one
+      // split's half (16 KB per wavefront for 256 x 256 tiles) are in flight together.
+      constexpr int NB = WM * WN, H = (NB + 1) / 2;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int m = m0 + (wm * WM + i) * 16 + 4 * (lane >> 4) + rr;
-          const size_t n = static_cast<size_t>(tn * BFR + wn * WN + j) * 16 + (lane & 15);
-          if (m < g.M && n < np) coherent_store(&g.partials[(static_cast<size_t>(split) * g.M + m) * np + n], acc[i][j][rr]);
+      for (int h = 0; h < 2; ++h) {
+        f32x4 sum[H];
+#pragma unroll 1
+        for (int sp = 0; sp < g.splits; ++sp) {
+          f32x4 v[H];
+#pragma unroll
+          for (int q = 0; q < H; ++q) {
+            const int bq = min(h * H + q, NB - 1);
+            v[q] = coherent_load16<f32x4>(&part[pidx(sp, bq / WN, bq % WN)]);
+          }
+#pragma unroll
+          for (int q = 0; q < H; ++q) sum[q] = sp == 0 ? v[q] : sum[q] + v[q];
         }
-    unsigned* counter = &g.counters[tm * n_big + tn];
-    if (!arrive_last(counter, g.splits, &last_s)) return;
-    if (tid == 0) reset_counter(counter);
+#pragma unroll
+        for (int q = 0; q < H; ++q)
+          if (h * H + q < NB) acc[(h * H + q) / WN][(h * H + q) % WN] = sum[q];
+      }
+    }
   }
 
   if constexpr (EPI == EPI_ARGMAX) {
@@ -392,46 +418,6 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
           lse_s[r * NWN + wn] = make_float2(mx, sm);
         }
       }
-    }
-  } else if (g.splits > 1) {
-    // the accumulators are dead here: this workgroup's partials are in memory
-#pragma unroll 1
-    for (int sub = 0; sub < SUB; ++sub) {
-      const int tile_n = tn * SUB + sub;
-      __syncthreads();
-      // every thread requests all split partials of 4 element pairs before summing
-      // them in split order (8-byte device-coherent loads)
-      constexpr int kMaxSplits = 8;
-      constexpr int PAIRS = BM * kBN / 2 / NT;
-      static_assert(PAIRS % 4 == 0, "pairs per thread");
-#pragma unroll 1
-      for (int e0 = 0; e0 < PAIRS; e0 += 4) {
-        float2 pv[4][kMaxSplits];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = tid + (e0 + e) * NT, r = idx / (kBN / 2), c = 2 * (idx % (kBN / 2));
-          const int m = min(m0 + r, g.M - 1);
-#pragma unroll
-          for (int sp = 0; sp < kMaxSplits; ++sp)
-            if (sp < g.splits)
-              pv[e][sp] = coherent_load2(&g.partials[(static_cast<size_t>(sp) * g.M + m) * np + tile_n * kBN + c]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = tid + (e0 + e) * NT, r = idx / (kBN / 2), c = 2 * (idx % (kBN / 2));
-          float2 v = make_float2(0.f, 0.f);
-#pragma unroll
-          for (int sp = 0; sp < kMaxSplits; ++sp)
-            if (sp < g.splits) {
-              v.x += pv[e][sp].x;
-              v.y += pv[e][sp].y;
-            }
-          tile[r][c] = v.x;
-          tile[r][c + 1] = v.y;
-        }
-      }
-      __syncthreads();
-      if (tile_n < g.n_tiles) epilogue_tile<bf16, EPI, BM, NT>(g, tile, rs_s, tile_n, m0, M, nullptr);
     }
   } else {
 #pragma unroll

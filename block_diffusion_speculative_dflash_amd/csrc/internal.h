@@ -159,6 +159,17 @@ hipError_t launch_commit_rows(int32_t* ctx_len, const int32_t* n_rows, int batch
 // [0, rows_per_seq]; out-of-range counts set err_bit), numbered consecutively in
 // sequence order.  seq_row0[b] = first row of b, seq_row0[B] = number of live rows;
 // row_map[m] = b * rows_per_seq + i, the uncompacted row of live row m.  One workgroup.
+// (sin, cos) of every rotation pair at every row's position: tab[(b * rows_per_seq +
+// i) * head_dim / 2 + d] for the position max(ctx_len[b], 0) + i, computed as the
+// GEMM epilogues compute it (angle reduced in double precision).
+struct RopeTabArgs {
+  const int32_t* ctx_len;  // [B]
+  float2* tab;
+  int batch, rows_per_seq, head_dim;
+  float theta;
+};
+hipError_t launch_rope_table(const RopeTabArgs& a, hipStream_t stream);
+
 struct CompactArgs {
   const int32_t* counts;  // [B]
   int32_t* seq_row0;      // [B + 1]

@@ -112,6 +112,28 @@ hipError_t launch_compact_rows(const CompactArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(kThreads) void rope_table_kernel(RopeTabArgs a) {
+  const int half = a.head_dim / 2;
+  const long long n = static_cast<long long>(a.batch) * a.rows_per_seq * half;
+  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  if (idx >= n) return;
+  const int d = static_cast<int>(idx % half);
+  const long long row = idx / half;
+  const int b = static_cast<int>(row / a.rows_per_seq), i = static_cast<int>(row % a.rows_per_seq);
+  float sn, cs;
+  rope_sincos(max(a.ctx_len[b], 0) + i, rope_inv_freq(d, a.head_dim, a.theta), &sn, &cs);
+  a.tab[idx] = make_float2(sn, cs);
+}
+
+hipError_t launch_rope_table(const RopeTabArgs& a, hipStream_t stream) {
+  if (a.batch <= 0 || a.rows_per_seq <= 0 || a.head_dim < 2) return hipErrorInvalidValue;
+  const long long n = static_cast<long long>(a.batch) * a.rows_per_seq * (a.head_dim / 2);
+  const long long blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > (1ll << 31) - 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(bool f32, const EmbedArgs& a, hipStream_t stream) {
   const dim3 grid(a.batch * a.block_k);
   if (!f32) hipLaunchKernelGGL(embed_kernel<bf16>, grid, dim3(kThreads), 0, stream, a);
