@@ -164,8 +164,15 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
     auto chunk = [&](auto cc) {
       constexpr int c = decltype(cc)::value;
       constexpr int MM = WM * WN, NR = WM + WN;
+      // MFMAs spread evenly.  Eight wavefronts (one workgroup per CU): the reads in
+      // all chunks but the last (so they have landed when the step ends) and the DMA
+      // loads at the ends of chunks 0 .. LPW-2, the last two together, so none is
+      // issued right before the step's wait.  Four wavefronts (two workgroups per CU,
+      // whose steps interleave): reads and DMA loads spread over all chunks.
+      constexpr bool LATE_FREE = NW == 8 && LPW > 1;
+      constexpr int RC = LATE_FREE ? LPW - 1 : LPW;
       constexpr int q0 = c * MM / LPW, q1 = (c + 1) * MM / LPW;
-      constexpr int r0 = c * NR / LPW, r1 = (c + 1) * NR / LPW;
+      constexpr int r0 = c < RC ? c * NR / RC : NR, r1 = c < RC ? (c + 1) * NR / RC : NR;
 #pragma unroll
       for (int r = r0; r < r1; ++r) {
         if (r < WN) fbn[r] = *reinterpret_cast<const E8*>(st + (AFR + wn * WN + r) * 512 + lane * 8);
@@ -184,7 +191,13 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                            // LDS read
       }
       if constexpr (nm - per * nr > 0) __builtin_amdgcn_sched_group_barrier(0x008, nm - per * nr, 0);
-      if (dma) dma_1k(src[c] + static_cast<size_t>(ds) * stride[c], ldsoff[c] + db * C::STAGE);
+      if constexpr (!LATE_FREE) {
+        if (dma) dma_1k(src[c] + static_cast<size_t>(ds) * stride[c], ldsoff[c] + db * C::STAGE);
+      } else if constexpr (c < LPW - 1) {
+        if (dma) dma_1k(src[c] + static_cast<size_t>(ds) * stride[c], ldsoff[c] + db * C::STAGE);
+        if constexpr (c == LPW - 2)
+          if (dma) dma_1k(src[c + 1] + static_cast<size_t>(ds) * stride[c + 1], ldsoff[c + 1] + db * C::STAGE);
+      }
     };
     static_assert(LPW >= 1 && LPW <= 4, "one to four DMA loads per wavefront and stage");
     chunk(std::integral_constant<int, 0>{});
@@ -245,8 +258,23 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   // t+1 (stage t+1 landed at the end of step t-1).  The DMA of stage t+4 goes into
   // the buffer of stage t: every wavefront's reads of stage t completed (lgkmcnt 0)
   // before the barrier that ended step t-1, so four stages are in flight and a DMA
-  // has three steps to land.
-  for (int s = 0; s < S; s += 4) {
+  // has three steps to land.  Groups of four steps with every condition true (t + 4
+  // < S) run without branches; the last steps check theirs.
+  int s = 0;
+  for (; s + 8 <= S; s += 4) {
+#define DFLASH_FULL(u, fac, fbc, fan, fbn)                                    \
+  step_work((u + 1) & 3, fac, fbc, fan, fbn, true, s + u + 4, u);             \
+  asm volatile("" ::: "memory");                                              \
+  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * LPW));                          \
+  __builtin_amdgcn_s_barrier();                                               \
+  asm volatile("" ::: "memory");
+    DFLASH_FULL(0, fa0, fb0, fa1, fb1)
+    DFLASH_FULL(1, fa1, fb1, fa0, fb0)
+    DFLASH_FULL(2, fa0, fb0, fa1, fb1)
+    DFLASH_FULL(3, fa1, fb1, fa0, fb0)
+#undef DFLASH_FULL
+  }
+  for (; s < S; s += 4) {
 #define DFLASH_STEP(u, fac, fbc, fan, fbn)                                    \
   if (s + u < S) {                                                            \
     step_work((u + 1) & 3, fac, fbc, fan, fbn, s + u + 4 < S, s + u + 4, u);  \
