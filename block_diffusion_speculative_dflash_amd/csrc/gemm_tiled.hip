@@ -37,7 +37,7 @@ namespace dflash {
 
 template <int NWM, int NWN, int WM, int WN>
 struct TileCfg {
-  static constexpr int NW = NWM * NWN, NT = 64 * NW;
+  static constexpr int NW = NWM * NWN, NT = 64 * NW, WM_ = WM, WN_ = WN;
   static constexpr int AFR = NWM * WM, BFR = NWN * WN, FR = AFR + BFR;
   static constexpr int BM = 16 * AFR, BN = 16 * BFR, SUB = BFR / 4;
   static constexpr int LPW = FR / NW;      // DMA loads per wavefront per stage
@@ -61,6 +61,16 @@ __device__ __forceinline__ unsigned long long dpp_max_key(unsigned long long k) 
       __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(k >> 32)), CTRL, 0xF, 0xF, true));
   const unsigned long long o = (static_cast<unsigned long long>(hi) << 32) | lo;
   return o > k ? o : k;
+}
+
+// Element (16-byte unit) of split sp's partial of tile (tm, tn), wavefront w, 16 x 16
+// block (i, j), lane l: [split][tile, m fastest][wavefront][i][j][lane].
+template <typename C>
+__device__ __forceinline__ size_t tiled_part_index(int sp, int m_tiles, int n_big, int tm, int tn, int w, int i, int j,
+                                                   int l) {
+  const size_t tiles_all = static_cast<size_t>(m_tiles) * n_big;
+  const size_t tile = static_cast<size_t>(tn) * m_tiles + tm;
+  return ((((static_cast<size_t>(sp) * tiles_all + tile) * C::NW + w) * C::WM_ + i) * C::WN_ + j) * kWave + l;
 }
 
 constexpr int vmcnt_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -87,7 +97,6 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   __shared__ __attribute__((aligned(1024))) char smem[C::BYTES];
   __shared__ __attribute__((aligned(16))) float rs_s[BM];
   __shared__ unsigned long long best_s[BM];
-  __shared__ int last_s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % NWM, wn = wave / NWM;
@@ -300,45 +309,15 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
 
   if constexpr (EPI != EPI_ARGMAX && EPI != EPI_SAMPLE) {  // the LM head never splits K
     if (g.splits > 1) {
-      // Split K.  Partials are kept in the accumulators' own layout (one 16-byte
-      // value per lane and 16 x 16 block), so every store and load moves a whole 1 KB
-      // per wavefront.  The last split to arrive reloads all of them, its own
-      // included, and sums them in split order (the same sum whichever split that is),
-      // then carries on with the epilogue as an unsplit tile would.
-      const size_t tiles_all = static_cast<size_t>(g.m_tiles) * n_big;
-      const size_t tile_id = static_cast<size_t>(tm) * n_big + tn;
+      // Split K: the partial tile goes out in the accumulators' own layout (one
+      // 16-byte value per lane and 16 x 16 block, a whole 1 KB per wavefront store);
+      // gemm_tiled_reduce_kernel, launched next, sums the splits and runs the epilogue
       f32x4* part = reinterpret_cast<f32x4*>(g.partials);
-      auto pidx = [&](int sp, int i, int j) -> size_t {
-        return ((((static_cast<size_t>(sp) * tiles_all + tile_id) * NW + wave) * WM + i) * WN + j) * kWave + lane;
-      };
 #pragma unroll
       for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int j = 0; j < WN; ++j) coherent_store16(&part[pidx(split, i, j)], acc[i][j]);
-      unsigned* counter = &g.counters[tm * n_big + tn];
-      if (!arrive_last(counter, g.splits, &last_s)) return;
-      if (tid == 0) reset_counter(counter);
-      // Half of the wavefront's blocks at a time, split after split: the loads of one
-      // split's half (16 KB per wavefront for 256 x 256 tiles) are in flight together.
-      constexpr int NB = WM * WN, H = (NB + 1) / 2;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x4 sum[H];
-#pragma unroll 1
-        for (int sp = 0; sp < g.splits; ++sp) {
-          f32x4 v[H];
-#pragma unroll
-          for (int q = 0; q < H; ++q) {
-            const int bq = min(h * H + q, NB - 1);
-            v[q] = coherent_load16<f32x4>(&part[pidx(sp, bq / WN, bq % WN)]);
-          }
-#pragma unroll
-          for (int q = 0; q < H; ++q) sum[q] = sp == 0 ? v[q] : sum[q] + v[q];
-        }
-#pragma unroll
-        for (int q = 0; q < H; ++q)
-          if (h * H + q < NB) acc[(h * H + q) / WN][(h * H + q) % WN] = sum[q];
-      }
+        for (int j = 0; j < WN; ++j) part[tiled_part_index<C>(split, g.m_tiles, n_big, tm, tn, wave, i, j, lane)] = acc[i][j];
+      return;
     }
   }
 
@@ -485,6 +464,66 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   }
 }
 
+// Split-K reduction and epilogue of the tiled GEMM: one workgroup (4 wavefronts) per
+// (tile, 64-column subtile).  The subtile's 16 x 16 blocks are summed over the splits
+// in split order (plain loads: the partials were written by the previous kernel),
+// placed in the LDS tile, and the subtile goes through the same fused epilogue as an
+// unsplit tile.
+template <int EPI, int NWM, int NWN, int WM, int WN>
+__global__ __launch_bounds__(kThreads) void gemm_tiled_reduce_kernel(GemmArgs g) {
+  using C = TileCfg<NWM, NWN, WM, WN>;
+  constexpr int BM = C::BM, SUB = C::SUB, AFR = C::AFR;
+  constexpr int NF = AFR * 4;                       // 16 x 16 blocks of one subtile
+  constexpr int FPW = NF / (kThreads / kWave);      // blocks per wavefront
+  static_assert(NF % (kThreads / kWave) == 0, "blocks split evenly over the wavefronts");
+  __shared__ __attribute__((aligned(16))) float tile[BM][kBN + 4];
+  __shared__ float rs_s[BM];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_big = (g.n_tiles + SUB - 1) / SUB;
+  const int sub = blockIdx.x % SUB, t = blockIdx.x / SUB;
+  const int tm = t % g.m_tiles, tn = t / g.m_tiles;
+  const int m0 = tm * BM, tile_n = tn * SUB + sub;
+  int M = g.M;
+  if (g.m_live != nullptr) M = min(M, max(*g.m_live, 0));
+  if (m0 >= M || tile_n >= g.n_tiles) return;  // uniform per workgroup
+  const f32x4* part = reinterpret_cast<const f32x4*>(g.partials);
+  // block f of the subtile: row block rb = f / 4, column block cb = SUB-relative f % 4
+  auto src = [&](int sp, int f) -> size_t {
+    const int rb = f >> 2, cb = sub * 4 + (f & 3);
+    const int wm = rb / WM, i = rb % WM, wn = cb / WN, j = cb % WN;
+    return tiled_part_index<C>(sp, g.m_tiles, n_big, tm, tn, wm + NWM * wn, i, j, lane);
+  };
+  f32x4 sum[FPW];
+#pragma unroll
+  for (int q = 0; q < FPW; ++q) sum[q] = part[src(0, wave * FPW + q)];
+  for (int sp = 1; sp < g.splits; ++sp) {
+    f32x4 v[FPW];
+#pragma unroll
+    for (int q = 0; q < FPW; ++q) v[q] = part[src(sp, wave * FPW + q)];
+#pragma unroll
+    for (int q = 0; q < FPW; ++q) sum[q] += v[q];
+  }
+  // MFMA layout: lane l, register r holds row 4 * (l / 16) + r, column l % 16
+#pragma unroll
+  for (int q = 0; q < FPW; ++q) {
+    const int f = wave * FPW + q, rb = f >> 2, cb = f & 3;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) tile[rb * 16 + 4 * (lane >> 4) + rr][cb * 16 + (lane & 15)] = sum[q][rr];
+  }
+  for (int r = tid; r < BM; r += kThreads) {
+    float f = 1.f;
+    if (g.ssq_in != nullptr && m0 + r < g.M) {
+      const float* row = g.ssq_in + static_cast<size_t>(m0 + r) * g.np_in;
+      float ssum = 0.f;
+      for (int k = 0; k < g.np_in; ++k) ssum += row[k];
+      f = 1.f / sqrtf(ssum / static_cast<float>(g.norm_dim) + g.eps);
+    }
+    rs_s[r] = f;
+  }
+  __syncthreads();
+  epilogue_tile<bf16, EPI, BM, kThreads>(g, tile, rs_s, tile_n, m0, M, nullptr);
+}
+
 template <int EPI, int NWM, int NWN, int WM, int WN>
 static hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
   using C = TileCfg<NWM, NWN, WM, WN>;
@@ -492,6 +531,16 @@ static hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t s
   const long long grid = static_cast<long long>(p.m_tiles) * n_big * p.splits;
   if (p.m_tiles != (a.M + C::BM - 1) / C::BM || grid <= 0 || grid > (1ll << 31) - 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_tiled_kernel<EPI, NWM, NWN, WM, WN>), dim3(static_cast<unsigned>(grid)), dim3(C::NT), 0, s, a);
+  if (p.splits > 1) {
+    if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) {
+      return hipErrorInvalidValue;
+    } else {
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      const long long rgrid = static_cast<long long>(p.m_tiles) * n_big * C::SUB;
+      hipLaunchKernelGGL((gemm_tiled_reduce_kernel<EPI, NWM, NWN, WM, WN>), dim3(static_cast<unsigned>(rgrid)),
+                         dim3(kThreads), 0, s, a);
+    }
+  }
   return hipGetLastError();
 }
 
