@@ -51,16 +51,15 @@ struct TileCfg {
   static_assert(BFR % 4 == 0, "whole 64-column subtiles");
 };
 
-// Larger of a 64-bit key and the key of the lane DPP control CTRL selects (a
-// permutation inside each row of 16 lanes).
+// Larger (smaller) of a value and the value of the lane the DPP control CTRL selects
+// (a permutation inside each row of 16 lanes).
 template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp_max_key(unsigned long long k) {
-  const uint32_t lo =
-      static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(k)), CTRL, 0xF, 0xF, true));
-  const uint32_t hi = static_cast<uint32_t>(
-      __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(k >> 32)), CTRL, 0xF, 0xF, true));
-  const unsigned long long o = (static_cast<unsigned long long>(hi) << 32) | lo;
-  return o > k ? o : k;
+__device__ __forceinline__ float dpp_max_f32(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_min_u32(uint32_t x) {
+  return min(x, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, true)));
 }
 
 // Element (16-byte unit) of split sp's partial of tile (tm, tn), wavefront w, 16 x 16
@@ -337,40 +336,49 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
           }
         }
     }
-    // split-vocab argmax straight from the accumulators, without branches: per lane
-    // and row the largest 64-bit key of its WN columns (columns past N count as key
-    // 0), then across the 16 lanes that share the row with DPP (xor 1, xor 2, half-row
-    // mirror, row mirror), then across the NWN column wavefronts through an LDS max
-    uint32_t nlo[WN], ok[WN];
+    // split-vocab argmax straight from the accumulators, without branches: per row the
+    // largest scaled logit of the tile's columns (columns past N excluded), across the
+    // 16 lanes that share the row with DPP (xor 1, xor 2, half-row mirror, row mirror),
+    // then the smallest column holding it the same way, then the row's 64-bit key
+    // (order-preserving value bits, ~column) across the NWN column wavefronts through
+    // an LDS max.  Equal values go to the smallest column; NaN logits are never picked.
+    uint32_t ncol[WN];
 #pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const int n = (tn * BFR + wn * WN + j) * 16 + (lane & 15);
-      nlo[j] = 0xFFFFFFFFu - static_cast<uint32_t>(n);
-      ok[j] = n < g.N ? 0xFFFFFFFFu : 0u;
-    }
+    for (int j = 0; j < WN; ++j) ncol[j] = static_cast<uint32_t>((tn * BFR + wn * WN + j) * 16 + (lane & 15));
+    // FULL: every column of the tile is below N (all tiles but the last), no masks
+    auto argmax_rows = [&](auto full) {
+      constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      const float4 f4 = *reinterpret_cast<const float4*>(&rs_s[(wm * WM + i) * 16 + 4 * (lane >> 4)]);
+      for (int i = 0; i < WM; ++i) {
+        const float4 f4 = *reinterpret_cast<const float4*>(&rs_s[(wm * WM + i) * 16 + 4 * (lane >> 4)]);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = (wm * WM + i) * 16 + 4 * (lane >> 4) + rr;
-        const float f = rr == 0 ? f4.x : (rr == 1 ? f4.y : (rr == 2 ? f4.z : f4.w));
-        unsigned long long key = 0ull;
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = (wm * WM + i) * 16 + 4 * (lane >> 4) + rr;
+          const float f = rr == 0 ? f4.x : (rr == 1 ? f4.y : (rr == 2 ? f4.z : f4.w));
+          float v[WN], mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          const uint32_t u = __float_as_uint(acc[i][j][rr] * f);
-          const uint32_t o = u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
-          const unsigned long long kj =
-              (static_cast<unsigned long long>(o & ok[j]) << 32) | static_cast<unsigned long long>(nlo[j] & ok[j]);
-          key = kj > key ? kj : key;
+          for (int j = 0; j < WN; ++j) {
+            v[j] = acc[i][j][rr] * f;
+            mx = fmaxf(mx, FULL || ncol[j] < static_cast<uint32_t>(g.N) ? v[j] : -INFINITY);
+          }
+          mx = dpp_max_f32<0xB1>(mx);   // quad_perm [1,0,3,2]
+          mx = dpp_max_f32<0x4E>(mx);   // quad_perm [2,3,0,1]
+          mx = dpp_max_f32<0x141>(mx);  // row_half_mirror
+          mx = dpp_max_f32<0x140>(mx);  // row_mirror
+          uint32_t col = 0xFFFFFFFFu;
+#pragma unroll
+          for (int j = WN - 1; j >= 0; --j)
+            col = (FULL || ncol[j] < static_cast<uint32_t>(g.N)) && v[j] == mx ? ncol[j] : col;
+          col = dpp_min_u32<0xB1>(col);
+          col = dpp_min_u32<0x4E>(col);
+          col = dpp_min_u32<0x141>(col);
+          col = dpp_min_u32<0x140>(col);
+          if ((lane & 15) == 0 && col != 0xFFFFFFFFu) atomicMax(&best_s[r], argmax_key(mx, static_cast<int>(col)));
         }
-        key = dpp_max_key<0xB1>(key);   // quad_perm [1,0,3,2]
-        key = dpp_max_key<0x4E>(key);   // quad_perm [2,3,0,1]
-        key = dpp_max_key<0x141>(key);  // row_half_mirror
-        key = dpp_max_key<0x140>(key);  // row_mirror
-        if ((lane & 15) == 0 && key != 0ull) atomicMax(&best_s[r], key);
       }
-    }
+    };
+    if ((tn + 1) * C::BN <= g.N) argmax_rows(std::true_type{});
+    else argmax_rows(std::false_type{});
   } else if constexpr (EPI == EPI_SAMPLE) {
     // sampled drafts straight from the accumulators: for each pair of adjacent 16 x 16
     // column blocks (2p, 2p + 1) one Philox block gives the noise of the lane's 4 rows
