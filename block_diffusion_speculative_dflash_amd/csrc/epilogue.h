@@ -21,13 +21,69 @@
 
 namespace dflash {
 
+// Targets of one thread's rows in the QKV / INJECT epilogue with the angle table
+// (4 threads per row; pass `it` covers row (tid >> 2) + (NT / 4) * it of the tile).
+// They are the same for every 64-column subtile of a tile, so a caller that runs
+// several subtiles computes them once (epilogue_rows) and hands them in.
+template <int BM, int NT>
+struct EpiRows {
+  static constexpr int RPP = NT / 4, IT = (BM + RPP - 1) / RPP;
+  int b[IT], i[IT], pos[IT];
+  bool live[IT];
+};
+
+// Which rows a QKV / INJECT call writes: row m is (sequence b, block row i) at
+// position max(ctx_len[b], 0) + i.  Returns false for rows it skips.  `lead`: the
+// thread that reports out-of-range row counts.
+template <int EPI>
+__device__ __forceinline__ bool epilogue_row_target(const GemmArgs& g, int m, bool lead, int& b, int& i, int& pos) {
+  b = m / g.rows_per_seq;
+  i = m % g.rows_per_seq;
+  if (g.row_map != nullptr) {
+    const int e = g.row_map[m];
+    b = e / g.rows_per_seq;
+    i = e % g.rows_per_seq;
+  }
+  int n_valid = g.rows_per_seq;
+  if constexpr (EPI == EPI_INJECT) {
+    const int nr = g.n_rows[b];
+    if ((nr < 0 || nr > g.rows_per_seq) && i == 0 && lead) atomicOr(g.dev_error, kErrRows);
+    n_valid = min(max(nr, 0), g.rows_per_seq);
+  }
+  if (i >= n_valid) return false;
+  pos = max(g.ctx_len[b], 0) + i;
+  // A call with more than C - s ring rows for one sequence: rows i and i + (C - s)
+  // share a slot, and writes in position order leave the later one, so the earlier
+  // row is not written at all (no two writers race on a slot).
+  if constexpr (EPI == EPI_INJECT)
+    if (pos >= g.sink && i + (g.cache_slots - g.sink) < n_valid) return false;
+  return true;
+}
+
+template <int EPI, int BM, int NT>
+__device__ __forceinline__ void epilogue_rows(const GemmArgs& g, int m0, int m_end, EpiRows<BM, NT>& er) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < EpiRows<BM, NT>::IT; ++it) {
+    const int r = (tid >> 2) + EpiRows<BM, NT>::RPP * it, m = m0 + r;
+    int b = 0, i = 0, pos = 0;
+    er.live[it] = r < BM && m < m_end && epilogue_row_target<EPI>(g, m, (tid & 3) == 0, b, i, pos);
+    er.b[it] = b;
+    er.i[it] = i;
+    er.pos[it] = pos;
+  }
+}
+
 // Rows m >= m_end are skipped (g.M, or the live rows of compacted blocks).
 // hres: RESID only, the residual tile prefetched by the caller (row pass `it` of
 // this thread, 8 columns), or nullptr to read it here.  COH: the outputs (and the
 // residual read here) are device-coherent, for a consumer inside the same launch.
-template <typename TIN, int EPI, int BM, int NT, bool COH = false>
+// ROWS: QKV / INJECT with the angle table, `rows` holds the rows' targets from
+// epilogue_rows; otherwise they are found here.
+template <typename TIN, int EPI, int BM, int NT, bool COH = false, bool ROWS = false>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*tile)[kBN + 4], const float* rs,
-                                              int tile_n, int m0, int m_end, const float (*hres)[8]) {
+                                              int tile_n, int m0, int m_end, const float (*hres)[8],
+                                              EpiRows<BM, NT> rows = EpiRows<BM, NT>{}) {
   typedef typename ActOf<TIN>::type TA;
   const int tid = threadIdx.x;
   bool bad = false;
@@ -136,30 +192,8 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
       kind = hd < g.n_kv_heads ? 1 : 2;
       head = kind == 1 ? hd : hd - g.n_kv_heads;
     }
-    // Which rows this call writes, and where: row m is (sequence b, block row i) at
-    // position max(ctx_len[b], 0) + i.  Returns false for rows it skips.
     auto row_target = [&](int m, int lead, int& b, int& i, int& pos) -> bool {
-      b = m / g.rows_per_seq;
-      i = m % g.rows_per_seq;
-      if (g.row_map != nullptr) {
-        const int e = g.row_map[m];
-        b = e / g.rows_per_seq;
-        i = e % g.rows_per_seq;
-      }
-      int n_valid = g.rows_per_seq;
-      if constexpr (EPI == EPI_INJECT) {
-        const int nr = g.n_rows[b];
-        if ((nr < 0 || nr > g.rows_per_seq) && i == 0 && lead) atomicOr(g.dev_error, kErrRows);
-        n_valid = min(max(nr, 0), g.rows_per_seq);
-      }
-      if (i >= n_valid) return false;
-      pos = max(g.ctx_len[b], 0) + i;
-      // A call with more than C - s ring rows for one sequence: rows i and
-      // i + (C - s) share a slot, and writes in position order leave the later one,
-      // so the earlier row is not written at all (no two writers race on a slot).
-      if constexpr (EPI == EPI_INJECT)
-        if (pos >= g.sink && i + (g.cache_slots - g.sink) < n_valid) return false;
-      return true;
+      return epilogue_row_target<EPI>(g, m, lead != 0, b, i, pos);
     };
     auto row_dst = [&](int m, int b, int pos) -> TA* {
       if constexpr (EPI == EPI_QKV) {
@@ -178,17 +212,13 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
       constexpr int RPP = NT / 4;
       constexpr int IT = (BM + RPP - 1) / RPP;
       const int p0 = (tid & 3) * 8, d0 = sub * 32 + p0;
-      bool live[IT];
-      int rb[IT], rpos[IT];
+      EpiRows<BM, NT> er = rows;
+      if constexpr (!ROWS) epilogue_rows<EPI, BM, NT>(g, m0, m_end, er);
       float4 sc[IT][4];
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
-        const int r = (tid >> 2) + RPP * it, m = m0 + r;
-        int b = 0, i = 0, pos = 0;
-        live[it] = r < BM && m < m_end && row_target(m, (tid & 3) == 0, b, i, pos);
-        rb[it] = b;
-        rpos[it] = pos;
-        if (live[it] && kind != 2) {
+        const int b = er.b[it], i = er.i[it];
+        if (er.live[it] && kind != 2) {
           const float4* tp = reinterpret_cast<const float4*>(g.rope_tab + (static_cast<size_t>(b) * g.rows_per_seq + i) * half + d0);
 #pragma unroll
           for (int q = 0; q < 4; ++q) sc[it][q] = tp[q];
@@ -196,7 +226,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
       }
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
-        if (!live[it]) continue;
+        if (!er.live[it]) continue;
         const int r = (tid >> 2) + RPP * it, m = m0 + r;
         const float f = rs[r];
         float x1[8], x2[8];
@@ -220,7 +250,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, const float (*t
           y1[q] = to_act<TA>(v1, bad);
           y2[q] = to_act<TA>(v2, bad);
         }
-        TA* dst = row_dst(m, rb[it], rpos[it]);
+        TA* dst = row_dst(m, er.b[it], er.pos[it]);
         put16<COH>(dst + d0, y1);
         put16<COH>(dst + d0 + half, y2);
       }

@@ -45,7 +45,10 @@ struct TileCfg {
   static constexpr int NST = 4;
   static constexpr int MAIN = NST * STAGE;
   static constexpr int TILE = BM * (kBN + 4) * 4;
-  static constexpr int BYTES = MAIN > TILE ? MAIN : TILE;
+  // epilogue subtiles per round: two when the LDS has room for both (with the rest of
+  // the kernel's LDS under 150 KB), else one
+  static constexpr int PAIR = (SUB % 2 == 0 && 2 * TILE <= 150 * 1024 - 3 * 1024) ? 2 : 1;
+  static constexpr int BYTES = MAIN > PAIR * TILE ? MAIN : PAIR * TILE;
   static_assert(FR % NW == 0, "chunks split evenly over the wavefronts");
   static_assert(WN % 2 == 0, "pairs of 16-column blocks (the sampled noise layout)");
   static_assert(BFR % 4 == 0, "whole 64-column subtiles");
@@ -435,22 +438,36 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
       }
     }
   } else {
+    // The tile goes through the fused epilogue 64 columns at a time, C::PAIR subtiles
+    // per round (each in its own LDS tile), the rows' QKV / INJECT targets found once.
+    constexpr bool ROWS = EPI == EPI_QKV || EPI == EPI_INJECT;  // with the angle table
+    EpiRows<BM, NT> er{};
+    if constexpr (ROWS)
+      if (g.rope_tab != nullptr) epilogue_rows<EPI, BM, NT>(g, m0, M, er);
+    constexpr int PAIR = C::PAIR;
+    float(*tiles)[BM][kBN + 4] = reinterpret_cast<float(*)[BM][kBN + 4]>(smem);
 #pragma unroll
-    for (int sub = 0; sub < SUB; ++sub) {
-      const int tile_n = tn * SUB + sub;
+    for (int s0 = 0; s0 < SUB; s0 += PAIR) {
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const int cb = wn * WN + j;  // column block of the workgroup tile
-        if (cb / 4 != sub) continue;
+        if (cb / 4 < s0 || cb / 4 >= s0 + PAIR) continue;
 #pragma unroll
         for (int i = 0; i < WM; ++i)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
-            tile[(wm * WM + i) * 16 + 4 * (lane >> 4) + rr][(cb & 3) * 16 + (lane & 15)] = acc[i][j][rr];
+            tiles[cb / 4 - s0][(wm * WM + i) * 16 + 4 * (lane >> 4) + rr][(cb & 3) * 16 + (lane & 15)] = acc[i][j][rr];
       }
       __syncthreads();
-      if (tile_n < g.n_tiles) epilogue_tile<bf16, EPI, BM, NT>(g, tile, rs_s, tile_n, m0, M, nullptr);
+#pragma unroll
+      for (int q = 0; q < PAIR; ++q) {
+        const int tile_n = tn * SUB + s0 + q;
+        if (s0 + q < SUB && tile_n < g.n_tiles) {
+          if (ROWS && g.rope_tab != nullptr) epilogue_tile<bf16, EPI, BM, NT, false, ROWS>(g, tiles[q], rs_s, tile_n, m0, M, nullptr, er);
+          else epilogue_tile<bf16, EPI, BM, NT>(g, tiles[q], rs_s, tile_n, m0, M, nullptr);
+        }
+      }
     }
   }
 
