@@ -64,6 +64,28 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_min_u32(uint32_t x) {
   return min(x, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, true)));
 }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+// The larger of a 64-bit key and the key of the lane CTRL selects.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max_key(unsigned long long k) {
+  const uint32_t lo =
+      static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(k)), CTRL, 0xF, 0xF, true));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(k >> 32)), CTRL, 0xF, 0xF, true));
+  const unsigned long long o = (static_cast<unsigned long long>(hi) << 32) | lo;
+  return o > k ? o : k;
+}
+// One butterfly round of the sampled epilogue's row reduction: the best key and the
+// merged log-sum-exp pair of this lane and the lane CTRL selects.
+template <int CTRL>
+__device__ __forceinline__ void dpp_sample_round(unsigned long long& key, float& mx, float& sm) {
+  key = dpp_max_key<CTRL>(key);
+  const float om = dpp_f32<CTRL>(mx), os = dpp_f32<CTRL>(sm);
+  lse_merge(mx, sm, om, os);
+}
 
 // Element (16-byte unit) of split sp's partial of tile (tm, tn), wavefront w, 16 x 16
 // block (i, j), lane l: [split][tile, m fastest][wavefront][i][j][lane].
@@ -386,8 +408,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
     // sampled drafts straight from the accumulators: for each pair of adjacent 16 x 16
     // column blocks (2p, 2p + 1) one Philox block gives the noise of the lane's 4 rows
     // x 2 columns; per row the best key of s + noise (s = logits / T) and the
-    // log-sum-exp pair of s go across the 16 lanes sharing the row (xor 1, 2, 4, 8),
-    // then across the NWN column wavefronts through LDS (the stage buffers are dead)
+    // log-sum-exp pair of s go across the 16 lanes sharing the row (DPP), then across
+    // the NWN column wavefronts through LDS (the stage buffers are dead)
     float2* lse_s = reinterpret_cast<float2*>(smem);  // [BM][NWN]
     const unsigned long long step = g.step_dev != nullptr ? *g.step_dev : g.step;
 #pragma unroll
@@ -424,13 +446,11 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
 #pragma unroll
           for (int j = 0; j < WN; ++j) sm += __builtin_amdgcn_exp2f((sv[j] - mx) * kLog2e);
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const unsigned long long other = __shfl_xor(key, o, kWave);
-          key = other > key ? other : key;
-          const float om = __shfl_xor(mx, o, kWave), os = __shfl_xor(sm, o, kWave);
-          lse_merge(mx, sm, om, os);
-        }
+        // across the 16 lanes of the row: DPP quad permutations, half-row and row mirrors
+        dpp_sample_round<0xB1>(key, mx, sm);
+        dpp_sample_round<0x4E>(key, mx, sm);
+        dpp_sample_round<0x141>(key, mx, sm);
+        dpp_sample_round<0x140>(key, mx, sm);
         if ((lane & 15) == 0) {
           if (key != 0ull) atomicMax(&best_s[r], key);
           lse_s[r * NWN + wn] = make_float2(mx, sm);
