@@ -128,7 +128,8 @@ size_t partial_bytes(const dflash_dims& d);
 
 struct Layout {
   size_t h, xa, ssq, q, kb, vb, o, act, cu, ssq_c, partials, counters, keys, attn_cnt, attn_o,
-      attn_ml, lse_part, v_part, v_cnt, v_rowlse, v_dec, v_keys, xa2, ssq2, sig, row_map, seq_row0, rope, total;
+      attn_ml, lse_part, v_part, v_cnt, v_rowlse, v_dec, v_keys, xa2, ssq2, sig, row_map, seq_row0, rope, taps_pk,
+      total;
   int v_chunks;
   int np_d, S_d, S_o, S_f;
   AttnPlan ap;
@@ -187,6 +188,8 @@ Layout layout(const dflash_dims& d) {
   L.seq_row0 = take((size_t(d.batch) + 1) * 4);
   // (sin, cos) of the rows' rotation angles for the tiled QKV / injection epilogues
   L.rope = take(std::max(Mb, Mi) * (d.head_dim / 2) * 8);
+  // the verify round's taps (B(k + 1) rows) fragment-packed for the tiled fusion GEMM
+  L.taps_pk = take(e == 2 ? size_t(round_up(d.batch * (d.block_k + 1), 64)) * d.n_taps * d.tap_dim * 2 : 0);
   L.total = off;
   return L;
 }
@@ -879,6 +882,19 @@ int dflash_fuse_inject(const dflash_dims* dims, const dflash_weights* w, const v
   a.gain = w->fuse_norm;
   a.ssq_out = c.at<float>(L.ssq_c);
   a.np_out = L.np_d;
+  {
+    // On the tiled kernel, the verify round's taps are fragment-packed first: the GEMM
+    // then streams contiguous 1 KB chunks instead of gathering 16 rows per load.
+    GemmArgs probe = a;
+    const GemmPlan fp = plan_gemm(EPI_FUSE, c, probe, true);
+    if (fp.tiled && !is_f32(d) && n_max <= d.block_k + 1 && a.K == a.S * kKStep) {
+      PackTapsArgs pk{taps, c.at<void>(L.taps_pk), K, Mi, a.S, c.row_map, c.m_live};
+      DF_CHECK(launch_pack_taps(pk, stream));
+      a.A = pk.out;
+      a.a_packed = 1;
+      a.row_map = nullptr;  // the packed rows are already the compacted ones
+    }
+  }
   if (int st = run_gemm(EPI_FUSE, c, a, true, stream)) return st;
 
   // K/V injection: the K and V head tiles of every layer's packed QKV region

@@ -97,6 +97,9 @@ struct GemmArgs {
   // rows, uncompacted
   const int32_t* m_live;
   const int32_t* row_map;
+  // tiled fusion GEMM: A is the taps already fragment-packed (compacted rows), not
+  // the caller's row-major taps
+  int a_packed;
 };
 
 struct GemmPlan {

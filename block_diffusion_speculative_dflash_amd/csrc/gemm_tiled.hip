@@ -114,7 +114,8 @@ template <int EPI, int NWM, int NWN, int WM, int WN>
 __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) {
   using C = TileCfg<NWM, NWN, WM, WN>;
   constexpr int AFR = C::AFR, BFR = C::BFR, BM = C::BM, SUB = C::SUB, LPW = C::LPW, NW = C::NW, NT = C::NT;
-  constexpr bool APK = EPI != EPI_FUSE;  // packed activations; the fusion GEMM reads row-major taps
+  // packed activations; the fusion GEMM reads row-major taps unless they were packed
+  const bool APK = EPI != EPI_FUSE || g.a_packed != 0;
   typedef typename std::conditional<EPI == EPI_FUSE, bf16, f16>::type E;
   typedef typename std::conditional<EPI == EPI_FUSE, bf16x8, f16x8>::type E8;
 
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   for (int j = 0; j < LPW; ++j) {
     const int c = wave + NW * j;
     if (c < AFR) {
-      if constexpr (APK) {
+      if (APK) {
         const int mb = min(tm * AFR + c, m_blocks - 1);
         src[j] = static_cast<const char*>(g.A) + ((static_cast<size_t>(mb) * g.S + s_lo) * 512 + lane * 8) * 2;
         stride[j] = 1024;

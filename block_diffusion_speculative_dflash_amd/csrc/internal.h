@@ -170,6 +170,18 @@ struct RopeTabArgs {
 };
 hipError_t launch_rope_table(const RopeTabArgs& a, hipStream_t stream);
 
+// Fragment packing of the fusion GEMM's A operand (the taps, bf16): live row m (row
+// row_map[m] of the caller's row-major taps when compacted, else row m) goes to
+// out[pa_index(m, k, steps)].
+struct PackTapsArgs {
+  const void* taps;  // [rows, lda] bf16
+  void* out;         // packed [ceil(rows / 16), steps, 64, 8] bf16
+  int lda, rows, steps;
+  const int32_t* row_map;  // or nullptr
+  const int32_t* m_live;   // or nullptr: all rows
+};
+hipError_t launch_pack_taps(const PackTapsArgs& a, hipStream_t stream);
+
 struct CompactArgs {
   const int32_t* counts;  // [B]
   int32_t* seq_row0;      // [B + 1]

@@ -112,6 +112,30 @@ hipError_t launch_compact_rows(const CompactArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// One thread per 16 bytes of the packed output, in output order: a wavefront writes one
+// contiguous 1 KB fragment (16 rows x 32 k) and reads 16 row pieces of 64 bytes.
+__global__ __launch_bounds__(kThreads) void pack_taps_kernel(PackTapsArgs a) {
+  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  const int lane = static_cast<int>(idx & 63);
+  const long long frag = idx >> 6;  // (row block, k step)
+  const int mb = static_cast<int>(frag / a.steps), st = static_cast<int>(frag % a.steps);
+  const int m = mb * 16 + (lane & 15);
+  if (m >= a.rows || (a.m_live != nullptr && m >= *a.m_live)) return;
+  const int row = a.row_map != nullptr ? a.row_map[m] : m;
+  const int k = st * kKStep + 8 * (lane >> 4);
+  const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const bf16*>(a.taps) + static_cast<size_t>(row) * a.lda + k);
+  *reinterpret_cast<uint4*>(static_cast<bf16*>(a.out) + pa_index(m, k, a.steps)) = v;
+}
+
+hipError_t launch_pack_taps(const PackTapsArgs& a, hipStream_t stream) {
+  if (a.rows <= 0 || a.steps <= 0 || a.lda < a.steps * kKStep || a.lda % 8 != 0) return hipErrorInvalidValue;
+  const long long n = static_cast<long long>((a.rows + 15) / 16) * a.steps * kWave;
+  const long long blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > (1ll << 31) - 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_taps_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(kThreads) void rope_table_kernel(RopeTabArgs a) {
   const int half = a.head_dim / 2;
   const long long n = static_cast<long long>(a.batch) * a.rows_per_seq * half;
