@@ -394,8 +394,18 @@ GemmPlan plan_gemm(int epi, const Ctx& c, GemmArgs& a, bool allow_split) {
   return p;
 }
 
+int device_cus(int* cus);
+
 int run_gemm(int epi, const Ctx& c, GemmArgs a, bool allow_split, hipStream_t s) {
   const GemmPlan p = plan_gemm(epi, c, a, allow_split);
+  a.persist = 0;
+  if (p.tiled && epi == EPI_ARGMAX && p.mt != kTile128) {
+    // the tiled LM head walks its tiles with one workgroup per CU once there are at
+    // least two tiles per CU: each tile's first loads overlap the previous epilogue
+    int cus = 0;
+    const long long tiles = static_cast<long long>(p.m_tiles) * ((p.n_tiles * kBN + tile_cols(p.mt) - 1) / tile_cols(p.mt));
+    if (device_cus(&cus) == DFLASH_OK && cus % 8 == 0 && tiles >= 2ll * cus) a.persist = cus;
+  }
   if (p.tiled) DF_CHECK(launch_gemm_tiled(epi, p, a, s));
   else DF_CHECK(launch_gemm(epi, is_f32(c.d), p, a, s));
   return DFLASH_OK;

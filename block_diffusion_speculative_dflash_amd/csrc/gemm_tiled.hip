@@ -111,7 +111,7 @@ __device__ __forceinline__ void dma_1k(const void* gp, uint32_t lds) {
 #pragma clang diagnostic pop
 
 template <int EPI, int NWM, int NWN, int WM, int WN>
-__global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) {
+__global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(NWM * NWN == 4 ? 2 : 1, 2))) void gemm_tiled_kernel(GemmArgs g) {
   using C = TileCfg<NWM, NWN, WM, WN>;
   constexpr int AFR = C::AFR, BFR = C::BFR, BM = C::BM, SUB = C::SUB, LPW = C::LPW, NW = C::NW, NT = C::NT;
   // packed activations; the fusion GEMM reads row-major taps unless they were packed
@@ -125,21 +125,29 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % NWM, wn = wave / NWM;
-  // XCD-contiguous renumbering, then (split, n tile, m tile) with m fastest
-  const int nwg = gridDim.x, x = blockIdx.x, xcd = x & 7, q = nwg >> 3, r8 = nwg & 7;
-  const int L = xcd * q + min(xcd, r8) + (x >> 3);
   const int n_big = (g.n_tiles + SUB - 1) / SUB;
-  const int tm = L % g.m_tiles, rest = L / g.m_tiles;
-  const int tn = rest % n_big, split = rest / n_big;
-  const int m0 = tm * BM;
   // compacted block rows: tiles past the live rows have nothing to do
   int M = g.M;
-  if (g.m_live != nullptr) {
-    M = min(M, max(*g.m_live, 0));
-    if (m0 >= M) return;  // uniform per workgroup
+  if (g.m_live != nullptr) M = min(M, max(*g.m_live, 0));
+  // Tiles (split, n tile, m tile), m fastest, renumbered XCD-contiguous.  One tile per
+  // workgroup, or (persistent LM head, one workgroup per CU) a stride through the
+  // XCD's run of tiles: tile L, L + nwg/8, ..., so the XCD's workgroups still work
+  // on neighbouring tiles at any time.
+  const int nwg = gridDim.x, x = blockIdx.x, xcd = x & 7;
+  int L, L_end, L_step;
+  if (EPI == EPI_ARGMAX && g.persist != 0) {
+    const int T = g.m_tiles * n_big, q = T >> 3, r8 = T & 7;
+    L = xcd * q + min(xcd, r8) + (x >> 3);
+    L_end = xcd * q + min(xcd, r8) + q + (xcd < r8 ? 1 : 0);
+    L_step = nwg >> 3;
+  } else {
+    const int q = nwg >> 3, r8 = nwg & 7;
+    L = xcd * q + min(xcd, r8) + (x >> 3);
+    L_end = L + 1;
+    L_step = 1;
   }
-  const int s_lo = split * g.steps_per_split;
-  const int S = min(g.S, s_lo + g.steps_per_split) - s_lo;  // steps of this split (>= 1)
+  while (L < L_end && (L % g.m_tiles) * BM >= M) L += L_step;
+  if (L >= L_end) return;  // uniform per workgroup
   const int m_blocks = (g.M + 15) >> 4;
 
   // per-chunk source addresses (at step s_lo) and per-step strides, LDS offsets
@@ -149,38 +157,38 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
     const int c = wave + NW * j;
-    if (c < AFR) {
-      if (APK) {
-        const int mb = min(tm * AFR + c, m_blocks - 1);
-        src[j] = static_cast<const char*>(g.A) + ((static_cast<size_t>(mb) * g.S + s_lo) * 512 + lane * 8) * 2;
-        stride[j] = 1024;
-      } else {
-        int row = min(tm * BM + c * 16 + (lane & 15), M - 1);
-        if (g.row_map != nullptr) row = g.row_map[row];  // compacted rows: gather the tap row
-        src[j] = static_cast<const char*>(g.A) +
-                 (static_cast<size_t>(row) * g.lda + static_cast<size_t>(s_lo) * kKStep + (lane >> 4) * 8) * 2;
-        stride[j] = kKStep * 2;
-      }
-    } else {
-      const int cb = c - AFR;
-      const int t = min(tn * SUB + cb / 4, g.n_tiles - 1);
-      size_t wt = t;
-      if constexpr (EPI == EPI_INJECT) wt = static_cast<size_t>(t / g.inj_tiles) * g.layer_tiles + g.inj_tile0 + t % g.inj_tiles;
-      src[j] = static_cast<const char*>(g.W) + (((wt * g.S + s_lo) * 4 + (cb & 3)) * 512 + lane * 8) * 2;
-      stride[j] = 4096;
-    }
+    stride[j] = c < AFR ? (APK ? 1024u : static_cast<uint32_t>(kKStep * 2)) : 4096u;
     ldsoff[j] = __builtin_amdgcn_readfirstlane(lds0 + c * 1024);
   }
+  auto set_src = [&](int tm, int tn, int s_lo) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int c = wave + NW * j;
+      if (c < AFR) {
+        if (APK) {
+          const int mb = min(tm * AFR + c, m_blocks - 1);
+          src[j] = static_cast<const char*>(g.A) + ((static_cast<size_t>(mb) * g.S + s_lo) * 512 + lane * 8) * 2;
+        } else {
+          int row = min(tm * BM + c * 16 + (lane & 15), M - 1);
+          if (g.row_map != nullptr) row = g.row_map[row];  // compacted rows: gather the tap row
+          src[j] = static_cast<const char*>(g.A) +
+                   (static_cast<size_t>(row) * g.lda + static_cast<size_t>(s_lo) * kKStep + (lane >> 4) * 8) * 2;
+        }
+      } else {
+        const int cb = c - AFR;
+        const int t = min(tn * SUB + cb / 4, g.n_tiles - 1);
+        size_t wt = t;
+        if constexpr (EPI == EPI_INJECT) wt = static_cast<size_t>(t / g.inj_tiles) * g.layer_tiles + g.inj_tile0 + t % g.inj_tiles;
+        src[j] = static_cast<const char*>(g.W) + (((wt * g.S + s_lo) * 4 + (cb & 3)) * 512 + lane * 8) * 2;
+      }
+    }
+  };
   auto issue = [&](int s, int buf) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) dma_1k(src[j] + static_cast<size_t>(s) * stride[j], ldsoff[j] + buf * C::STAGE);
   };
 
   f32x4 acc[WM][WN];
-#pragma unroll
-  for (int i = 0; i < WM; ++i)
-#pragma unroll
-    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   E8 fa0[WM], fb0[WN], fa1[WM], fb1[WN];
   auto read = [&](int buf, E8* fa, E8* fb) {
     const E* st = reinterpret_cast<const E*>(smem + buf * C::STAGE);
@@ -240,44 +248,75 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
     if constexpr (LPW > 3) chunk(std::integral_constant<int, 3>{});
   };
 
-  // RMSNorm factor of this tile's A rows (thread r < BM: row m0 + r).  The partial
-  // sums are loaded before the first DMA so their latency overlaps the prologue's.
-  float ssq_v[16];
-  const int r_own = tid < BM ? tid : BM - 1;
-  const bool rs_vec = g.ssq_in != nullptr && (g.np_in & 3) == 0 && g.np_in <= 64;
+  auto issue_prologue = [&](int S) {  // stages 0..3 in flight
+    issue(0, 0);
+    if (1 < S) issue(1, 1);
+    if (2 < S) issue(2, 2);
+    if (3 < S) issue(3, 3);
+  };
+
+  int prev_tm = -1;
+  for (bool first = true;; first = false) {
+  // lane and thread ids, opaque to the compiler on every tile: it would otherwise
+  // hoist the epilogue's per-lane row addresses out of a persistent workgroup's tile
+  // loop and keep them (spilled) across the main loop
+  int lane_t = lane, tid_t = tid;
+  if constexpr (EPI == EPI_ARGMAX) asm volatile("" : "+v"(lane_t), "+v"(tid_t));
+  const int tm = L % g.m_tiles, rest = L / g.m_tiles;
+  const int tn = rest % n_big, split = rest / n_big;
+  const int m0 = tm * BM;
+  const int s_lo = split * g.steps_per_split;
+  const int S = min(g.S, s_lo + g.steps_per_split) - s_lo;  // steps of this split (>= 1)
+  // a persistent workgroup's later tiles had their prologue issued during the
+  // previous tile's epilogue
+  if (first) set_src(tm, tn, s_lo);
+
+  // RMSNorm factor of this tile's A rows (thread r < BM: row m0 + r), kept while the
+  // m tile stays the same.  The row's partial sums are loaded all 16 back to back
+  // (clamped index, no branch: a branch per load made each wait for the previous) and
+  // summed before the DMA issue.  Summed after it, they would wait for every stage:
+  // the compiler counts only its own loads, not the DMA loads issued after them.
+  const bool new_rows = tm != prev_tm;
+  prev_tm = tm;
+  const int r_own = tid_t < BM ? tid_t : BM - 1;
+  const bool rs_vec = g.ssq_in != nullptr && (g.np_in & 3) == 0 && g.np_in >= 4 && g.np_in <= 64;
   const float* ssq_row =
       g.ssq_in != nullptr ? g.ssq_in + static_cast<size_t>(min(m0 + r_own, g.M - 1)) * g.np_in : nullptr;
-  if (rs_vec) {
+  float ssq_sum = 0.f;
+  if (rs_vec && new_rows) {
+    const float4* row4 = reinterpret_cast<const float4*>(ssq_row);
+    const int n4 = g.np_in >> 2;
+    float4 v[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (4 * t < g.np_in) v = reinterpret_cast<const float4*>(ssq_row)[t];
-      ssq_v[t] = (v.x + v.y) + (v.z + v.w);
-    }
+    for (int t = 0; t < 16; ++t) v[t] = row4[min(t, n4 - 1)];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) ssq_sum += t < n4 ? (v[t].x + v[t].y) + (v[t].z + v[t].w) : 0.f;
+    asm volatile("" ::"v"(ssq_sum));  // taken here, not sunk into the branch that uses it
   }
 
-  // prologue: stages 0..3 in flight, wait for 0 and 1
-  issue(0, 0);
-  if (1 < S) issue(1, 1);
-  if (2 < S) issue(2, 2);
-  if (3 < S) issue(3, 3);
+  // prologue: stages 0..3 in flight, wait for 0 and 1.  (On a persistent workgroup's
+  // later tiles the key stores of the previous tile are younger than the DMA loads;
+  // vector memory loads complete in order, so the count still covers stages 0 and 1.)
+  if (first) issue_prologue(S);
   if (3 < S) __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * LPW));
   else if (2 < S) __builtin_amdgcn_s_waitcnt(vmcnt_wait(LPW));
   else __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-  if (tid < BM) {
-    float f = 1.f;
-    if (g.ssq_in != nullptr && m0 + tid < g.M) {
-      float sum = 0.f;
-      if (rs_vec) {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) sum += ssq_v[t];
-      } else {
-        for (int t = 0; t < g.np_in; ++t) sum += ssq_row[t];
+  if (tid_t < BM) {
+    if (new_rows) {
+      float f = 1.f;
+      if (g.ssq_in != nullptr && m0 + tid_t < g.M) {
+        float sum = 0.f;
+        if (rs_vec) {
+          sum = ssq_sum;
+        } else {
+          for (int t = 0; t < g.np_in; ++t) sum += ssq_row[t];
+        }
+        f = 1.f / sqrtf(sum / static_cast<float>(g.norm_dim) + g.eps);
       }
-      f = 1.f / sqrtf(sum / static_cast<float>(g.norm_dim) + g.eps);
+      rs_s[tid_t] = f;  // the previous tile's epilogue read rs_s before its key barrier
     }
-    rs_s[tid] = f;
-    if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) best_s[tid] = 0ull;
+    // the same thread stored row tid_t's key of the previous tile
+    if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) best_s[tid_t] = 0ull;
   }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -294,6 +333,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   // before the barrier that ended step t-1, so four stages are in flight and a DMA
   // has three steps to land.  Groups of four steps with every condition true (t + 4
   // < S) run without branches; the last steps check theirs.
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   int s = 0;
   for (; s + 8 <= S; s += 4) {
 #define DFLASH_FULL(u, fac, fbc, fan, fbn)                                    \
@@ -329,8 +372,21 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
   }
   __syncthreads();  // every wavefront is done with the stage buffers
 
+  // persistent LM head: the next tile's first four stages go out now, so their loads
+  // overlap this tile's epilogue (which works from the accumulators, not the LDS)
+  int L_next = L_end;
+  if constexpr (EPI == EPI_ARGMAX) {
+    if (g.persist != 0) {
+      L_next = L + L_step;
+      while (L_next < L_end && (L_next % g.m_tiles) * BM >= M) L_next += L_step;
+      if (L_next < L_end) {
+        set_src(L_next % g.m_tiles, L_next / g.m_tiles, 0);
+        issue_prologue(g.S);
+      }
+    }
+  }
+
   float(*tile)[kBN + 4] = reinterpret_cast<float(*)[kBN + 4]>(smem);
-  const size_t np = static_cast<size_t>(g.n_tiles) * kBN;
 
   if constexpr (EPI != EPI_ARGMAX && EPI != EPI_SAMPLE) {  // the LM head never splits K
     if (g.splits > 1) {
@@ -341,7 +397,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
 #pragma unroll
       for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int j = 0; j < WN; ++j) part[tiled_part_index<C>(split, g.m_tiles, n_big, tm, tn, wave, i, j, lane)] = acc[i][j];
+        for (int j = 0; j < WN; ++j) part[tiled_part_index<C>(split, g.m_tiles, n_big, tm, tn, wave, i, j, lane_t)] = acc[i][j];
       return;
     }
   }
@@ -352,12 +408,12 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
       for (int i = 0; i < WM; ++i)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int r = (wm * WM + i) * 16 + 4 * (lane >> 4) + rr, m = m0 + r;
+          const int r = (wm * WM + i) * 16 + 4 * (lane_t >> 4) + rr, m = m0 + r;
           if (m >= M) continue;
           const size_t mo = g.row_map != nullptr ? g.row_map[m] : m;
 #pragma unroll
           for (int j = 0; j < WN; ++j) {
-            const int n = (tn * BFR + wn * WN + j) * 16 + (lane & 15);
+            const int n = (tn * BFR + wn * WN + j) * 16 + (lane_t & 15);
             if (n < g.N) g.logits[mo * g.N + n] = acc[i][j][rr] * rs_s[r];
           }
         }
@@ -370,16 +426,16 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
     // an LDS max.  Equal values go to the smallest column; NaN logits are never picked.
     uint32_t ncol[WN];
 #pragma unroll
-    for (int j = 0; j < WN; ++j) ncol[j] = static_cast<uint32_t>((tn * BFR + wn * WN + j) * 16 + (lane & 15));
+    for (int j = 0; j < WN; ++j) ncol[j] = static_cast<uint32_t>((tn * BFR + wn * WN + j) * 16 + (lane_t & 15));
     // FULL: every column of the tile is below N (all tiles but the last), no masks
     auto argmax_rows = [&](auto full) {
       constexpr bool FULL = decltype(full)::value;
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
-        const float4 f4 = *reinterpret_cast<const float4*>(&rs_s[(wm * WM + i) * 16 + 4 * (lane >> 4)]);
+        const float4 f4 = *reinterpret_cast<const float4*>(&rs_s[(wm * WM + i) * 16 + 4 * (lane_t >> 4)]);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int r = (wm * WM + i) * 16 + 4 * (lane >> 4) + rr;
+          const int r = (wm * WM + i) * 16 + 4 * (lane_t >> 4) + rr;
           const float f = rr == 0 ? f4.x : (rr == 1 ? f4.y : (rr == 2 ? f4.z : f4.w));
           float v[WN], mx = -INFINITY;
 #pragma unroll
@@ -399,7 +455,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
           col = dpp_min_u32<0x4E>(col);
           col = dpp_min_u32<0x141>(col);
           col = dpp_min_u32<0x140>(col);
-          if ((lane & 15) == 0 && col != 0xFFFFFFFFu) atomicMax(&best_s[r], argmax_key(mx, static_cast<int>(col)));
+          if ((lane_t & 15) == 0 && col != 0xFFFFFFFFu) atomicMax(&best_s[r], argmax_key(mx, static_cast<int>(col)));
         }
       }
     };
@@ -415,12 +471,12 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
     const unsigned long long step = g.step_dev != nullptr ? *g.step_dev : g.step;
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      const int rb = (wm * WM + i) * 16 + 4 * (lane >> 4);
+      const int rb = (wm * WM + i) * 16 + 4 * (lane_t >> 4);
       uint32_t h[WN / 2][8];
 #pragma unroll
       for (int p = 0; p < WN / 2; ++p) {
         const int cb = tn * BFR + wn * WN + 2 * p;  // even: BFR and WN are
-        philox_u32x8<true>(16ull * static_cast<unsigned>(cb >> 1) + static_cast<unsigned>(lane & 15),
+        philox_u32x8<true>(16ull * static_cast<unsigned>(cb >> 1) + static_cast<unsigned>(lane_t & 15),
                      static_cast<unsigned>((m0 + rb) >> 2), step, 0ull, g.seed, kStreamDraft, h[p]);
       }
 #pragma unroll
@@ -431,7 +487,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
         float sv[WN], mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
-          const int n = (tn * BFR + wn * WN + j) * 16 + (lane & 15);
+          const int n = (tn * BFR + wn * WN + j) * 16 + (lane_t & 15);
           sv[j] = -INFINITY;
           if (n < g.N && m < M) {
             const float z = acc[i][j][rr] * f;
@@ -452,7 +508,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
         dpp_sample_round<0x4E>(key, mx, sm);
         dpp_sample_round<0x141>(key, mx, sm);
         dpp_sample_round<0x140>(key, mx, sm);
-        if ((lane & 15) == 0) {
+        if ((lane_t & 15) == 0) {
           if (key != 0ull) atomicMax(&best_s[r], key);
           lse_s[r * NWN + wn] = make_float2(mx, sm);
         }
@@ -478,7 +534,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
         for (int i = 0; i < WM; ++i)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
-            tiles[cb / 4 - s0][(wm * WM + i) * 16 + 4 * (lane >> 4) + rr][(cb & 3) * 16 + (lane & 15)] = acc[i][j][rr];
+            tiles[cb / 4 - s0][(wm * WM + i) * 16 + 4 * (lane_t >> 4) + rr][(cb & 3) * 16 + (lane_t & 15)] = acc[i][j][rr];
       }
       __syncthreads();
 #pragma unroll
@@ -494,11 +550,11 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
 
   if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) {
     __syncthreads();
-    for (int r = tid; r < BM; r += NT)
+    for (int r = tid_t; r < BM; r += NT)
       if (m0 + r < M) g.keys[static_cast<size_t>(m0 + r) * g.n_parts + tn] = best_s[r];
     if constexpr (EPI == EPI_SAMPLE) {
       const float2* lse_s = reinterpret_cast<const float2*>(smem);
-      for (int r = tid; r < BM; r += NT) {
+      for (int r = tid_t; r < BM; r += NT) {
         if (m0 + r >= M) continue;
         float mx = -INFINITY, sm = 0.f;
 #pragma unroll
@@ -507,6 +563,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tiled_kernel(GemmArgs g) 
       }
     }
     // the row's draft is the largest tile key: launch_head_finalize, after this kernel
+  }
+  if (L_next >= L_end) return;
+  L = L_next;
   }
 }
 
@@ -574,8 +633,15 @@ template <int EPI, int NWM, int NWN, int WM, int WN>
 static hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
   using C = TileCfg<NWM, NWN, WM, WN>;
   const int n_big = (p.n_tiles + C::SUB - 1) / C::SUB;
-  const long long grid = static_cast<long long>(p.m_tiles) * n_big * p.splits;
+  long long grid = static_cast<long long>(p.m_tiles) * n_big * p.splits;
   if (p.m_tiles != (a.M + C::BM - 1) / C::BM || grid <= 0 || grid > (1ll << 31) - 1) return hipErrorInvalidValue;
+  if (a.persist != 0) {
+    // persistent LM head: one workgroup per CU (the 8-wavefront tiles hold one), the
+    // same number on every XCD, each with at least two tiles
+    if (EPI != EPI_ARGMAX || p.splits != 1 || C::NW != 8 || a.persist % 8 != 0 || grid < 2ll * a.persist)
+      return hipErrorInvalidValue;
+    grid = a.persist;
+  }
   hipLaunchKernelGGL((gemm_tiled_kernel<EPI, NWM, NWN, WM, WN>), dim3(static_cast<unsigned>(grid)), dim3(C::NT), 0, s, a);
   if (p.splits > 1) {
     if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SAMPLE) {
