@@ -351,25 +351,56 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     DFLASH_FULL(3, fa1, fb1, fa0, fb0)
 #undef DFLASH_FULL
   }
+  // Residual GEMM on 256 x 128 tiles: the epilogue's residual rows (NH 16-byte loads
+  // per thread, in the epilogue's own thread mapping) are loaded before the last four
+  // to seven steps, so their latency hides behind them instead of following the loop.
+  // They are younger than the DMA loads of the stages the first two remaining steps
+  // wait for, so those two waits allow NH more loads in flight.
+  constexpr bool HV_PRE = EPI == EPI_RESID && NWM == 4 && NWN == 2 && WM == 4 && WN == 4;
+  constexpr int RPP_E = NT / 8, IT_E = (BM + RPP_E - 1) / RPP_E;
+  constexpr int NH = HV_PRE ? 2 * SUB * IT_E : 0;
+  static_assert(2 * LPW + NH <= 63, "vmcnt range");
+  float hv_pre[HV_PRE ? SUB : 1][HV_PRE ? IT_E : 1][8];
+  if constexpr (HV_PRE) {
+    const int c8 = tid_t & 7;
+#pragma unroll
+    for (int q = 0; q < SUB; ++q)
+#pragma unroll
+      for (int it = 0; it < IT_E; ++it) {
+        const int m = min(m0 + (tid_t >> 3) + RPP_E * it, M - 1);  // rows past M: a valid row, unused
+        const int n0 = (tn * SUB + q) * kBN + c8 * 8;
+        const float4* hp = reinterpret_cast<const float4*>(g.h + static_cast<size_t>(m) * g.N + (n0 < g.N ? n0 : 0));
+        const float4 h0 = hp[0], h1 = hp[1];
+        hv_pre[q][it][0] = h0.x; hv_pre[q][it][1] = h0.y; hv_pre[q][it][2] = h0.z; hv_pre[q][it][3] = h0.w;
+        hv_pre[q][it][4] = h1.x; hv_pre[q][it][5] = h1.y; hv_pre[q][it][6] = h1.z; hv_pre[q][it][7] = h1.w;
+      }
+  }
+#define DFLASH_STEP(u, fac, fbc, fan, fbn, X)                                     \
+  if (s + u < S) {                                                                \
+    step_work((u + 1) & 3, fac, fbc, fan, fbn, s + u + 4 < S, s + u + 4, u);      \
+    if (s + u + 2 < S) {                                                          \
+      asm volatile("" ::: "memory");                                              \
+      if (s + u + 4 < S) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * LPW + (X)));  \
+      else if (s + u + 3 < S) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(LPW + (X))); \
+      else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(X));                           \
+      __builtin_amdgcn_s_barrier();                                               \
+      asm volatile("" ::: "memory");                                              \
+    }                                                                             \
+  }
+  if (s < S) {
+    DFLASH_STEP(0, fa0, fb0, fa1, fb1, NH)
+    DFLASH_STEP(1, fa1, fb1, fa0, fb0, NH)
+    DFLASH_STEP(2, fa0, fb0, fa1, fb1, 0)
+    DFLASH_STEP(3, fa1, fb1, fa0, fb0, 0)
+    s += 4;
+  }
   for (; s < S; s += 4) {
-#define DFLASH_STEP(u, fac, fbc, fan, fbn)                                    \
-  if (s + u < S) {                                                            \
-    step_work((u + 1) & 3, fac, fbc, fan, fbn, s + u + 4 < S, s + u + 4, u);  \
-    if (s + u + 2 < S) {                                                      \
-      asm volatile("" ::: "memory");                                          \
-      if (s + u + 4 < S) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * LPW));   \
-      else if (s + u + 3 < S) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(LPW));  \
-      else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));                       \
-      __builtin_amdgcn_s_barrier();                                           \
-      asm volatile("" ::: "memory");                                          \
-    }                                                                         \
+    DFLASH_STEP(0, fa0, fb0, fa1, fb1, 0)
+    DFLASH_STEP(1, fa1, fb1, fa0, fb0, 0)
+    DFLASH_STEP(2, fa0, fb0, fa1, fb1, 0)
+    DFLASH_STEP(3, fa1, fb1, fa0, fb0, 0)
   }
-    DFLASH_STEP(0, fa0, fb0, fa1, fb1)
-    DFLASH_STEP(1, fa1, fb1, fa0, fb0)
-    DFLASH_STEP(2, fa0, fb0, fa1, fb1)
-    DFLASH_STEP(3, fa1, fb1, fa0, fb0)
 #undef DFLASH_STEP
-  }
   __syncthreads();  // every wavefront is done with the stage buffers
 
   // persistent LM head: the next tile's first four stages go out now, so their loads
@@ -542,6 +573,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
         const int tile_n = tn * SUB + s0 + q;
         if (s0 + q < SUB && tile_n < g.n_tiles) {
           if (ROWS && g.rope_tab != nullptr) epilogue_tile<bf16, EPI, BM, NT, false, ROWS>(g, tiles[q], rs_s, tile_n, m0, M, nullptr, er);
+          else if constexpr (HV_PRE) epilogue_tile<bf16, EPI, BM, NT>(g, tiles[q], rs_s, tile_n, m0, M, hv_pre[s0 + q]);
           else epilogue_tile<bf16, EPI, BM, NT>(g, tiles[q], rs_s, tile_n, m0, M, nullptr);
         }
       }
