@@ -54,19 +54,28 @@ struct TileCfg {
   static_assert(BFR % 4 == 0, "whole 64-column subtiles");
 };
 
-// Larger (smaller) of a value and the value of the lane the DPP control CTRL selects
-// (a permutation inside each row of 16 lanes).
-template <int CTRL>
-__device__ __forceinline__ float dpp_max_f32(float x) {
-  return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true)));
-}
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_min_u32(uint32_t x) {
-  return min(x, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, true)));
-}
+// The value of the lane the DPP control CTRL selects (a permutation inside each row of
+// 16 lanes).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+// Max (min) over the four lanes l, l^16, l^32, l^48 (gfx950 lane-group swaps: called
+// with the same value as both operands, a swap leaves each lane its own value and its
+// partner's).
+__device__ __forceinline__ float lane_group_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ uint32_t lane_group_min(uint32_t x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const uint32_t y = min(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return min(static_cast<uint32_t>(b[0]), static_cast<uint32_t>(b[1]));
 }
 // The larger of a 64-bit key and the key of the lane CTRL selects.
 template <int CTRL>
@@ -224,6 +233,8 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
       for (int q = q0; q < q1; ++q) {
         const int i = q / WN, j = q % WN;
         if constexpr (EPI == EPI_FUSE) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        else if constexpr (EPI == EPI_ARGMAX)  // transposed: vocabulary x rows (see the argmax epilogue)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
         else acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
       constexpr int nm = q1 - q0, nr = r1 - r0, per = nm / (nr + 1);
@@ -434,60 +445,57 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   }
 
   if constexpr (EPI == EPI_ARGMAX) {
+    // The greedy LM head multiplies W A^T (the operands swapped): lane l, register r of
+    // block (i, j) holds row (wm WM + i) 16 + l % 16 and vocabulary column
+    // (tn BFR + wn WN + j) 16 + 4 (l / 16) + r, so a lane holds 4 WN columns of one row.
+    const int nbase = (tn * BFR + wn * WN) * 16 + 4 * (lane_t >> 4);
     if (g.logits != nullptr) {  // logits out (uniform branch; tests only)
 #pragma unroll
-      for (int i = 0; i < WM; ++i)
+      for (int i = 0; i < WM; ++i) {
+        const int r = (wm * WM + i) * 16 + (lane_t & 15), m = m0 + r;
+        if (m >= M) continue;
+        const size_t mo = g.row_map != nullptr ? g.row_map[m] : m;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = (wm * WM + i) * 16 + 4 * (lane_t >> 4) + rr, m = m0 + r;
-          if (m >= M) continue;
-          const size_t mo = g.row_map != nullptr ? g.row_map[m] : m;
+        for (int j = 0; j < WN; ++j)
 #pragma unroll
-          for (int j = 0; j < WN; ++j) {
-            const int n = (tn * BFR + wn * WN + j) * 16 + (lane_t & 15);
+          for (int rr = 0; rr < 4; ++rr) {
+            const int n = nbase + j * 16 + rr;
             if (n < g.N) g.logits[mo * g.N + n] = acc[i][j][rr] * rs_s[r];
           }
-        }
+      }
     }
-    // split-vocab argmax straight from the accumulators, without branches: per row the
-    // largest scaled logit of the tile's columns (columns past N excluded), across the
-    // 16 lanes that share the row with DPP (xor 1, xor 2, half-row mirror, row mirror),
-    // then the smallest column holding it the same way, then the row's 64-bit key
-    // (order-preserving value bits, ~column) across the NWN column wavefronts through
-    // an LDS max.  Equal values go to the smallest column; NaN logits are never picked.
-    uint32_t ncol[WN];
-#pragma unroll
-    for (int j = 0; j < WN; ++j) ncol[j] = static_cast<uint32_t>((tn * BFR + wn * WN + j) * 16 + (lane_t & 15));
+    // split-vocab argmax straight from the accumulators: per row the largest scaled
+    // logit of the wavefront's columns (columns past N excluded) in-lane, then across
+    // the four lanes l, l^16, l^32, l^48 that share the row (lane-group swaps), then the
+    // smallest column holding it the same way, then the row's 64-bit key (order-
+    // preserving value bits, ~column) across the NWN column wavefronts through an LDS
+    // max.  Equal values go to the smallest column; NaN logits are never picked.
     // FULL: every column of the tile is below N (all tiles but the last), no masks
     auto argmax_rows = [&](auto full) {
       constexpr bool FULL = decltype(full)::value;
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
-        const float4 f4 = *reinterpret_cast<const float4*>(&rs_s[(wm * WM + i) * 16 + 4 * (lane_t >> 4)]);
+        const int r = (wm * WM + i) * 16 + (lane_t & 15);
+        const float f = rs_s[r];
+        float v[WN][4], mx = -INFINITY;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = (wm * WM + i) * 16 + 4 * (lane_t >> 4) + rr;
-          const float f = rr == 0 ? f4.x : (rr == 1 ? f4.y : (rr == 2 ? f4.z : f4.w));
-          float v[WN], mx = -INFINITY;
+        for (int j = 0; j < WN; ++j)
 #pragma unroll
-          for (int j = 0; j < WN; ++j) {
-            v[j] = acc[i][j][rr] * f;
-            mx = fmaxf(mx, FULL || ncol[j] < static_cast<uint32_t>(g.N) ? v[j] : -INFINITY);
+          for (int rr = 0; rr < 4; ++rr) {
+            v[j][rr] = acc[i][j][rr] * f;
+            mx = fmaxf(mx, FULL || nbase + j * 16 + rr < g.N ? v[j][rr] : -INFINITY);
           }
-          mx = dpp_max_f32<0xB1>(mx);   // quad_perm [1,0,3,2]
-          mx = dpp_max_f32<0x4E>(mx);   // quad_perm [2,3,0,1]
-          mx = dpp_max_f32<0x141>(mx);  // row_half_mirror
-          mx = dpp_max_f32<0x140>(mx);  // row_mirror
-          uint32_t col = 0xFFFFFFFFu;
+        mx = lane_group_max(mx);
+        uint32_t col = 0xFFFFFFFFu;
 #pragma unroll
-          for (int j = WN - 1; j >= 0; --j)
-            col = (FULL || ncol[j] < static_cast<uint32_t>(g.N)) && v[j] == mx ? ncol[j] : col;
-          col = dpp_min_u32<0xB1>(col);
-          col = dpp_min_u32<0x4E>(col);
-          col = dpp_min_u32<0x141>(col);
-          col = dpp_min_u32<0x140>(col);
-          if ((lane_t & 15) == 0 && col != 0xFFFFFFFFu) atomicMax(&best_s[r], argmax_key(mx, static_cast<int>(col)));
-        }
+        for (int j = WN - 1; j >= 0; --j)
+#pragma unroll
+          for (int rr = 3; rr >= 0; --rr) {
+            const int n = nbase + j * 16 + rr;
+            col = (FULL || n < g.N) && v[j][rr] == mx ? static_cast<uint32_t>(n) : col;
+          }
+        col = lane_group_min(col);
+        if ((lane_t >> 4) == 0 && col != 0xFFFFFFFFu) atomicMax(&best_s[r], argmax_key(mx, static_cast<int>(col)));
       }
     };
     if ((tn + 1) * C::BN <= g.N) argmax_rows(std::true_type{});
