@@ -34,7 +34,7 @@
 namespace dflash {
 
 template <typename T, int DH, int NW, int KG>
-__global__ __launch_bounds__(64 * NW * KG) __attribute__((amdgpu_waves_per_eu(NW * KG <= 4 ? 4 : 2, 4))) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW * KG) void attention_kernel(AttnArgs a) {
   __shared__ AttnLds<T, DH, NW, KG> lds;
   attention_body<T, DH, NW, KG, false>(a, blockIdx.x, lds);
 }
