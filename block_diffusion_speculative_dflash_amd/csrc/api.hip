@@ -399,9 +399,11 @@ int device_cus(int* cus);
 int run_gemm(int epi, const Ctx& c, GemmArgs a, bool allow_split, hipStream_t s) {
   const GemmPlan p = plan_gemm(epi, c, a, allow_split);
   a.persist = 0;
-  if (p.tiled && epi == EPI_ARGMAX && p.mt != kTile128) {
-    // the tiled LM head walks its tiles with one workgroup per CU once there are at
-    // least two tiles per CU: each tile's first loads overlap the previous epilogue
+  // the tiled greedy LM head, and SwiGLU on 256-row tiles (whose epilogues work from the
+  // accumulators), walk their tiles with one workgroup per CU once there are at least
+  // two tiles per CU: each tile's first loads overlap the previous epilogue
+  if (p.tiled && p.splits == 1 &&
+      (epi == EPI_ARGMAX ? p.mt != kTile128 : (epi == EPI_SWIGLU && (p.mt == kTile256 || p.mt == kTile256x128)))) {
     int cus = 0;
     const long long tiles = static_cast<long long>(p.m_tiles) * ((p.n_tiles * kBN + tile_cols(p.mt) - 1) / tile_cols(p.mt));
     if (device_cus(&cus) == DFLASH_OK && cus % 8 == 0 && tiles >= 2ll * cus) a.persist = cus;

@@ -89,8 +89,9 @@ struct GemmArgs {
   const unsigned long long* step_dev;  // when set, the step is read from here at run time
   float2* lse_part;
   int n_parts;
-  // ARGMAX, tiled: the grid is one workgroup per CU (a multiple of 8), each walking
-  // a stride of its XCD's tiles; 0: one workgroup per tile
+  // tiled greedy LM head or SwiGLU on tiles whose epilogue works from the accumulators:
+  // the grid is one workgroup per CU (a multiple of 8), each walking a stride of its
+  // XCD's tiles; 0: one workgroup per tile
   int persist;
   // compacted rows (tiled GEMMs of a draft step with per-sequence block lengths or
   // of an injection with per-sequence row counts): rows at or beyond *m_live do not

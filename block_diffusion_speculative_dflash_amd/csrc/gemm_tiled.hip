@@ -106,6 +106,13 @@ __device__ __forceinline__ size_t tiled_part_index(int sp, int m_tiles, int n_bi
   return ((((static_cast<size_t>(sp) * tiles_all + tile) * C::NW + w) * C::WM_ + i) * C::WN_ + j) * kWave + l;
 }
 
+// Whether a tiled GEMM computes its tile transposed (see gemm_tiled_kernel): the greedy
+// LM head, and SwiGLU when every wavefront covers whole 64-column subtiles.
+template <int EPI, int WN>
+constexpr bool tiled_trans() {
+  return EPI == EPI_ARGMAX || (EPI == EPI_SWIGLU && WN % 4 == 0);
+}
+
 constexpr int vmcnt_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 // vmcnt <= n and every LDS read of this wavefront complete (lgkmcnt 0)
 constexpr int vm_lgkm_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
@@ -123,6 +130,12 @@ template <int EPI, int NWM, int NWN, int WM, int WN>
 __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(NWM * NWN == 4 ? 2 : 1, 2))) void gemm_tiled_kernel(GemmArgs g) {
   using C = TileCfg<NWM, NWN, WM, WN>;
   constexpr int AFR = C::AFR, BFR = C::BFR, BM = C::BM, SUB = C::SUB, LPW = C::LPW, NW = C::NW, NT = C::NT;
+  // TRANS: the product is computed transposed (W A^T, each MFMA's operands swapped), so
+  // a lane holds 4 consecutive output columns of one row, and the epilogue runs from
+  // the accumulators (the greedy LM head; SwiGLU where every wavefront covers whole
+  // 64-column subtiles).  PERS: such launches may be persistent.
+  constexpr bool TRANS = tiled_trans<EPI, WN>();
+  constexpr bool PERS = TRANS;
   // packed activations; the fusion GEMM reads row-major taps unless they were packed
   const bool APK = EPI != EPI_FUSE || g.a_packed != 0;
   typedef typename std::conditional<EPI == EPI_FUSE, bf16, f16>::type E;
@@ -144,7 +157,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   // on neighbouring tiles at any time.
   const int nwg = gridDim.x, x = blockIdx.x, xcd = x & 7;
   int L, L_end, L_step;
-  if (EPI == EPI_ARGMAX && g.persist != 0) {
+  if (PERS && g.persist != 0) {
     const int T = g.m_tiles * n_big, q = T >> 3, r8 = T & 7;
     L = xcd * q + min(xcd, r8) + (x >> 3);
     L_end = xcd * q + min(xcd, r8) + q + (xcd < r8 ? 1 : 0);
@@ -233,7 +246,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
       for (int q = q0; q < q1; ++q) {
         const int i = q / WN, j = q % WN;
         if constexpr (EPI == EPI_FUSE) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        else if constexpr (EPI == EPI_ARGMAX)  // transposed: vocabulary x rows (see the argmax epilogue)
+        else if constexpr (TRANS)  // columns x rows
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
         else acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   // hoist the epilogue's per-lane row addresses out of a persistent workgroup's tile
   // loop and keep them (spilled) across the main loop
   int lane_t = lane, tid_t = tid;
-  if constexpr (EPI == EPI_ARGMAX) asm volatile("" : "+v"(lane_t), "+v"(tid_t));
+  if constexpr (PERS) asm volatile("" : "+v"(lane_t), "+v"(tid_t));
   const int tm = L % g.m_tiles, rest = L / g.m_tiles;
   const int tn = rest % n_big, split = rest / n_big;
   const int m0 = tm * BM;
@@ -414,10 +427,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #undef DFLASH_STEP
   __syncthreads();  // every wavefront is done with the stage buffers
 
-  // persistent LM head: the next tile's first four stages go out now, so their loads
+  // persistent launch: the next tile's first four stages go out now, so their loads
   // overlap this tile's epilogue (which works from the accumulators, not the LDS)
   int L_next = L_end;
-  if constexpr (EPI == EPI_ARGMAX) {
+  if constexpr (PERS) {
     if (g.persist != 0) {
       L_next = L + L_step;
       while (L_next < L_end && (L_next % g.m_tiles) * BM >= M) L_next += L_step;
@@ -553,6 +566,48 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
         }
       }
     }
+  } else if constexpr (EPI == EPI_SWIGLU && TRANS) {
+    // SwiGLU from the accumulators: wavefront column blocks 4s, 4s + 1 are the gate
+    // columns and 4s + 2, 4s + 3 the up columns of 64-column subtile s (32 FFN
+    // columns); a lane holds 4 consecutive FFN columns of one row and writes them as
+    // one 8-byte piece of the packed down-projection operand.  Columns past ffn are
+    // the down projection's K padding and get zeros.
+    typedef typename ActOf<bf16>::type TA;
+    typedef TA TA4 __attribute__((ext_vector_type(4)));
+    TA* act = static_cast<TA*>(g.out);
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const int r = (wm * WM + i) * 16 + (lane_t & 15), m = m0 + r;
+      const float f = rs_s[r];
+#pragma unroll
+      for (int sj = 0; sj < WN / 4; ++sj)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int tile_n = tn * SUB + (wn * WN) / 4 + sj;  // 64-column subtile
+          const int c0 = tile_n * 32 + h * 16 + 4 * (lane_t >> 4);
+          TA4 y;
+          bool sat = false;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            float v = 0.f;
+            if (c0 + rr < g.ffn) {
+              const float gq = acc[i][4 * sj + h][rr] * f, uq = acc[i][4 * sj + 2 + h][rr] * f;
+              v = gq * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gq * kLog2e)) * uq;
+            }
+            y[rr] = to_act<TA>(v, sat);
+          }
+          // rows past M (compacted away) and subtiles past n_tiles (the last tile of a
+          // ragged N) do not exist: nothing stored, nothing reported
+          if (m < M && tile_n < g.n_tiles) {
+            *reinterpret_cast<TA4*>(act + pa_index(m, c0, g.out_steps)) = y;
+            bad = bad || sat;
+          }
+        }
+    }
+    report_overflow(bad, g.dev_error);
+    // a later tile of a persistent workgroup rewrites rs_s for new rows
+    if (L_next < L_end) __syncthreads();
   } else {
     // The tile goes through the fused epilogue 64 columns at a time, C::PAIR subtiles
     // per round (each in its own LDS tile), the rows' QKV / INJECT targets found once.
@@ -648,12 +703,16 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_reduce_kernel(GemmArgs g)
 #pragma unroll
     for (int q = 0; q < FPW; ++q) sum[q] += v[q];
   }
-  // MFMA layout: lane l, register r holds row 4 * (l / 16) + r, column l % 16
+  // MFMA layout: lane l, register r holds row 4 * (l / 16) + r, column l % 16 (a
+  // transposed product: row l % 16, column 4 * (l / 16) + r)
 #pragma unroll
   for (int q = 0; q < FPW; ++q) {
     const int f = wave * FPW + q, rb = f >> 2, cb = f & 3;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) tile[rb * 16 + 4 * (lane >> 4) + rr][cb * 16 + (lane & 15)] = sum[q][rr];
+    for (int rr = 0; rr < 4; ++rr) {
+      if constexpr (tiled_trans<EPI, WN>()) tile[rb * 16 + (lane & 15)][cb * 16 + 4 * (lane >> 4) + rr] = sum[q][rr];
+      else tile[rb * 16 + 4 * (lane >> 4) + rr][cb * 16 + (lane & 15)] = sum[q][rr];
+    }
   }
   for (int r = tid; r < BM; r += kThreads) {
     float f = 1.f;
@@ -676,9 +735,9 @@ static hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t s
   long long grid = static_cast<long long>(p.m_tiles) * n_big * p.splits;
   if (p.m_tiles != (a.M + C::BM - 1) / C::BM || grid <= 0 || grid > (1ll << 31) - 1) return hipErrorInvalidValue;
   if (a.persist != 0) {
-    // persistent LM head: one workgroup per CU (the 8-wavefront tiles hold one), the
+    // persistent launch: one workgroup per CU (the 8-wavefront tiles hold one), the
     // same number on every XCD, each with at least two tiles
-    if (EPI != EPI_ARGMAX || p.splits != 1 || C::NW != 8 || a.persist % 8 != 0 || grid < 2ll * a.persist)
+    if (!tiled_trans<EPI, WN>() || p.splits != 1 || C::NW != 8 || a.persist % 8 != 0 || grid < 2ll * a.persist)
       return hipErrorInvalidValue;
     grid = a.persist;
   }
