@@ -71,6 +71,14 @@ __device__ __forceinline__ float lane_group_max(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+__device__ __forceinline__ float lane_group_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 __device__ __forceinline__ uint32_t lane_group_min(uint32_t x) {
   const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
   const uint32_t y = min(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
@@ -107,10 +115,12 @@ __device__ __forceinline__ size_t tiled_part_index(int sp, int m_tiles, int n_bi
 }
 
 // Whether a tiled GEMM computes its tile transposed (see gemm_tiled_kernel): the greedy
-// LM head, and SwiGLU when every wavefront covers whole 64-column subtiles.
-template <int EPI, int WN>
+// LM head, SwiGLU when every wavefront covers whole 64-column subtiles, and the
+// residual GEMM on 256 x 128 tiles.
+template <int EPI, int NWM, int NWN, int WM, int WN>
 constexpr bool tiled_trans() {
-  return EPI == EPI_ARGMAX || (EPI == EPI_SWIGLU && WN % 4 == 0);
+  return EPI == EPI_ARGMAX || (EPI == EPI_SWIGLU && WN % 4 == 0) ||
+         (EPI == EPI_RESID && NWM == 4 && NWN == 2 && WM == 4 && WN == 4);
 }
 
 constexpr int vmcnt_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -132,10 +142,10 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   constexpr int AFR = C::AFR, BFR = C::BFR, BM = C::BM, SUB = C::SUB, LPW = C::LPW, NW = C::NW, NT = C::NT;
   // TRANS: the product is computed transposed (W A^T, each MFMA's operands swapped), so
   // a lane holds 4 consecutive output columns of one row, and the epilogue runs from
-  // the accumulators (the greedy LM head; SwiGLU where every wavefront covers whole
-  // 64-column subtiles).  PERS: such launches may be persistent.
-  constexpr bool TRANS = tiled_trans<EPI, WN>();
-  constexpr bool PERS = TRANS;
+  // the accumulators (see tiled_trans).  PERS: such launches may be persistent (not
+  // the residual GEMM: its grids are one tile per CU).
+  constexpr bool TRANS = tiled_trans<EPI, NWM, NWN, WM, WN>();
+  constexpr bool PERS = TRANS && EPI != EPI_RESID;
   // packed activations; the fusion GEMM reads row-major taps unless they were packed
   const bool APK = EPI != EPI_FUSE || g.a_packed != 0;
   typedef typename std::conditional<EPI == EPI_FUSE, bf16, f16>::type E;
@@ -375,29 +385,29 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
     DFLASH_FULL(3, fa1, fb1, fa0, fb0)
 #undef DFLASH_FULL
   }
-  // Residual GEMM on 256 x 128 tiles: the epilogue's residual rows (NH 16-byte loads
-  // per thread, in the epilogue's own thread mapping) are loaded before the last four
-  // to seven steps, so their latency hides behind them instead of following the loop.
-  // They are younger than the DMA loads of the stages the first two remaining steps
-  // wait for, so those two waits allow NH more loads in flight.
-  constexpr bool HV_PRE = EPI == EPI_RESID && NWM == 4 && NWN == 2 && WM == 4 && WN == 4;
-  constexpr int RPP_E = NT / 8, IT_E = (BM + RPP_E - 1) / RPP_E;
-  constexpr int NH = HV_PRE ? 2 * SUB * IT_E : 0;
+  // Residual GEMM on 256 x 128 tiles (computed transposed): the epilogue's residual
+  // values (a 16-byte piece per 16 x 16 block: the lane's row and 4 columns) and the
+  // next RMSNorm's gains of the lane's columns are loaded before the last four to seven
+  // steps, so their latency hides behind them instead of following the loop.  They are
+  // younger than the DMA loads of the stages the first two remaining steps wait for, so
+  // those two waits allow NH more loads in flight.
+  constexpr bool HV_PRE = EPI == EPI_RESID && TRANS;
+  constexpr int NH = HV_PRE ? WM * WN + WN : 0;
   static_assert(2 * LPW + NH <= 63, "vmcnt range");
-  float hv_pre[HV_PRE ? SUB : 1][HV_PRE ? IT_E : 1][8];
+  float4 hv_pre[HV_PRE ? WM : 1][HV_PRE ? WN : 1];
+  uint2 gn_pre[HV_PRE ? WN : 1];  // 4 gains (bf16) of block j's columns
   if constexpr (HV_PRE) {
-    const int c8 = tid_t & 7;
 #pragma unroll
-    for (int q = 0; q < SUB; ++q)
+    for (int j = 0; j < WN; ++j) {
+      const int n0 = (tn * BFR + wn * WN + j) * 16 + 4 * (lane_t >> 4);
+      const int nc = n0 < g.N ? n0 : 0;  // columns past N: a valid piece, unused
+      gn_pre[j] = *reinterpret_cast<const uint2*>(static_cast<const bf16*>(g.gain) + nc);
 #pragma unroll
-      for (int it = 0; it < IT_E; ++it) {
-        const int m = min(m0 + (tid_t >> 3) + RPP_E * it, M - 1);  // rows past M: a valid row, unused
-        const int n0 = (tn * SUB + q) * kBN + c8 * 8;
-        const float4* hp = reinterpret_cast<const float4*>(g.h + static_cast<size_t>(m) * g.N + (n0 < g.N ? n0 : 0));
-        const float4 h0 = hp[0], h1 = hp[1];
-        hv_pre[q][it][0] = h0.x; hv_pre[q][it][1] = h0.y; hv_pre[q][it][2] = h0.z; hv_pre[q][it][3] = h0.w;
-        hv_pre[q][it][4] = h1.x; hv_pre[q][it][5] = h1.y; hv_pre[q][it][6] = h1.z; hv_pre[q][it][7] = h1.w;
+      for (int i = 0; i < WM; ++i) {
+        const int m = min(m0 + (wm * WM + i) * 16 + (lane_t & 15), M - 1);  // rows past M: a valid row, unused
+        hv_pre[i][j] = *reinterpret_cast<const float4*>(g.h + static_cast<size_t>(m) * g.N + nc);
       }
+    }
   }
 #define DFLASH_STEP(u, fac, fbc, fan, fbn, X)                                     \
   if (s + u < S) {                                                                \
@@ -566,6 +576,49 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
         }
       }
     }
+  } else if constexpr (EPI == EPI_RESID && TRANS) {
+    // Residual add from the accumulators: a lane holds 4 consecutive columns of one row
+    // per 16 x 16 block; x = acc * rs + h goes back to the residual stream (16 bytes) and,
+    // times the next RMSNorm's gain, into the packed next operand (8 bytes); the row's
+    // sum of x^2 over each 64-column subtile (its 4 blocks, then the four lanes l, l^16,
+    // l^32, l^48) is that subtile's RMSNorm partial.
+    typedef typename ActOf<bf16>::type TA;
+    typedef TA TA4 __attribute__((ext_vector_type(4)));
+    TA* out = static_cast<TA*>(g.out);
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const int r = (wm * WM + i) * 16 + (lane_t & 15), m = m0 + r;
+      const float f = rs_s[r];
+      const bool row_ok = m < M;
+#pragma unroll
+      for (int sj = 0; sj < WN / 4; ++sj) {
+        const int tile_n = tn * SUB + (wn * WN) / 4 + sj;  // 64-column subtile
+        float ss = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 4 * sj + jj;
+          const int n0 = (tn * BFR + wn * WN + j) * 16 + 4 * (lane_t >> 4);
+          const float4 hv = hv_pre[i][j];
+          const float x[4] = {acc[i][j][0] * f + hv.x, acc[i][j][1] * f + hv.y, acc[i][j][2] * f + hv.z,
+                              acc[i][j][3] * f + hv.w};
+          const bf16* gq = reinterpret_cast<const bf16*>(&gn_pre[j]);
+          TA4 y;
+          bool sat = false;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) y[k] = to_act<TA>(x[k] * to_f32(gq[k]), sat);
+          if (row_ok && n0 < g.N) {
+            *reinterpret_cast<TA4*>(out + pa_index(m, n0, g.out_steps)) = y;
+            *reinterpret_cast<float4*>(g.h + static_cast<size_t>(m) * g.N + n0) = make_float4(x[0], x[1], x[2], x[3]);
+            ss += (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]);
+            bad = bad || sat;
+          }
+        }
+        ss = lane_group_sum(ss);
+        if ((lane_t >> 4) == 0 && row_ok && tile_n < g.n_tiles) g.ssq_out[static_cast<size_t>(m) * g.np_out + tile_n] = ss;
+      }
+    }
+    report_overflow(bad, g.dev_error);
   } else if constexpr (EPI == EPI_SWIGLU && TRANS) {
     // SwiGLU from the accumulators: wavefront column blocks 4s, 4s + 1 are the gate
     // columns and 4s + 2, 4s + 3 the up columns of 64-column subtile s (32 FFN
@@ -636,7 +689,6 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
         const int tile_n = tn * SUB + s0 + q;
         if (s0 + q < SUB && tile_n < g.n_tiles) {
           if (ROWS && g.rope_tab != nullptr) epilogue_tile<bf16, EPI, BM, NT, false, ROWS>(g, tiles[q], rs_s, tile_n, m0, M, nullptr, er);
-          else if constexpr (HV_PRE) epilogue_tile<bf16, EPI, BM, NT>(g, tiles[q], rs_s, tile_n, m0, M, hv_pre[s0 + q]);
           else epilogue_tile<bf16, EPI, BM, NT>(g, tiles[q], rs_s, tile_n, m0, M, nullptr);
         }
       }
@@ -710,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_reduce_kernel(GemmArgs g)
     const int f = wave * FPW + q, rb = f >> 2, cb = f & 3;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      if constexpr (tiled_trans<EPI, WN>()) tile[rb * 16 + (lane & 15)][cb * 16 + 4 * (lane >> 4) + rr] = sum[q][rr];
+      if constexpr (tiled_trans<EPI, NWM, NWN, WM, WN>()) tile[rb * 16 + (lane & 15)][cb * 16 + 4 * (lane >> 4) + rr] = sum[q][rr];
       else tile[rb * 16 + 4 * (lane >> 4) + rr][cb * 16 + (lane & 15)] = sum[q][rr];
     }
   }
@@ -737,7 +789,8 @@ static hipError_t launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t s
   if (a.persist != 0) {
     // persistent launch: one workgroup per CU (the 8-wavefront tiles hold one), the
     // same number on every XCD, each with at least two tiles
-    if (!tiled_trans<EPI, WN>() || p.splits != 1 || C::NW != 8 || a.persist % 8 != 0 || grid < 2ll * a.persist)
+    if (!tiled_trans<EPI, NWM, NWN, WM, WN>() || EPI == EPI_RESID || p.splits != 1 || C::NW != 8 ||
+        a.persist % 8 != 0 || grid < 2ll * a.persist)
       return hipErrorInvalidValue;
     grid = a.persist;
   }
