@@ -3,7 +3,8 @@
 // Once the draft batch has hundreds of rows the projections are compute-bound, and a
 // kernel that streams W once per 64-row block (the weight-streaming GEMM) would read
 // every weight matrix M/64 times.  Here one workgroup owns a BM x BN output tile
-// (256 x 256 with 8 wavefronts, or 128 x 128 with 4) and walks K in 32-wide steps:
+// (256 x 256, 128 x 384 or 256 x 128 with 8 wavefronts, 128 x 128 with 4) and walks K
+// in 32-wide steps:
 //
 //  * Both operands are fragment-packed (weights by dflash_pack_weights, activations
 //    by the producing epilogue), so one K step of a 16-row (or 16-column) block is
@@ -20,12 +21,17 @@
 //    wait-count pass does not drain it before every LDS read; the kernel waits with
 //    explicit vmcnt counts instead (every wavefront issues the same number of DMA
 //    loads per stage; rows/columns past the end re-load a valid chunk).
-//  * K may be split over workgroups (fp32 partial tiles, last arriver reduces in
-//    split order); the output tile then goes through LDS 64 columns at a time into
-//    the same fused epilogues as the weight-streaming GEMM.
+//  * The output tile goes through LDS 64 columns at a time into the same fused
+//    epilogues as the weight-streaming GEMM, or (greedy LM head, SwiGLU on 256 x 256
+//    tiles, residual on 256 x 128) the product is computed transposed and the
+//    epilogue works from the accumulators: a lane holds 4 consecutive columns of one
+//    row.  K may be split over workgroups: fp32 partial tiles in the accumulators'
+//    layout, summed in split order by gemm_tiled_reduce_kernel, which runs the epilogue.
 //  * Workgroup x runs on XCD x mod 8; tiles are renumbered so each XCD works on a
 //    contiguous run of tiles, m fastest, so the workgroups that share a weight tile
-//    share that XCD's L2.
+//    share that XCD's L2.  The LM head and those SwiGLU launches may be persistent:
+//    one workgroup per CU walks a stride of its XCD's tiles and issues the next
+//    tile's first loads before the current tile's epilogue.
 #include <type_traits>
 
 #include "common.h"

@@ -139,3 +139,20 @@ def test_fullsize_compacted_blocks(name):
     pre = np.minimum(ctx, w.prefill)
     run = ParityRun(d, W, ctx, synth.make_anchors(d), pre, sample=sample, seed=0)
     run_steps(f"compacted {name}", run, a_tab, 2, block_lens=lens)
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_split_transposed_tiles():
+    """The MiMo-shaped SWA drafter at batch 32 (256 block rows): the tile planner takes
+    256 x 128 tiles for the projections and splits O and down 8 ways, so their
+    transposed residual products go through the split-K reduction; SwiGLU runs
+    transposed (unsplit) and the LM head persistent on the same tile shape."""
+    w = replace(configs.C3, dims=replace(configs.C3.dims, batch=32))
+    d = w.dims
+    ctx = synth.make_context_lengths(w, seed=0)
+    sample = [0, 11, 22, 31]
+    say(f"[fullsize] split tiles: B={d.batch} k={d.block_k} L={d.n_layers} V={d.vocab} sample={sample}")
+    W = synth.make_weights(d, seed=0, device="cuda")
+    pre = np.minimum(ctx, w.prefill)
+    run = ParityRun(d, W, ctx, synth.make_anchors(d), pre, sample=sample, seed=0)
+    run_steps("split tiles", run, planted_schedule(w, 4), 2)
