@@ -100,7 +100,7 @@ class HipEvents:
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs the DFlash step on one GPU only (the data-parallel "
+        print(json.dumps({"error": "this library runs the DFlash step on one GPU only (the data-parallel "
                           "shard of one GPU is the whole measurement); run with --gpus 1",
                           "n_gpus": args.gpus}), flush=True)
         return 2

@@ -64,7 +64,7 @@ extern "C" {
 typedef enum {
   DFLASH_OK = 0,
   DFLASH_E_INVALID = -1,     /* bad dims, NULL or misaligned pointer, bad argument */
-  DFLASH_E_UNSUPPORTED = -2, /* valid but not handled by this build (e.g. head_dim) */
+  DFLASH_E_UNSUPPORTED = -2, /* valid but not handled by this library (e.g. head_dim) */
   DFLASH_E_WORKSPACE = -3,   /* workspace NULL or smaller than dflash_workspace_bytes */
   DFLASH_E_HIP = -4,         /* a HIP runtime call or kernel launch failed */
   DFLASH_E_TOO_LARGE = -5    /* dflash_draft_step_noalloc: the dims need more than its scratch */
