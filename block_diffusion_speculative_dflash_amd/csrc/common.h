@@ -39,14 +39,13 @@ constexpr long long kSpinLimit = 1ll << 22;
 // finite value beyond the largest finite fp16 (65504) saturates to +-65504 instead
 // of becoming an infinity, and a value that is not finite passes through; both set
 // `bad`, which the caller reports as kErrOverflow.  fp32 values pass unchanged.
+// Selects, not branches: an epilogue converts dozens of values per lane.
 template <typename T> __device__ __forceinline__ T to_act(float x, bool& bad);
 template <> __device__ __forceinline__ float to_act<float>(float x, bool&) { return x; }
 template <> __device__ __forceinline__ f16 to_act<f16>(float x, bool& bad) {
-  if (!(fabsf(x) <= 65504.f)) {
-    bad = true;
-    if (fabsf(x) > 65504.f) x = copysignf(65504.f, x);  // NaN stays NaN
-  }
-  return static_cast<f16>(x);
+  const float a = fabsf(x);
+  bad = bad || !(a <= 65504.f);
+  return static_cast<f16>(a > 65504.f ? copysignf(65504.f, x) : x);  // NaN stays NaN
 }
 __device__ __forceinline__ void report_overflow(bool bad, uint32_t* dev_error) {
   if (bad && dev_error != nullptr) atomicOr(dev_error, kErrOverflow);

@@ -649,12 +649,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
           bool sat = false;
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            float v = 0.f;
-            if (c0 + rr < g.ffn) {
-              const float gq = acc[i][4 * sj + h][rr] * f, uq = acc[i][4 * sj + 2 + h][rr] * f;
-              v = gq * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gq * kLog2e)) * uq;
-            }
-            y[rr] = to_act<TA>(v, sat);
+            const float gq = acc[i][4 * sj + h][rr] * f, uq = acc[i][4 * sj + 2 + h][rr] * f;
+            const float v = gq * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gq * kLog2e)) * uq;
+            y[rr] = to_act<TA>(c0 + rr < g.ffn ? v : 0.f, sat);
           }
           // rows past M (compacted away) and subtiles past n_tiles (the last tile of a
           // ragged N) do not exist: nothing stored, nothing reported
