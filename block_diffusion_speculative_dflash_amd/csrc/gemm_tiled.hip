@@ -377,6 +377,18 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
   for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // persistent launch: the workgroup's next tile, and whether its first three stages
+  // are issued during this tile's last K steps (XT: whole groups of four steps, at
+  // least two of them, so the tail is exactly the last four steps and issues no stage
+  // of this tile)
+  int L_next = L_end;
+  if constexpr (PERS) {
+    if (g.persist != 0) {
+      L_next = L + L_step;
+      while (L_next < L_end && (L_next % g.m_tiles) * BM >= M) L_next += L_step;
+    }
+  }
+  const bool XT = PERS && L_next < L_end && (S & 3) == 0 && S >= 8;
   int s = 0;
   for (; s + 8 <= S; s += 4) {
 #define DFLASH_FULL(u, fac, fbc, fan, fbn)                                    \
@@ -415,17 +427,25 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
       }
     }
   }
-#define DFLASH_STEP(u, fac, fbc, fan, fbn, X)                                     \
-  if (s + u < S) {                                                                \
-    step_work((u + 1) & 3, fac, fbc, fan, fbn, s + u + 4 < S, s + u + 4, u);      \
-    if (s + u + 2 < S) {                                                          \
-      asm volatile("" ::: "memory");                                              \
-      if (s + u + 4 < S) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * LPW + (X)));  \
-      else if (s + u + 3 < S) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(LPW + (X))); \
-      else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(X));                           \
-      __builtin_amdgcn_s_barrier();                                               \
-      asm volatile("" ::: "memory");                                              \
-    }                                                                             \
+  // XT: from here on the DMA sources are the next tile's; its stage v (v < 3) goes into
+  // buffer v at step S - 4 + v, whose stage was read during the previous step, before
+  // that step's barrier (stage 3 waits for the barrier after the loop: the step before
+  // S - 1 ends without one).  The waits of steps S - 4 and S - 3 then have two stages'
+  // loads younger than the one they wait for, as in the main loop.
+  if (XT) set_src(L_next % g.m_tiles, L_next / g.m_tiles, 0);
+#define DFLASH_STEP(u, fac, fbc, fan, fbn, X)                                                       \
+  if (s + u < S) {                                                                                  \
+    const bool cur_ = s + u + 4 < S;                                                                \
+    step_work((u + 1) & 3, fac, fbc, fan, fbn, cur_ || (XT && s + u + 4 - S < 3),                   \
+              cur_ ? s + u + 4 : s + u + 4 - S, u);                                                 \
+    if (s + u + 2 < S) {                                                                            \
+      asm volatile("" ::: "memory");                                                                \
+      if (cur_ || XT) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * LPW + (X)));                      \
+      else if (s + u + 3 < S) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(LPW + (X)));                  \
+      else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(X));                                             \
+      __builtin_amdgcn_s_barrier();                                                                 \
+      asm volatile("" ::: "memory");                                                                \
+    }                                                                                               \
   }
   if (s < S) {
     DFLASH_STEP(0, fa0, fb0, fa1, fb1, NH)
@@ -443,14 +463,14 @@ __global__ __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(
 #undef DFLASH_STEP
   __syncthreads();  // every wavefront is done with the stage buffers
 
-  // persistent launch: the next tile's first four stages go out now, so their loads
-  // overlap this tile's epilogue (which works from the accumulators, not the LDS)
-  int L_next = L_end;
+  // persistent launch: the next tile's first four stages are in flight from here on,
+  // so their loads overlap this tile's epilogue (which works from the accumulators, not
+  // the LDS)
   if constexpr (PERS) {
-    if (g.persist != 0) {
-      L_next = L + L_step;
-      while (L_next < L_end && (L_next % g.m_tiles) * BM >= M) L_next += L_step;
-      if (L_next < L_end) {
+    if (L_next < L_end) {
+      if (XT) {
+        issue(3, 3);
+      } else {
         set_src(L_next % g.m_tiles, L_next / g.m_tiles, 0);
         issue_prologue(g.S);
       }
