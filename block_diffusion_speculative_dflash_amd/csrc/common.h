@@ -147,14 +147,63 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// (value, index) max with ties to the smaller index
+// The value of the lane the DPP control CTRL selects (a permutation inside each row of
+// 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, true));
+}
+// Max (min, sum) over the four lanes l, l^16, l^32, l^48 (gfx950 lane-group swaps:
+// called with the same value as both operands, a swap leaves each lane its own value
+// and its partner's).
+__device__ __forceinline__ float lane_group_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lane_group_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ uint32_t lane_group_min(uint32_t x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const uint32_t y = min(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return min(static_cast<uint32_t>(b[0]), static_cast<uint32_t>(b[1]));
+}
+
+// (value, index) max over the wavefront, ties to the smaller index; every lane gets
+// it.  The max by DPP inside each row of 16 lanes (quad permutations xor 1 and xor 2,
+// half-row mirror, row mirror) and the lane-group swaps across the four rows, then the
+// smallest index among the lanes holding it the same way: no LDS round trips.  A NaN
+// value is never picked (it counts as -inf).  Indices are non-negative.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, kWave);
-    const int oi = __shfl_xor(i, o, kWave);
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
-  }
+  const float x = v != v ? -INFINITY : v;
+  float m = x;
+  m = fmaxf(m, dpp_f32<0xB1>(m));
+  m = fmaxf(m, dpp_f32<0x4E>(m));
+  m = fmaxf(m, dpp_f32<0x141>(m));
+  m = fmaxf(m, dpp_f32<0x140>(m));
+  m = lane_group_max(m);
+  uint32_t c = x == m ? static_cast<uint32_t>(i) : 0xFFFFFFFFu;
+  c = min(c, dpp_u32<0xB1>(c));
+  c = min(c, dpp_u32<0x4E>(c));
+  c = min(c, dpp_u32<0x141>(c));
+  c = min(c, dpp_u32<0x140>(c));
+  c = lane_group_min(c);
+  v = m;
+  i = static_cast<int>(c);
 }
 
 // Order-preserving map of a float onto uint32 (larger float -> larger integer).

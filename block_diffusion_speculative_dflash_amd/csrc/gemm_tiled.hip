@@ -60,37 +60,6 @@ struct TileCfg {
   static_assert(BFR % 4 == 0, "whole 64-column subtiles");
 };
 
-// The value of the lane the DPP control CTRL selects (a permutation inside each row of
-// 16 lanes).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-// Max (min) over the four lanes l, l^16, l^32, l^48 (gfx950 lane-group swaps: called
-// with the same value as both operands, a swap leaves each lane its own value and its
-// partner's).
-__device__ __forceinline__ float lane_group_max(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const unsigned w = __float_as_uint(y);
-  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float lane_group_sum(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const unsigned w = __float_as_uint(y);
-  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-__device__ __forceinline__ uint32_t lane_group_min(uint32_t x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  const uint32_t y = min(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
-  return min(static_cast<uint32_t>(b[0]), static_cast<uint32_t>(b[1]));
-}
 // The larger of a 64-bit key and the key of the lane CTRL selects.
 template <int CTRL>
 __device__ __forceinline__ unsigned long long dpp_max_key(unsigned long long k) {
