@@ -156,3 +156,21 @@ def test_fullsize_split_transposed_tiles():
     pre = np.minimum(ctx, w.prefill)
     run = ParityRun(d, W, ctx, synth.make_anchors(d), pre, sample=sample, seed=0)
     run_steps("split tiles", run, planted_schedule(w, 4), 2)
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_persistent_tiles_k_steps_not_multiple_of_four():
+    """The same drafter with hidden 4032: the projections that read the hidden state
+    take 126 K steps, not a whole number of groups of four, so the persistent LM head
+    and SwiGLU issue each next tile's first stages after the K loop rather than during
+    its last steps; O, down and the fusion GEMM end in a half-filled 128-column tile
+    (63 column tiles), and the RMSNorm partial sums (63 per row) take the scalar sum."""
+    w = replace(configs.C3, dims=replace(configs.C3.dims, batch=32, hidden=4032))
+    d = w.dims
+    ctx = synth.make_context_lengths(w, seed=1)
+    sample = [3, 16, 29]
+    say(f"[fullsize] hidden 4032: B={d.batch} k={d.block_k} L={d.n_layers} V={d.vocab} sample={sample}")
+    W = synth.make_weights(d, seed=1, device="cuda")
+    pre = np.minimum(ctx, w.prefill)
+    run = ParityRun(d, W, ctx, synth.make_anchors(d), pre, sample=sample, seed=1)
+    run_steps("hidden 4032", run, planted_schedule(w, 4), 2)
